@@ -1,0 +1,191 @@
+/*
+ * iabn.h -- C ABI of the MI355X (gfx950) In-Place Activated BatchNorm library.
+ *
+ * The method: "In-Place Activated BatchNorm for Memory-Optimized Training of DNNs"
+ * (Rota Bulo, Porzi, Kontschieder), as summarised on the paperlayer page of arXiv
+ * 1712.02616v3.  Section 3 ("In-Place Activated Batch Normalization") fuses batch
+ * normalisation with an invertible activation into one layer that keeps a single
+ * buffer: the forward writes y over x, and the backward rebuilds everything it
+ * needs from y by inverting the activation and the scale-and-shift.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors hold N*C*H*W elements of the storage dtype, contiguous, in layout
+ *     NCHW (element (n,c,h,w) at ((n*C + c)*H + h)*W + w) or NHWC (at
+ *     ((n*H + h)*W + w)*C + c).  Device pointers.  Element pointers must be
+ *     aligned to their element size; 16-byte alignment (and H*W, resp. C, a
+ *     multiple of 16/element-size) enables the 128-bit vector path, anything
+ *     else takes the scalar path with identical results.
+ *   - Per-channel vectors (gamma, beta, statistics, gradients) are fp32 device
+ *     arrays of length C, for both storage dtypes.  Arithmetic is fp32, with the
+ *     per-channel finishing steps in fp64.
+ *   - m = N*H*W is the reduction length of one channel.
+ *   - The caller owns every buffer, including the workspace.  The library never
+ *     allocates, frees or synchronises; it is stateless and reentrant.  Calls
+ *     are enqueued on `stream` and return once launched.  The status reports
+ *     argument validation (done before any HIP call) and launch errors; faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Results are bitwise deterministic for a given shape, layout, dtype and
+ *     pointer alignment: no floating-point atomics, fixed reduction orders.
+ *   - Preconditions that are not checked: gamma_c != 0 in the backward (the
+ *     affine step must be invertible), finite inputs (NaN propagates), and no
+ *     overlap between buffers other than the aliasing each call allows.
+ */
+#ifndef IABN_H
+#define IABN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum iabn_status {
+    IABN_OK = 0,
+    IABN_ERR_INVALID_ARG = 1,   /* a size, enum, scalar or pointer is not acceptable  */
+    IABN_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement        */
+    IABN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than iabn_workspace_size */
+    IABN_ERR_MISALIGNED = 4,    /* a pointer is not aligned to its element size       */
+    IABN_ERR_HIP = 5            /* the HIP runtime reported an error at launch        */
+} iabn_status;
+
+typedef enum iabn_layout { IABN_NCHW = 0, IABN_NHWC = 1 } iabn_layout;
+
+/* storage dtype of x / y / dy / dx */
+typedef enum iabn_dtype { IABN_F32 = 0, IABN_BF16 = 1 } iabn_dtype;
+
+/* Invertible activations (section 3, "INPLACE-ABN"; section 4, "Experimental
+ * setup" uses leaky ReLU with slope 0.01).  act_param is the leaky slope
+ * (must be > 0) or the ELU alpha (must be > 0); identity ignores it.
+ *   leaky ReLU: y = z > 0 ? z : a*z        ELU: y = z > 0 ? z : alpha*(exp(z)-1) */
+typedef enum iabn_act {
+    IABN_ACT_IDENTITY = 0,
+    IABN_ACT_LEAKY_RELU = 1,
+    IABN_ACT_ELU = 2
+} iabn_act;
+
+/* Human-readable name of a status code (static storage). */
+const char *iabn_status_string(iabn_status status);
+
+/* Library ABI version: major*10000 + minor*100 + patch. */
+int iabn_version(void);
+
+/* Bytes of device workspace that iabn_forward_train, iabn_forward_stats,
+ * iabn_backward and iabn_backward_reduce need for this shape (0 for an empty
+ * problem).  Depends only on the arguments, never on the device.  One buffer
+ * serves forward and backward of the same shape.  Returns 0 for invalid
+ * arguments too. */
+size_t iabn_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W,
+                           iabn_layout layout, iabn_dtype dtype);
+
+/* Training forward, in place (section 3, "Batch Normalization Review" and
+ * "INPLACE-ABN"; the single stored buffer of section 1):
+ *   mu_c, var_c = empirical mean and biased variance of channel c over its m
+ *   elements; invstd_c = 1/sqrt(var_c + eps);
+ *   y = act(gamma_c * (x - mu_c) * invstd_c + beta_c), written over x.
+ *   x_inout      in: x, out: y (same buffer, storage dtype, `layout`)
+ *   gamma, beta  in: fp32 [C]
+ *   running_mean, running_var  in/out fp32 [C], both or neither may be NULL:
+ *                new = (1 - momentum)*old + momentum*batch, where the batch
+ *                variance is the unbiased var_c*m/(m-1)
+ *   save_mean, save_invstd     out fp32 [C]: mu_c and invstd_c
+ *   eps >= 0, 0 <= momentum <= 1; training needs m >= 2.  C == 0 is a no-op.
+ *   workspace    device, >= iabn_workspace_size bytes, 16-byte aligned; its
+ *                contents on entry do not matter.
+ * Equivalent to iabn_forward_stats followed by iabn_forward_apply. */
+iabn_status iabn_forward_train(void *x_inout,
+                               int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype,
+                               const float *gamma, const float *beta,
+                               float *running_mean, float *running_var,
+                               float *save_mean, float *save_invstd,
+                               iabn_act act, float act_param, float eps, float momentum,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* First stage of iabn_forward_train: reads x, computes the statistics, writes
+ * save_mean / save_invstd, updates the running statistics, and leaves the
+ * per-channel affine constants in the workspace for iabn_forward_apply.  x is
+ * not modified.  Arguments as for iabn_forward_train. */
+iabn_status iabn_forward_stats(const void *x,
+                               int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype,
+                               const float *gamma, const float *beta,
+                               float *running_mean, float *running_var,
+                               float *save_mean, float *save_invstd,
+                               float eps, float momentum,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Second stage of iabn_forward_train: y = act(...) written over x, from the
+ * constants iabn_forward_stats left in the same workspace, on the same stream,
+ * for the same x, shape, layout and dtype. */
+iabn_status iabn_forward_apply(void *x_inout,
+                               int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype,
+                               iabn_act act, float act_param,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Inference forward, in place, with the running statistics:
+ *   y = act(gamma_c * (x - running_mean_c) / sqrt(running_var_c + eps) + beta_c)
+ * written over x.  All per-channel inputs are fp32 [C] and required.  Needs no
+ * workspace.  An empty tensor (any extent 0) is a no-op. */
+iabn_status iabn_forward_eval(void *x_inout,
+                              int64_t N, int64_t C, int64_t H, int64_t W,
+                              iabn_layout layout, iabn_dtype dtype,
+                              const float *gamma, const float *beta,
+                              const float *running_mean, const float *running_var,
+                              iabn_act act, float act_param, float eps,
+                              hipStream_t stream);
+
+/* Training backward from the stored output alone (section 3, "INPLACE-ABN" I
+ * and II; Appendix, "Derivation of Gradient"):
+ *   z = act^-1(y), dz = act'(z)*dy (both from y), xhat = (z - beta_c)/gamma_c,
+ *   dbeta_c = sum dz, dgamma_c = sum dz*xhat,
+ *   dx = gamma_c*invstd_c*(dz - dbeta_c/m - xhat*dgamma_c/m).
+ *   y, dy        in, storage dtype, `layout`; y is never modified
+ *   dx           out, storage dtype; may be exactly dy (in place), must not
+ *                overlap y, and must not partly overlap dy
+ *   gamma, beta  in fp32 [C], the values the forward used (gamma_c != 0)
+ *   save_invstd  in fp32 [C], from the forward
+ *   dgamma, dbeta out fp32 [C]
+ *   Needs m >= 2.  C == 0 is a no-op.  Workspace as for the forward.
+ * The ELU inverse clamps y/alpha to at least -1 + 2^-24, which only rounding of
+ * the stored y can reach.  Equivalent to iabn_backward_reduce followed by
+ * iabn_backward_apply. */
+iabn_status iabn_backward(const void *y, const void *dy, void *dx,
+                          int64_t N, int64_t C, int64_t H, int64_t W,
+                          iabn_layout layout, iabn_dtype dtype,
+                          const float *gamma, const float *beta, const float *save_invstd,
+                          float *dgamma, float *dbeta,
+                          iabn_act act, float act_param,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* First stage of iabn_backward: the per-channel sums, dgamma and dbeta, and the
+ * per-channel coefficients of dx left in the workspace. */
+iabn_status iabn_backward_reduce(const void *y, const void *dy,
+                                 int64_t N, int64_t C, int64_t H, int64_t W,
+                                 iabn_layout layout, iabn_dtype dtype,
+                                 const float *gamma, const float *beta, const float *save_invstd,
+                                 float *dgamma, float *dbeta,
+                                 iabn_act act, float act_param,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Second stage of iabn_backward: dx from y, dy and the coefficients that
+ * iabn_backward_reduce left in the same workspace (same stream, shapes, act). */
+iabn_status iabn_backward_apply(const void *y, const void *dy, void *dx,
+                                int64_t N, int64_t C, int64_t H, int64_t W,
+                                iabn_layout layout, iabn_dtype dtype,
+                                iabn_act act, float act_param,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IABN_H */

@@ -1,0 +1,296 @@
+// C ABI of the In-Place ABN library: argument validation (before any HIP call),
+// plan selection, and launches on the caller's stream.  Declared in iabn.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "iabn.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+using namespace iabn;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool finite_pos(float v) { return v > 0.f && isfinite(v); }
+
+iabn_status check_shape(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
+                        iabn_dtype dtype)
+{
+    if (layout != IABN_NCHW && layout != IABN_NHWC) return IABN_ERR_INVALID_ARG;
+    if (dtype != IABN_F32 && dtype != IABN_BF16) return IABN_ERR_INVALID_ARG;
+    if (N < 0 || C < 0 || H < 0 || W < 0) return IABN_ERR_INVALID_ARG;
+    // keep every index product well inside int64 and every grid inside 2^31 workgroups
+    const double numel = double(N) * double(C) * double(H) * double(W);
+    if (numel > 9.0e15) return IABN_ERR_UNSUPPORTED;
+    return IABN_OK;
+}
+
+iabn_status check_act(iabn_act act, float a)
+{
+    switch (act) {
+    case IABN_ACT_IDENTITY: return IABN_OK;
+    case IABN_ACT_LEAKY_RELU:
+    case IABN_ACT_ELU: return finite_pos(a) ? IABN_OK : IABN_ERR_INVALID_ARG;
+    default: return IABN_ERR_INVALID_ARG;
+    }
+}
+
+iabn_status check_channel_vec(const float* p, bool required)
+{
+    if (!p) return required ? IABN_ERR_INVALID_ARG : IABN_OK;
+    return aligned(p, 4) ? IABN_OK : IABN_ERR_MISALIGNED;
+}
+
+iabn_status check_tensor(const void* p, iabn_dtype dtype)
+{
+    if (!p) return IABN_ERR_INVALID_ARG;
+    return aligned(p, dtype == IABN_F32 ? 4 : 2) ? IABN_OK : IABN_ERR_MISALIGNED;
+}
+
+Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
+              bool ptrs16)
+{
+    const bool vec = ptrs16 && vec_shape_ok(C, H * W, layout, dtype);
+    return make_plan(N, C, H, W, layout, dtype, vec);
+}
+
+size_t workspace_bytes_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
+                           iabn_dtype dtype)
+{
+    const size_t a = make_plan(N, C, H, W, layout, dtype, false).bytes;
+    if (!vec_shape_ok(C, H * W, layout, dtype)) return a;
+    const size_t b = make_plan(N, C, H, W, layout, dtype, true).bytes;
+    return a > b ? a : b;
+}
+
+iabn_status check_workspace(const void* ws, size_t bytes, const Plan& pl)
+{
+    if (pl.bytes == 0) return IABN_OK;
+    if (!ws || bytes < pl.bytes) return IABN_ERR_WORKSPACE;
+    return aligned(ws, 16) ? IABN_OK : IABN_ERR_MISALIGNED;
+}
+
+iabn_status launched()
+{
+    return hipGetLastError() == hipSuccess ? IABN_OK : IABN_ERR_HIP;
+}
+
+bool overlap(const void* a, const void* b, size_t bytes)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
+#define IABN_TRY(expr)                          \
+    do {                                        \
+        const iabn_status st_ = (expr);         \
+        if (st_ != IABN_OK) return st_;         \
+    } while (0)
+
+// Validation shared by iabn_forward_train and iabn_forward_stats.
+iabn_status check_forward_train(const void* x, int64_t N, int64_t C, int64_t H, int64_t W,
+                                iabn_layout layout, iabn_dtype dtype, const float* gamma,
+                                const float* beta, float* rm, float* rv, float* save_mean,
+                                float* save_invstd, float eps, float momentum)
+{
+    IABN_TRY(check_shape(N, C, H, W, layout, dtype));
+    if (!(eps >= 0.f) || !isfinite(eps)) return IABN_ERR_INVALID_ARG;
+    if (!(momentum >= 0.f && momentum <= 1.f)) return IABN_ERR_INVALID_ARG;
+    if ((rm == nullptr) != (rv == nullptr)) return IABN_ERR_INVALID_ARG;
+    if (C == 0) return IABN_OK;
+    if (N * H * W < 2) return IABN_ERR_INVALID_ARG;
+    IABN_TRY(check_tensor(x, dtype));
+    IABN_TRY(check_channel_vec(gamma, true));
+    IABN_TRY(check_channel_vec(beta, true));
+    IABN_TRY(check_channel_vec(rm, false));
+    IABN_TRY(check_channel_vec(rv, false));
+    IABN_TRY(check_channel_vec(save_mean, true));
+    IABN_TRY(check_channel_vec(save_invstd, true));
+    return IABN_OK;
+}
+
+iabn_status check_backward(const void* y, const void* dy, const void* dx, int64_t N, int64_t C,
+                           int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
+                           iabn_act act, float a)
+{
+    IABN_TRY(check_shape(N, C, H, W, layout, dtype));
+    IABN_TRY(check_act(act, a));
+    if (C == 0) return IABN_OK;
+    if (N * H * W < 2) return IABN_ERR_INVALID_ARG;
+    IABN_TRY(check_tensor(y, dtype));
+    IABN_TRY(check_tensor(dy, dtype));
+    IABN_TRY(check_tensor(dx, dtype));
+    const size_t bytes = size_t(N * C * H * W) * (dtype == IABN_F32 ? 4 : 2);
+    if (overlap(dx, y, bytes)) return IABN_ERR_INVALID_ARG;
+    if (dx != dy && overlap(dx, dy, bytes)) return IABN_ERR_INVALID_ARG;
+    return IABN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* iabn_status_string(iabn_status status)
+{
+    switch (status) {
+    case IABN_OK: return "ok";
+    case IABN_ERR_INVALID_ARG: return "invalid argument";
+    case IABN_ERR_UNSUPPORTED: return "unsupported";
+    case IABN_ERR_WORKSPACE: return "workspace missing or too small";
+    case IABN_ERR_MISALIGNED: return "misaligned pointer";
+    case IABN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int iabn_version(void) { return 100; }
+
+size_t iabn_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
+                           iabn_dtype dtype)
+{
+    if (check_shape(N, C, H, W, layout, dtype) != IABN_OK) return 0;
+    if (N * C * H * W == 0) return 0;
+    return workspace_bytes_for(N, C, H, W, layout, dtype);
+}
+
+iabn_status iabn_forward_stats(const void* x, int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype, const float* gamma,
+                               const float* beta, float* running_mean, float* running_var,
+                               float* save_mean, float* save_invstd, float eps, float momentum,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    IABN_TRY(check_forward_train(x, N, C, H, W, layout, dtype, gamma, beta, running_mean,
+                                 running_var, save_mean, save_invstd, eps, momentum));
+    if (C == 0) return IABN_OK;
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(x, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
+    launch_forward_stats(pl, x, gamma, beta, running_mean, running_var, save_mean, save_invstd,
+                         eps, momentum, workspace, stream);
+    return launched();
+}
+
+iabn_status iabn_forward_apply(void* x_inout, int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype, iabn_act act,
+                               float act_param, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    IABN_TRY(check_shape(N, C, H, W, layout, dtype));
+    IABN_TRY(check_act(act, act_param));
+    if (C == 0) return IABN_OK;
+    if (N * H * W < 2) return IABN_ERR_INVALID_ARG;
+    IABN_TRY(check_tensor(x_inout, dtype));
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(x_inout, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
+    launch_forward_apply(pl, x_inout, act, act_param, workspace, stream);
+    return launched();
+}
+
+iabn_status iabn_forward_train(void* x_inout, int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype, const float* gamma,
+                               const float* beta, float* running_mean, float* running_var,
+                               float* save_mean, float* save_invstd, iabn_act act,
+                               float act_param, float eps, float momentum, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    IABN_TRY(check_act(act, act_param));
+    IABN_TRY(check_forward_train(x_inout, N, C, H, W, layout, dtype, gamma, beta, running_mean,
+                                 running_var, save_mean, save_invstd, eps, momentum));
+    if (C == 0) return IABN_OK;
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(x_inout, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
+    launch_forward_stats(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
+                         save_invstd, eps, momentum, workspace, stream);
+    launch_forward_apply(pl, x_inout, act, act_param, workspace, stream);
+    return launched();
+}
+
+iabn_status iabn_forward_eval(void* x_inout, int64_t N, int64_t C, int64_t H, int64_t W,
+                              iabn_layout layout, iabn_dtype dtype, const float* gamma,
+                              const float* beta, const float* running_mean,
+                              const float* running_var, iabn_act act, float act_param, float eps,
+                              hipStream_t stream)
+{
+    IABN_TRY(check_shape(N, C, H, W, layout, dtype));
+    IABN_TRY(check_act(act, act_param));
+    if (!(eps >= 0.f) || !isfinite(eps)) return IABN_ERR_INVALID_ARG;
+    if (N * C * H * W == 0) return IABN_OK;
+    IABN_TRY(check_tensor(x_inout, dtype));
+    IABN_TRY(check_channel_vec(gamma, true));
+    IABN_TRY(check_channel_vec(beta, true));
+    IABN_TRY(check_channel_vec(running_mean, true));
+    IABN_TRY(check_channel_vec(running_var, true));
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(x_inout, 16));
+    launch_forward_eval(pl, x_inout, gamma, beta, running_mean, running_var, eps, act, act_param,
+                        stream);
+    return launched();
+}
+
+iabn_status iabn_backward_reduce(const void* y, const void* dy, int64_t N, int64_t C, int64_t H,
+                                 int64_t W, iabn_layout layout, iabn_dtype dtype,
+                                 const float* gamma, const float* beta, const float* save_invstd,
+                                 float* dgamma, float* dbeta, iabn_act act, float act_param,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    // dx plays no part in the reduction; dy stands in for it in the shared checks
+    IABN_TRY(check_shape(N, C, H, W, layout, dtype));
+    IABN_TRY(check_act(act, act_param));
+    if (C == 0) return IABN_OK;
+    if (N * H * W < 2) return IABN_ERR_INVALID_ARG;
+    IABN_TRY(check_tensor(y, dtype));
+    IABN_TRY(check_tensor(dy, dtype));
+    IABN_TRY(check_channel_vec(gamma, true));
+    IABN_TRY(check_channel_vec(beta, true));
+    IABN_TRY(check_channel_vec(save_invstd, true));
+    IABN_TRY(check_channel_vec(dgamma, true));
+    IABN_TRY(check_channel_vec(dbeta, true));
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(y, 16) && aligned(dy, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
+    launch_backward_reduce(pl, y, dy, gamma, beta, save_invstd, dgamma, dbeta, act, act_param,
+                           workspace, stream);
+    return launched();
+}
+
+iabn_status iabn_backward_apply(const void* y, const void* dy, void* dx, int64_t N, int64_t C,
+                                int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
+                                iabn_act act, float act_param, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    IABN_TRY(check_backward(y, dy, dx, N, C, H, W, layout, dtype, act, act_param));
+    if (C == 0) return IABN_OK;
+    const Plan pl = plan_for(N, C, H, W, layout, dtype,
+                             aligned(y, 16) && aligned(dy, 16) && aligned(dx, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
+    launch_backward_apply(pl, y, dy, dx, act, act_param, workspace, stream);
+    return launched();
+}
+
+iabn_status iabn_backward(const void* y, const void* dy, void* dx, int64_t N, int64_t C,
+                          int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
+                          const float* gamma, const float* beta, const float* save_invstd,
+                          float* dgamma, float* dbeta, iabn_act act, float act_param,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    IABN_TRY(check_backward(y, dy, dx, N, C, H, W, layout, dtype, act, act_param));
+    if (C == 0) return IABN_OK;
+    IABN_TRY(check_channel_vec(gamma, true));
+    IABN_TRY(check_channel_vec(beta, true));
+    IABN_TRY(check_channel_vec(save_invstd, true));
+    IABN_TRY(check_channel_vec(dgamma, true));
+    IABN_TRY(check_channel_vec(dbeta, true));
+    const Plan pr = plan_for(N, C, H, W, layout, dtype, aligned(y, 16) && aligned(dy, 16));
+    const Plan pa = plan_for(N, C, H, W, layout, dtype,
+                             aligned(y, 16) && aligned(dy, 16) && aligned(dx, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pr));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pa));
+    launch_backward_reduce(pr, y, dy, gamma, beta, save_invstd, dgamma, dbeta, act, act_param,
+                           workspace, stream);
+    launch_backward_apply(pa, y, dy, dx, act, act_param, workspace, stream);
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,397 @@
+// Backward kernels of In-Place Activated BatchNorm: everything from the stored
+// output y (section 3 of the paperlayer summary of "In-Place Activated BatchNorm
+// for Memory-Optimized Training of DNNs", "INPLACE-ABN" I and II, and the
+// Appendix on rebuilding the discarded buffers during the backward pass).
+//
+// Per element, in registers: z = act^-1(y), dz = act'(z)*dy (both read off y),
+// and t = z - beta_c, so that xhat = t/gamma_c.
+//
+// Three launches:
+//   bwd_reduce_*  one workgroup per (channel tile, partial): sums of dz and dz*t
+//   bwd_finalize  one wave per channel, fixed-order fp64 sums of the partials:
+//                 dbeta = sum dz, dgamma = (sum dz*t)/gamma, and the constants
+//                 {A = gamma*invstd, B = -A*dgamma/(m*gamma), Cc = -A*dbeta/m, beta}
+//   bwd_apply     dx = A*dz + B*(z - beta) + Cc
+//                    = gamma*invstd*(dz - dbeta/m - xhat*dgamma/m)
+// The affine recovery is thus folded into O(1) per-channel constants (form II),
+// while the reductions keep the centred t = z - beta of form I so that a large
+// |beta/gamma| does not cancel.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace iabn {
+
+constexpr int kUnrollB = 4;
+
+template <int ACT, int V>
+__device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy)[V],
+                                           const float (&beta)[V], float a, float inv_a,
+                                           float (&sdz)[V], float (&sdzt)[V])
+{
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float z, slope;
+        act_invert<ACT>(y[e], a, inv_a, z, slope);
+        const float dz = slope * dy[e];
+        sdz[e] += dz;
+        sdzt[e] = fmaf(dz, z - beta[e], sdzt[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NCHW: workgroup b covers channel c = b / P, partial p = b % P.
+template <int DT, int V, int ACT>
+__global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
+    const void* __restrict__ y, const void* __restrict__ dy, int64_t C, int64_t HW, int64_t m,
+    int64_t unit, int64_t P, const float* __restrict__ beta, float a, float inv_a,
+    float* __restrict__ part_dz, float* __restrict__ part_dzt)
+{
+    const int64_t b = blockIdx.x;
+    const int64_t c = b / P;
+    const int64_t p = b - c * P;
+    const int64_t HWv = HW / V;
+    const int64_t j1 = dmin(p * unit + unit, m) / V;
+    int64_t j = p * unit / V + threadIdx.x;
+
+    float bc[V], sdz[V], sdzt[V];
+    const float bb = beta[c];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { bc[e] = bb; sdz[e] = 0.f; sdzt[e] = 0.f; }
+
+    ChannelWalk w;
+    w.init(j < j1 ? j : 0, c, C, HWv, kThreads);
+    for (; j + (kUnrollB - 1) * kThreads < j1; j += kUnrollB * kThreads) {
+        float vy[kUnrollB][V], vd[kUnrollB][V];
+#pragma unroll
+        for (int u = 0; u < kUnrollB; ++u) {
+            load_elems<DT, V>(y, w.addr * V, vy[u]);
+            load_elems<DT, V>(dy, w.addr * V, vd[u]);
+            w.step();
+        }
+#pragma unroll
+        for (int u = 0; u < kUnrollB; ++u) accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
+    }
+    for (; j < j1; j += kThreads) {
+        float vy[V], vd[V];
+        load_elems<DT, V>(y, w.addr * V, vy);
+        load_elems<DT, V>(dy, w.addr * V, vd);
+        w.step();
+        accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+    }
+    float S1 = 0.f, S2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) { S1 += sdz[e]; S2 += sdzt[e]; }
+    S1 = wave_sum(S1);
+    S2 = wave_sum(S2);
+    __shared__ float sh[2][kThreads / kWave];
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) { sh[0][wave] = S1; sh[1][wave] = S2; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t1 = sh[0][0], t2 = sh[1][0];
+#pragma unroll
+        for (int k = 1; k < kThreads / kWave; ++k) { t1 += sh[0][k]; t2 += sh[1][k]; }
+        part_dz[c * P + p] = t1;
+        part_dzt[c * P + p] = t2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NHWC: workgroup b covers channel slice b % slices and partial b / slices.
+template <int DT, int V, int ACT>
+__global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
+    const void* __restrict__ y, const void* __restrict__ dy, int64_t m, int64_t Cv, int tpr,
+    int64_t slices, int64_t unit, int64_t P, const float* __restrict__ beta, float a,
+    float inv_a, float* __restrict__ part_dz, float* __restrict__ part_dzt)
+{
+    const int64_t b = blockIdx.x;
+    const int64_t p = b / slices;
+    const int64_t sl = b - p * slices;
+    const int t = threadIdx.x;
+    const int rs = t / tpr;
+    const int rpi = kThreads / tpr;
+    const int64_t col = sl * tpr + (t - rs * tpr);
+    const bool active = col < Cv;
+    const int64_t r1 = dmin(p * unit + unit, m);
+    int64_t r = p * unit + rs;
+
+    float bc[V], sdz[V], sdzt[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { bc[e] = 0.f; sdz[e] = 0.f; sdzt[e] = 0.f; }
+    if (active) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) bc[e] = beta[col * V + e];
+        for (; r + (kUnrollB - 1) * rpi < r1; r += kUnrollB * rpi) {
+            float vy[kUnrollB][V], vd[kUnrollB][V];
+#pragma unroll
+            for (int u = 0; u < kUnrollB; ++u) {
+                const int64_t i = ((r + u * rpi) * Cv + col) * V;
+                load_elems<DT, V>(y, i, vy[u]);
+                load_elems<DT, V>(dy, i, vd[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnrollB; ++u) accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
+        }
+        for (; r < r1; r += rpi) {
+            float vy[V], vd[V];
+            const int64_t i = (r * Cv + col) * V;
+            load_elems<DT, V>(y, i, vy);
+            load_elems<DT, V>(dy, i, vd);
+            accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+        }
+    }
+    __shared__ float sh_a[V][kThreads];
+    __shared__ float sh_b[V][kThreads];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { sh_a[e][t] = sdz[e]; sh_b[e][t] = sdzt[e]; }
+    for (int s = rpi / 2; s >= 1; s >>= 1) {
+        __syncthreads();
+        if (rs < s) {
+            const int o = t + s * tpr;
+#pragma unroll
+            for (int e = 0; e < V; ++e) { sdz[e] += sh_a[e][o]; sdzt[e] += sh_b[e][o]; }
+        }
+        __syncthreads();
+        if (rs < s) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) { sh_a[e][t] = sdz[e]; sh_b[e][t] = sdzt[e]; }
+        }
+    }
+    if (rs == 0 && active) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const int64_t ch = col * V + e;
+            part_dz[ch * P + p] = sdz[e];
+            part_dzt[ch * P + p] = sdzt[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per channel: fixed-order fp64 sums of the P partials.
+__global__ __launch_bounds__(kThreads) void k_bwd_finalize(
+    int64_t C, int64_t m, int64_t P, const float* __restrict__ part_dz,
+    const float* __restrict__ part_dzt, const float* __restrict__ gamma,
+    const float* __restrict__ beta, const float* __restrict__ invstd,
+    float* __restrict__ dgamma, float* __restrict__ dbeta, float4* __restrict__ consts)
+{
+    const int64_t c = int64_t(blockIdx.x) * kFinalizePerBlock + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (c >= C) return;
+    double s1 = 0.0, s2 = 0.0;
+    for (int64_t p = lane; p < P; p += kWave) {
+        s1 += double(part_dz[c * P + p]);
+        s2 += double(part_dzt[c * P + p]);
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if (lane == 0) {
+        const double g = double(gamma[c]);
+        const double db = s1;
+        const double dg = s2 / g;
+        dbeta[c] = float(db);
+        dgamma[c] = float(dg);
+        const double A = g * double(invstd[c]);
+        const double md = double(m);
+        consts[c] = make_float4(float(A), float(-A * dg / (md * g)), float(-A * db / md), beta[c]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dx = A*dz + B*(z - beta) + Cc.  dx may be the same buffer as dy: each element
+// of dy is read by the thread that then writes the same element of dx.
+template <int ACT, int V>
+__device__ __forceinline__ void dx_one(const float (&vy)[V], float (&vd)[V], const float4 (&k)[V],
+                                       float a, float inv_a)
+{
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float z, slope;
+        act_invert<ACT>(vy[e], a, inv_a, z, slope);
+        const float dz = slope * vd[e];
+        vd[e] = fmaf(k[e].x, dz, fmaf(k[e].y, z - k[e].w, k[e].z));
+    }
+}
+
+template <int DT, int V, int ACT>
+__global__ __launch_bounds__(kThreads) void k_bwd_apply_nchw(
+    const void* __restrict__ y, const void* dy, void* dx, int64_t nvec, int64_t C, int64_t HWv,
+    const float4* __restrict__ consts, float a, float inv_a)
+{
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    FlatNCHWWalk w;
+    w.init(v < nvec ? v : 0, C, HWv, stride);
+    for (; v + (kUnrollB - 1) * stride < nvec; v += kUnrollB * stride) {
+        float vy[kUnrollB][V], vd[kUnrollB][V];
+        float4 k[kUnrollB][V];
+#pragma unroll
+        for (int u = 0; u < kUnrollB; ++u) {
+            load_elems<DT, V>(y, (v + u * stride) * V, vy[u]);
+            load_elems<DT, V>(dy, (v + u * stride) * V, vd[u]);
+            const float4 kc = consts[w.c];
+#pragma unroll
+            for (int e = 0; e < V; ++e) k[u][e] = kc;
+            w.step();
+        }
+#pragma unroll
+        for (int u = 0; u < kUnrollB; ++u) {
+            dx_one<ACT, V>(vy[u], vd[u], k[u], a, inv_a);
+            store_elems<DT, V>(dx, (v + u * stride) * V, vd[u]);
+        }
+    }
+    for (; v < nvec; v += stride) {
+        float vy[V], vd[V];
+        float4 k[V];
+        load_elems<DT, V>(y, v * V, vy);
+        load_elems<DT, V>(dy, v * V, vd);
+        const float4 kc = consts[w.c];
+#pragma unroll
+        for (int e = 0; e < V; ++e) k[e] = kc;
+        w.step();
+        dx_one<ACT, V>(vy, vd, k, a, inv_a);
+        store_elems<DT, V>(dx, v * V, vd);
+    }
+}
+
+template <int DT, int V, int ACT, bool FIXED>
+__global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
+    const void* __restrict__ y, const void* dy, void* dx, int64_t nvec, int64_t Cv,
+    const float4* __restrict__ consts, float a, float inv_a)
+{
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if constexpr (FIXED) {
+        if (v >= nvec) return;
+        const int64_t c0 = (v % Cv) * V;
+        float4 k[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) k[e] = consts[c0 + e];
+        for (; v + (kUnrollB - 1) * stride < nvec; v += kUnrollB * stride) {
+            float vy[kUnrollB][V], vd[kUnrollB][V];
+#pragma unroll
+            for (int u = 0; u < kUnrollB; ++u) {
+                load_elems<DT, V>(y, (v + u * stride) * V, vy[u]);
+                load_elems<DT, V>(dy, (v + u * stride) * V, vd[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnrollB; ++u) {
+                dx_one<ACT, V>(vy[u], vd[u], k, a, inv_a);
+                store_elems<DT, V>(dx, (v + u * stride) * V, vd[u]);
+            }
+        }
+        for (; v < nvec; v += stride) {
+            float vy[V], vd[V];
+            load_elems<DT, V>(y, v * V, vy);
+            load_elems<DT, V>(dy, v * V, vd);
+            dx_one<ACT, V>(vy, vd, k, a, inv_a);
+            store_elems<DT, V>(dx, v * V, vd);
+        }
+    } else {
+        for (; v < nvec; v += stride) {
+            const int64_t c0 = (v % Cv) * V;
+            float vy[V], vd[V];
+            float4 k[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) k[e] = consts[c0 + e];
+            load_elems<DT, V>(y, v * V, vy);
+            load_elems<DT, V>(dy, v * V, vd);
+            dx_one<ACT, V>(vy, vd, k, a, inv_a);
+            store_elems<DT, V>(dx, v * V, vd);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+
+template <int DT, int V, int ACT>
+static void launch_reduce_dva(const Plan& pl, const void* y, const void* dy, const float* beta,
+                              float a, float ia, float* pa, float* pb, hipStream_t s)
+{
+    if (pl.layout == kNCHW)
+        hipLaunchKernelGGL((k_bwd_reduce_nchw<DT, V, ACT>), dim3(pl.reduce_blocks), dim3(kThreads),
+                           0, s, y, dy, pl.C, pl.HW, pl.m, pl.unit, pl.P, beta, a, ia, pa, pb);
+    else
+        hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT>), dim3(pl.reduce_blocks), dim3(kThreads),
+                           0, s, y, dy, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit, pl.P, beta, a,
+                           ia, pa, pb);
+}
+
+template <int DT, int V>
+static void launch_reduce_dv(const Plan& pl, const void* y, const void* dy, const float* beta,
+                             int act, float a, float ia, float* pa, float* pb, hipStream_t s)
+{
+    switch (act) {
+    case kLeaky: launch_reduce_dva<DT, V, kLeaky>(pl, y, dy, beta, a, ia, pa, pb, s); break;
+    case kElu: launch_reduce_dva<DT, V, kElu>(pl, y, dy, beta, a, ia, pa, pb, s); break;
+    default: launch_reduce_dva<DT, V, kIdentity>(pl, y, dy, beta, a, ia, pa, pb, s); break;
+    }
+}
+
+void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const float* gamma,
+                            const float* beta, const float* invstd, float* dgamma, float* dbeta,
+                            int act, float a, void* ws, hipStream_t s)
+{
+    char* wsb = static_cast<char*>(ws);
+    float* pa = reinterpret_cast<float*>(wsb + pl.off_part_a);
+    float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
+    float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
+    const float ia = act == kIdentity ? 1.f : 1.f / a;
+    if (pl.dtype == kF32) {
+        if (pl.vec) launch_reduce_dv<kF32, 4>(pl, y, dy, beta, act, a, ia, pa, pb, s);
+        else launch_reduce_dv<kF32, 1>(pl, y, dy, beta, act, a, ia, pa, pb, s);
+    } else {
+        if (pl.vec) launch_reduce_dv<kBF16, 8>(pl, y, dy, beta, act, a, ia, pa, pb, s);
+        else launch_reduce_dv<kBF16, 1>(pl, y, dy, beta, act, a, ia, pa, pb, s);
+    }
+    hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinalizePerBlock))),
+                       dim3(kThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta, invstd,
+                       dgamma, dbeta, consts);
+}
+
+template <int DT, int V, int ACT>
+static void launch_bapply_dva(const Plan& pl, const void* y, const void* dy, void* dx,
+                              const float4* k, float a, float ia, hipStream_t s)
+{
+    const int64_t nvec = pl.numel / V;
+    const dim3 grid(unsigned(pl.apply_blocks));
+    if (pl.layout == kNCHW)
+        hipLaunchKernelGGL((k_bwd_apply_nchw<DT, V, ACT>), grid, dim3(kThreads), 0, s, y, dy, dx,
+                           nvec, pl.C, pl.HW / V, k, a, ia);
+    else if (pl.fixed_col)
+        hipLaunchKernelGGL((k_bwd_apply_nhwc<DT, V, ACT, true>), grid, dim3(kThreads), 0, s, y, dy,
+                           dx, nvec, pl.C / V, k, a, ia);
+    else
+        hipLaunchKernelGGL((k_bwd_apply_nhwc<DT, V, ACT, false>), grid, dim3(kThreads), 0, s, y,
+                           dy, dx, nvec, pl.C / V, k, a, ia);
+}
+
+template <int DT, int V>
+static void launch_bapply_dv(const Plan& pl, const void* y, const void* dy, void* dx,
+                             const float4* k, int act, float a, float ia, hipStream_t s)
+{
+    switch (act) {
+    case kLeaky: launch_bapply_dva<DT, V, kLeaky>(pl, y, dy, dx, k, a, ia, s); break;
+    case kElu: launch_bapply_dva<DT, V, kElu>(pl, y, dy, dx, k, a, ia, s); break;
+    default: launch_bapply_dva<DT, V, kIdentity>(pl, y, dy, dx, k, a, ia, s); break;
+    }
+}
+
+void launch_backward_apply(const Plan& pl, const void* y, const void* dy, void* dx, int act,
+                           float a, void* ws, hipStream_t s)
+{
+    const float4* k = reinterpret_cast<const float4*>(static_cast<char*>(ws) + pl.off_const);
+    const float ia = act == kIdentity ? 1.f : 1.f / a;
+    if (pl.dtype == kF32) {
+        if (pl.vec) launch_bapply_dv<kF32, 4>(pl, y, dy, dx, k, act, a, ia, s);
+        else launch_bapply_dv<kF32, 1>(pl, y, dy, dx, k, act, a, ia, s);
+    } else {
+        if (pl.vec) launch_bapply_dv<kBF16, 8>(pl, y, dy, dx, k, act, a, ia, s);
+        else launch_bapply_dv<kBF16, 1>(pl, y, dy, dx, k, act, a, ia, s);
+    }
+}
+
+}  // namespace iabn

@@ -1,0 +1,210 @@
+// Device helpers for the In-Place ABN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace iabn {
+
+__device__ __forceinline__ int64_t dmin(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// ---------------------------------------------------------------------------
+// storage access: V consecutive elements <-> V floats.
+// fp32: V = 4 (one 128-bit access) or 1.  bf16: V = 8 (one 128-bit access) or 1.
+
+template <int DT, int V>
+__device__ __forceinline__ void load_elems(const void* base, int64_t i, float (&v)[V])
+{
+    if constexpr (DT == kF32) {
+        const float* p = static_cast<const float*>(base) + i;
+        if constexpr (V == 4) {
+            const float4 q = *reinterpret_cast<const float4*>(p);
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else {
+            static_assert(V == 1, "fp32 access width");
+            v[0] = *p;
+        }
+    } else {
+        const uint16_t* p = static_cast<const uint16_t*>(base) + i;
+        if constexpr (V == 8) {
+            const uint4 q = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = __uint_as_float(w[k] << 16);
+                v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+            }
+        } else {
+            static_assert(V == 1, "bf16 access width");
+            v[0] = __uint_as_float(uint32_t(*p) << 16);
+        }
+    }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const bf16x2_t t = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, t);
+}
+
+template <int DT, int V>
+__device__ __forceinline__ void store_elems(void* base, int64_t i, const float (&v)[V])
+{
+    if constexpr (DT == kF32) {
+        float* p = static_cast<float*>(base) + i;
+        if constexpr (V == 4) {
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+            *p = v[0];
+        }
+    } else {
+        uint16_t* p = static_cast<uint16_t*>(base) + i;
+        if constexpr (V == 8) {
+            uint4 q;
+            q.x = pack_bf16x2(v[0], v[1]);
+            q.y = pack_bf16x2(v[2], v[3]);
+            q.z = pack_bf16x2(v[4], v[5]);
+            q.w = pack_bf16x2(v[6], v[7]);
+            *reinterpret_cast<uint4*>(p) = q;
+        } else {
+            *p = __builtin_bit_cast(uint16_t, (__bf16)v[0]);
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* base, int64_t i)
+{
+    float v[1];
+    load_elems<DT, 1>(base, i, v);
+    return v[0];
+}
+
+// ---------------------------------------------------------------------------
+// invertible activations.  Forward branches on z > 0; the backward reads the
+// branch off the stored y (y > 0), which agrees with z > 0 for every slope > 0.
+
+template <int ACT>
+__device__ __forceinline__ float act_forward(float z, float a)
+{
+    if constexpr (ACT == kLeaky) return z > 0.f ? z : a * z;
+    else if constexpr (ACT == kElu) return z > 0.f ? z : a * expm1f(z);
+    else return z;
+}
+
+// From a stored y: the pre-activation z = act^-1(y) and the slope act'(z).
+// ELU: act'(z) = alpha*exp(z) = y + alpha; the inverse clamps y/alpha at -1 + 2^-24.
+template <int ACT>
+__device__ __forceinline__ void act_invert(float y, float a, float inv_a, float& z, float& slope)
+{
+    if constexpr (ACT == kLeaky) {
+        const bool pos = y > 0.f;
+        z = pos ? y : y * inv_a;
+        slope = pos ? 1.f : a;
+    } else if constexpr (ACT == kElu) {
+        const bool pos = y > 0.f;
+        const float u = fmaxf(y * inv_a, -1.f + 0x1p-24f);
+        z = pos ? y : log1pf(u);
+        slope = pos ? 1.f : y + a;
+    } else {
+        z = y;
+        slope = 1.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chan et al. pairwise update of (count, mean, M2): merge b into a.
+template <typename F>
+__device__ __forceinline__ void chan_merge(F& n, F& mean, F& m2, F nb, F mb, F m2b)
+{
+    if (nb > F(0)) {
+        const F nn = n + nb;
+        const F f = nb / nn;
+        const F d = mb - mean;
+        mean = mean + d * f;
+        m2 = m2 + m2b + d * d * n * f;
+        n = nn;
+    }
+}
+
+// lane 0 of the wave ends with the Chan merge of all 64 lanes, in a fixed order
+template <typename F>
+__device__ __forceinline__ void wave_chan(F& n, F& mean, F& m2)
+{
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+        const F nb = __shfl_xor(n, off, kWave);
+        const F mb = __shfl_xor(mean, off, kWave);
+        const F m2b = __shfl_xor(m2, off, kWave);
+        chan_merge(n, mean, m2, nb, mb, m2b);
+    }
+}
+
+template <typename F>
+__device__ __forceinline__ F wave_sum(F v)
+{
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Walk of an NCHW channel: channel-local vector index j = n*HWv + o maps to the
+// global vector address (n*C + c)*HWv + o.  Advancing j by a fixed stride needs
+// no division: o += r, n += q with a carry.
+struct ChannelWalk {
+    int64_t addr;      // global vector address of the current position
+    int64_t o;         // offset inside the plane (vectors)
+    int64_t hwv;       // vectors per plane
+    int64_t d_addr;    // address step without carry: q*C*HWv + r
+    int64_t d_carry;   // extra step on carry: C*HWv - HWv
+    int64_t r;
+
+    __host__ __device__ __forceinline__ void init(int64_t j, int64_t c, int64_t C, int64_t HWv, int64_t stride)
+    {
+        const int64_t n = j / HWv;
+        o = j - n * HWv;
+        hwv = HWv;
+        addr = (n * C + c) * HWv + o;
+        const int64_t q = stride / HWv;
+        r = stride - q * HWv;
+        d_addr = q * C * HWv + r;
+        d_carry = C * HWv - HWv;
+    }
+    __host__ __device__ __forceinline__ void step()
+    {
+        o += r;
+        addr += d_addr;
+        if (o >= hwv) { o -= hwv; addr += d_carry; }
+    }
+};
+
+// Walk of a flat NCHW tensor: vector v has channel ((v / HWv) % C).  Advancing v
+// by a fixed stride updates the in-plane offset and the channel with carries.
+struct FlatNCHWWalk {
+    int64_t o, c, hwv, C, r, qc;
+    __host__ __device__ __forceinline__ void init(int64_t v, int64_t C_, int64_t HWv, int64_t stride)
+    {
+        hwv = HWv; C = C_;
+        const int64_t plane = v / HWv;
+        o = v - plane * HWv;
+        c = plane % C;
+        const int64_t q = stride / HWv;
+        r = stride - q * HWv;
+        qc = q % C;
+    }
+    __host__ __device__ __forceinline__ void step()
+    {
+        o += r;
+        c += qc;
+        if (o >= hwv) { o -= hwv; c += 1; }
+        if (c >= C) c -= C;
+    }
+};
+
+}  // namespace iabn

@@ -1,0 +1,443 @@
+// Forward kernels of In-Place Activated BatchNorm (training and inference).
+//
+// Training forward (section 3 of the paperlayer summary of "In-Place Activated
+// BatchNorm for Memory-Optimized Training of DNNs", "Batch Normalization Review"
+// and "INPLACE-ABN"): per-channel empirical mean and biased variance over the
+// m = N*H*W elements, then y = act(gamma*xhat + beta) written over x, so that
+// the layer keeps a single buffer.
+//
+// Three launches:
+//   stats_*      one workgroup per (channel tile, partial); streams x once and
+//                writes (mean, M2) of its elements, shifted by a pivot K_c
+//   fwd_finalize one wave per channel; fixed-order Chan merge of the partials in
+//                fp64; statistics, running statistics, and the constants
+//                {K_c, d_c = mean_c - K_c, s_c = gamma_c*invstd_c, beta_c}
+//   fwd_apply    elementwise y = act(((x - K_c) - d_c)*s_c + beta_c), in place
+//
+// The pivot K_c is the channel's first element (n = 0, h = 0, w = 0).  x - K_c
+// is exact in fp32 whenever x is within a factor two of K_c, so the centred value
+// keeps full precision even when |mean| >> std: the mean is only ever handled as
+// the small offset d_c, never as an fp32 number of its own.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace iabn {
+
+constexpr int kUnroll = 4;
+
+// ---------------------------------------------------------------------------
+// NCHW statistics: workgroup b covers channel c = b / P, partial p = b % P, i.e.
+// the channel-local elements [p*unit, min((p+1)*unit, m)).
+template <int DT, int V>
+__global__ __launch_bounds__(kThreads) void k_stats_nchw(
+    const void* __restrict__ x, int64_t C, int64_t HW, int64_t m, int64_t unit, int64_t P,
+    float* __restrict__ part_mean, float* __restrict__ part_m2)
+{
+    const int64_t b = blockIdx.x;
+    const int64_t c = b / P;
+    const int64_t p = b - c * P;
+    const int64_t HWv = HW / V;
+    const int64_t j1 = dmin(p * unit + unit, m) / V;
+    int64_t j = p * unit / V + threadIdx.x;
+
+    const float K = load_one<DT>(x, c * HW);
+    float s1[V], s2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { s1[e] = 0.f; s2[e] = 0.f; }
+    int cnt = 0;
+
+    ChannelWalk w;
+    w.init(j < j1 ? j : 0, c, C, HWv, kThreads);
+    // main loop: kUnroll vectors in flight per thread
+    for (; j + (kUnroll - 1) * kThreads < j1; j += kUnroll * kThreads) {
+        float v[kUnroll][V];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            load_elems<DT, V>(x, w.addr * V, v[u]);
+            w.step();
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = v[u][e] - K;
+                s1[e] += d;
+                s2[e] = fmaf(d, d, s2[e]);
+            }
+        cnt += kUnroll;
+    }
+    for (; j < j1; j += kThreads) {
+        float v[V];
+        load_elems<DT, V>(x, w.addr * V, v);
+        w.step();
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float d = v[e] - K;
+            s1[e] += d;
+            s2[e] = fmaf(d, d, s2[e]);
+        }
+        cnt += 1;
+    }
+
+    float S1 = 0.f, S2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) { S1 += s1[e]; S2 += s2[e]; }
+    float n = float(cnt * V);
+    float mean = cnt ? S1 / n : 0.f;
+    float m2 = cnt ? fmaxf(S2 - S1 * mean, 0.f) : 0.f;
+    wave_chan(n, mean, m2);
+
+    __shared__ float sh[3][kThreads / kWave];
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        sh[0][wave] = n; sh[1][wave] = mean; sh[2][wave] = m2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float tn = sh[0][0], tm = sh[1][0], t2 = sh[2][0];
+#pragma unroll
+        for (int k = 1; k < kThreads / kWave; ++k) chan_merge(tn, tm, t2, sh[0][k], sh[1][k], sh[2][k]);
+        part_mean[c * P + p] = tm;
+        part_m2[c * P + p] = t2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NHWC statistics: workgroup b covers channel slice sl = b % slices (tpr vectors
+// of V channels) and partial p = b / slices, i.e. rows [p*unit, min((p+1)*unit, m)).
+// Thread t owns channel vector col = sl*tpr + t % tpr and walks rows t / tpr,
+// t / tpr + 256/tpr, ...; the row slots are then merged by an LDS tree.
+template <int DT, int V>
+__global__ __launch_bounds__(kThreads) void k_stats_nhwc(
+    const void* __restrict__ x, int64_t m, int64_t Cv, int tpr, int64_t slices, int64_t unit,
+    int64_t P, float* __restrict__ part_mean, float* __restrict__ part_m2)
+{
+    const int64_t b = blockIdx.x;
+    const int64_t p = b / slices;
+    const int64_t sl = b - p * slices;
+    const int t = threadIdx.x;
+    const int rs = t / tpr;               // row slot
+    const int rpi = kThreads / tpr;       // rows per step
+    const int64_t col = sl * tpr + (t - rs * tpr);
+    const bool active = col < Cv;
+    const int64_t r1 = dmin(p * unit + unit, m);
+    int64_t r = p * unit + rs;
+
+    float K[V];
+    float s1[V], s2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { K[e] = 0.f; s1[e] = 0.f; s2[e] = 0.f; }
+    int cnt = 0;
+    if (active) {
+        load_elems<DT, V>(x, col * V, K);
+        for (; r + (kUnroll - 1) * rpi < r1; r += kUnroll * rpi) {
+            float v[kUnroll][V];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) load_elems<DT, V>(x, ((r + u * rpi) * Cv + col) * V, v[u]);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float d = v[u][e] - K[e];
+                    s1[e] += d;
+                    s2[e] = fmaf(d, d, s2[e]);
+                }
+            cnt += kUnroll;
+        }
+        for (; r < r1; r += rpi) {
+            float v[V];
+            load_elems<DT, V>(x, (r * Cv + col) * V, v);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = v[e] - K[e];
+                s1[e] += d;
+                s2[e] = fmaf(d, d, s2[e]);
+            }
+            cnt += 1;
+        }
+    }
+    float n = float(cnt);
+    float mean[V], m2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        mean[e] = cnt ? s1[e] / n : 0.f;
+        m2[e] = cnt ? fmaxf(s2[e] - s1[e] * mean[e], 0.f) : 0.f;
+    }
+
+    __shared__ float sh_n[kThreads];
+    __shared__ float sh_mean[V][kThreads];
+    __shared__ float sh_m2[V][kThreads];
+    sh_n[t] = n;
+#pragma unroll
+    for (int e = 0; e < V; ++e) { sh_mean[e][t] = mean[e]; sh_m2[e][t] = m2[e]; }
+    for (int s = rpi / 2; s >= 1; s >>= 1) {
+        __syncthreads();
+        if (rs < s) {
+            const int o = t + s * tpr;
+            const float nb = sh_n[o];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float nn = n;
+                chan_merge(nn, mean[e], m2[e], nb, sh_mean[e][o], sh_m2[e][o]);
+            }
+            if (nb > 0.f) n += nb;
+        }
+        __syncthreads();
+        if (rs < s) {
+            sh_n[t] = n;
+#pragma unroll
+            for (int e = 0; e < V; ++e) { sh_mean[e][t] = mean[e]; sh_m2[e][t] = m2[e]; }
+        }
+    }
+    if (rs == 0 && active) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const int64_t ch = col * V + e;
+            part_mean[ch * P + p] = mean[e];
+            part_m2[ch * P + p] = m2[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per channel: fixed-order Chan merge of the channel's P partials in
+// fp64, then the statistics, the running statistics and the apply constants.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_fwd_finalize(
+    const void* __restrict__ x, int layout, int64_t C, int64_t HW, int64_t m, int64_t P,
+    int64_t unit, const float* __restrict__ part_mean, const float* __restrict__ part_m2,
+    const float* __restrict__ gamma, const float* __restrict__ beta,
+    float* __restrict__ running_mean, float* __restrict__ running_var,
+    float* __restrict__ save_mean, float* __restrict__ save_invstd,
+    float eps, float momentum, float4* __restrict__ consts)
+{
+    const int64_t c = int64_t(blockIdx.x) * kFinalizePerBlock + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (c >= C) return;
+    double n = 0.0, mean = 0.0, m2 = 0.0;
+    for (int64_t p = lane; p < P; p += kWave) {
+        const double nb = double(dmin(unit, m - p * unit));
+        chan_merge(n, mean, m2, nb, double(part_mean[c * P + p]), double(part_m2[c * P + p]));
+    }
+    wave_chan(n, mean, m2);
+    if (lane == 0) {
+        const float K = load_one<DT>(x, layout == kNCHW ? c * HW : c);
+        const double var = m2 / double(m);
+        const double invstd = 1.0 / sqrt(var + double(eps));
+        const double mu = double(K) + mean;
+        save_mean[c] = float(mu);
+        save_invstd[c] = float(invstd);
+        if (running_mean) {
+            const double mom = double(momentum);
+            running_mean[c] = float((1.0 - mom) * double(running_mean[c]) + mom * mu);
+            running_var[c] = float((1.0 - mom) * double(running_var[c])
+                                   + mom * var * double(m) / double(m - 1));
+        }
+        consts[c] = make_float4(K, float(mean), float(double(gamma[c]) * invstd), beta[c]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Elementwise y = act(((x - K) - d)*s + beta), in place.  Training reads the
+// constants from the workspace; inference forms them from the running
+// statistics: K = running_mean, d = 0, s = gamma/sqrt(running_var + eps).
+struct TrainConsts {
+    const float4* consts;
+    __device__ __forceinline__ float4 get(int64_t c) const { return consts[c]; }
+};
+struct EvalConsts {
+    const float* gamma;
+    const float* beta;
+    const float* rm;
+    const float* rv;
+    float eps;
+    __device__ __forceinline__ float4 get(int64_t c) const
+    {
+        return make_float4(rm[c], 0.f, gamma[c] / sqrtf(rv[c] + eps), beta[c]);
+    }
+};
+
+template <int ACT, int V>
+__device__ __forceinline__ void apply_one(float (&v)[V], const float4& k, float a)
+{
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - k.x) - k.y, k.z, k.w), a);
+}
+
+template <int DT, int V, int ACT, typename CS>
+__global__ __launch_bounds__(kThreads) void k_apply_nchw(
+    void* x, int64_t nvec, int64_t C, int64_t HWv, CS cs, float a)
+{
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    FlatNCHWWalk w;
+    w.init(v < nvec ? v : 0, C, HWv, stride);
+    for (; v + (kUnroll - 1) * stride < nvec; v += kUnroll * stride) {
+        float val[kUnroll][V];
+        float4 k[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            load_elems<DT, V>(x, (v + u * stride) * V, val[u]);
+            k[u] = cs.get(w.c);
+            w.step();
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            apply_one<ACT, V>(val[u], k[u], a);
+            store_elems<DT, V>(x, (v + u * stride) * V, val[u]);
+        }
+    }
+    for (; v < nvec; v += stride) {
+        float val[V];
+        load_elems<DT, V>(x, v * V, val);
+        const float4 k = cs.get(w.c);
+        w.step();
+        apply_one<ACT, V>(val, k, a);
+        store_elems<DT, V>(x, v * V, val);
+    }
+}
+
+// NHWC: vector v covers channels (v % Cv)*V .. +V.  With FIXED the stride is a
+// multiple of Cv and each thread loads its V channel constants once.
+template <int DT, int V, int ACT, bool FIXED, typename CS>
+__global__ __launch_bounds__(kThreads) void k_apply_nhwc(
+    void* x, int64_t nvec, int64_t Cv, CS cs, float a)
+{
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if constexpr (FIXED) {
+        if (v >= nvec) return;
+        const int64_t c0 = (v % Cv) * V;
+        float4 k[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) k[e] = cs.get(c0 + e);
+        for (; v + (kUnroll - 1) * stride < nvec; v += kUnroll * stride) {
+            float val[kUnroll][V];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) load_elems<DT, V>(x, (v + u * stride) * V, val[u]);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    val[u][e] = act_forward<ACT>(fmaf((val[u][e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+                store_elems<DT, V>(x, (v + u * stride) * V, val[u]);
+            }
+        }
+        for (; v < nvec; v += stride) {
+            float val[V];
+            load_elems<DT, V>(x, v * V, val);
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                val[e] = act_forward<ACT>(fmaf((val[e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+            store_elems<DT, V>(x, v * V, val);
+        }
+    } else {
+        for (; v < nvec; v += stride) {
+            const int64_t c0 = (v % Cv) * V;
+            float val[V];
+            load_elems<DT, V>(x, v * V, val);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float4 k = cs.get(c0 + e);
+                val[e] = act_forward<ACT>(fmaf((val[e] - k.x) - k.y, k.z, k.w), a);
+            }
+            store_elems<DT, V>(x, v * V, val);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+
+template <int DT, int V>
+static void launch_stats_dv(const Plan& pl, const void* x, float* pa, float* pb, hipStream_t s)
+{
+    if (pl.layout == kNCHW)
+        hipLaunchKernelGGL((k_stats_nchw<DT, V>), dim3(pl.reduce_blocks), dim3(kThreads), 0, s,
+                           x, pl.C, pl.HW, pl.m, pl.unit, pl.P, pa, pb);
+    else
+        hipLaunchKernelGGL((k_stats_nhwc<DT, V>), dim3(pl.reduce_blocks), dim3(kThreads), 0, s,
+                           x, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit, pl.P, pa, pb);
+}
+
+void launch_forward_stats(const Plan& pl, const void* x, const float* gamma, const float* beta,
+                          float* running_mean, float* running_var, float* save_mean,
+                          float* save_invstd, float eps, float momentum, void* ws, hipStream_t s)
+{
+    char* wsb = static_cast<char*>(ws);
+    float* pa = reinterpret_cast<float*>(wsb + pl.off_part_a);
+    float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
+    float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
+    if (pl.dtype == kF32) {
+        if (pl.vec) launch_stats_dv<kF32, 4>(pl, x, pa, pb, s);
+        else launch_stats_dv<kF32, 1>(pl, x, pa, pb, s);
+    } else {
+        if (pl.vec) launch_stats_dv<kBF16, 8>(pl, x, pa, pb, s);
+        else launch_stats_dv<kBF16, 1>(pl, x, pa, pb, s);
+    }
+    const dim3 grid(unsigned(ceil_div(pl.C, kFinalizePerBlock)));
+    if (pl.dtype == kF32)
+        hipLaunchKernelGGL((k_fwd_finalize<kF32>), grid, dim3(kThreads), 0, s, x, pl.layout, pl.C,
+                           pl.HW, pl.m, pl.P, pl.unit, pa, pb, gamma, beta, running_mean,
+                           running_var, save_mean, save_invstd, eps, momentum, consts);
+    else
+        hipLaunchKernelGGL((k_fwd_finalize<kBF16>), grid, dim3(kThreads), 0, s, x, pl.layout, pl.C,
+                           pl.HW, pl.m, pl.P, pl.unit, pa, pb, gamma, beta, running_mean,
+                           running_var, save_mean, save_invstd, eps, momentum, consts);
+}
+
+template <int DT, int V, int ACT, typename CS>
+static void launch_apply_dva(const Plan& pl, void* x, CS cs, float a, hipStream_t s)
+{
+    const int64_t nvec = pl.numel / V;
+    const dim3 grid(unsigned(pl.apply_blocks));
+    if (pl.layout == kNCHW)
+        hipLaunchKernelGGL((k_apply_nchw<DT, V, ACT, CS>), grid, dim3(kThreads), 0, s, x, nvec,
+                           pl.C, pl.HW / V, cs, a);
+    else if (pl.fixed_col)
+        hipLaunchKernelGGL((k_apply_nhwc<DT, V, ACT, true, CS>), grid, dim3(kThreads), 0, s, x,
+                           nvec, pl.C / V, cs, a);
+    else
+        hipLaunchKernelGGL((k_apply_nhwc<DT, V, ACT, false, CS>), grid, dim3(kThreads), 0, s, x,
+                           nvec, pl.C / V, cs, a);
+}
+
+template <int DT, int V, typename CS>
+static void launch_apply_dv(const Plan& pl, void* x, CS cs, int act, float a, hipStream_t s)
+{
+    switch (act) {
+    case kLeaky: launch_apply_dva<DT, V, kLeaky>(pl, x, cs, a, s); break;
+    case kElu: launch_apply_dva<DT, V, kElu>(pl, x, cs, a, s); break;
+    default: launch_apply_dva<DT, V, kIdentity>(pl, x, cs, a, s); break;
+    }
+}
+
+template <typename CS>
+static void launch_apply(const Plan& pl, void* x, CS cs, int act, float a, hipStream_t s)
+{
+    if (pl.dtype == kF32) {
+        if (pl.vec) launch_apply_dv<kF32, 4>(pl, x, cs, act, a, s);
+        else launch_apply_dv<kF32, 1>(pl, x, cs, act, a, s);
+    } else {
+        if (pl.vec) launch_apply_dv<kBF16, 8>(pl, x, cs, act, a, s);
+        else launch_apply_dv<kBF16, 1>(pl, x, cs, act, a, s);
+    }
+}
+
+void launch_forward_apply(const Plan& pl, void* x, int act, float a, void* ws, hipStream_t s)
+{
+    TrainConsts cs{reinterpret_cast<const float4*>(static_cast<char*>(ws) + pl.off_const)};
+    launch_apply(pl, x, cs, act, a, s);
+}
+
+void launch_forward_eval(const Plan& pl, void* x, const float* gamma, const float* beta,
+                         const float* rm, const float* rv, float eps, int act, float a,
+                         hipStream_t s)
+{
+    EvalConsts cs{gamma, beta, rm, rv, eps};
+    launch_apply(pl, x, cs, act, a, s);
+}
+
+}  // namespace iabn

@@ -1,0 +1,28 @@
+// Host launchers of the In-Place ABN kernels.  They enqueue on `s` and return;
+// arguments are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "plan.hpp"
+
+namespace iabn {
+
+void launch_forward_stats(const Plan& pl, const void* x, const float* gamma, const float* beta,
+                          float* running_mean, float* running_var, float* save_mean,
+                          float* save_invstd, float eps, float momentum, void* ws, hipStream_t s);
+
+void launch_forward_apply(const Plan& pl, void* x, int act, float a, void* ws, hipStream_t s);
+
+void launch_forward_eval(const Plan& pl, void* x, const float* gamma, const float* beta,
+                         const float* rm, const float* rv, float eps, int act, float a,
+                         hipStream_t s);
+
+void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const float* gamma,
+                            const float* beta, const float* invstd, float* dgamma, float* dbeta,
+                            int act, float a, void* ws, hipStream_t s);
+
+void launch_backward_apply(const Plan& pl, const void* y, const void* dy, void* dx, int act,
+                           float a, void* ws, hipStream_t s);
+
+}  // namespace iabn

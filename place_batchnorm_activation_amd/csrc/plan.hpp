@@ -1,0 +1,144 @@
+// Tiling plan for the In-Place ABN kernels (host side).
+//
+// A plan depends only on the shape, layout, dtype and whether the 128-bit vector
+// path applies -- never on the device -- so a given problem always reduces in the
+// same order and the results are bitwise reproducible.
+//
+// Reduction tiling (forward statistics and backward sums).  Every channel's m
+// elements are cut into P "partials" of `unit` elements (the last one ragged):
+//   NCHW: the channel-local index j = n*HW + hw is cut into runs of `unit`; one
+//         workgroup per (channel, partial): grid = C * P.
+//   NHWC: the m rows are cut into runs of `unit` rows; the C channels into
+//         `slices` of `tpr` vectors (tpr threads per row, 256/tpr rows in flight
+//         per workgroup); grid = slices * P, slice index fastest.
+// Each workgroup writes one partial per channel it covers; a finishing kernel
+// combines the P partials of a channel in a fixed order.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace iabn {
+
+constexpr int kThreads = 256;          // workgroup size of every kernel
+constexpr int kWave = 64;              // CDNA wavefront
+constexpr int kFinalizePerBlock = kThreads / kWave;  // one wave per channel
+
+enum Layout { kNCHW = 0, kNHWC = 1 };
+enum DType { kF32 = 0, kBF16 = 1 };
+enum Act { kIdentity = 0, kLeaky = 1, kElu = 2 };
+
+struct Plan {
+    int64_t N = 0, C = 0, HW = 0, m = 0, numel = 0;
+    int layout = 0, dtype = 0, esize = 4;
+    bool vec = false;    // 128-bit accesses
+    int V = 1;           // elements per access
+    // reduction tiling
+    int64_t P = 1;       // partials per channel
+    int64_t unit = 1;    // NCHW: channel-local elements per partial; NHWC: rows per partial
+    int tpr = 1;         // NHWC: threads per row
+    int64_t slices = 1;  // NHWC: channel slices
+    int64_t reduce_blocks = 0;
+    // elementwise tiling
+    int64_t apply_blocks = 0;
+    bool fixed_col = false;  // NHWC: each thread keeps one channel group for the whole walk
+    // workspace sections (bytes, 256-aligned)
+    size_t off_part_a = 0, off_part_b = 0, off_const = 0, bytes = 0;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t align_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+inline int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+inline int64_t gcd64(int64_t a, int64_t b)
+{
+    while (b) { const int64_t t = a % b; a = b; b = t; }
+    return a;
+}
+
+// Workgroups an elementwise kernel launches: enough to keep every CU busy with
+// several waves while each thread still walks a few vectors.
+constexpr int64_t kApplyBlocksMax = 2048;
+// Workgroups a reduction aims for.
+constexpr int64_t kReduceBlocksTarget = 2048;
+
+inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, int dtype, bool vec)
+{
+    Plan p;
+    p.N = N; p.C = C; p.HW = H * W; p.m = N * p.HW; p.numel = p.m * C;
+    p.layout = layout; p.dtype = dtype;
+    p.esize = dtype == kF32 ? 4 : 2;
+    p.vec = vec;
+    p.V = vec ? 16 / p.esize : 1;
+    if (p.numel == 0) return p;
+    const int V = p.V;
+
+    if (layout == kNCHW) {
+        // vectors never straddle planes: HW % V == 0 on the vector path
+        const int64_t vc = p.m / V;                          // vectors per channel
+        const int64_t want = ceil_div(kReduceBlocksTarget, C);
+        const int64_t cap = max64(1, ceil_div(vc, 2 * kThreads));  // >= ~2 vectors per thread
+        int64_t P = max64(1, min64(want, cap));
+        p.unit = ceil_div(vc, P) * V;
+        p.P = ceil_div(p.m, p.unit);
+        p.reduce_blocks = C * p.P;
+    } else {
+        const int64_t cv = C / V;                            // vectors per row
+        // partial traffic (8 B per channel and partial) kept to ~2% of the data
+        const int64_t p_budget = max64(1, (p.m * p.esize) / 400);
+        int tpr = 1;
+        while (tpr < cv && tpr < kThreads) tpr <<= 1;
+        auto choose_P = [&](int t) {
+            const int64_t rpi = kThreads / t;               // rows per step of a workgroup
+            const int64_t p_iter = max64(1, p.m / (4 * rpi)); // >= ~4 steps per thread
+            return max64(1, min64(p_budget, p_iter));
+        };
+        int64_t slices = ceil_div(cv, tpr);
+        int64_t P = choose_P(tpr);
+        // narrower slices (down to 4 lanes, 64 bytes per row segment) while short of work
+        while (slices * P < kReduceBlocksTarget / 2 && tpr > 4) {
+            tpr >>= 1;
+            slices = ceil_div(cv, tpr);
+            P = choose_P(tpr);
+        }
+        P = min64(P, max64(1, ceil_div(kReduceBlocksTarget, slices)));
+        p.tpr = tpr;
+        p.slices = slices;
+        p.unit = ceil_div(p.m, P);
+        p.P = ceil_div(p.m, p.unit);
+        p.reduce_blocks = slices * p.P;
+    }
+
+    const int64_t nvec = p.numel / V;
+    p.apply_blocks = max64(1, min64(kApplyBlocksMax, ceil_div(nvec, kThreads)));
+    if (layout == kNHWC) {
+        // keep each thread on one channel group: stride (blocks*256) % (C/V) == 0
+        const int64_t cv = C / V;
+        const int64_t need = cv / gcd64(cv, kThreads);      // blocks must be a multiple of this
+        if (need <= kApplyBlocksMax) {
+            p.apply_blocks = max64(need, (p.apply_blocks / need) * need);
+            p.fixed_col = true;
+        }
+    }
+
+    // The constants come first, at an offset that does not depend on the plan, so
+    // that a stage planned for the vector path and one planned for the scalar path
+    // (different pointer alignment) agree on where they are.
+    size_t off = 0;
+    const size_t part_bytes = (size_t)(p.P * C) * sizeof(float);
+    p.off_const = off;  off = (size_t)align_up((int64_t)(off + (size_t)C * 16), 256);
+    p.off_part_a = off; off = (size_t)align_up((int64_t)(off + part_bytes), 256);
+    p.off_part_b = off; off = (size_t)align_up((int64_t)(off + part_bytes), 256);
+    p.bytes = off;
+    return p;
+}
+
+// Whether the 128-bit path applies to this shape (pointer alignment is checked apart).
+inline bool vec_shape_ok(int64_t C, int64_t HW, int layout, int dtype)
+{
+    const int V = 16 / (dtype == kF32 ? 4 : 2);
+    return layout == kNCHW ? (HW % V == 0) : (C % V == 0);
+}
+
+}  // namespace iabn

@@ -1,0 +1,136 @@
+"""Shared helpers of the parity tests and the smoke check: run the HIP path through
+the binding, run the fp64 oracle on the same input bits, and compare.
+
+Error metric (per tensor): max_i |g_i - o_i| / (|o_i| + rms_c(o)), where rms_c is
+the RMS of the oracle's values over the channel of element i (for per-channel
+vectors: over all C entries).  Gates: 1e-5 for fp32 storage, 2e-2 for bf16
+storage (fp32 arithmetic in both cases).
+
+Stage-wise gating: the forward is checked against the oracle run on the same x
+bits; the backward against the oracle run on the GPU's own stored y bits and
+save_invstd (the from-y backward is a function of exactly those).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def f32(v: float) -> float:
+    """The fp32 value the library receives for a scalar argument."""
+    return float(np.float32(v))
+
+
+def rel_err_tensor(g: np.ndarray, o: np.ndarray) -> float:
+    """g, o: fp64 [N, C, H, W]."""
+    rms = np.sqrt(np.mean(o * o, axis=(0, 2, 3), keepdims=True))
+    return float(np.max(np.abs(g - o) / (np.abs(o) + rms + 1e-300))) if g.size else 0.0
+
+
+def rel_err_vec(g: np.ndarray, o: np.ndarray) -> float:
+    rms = np.sqrt(np.mean(o * o))
+    return float(np.max(np.abs(g - o) / (np.abs(o) + rms + 1e-300))) if g.size else 0.0
+
+
+def storage_shape(wl: workloads.Workload) -> tuple:
+    return (wl.N, wl.C, wl.H, wl.W) if wl.layout == "NCHW" else (wl.N, wl.H, wl.W, wl.C)
+
+
+def to_device(a: np.ndarray, wl: workloads.Workload, device="cuda") -> torch.Tensor:
+    return workloads.to_torch(a, wl.dtype).reshape(storage_shape(wl)).to(device)
+
+
+def to_nchw64(t: torch.Tensor, wl: workloads.Workload) -> np.ndarray:
+    return workloads.from_storage(workloads.from_torch(t, wl.dtype), wl.N, wl.C, wl.H, wl.W,
+                                  wl.layout, wl.dtype)
+
+
+@dataclasses.dataclass
+class GpuRun:
+    y: torch.Tensor
+    dx: Optional[torch.Tensor]
+    save_mean: np.ndarray
+    save_invstd: np.ndarray
+    running_mean: np.ndarray
+    running_var: np.ndarray
+    dgamma: Optional[np.ndarray]
+    dbeta: Optional[np.ndarray]
+
+
+def run_gpu(inp: workloads.Inputs, backward: bool = True, dx_over_dy: bool = False,
+            device="cuda") -> GpuRun:
+    """Training forward (in place) and backward through the C ABI."""
+    import place_batchnorm_activation_amd as iabn
+    wl = inp.wl
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+    x = to_device(inp.x, wl, device)
+    g = torch.from_numpy(inp.gamma).to(device)
+    b = torch.from_numpy(inp.beta).to(device)
+    rm = torch.from_numpy(inp.running_mean).to(device)
+    rv = torch.from_numpy(inp.running_var).to(device)
+    sm = torch.empty(C, device=device)
+    si = torch.empty(C, device=device)
+    ws = iabn.workspace(N, C, H, W, wl.layout, x.dtype, device)
+    iabn.iabn_forward_train(x, N, C, H, W, wl.layout, g, b, rm, rv, sm, si, wl.act,
+                            wl.act_param, wl.eps, wl.momentum, ws)
+    dx = dg = db = None
+    if backward:
+        dy = to_device(inp.dy, wl, device)
+        dx = dy if dx_over_dy else torch.empty_like(dy)
+        dgt = torch.empty(C, device=device)
+        dbt = torch.empty(C, device=device)
+        iabn.iabn_backward(x, dy, dx, N, C, H, W, wl.layout, g, b, si, dgt, dbt, wl.act,
+                           wl.act_param, ws)
+        dg, db = dgt.cpu().numpy(), dbt.cpu().numpy()
+    torch.cuda.synchronize()
+    return GpuRun(y=x, dx=dx, save_mean=sm.cpu().numpy(), save_invstd=si.cpu().numpy(),
+                  running_mean=rm.cpu().numpy(), running_var=rv.cpu().numpy(), dgamma=dg,
+                  dbeta=db)
+
+
+def check_forward(inp: workloads.Inputs, run: GpuRun, channels=None) -> dict:
+    """Forward errors against the oracle on the same x bits (optionally a channel subset)."""
+    wl = inp.wl
+    x = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    y = to_nchw64(run.y, wl)
+    sel = slice(None) if channels is None else np.asarray(channels)
+    f = oracle.forward_train(x[:, sel], inp.gamma[sel], inp.beta[sel], wl.act, f32(wl.act_param),
+                             f32(wl.eps), f32(wl.momentum), inp.running_mean[sel],
+                             inp.running_var[sel], storage=wl.dtype)
+    return {
+        "y": rel_err_tensor(y[:, sel], f["y"]),
+        "save_mean": rel_err_vec(run.save_mean[sel], f["mean"]),
+        "save_invstd": rel_err_vec(run.save_invstd[sel], f["invstd"]),
+        "running_mean": rel_err_vec(run.running_mean[sel], f["running_mean"]),
+        "running_var": rel_err_vec(run.running_var[sel], f["running_var"]),
+    }
+
+
+def check_backward(inp: workloads.Inputs, run: GpuRun, channels=None) -> dict:
+    """Backward errors against the oracle fed the GPU's own y bits and save_invstd."""
+    wl = inp.wl
+    y = to_nchw64(run.y, wl)
+    dy = workloads.from_storage(inp.dy, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    dx = to_nchw64(run.dx, wl)
+    sel = slice(None) if channels is None else np.asarray(channels)
+    o = oracle.backward_from_y(y[:, sel], dy[:, sel], inp.gamma[sel], inp.beta[sel],
+                               run.save_invstd[sel].astype(np.float64), wl.act, f32(wl.act_param))
+    return {
+        "dx": rel_err_tensor(dx[:, sel], o["dx"]),
+        "dgamma": rel_err_vec(run.dgamma[sel], o["dgamma"]),
+        "dbeta": rel_err_vec(run.dbeta[sel], o["dbeta"]),
+    }
+
+
+def assert_within(errs: dict, dtype: str, what: str = "") -> None:
+    tol = TOL[dtype]
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    assert not bad, "%s errors above %g: %s (all: %s)" % (what, tol, bad, errs)

@@ -1,0 +1,171 @@
+// Host-side replay of the kernels' index arithmetic (CPU only, no GPU calls).
+//
+// For many shapes it builds the library's own Plan and walks every thread of every
+// reduction and elementwise kernel exactly as the kernels' loops do -- with the
+// library's own ChannelWalk / FlatNCHWWalk helpers -- and checks that each access
+// stays inside its buffer, that the walks agree with the direct index formulas,
+// and that every element is visited exactly once.  Exit status 0 means all held.
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+#include "device.hpp"
+#include "plan.hpp"
+
+using namespace iabn;
+
+static int failures = 0;
+#define CHECK(cond, ...)                                                 \
+    do {                                                                 \
+        if (!(cond)) {                                                   \
+            if (failures < 20) { std::printf("FAIL %s:%d ", __FILE__, __LINE__); \
+                                 std::printf(__VA_ARGS__); std::printf("\n"); } \
+            ++failures;                                                  \
+        }                                                                \
+    } while (0)
+
+struct Shape { int64_t N, C, H, W; int layout, dtype; };
+
+static void check_plan(const Shape& s, bool vec)
+{
+    const Plan pl = make_plan(s.N, s.C, s.H, s.W, s.layout, s.dtype, vec);
+    const int V = pl.V;
+    const int64_t numel = pl.numel, nvec = numel / V, C = pl.C, m = pl.m;
+    if (numel == 0) return;
+    CHECK(numel % V == 0, "numel %% V");
+    CHECK(pl.P >= 1 && pl.unit >= 1, "P/unit");
+    CHECK(pl.P * pl.unit >= m && (pl.P - 1) * pl.unit < m, "partials cover m exactly");
+    CHECK(pl.reduce_blocks < (int64_t(1) << 31) && pl.apply_blocks < (int64_t(1) << 31), "grid");
+    CHECK(pl.off_const == 0 && pl.off_part_a >= size_t(C) * 16, "const section");
+    CHECK(pl.off_part_b >= pl.off_part_a + size_t(pl.P * C) * 4, "part a section");
+    CHECK(pl.bytes >= pl.off_part_b + size_t(pl.P * C) * 4, "part b section");
+    CHECK(pl.off_part_a % 256 == 0 && pl.off_part_b % 256 == 0, "alignment");
+
+    std::vector<uint8_t> seen(size_t(nvec), 0);
+    // ---- reduction kernels (statistics and backward sums share the tiling)
+    if (pl.layout == kNCHW) {
+        const int64_t HWv = pl.HW / V;
+        CHECK(pl.HW % V == 0 && pl.unit % V == 0, "NCHW vector alignment");
+        CHECK(pl.reduce_blocks == C * pl.P, "NCHW grid");
+        for (int64_t b = 0; b < pl.reduce_blocks; ++b) {
+            const int64_t c = b / pl.P, p = b - c * pl.P;
+            CHECK(c * pl.HW < numel, "pivot");
+            const int64_t j1 = std::min(p * pl.unit + pl.unit, m) / V;
+            for (int t = 0; t < kThreads; ++t) {
+                int64_t j = p * pl.unit / V + t;
+                ChannelWalk w;
+                w.init(j < j1 ? j : 0, c, C, HWv, kThreads);
+                for (; j < j1; j += kThreads) {
+                    const int64_t direct = ((j / HWv) * C + c) * HWv + j % HWv;
+                    CHECK(w.addr == direct, "ChannelWalk b=%lld t=%d j=%lld", (long long)b, t,
+                          (long long)j);
+                    CHECK(w.addr >= 0 && w.addr < nvec, "reduce bounds");
+                    if (w.addr >= 0 && w.addr < nvec) seen[size_t(w.addr)]++;
+                    w.step();
+                }
+            }
+        }
+    } else {
+        const int64_t Cv = C / V;
+        CHECK(C % V == 0, "NHWC vector alignment");
+        CHECK(kThreads % pl.tpr == 0, "tpr divides the workgroup");
+        CHECK(pl.slices * pl.tpr >= Cv, "slices cover the row");
+        CHECK(pl.reduce_blocks == pl.slices * pl.P, "NHWC grid");
+        const int rpi = kThreads / pl.tpr;
+        for (int64_t b = 0; b < pl.reduce_blocks; ++b) {
+            const int64_t p = b / pl.slices, sl = b - p * pl.slices;
+            const int64_t r1 = std::min(p * pl.unit + pl.unit, m);
+            for (int t = 0; t < kThreads; ++t) {
+                const int rs = t / pl.tpr;
+                const int64_t col = sl * pl.tpr + (t - rs * pl.tpr);
+                if (col >= Cv) continue;
+                for (int64_t r = p * pl.unit + rs; r < r1; r += rpi) {
+                    const int64_t a = r * Cv + col;
+                    CHECK(a >= 0 && a < nvec, "NHWC reduce bounds");
+                    if (a >= 0 && a < nvec) seen[size_t(a)]++;
+                }
+                // LDS tree partners stay inside the workgroup
+                for (int st = rpi / 2; st >= 1; st >>= 1)
+                    if (rs < st) CHECK(t + st * pl.tpr < kThreads, "LDS partner");
+            }
+        }
+    }
+    for (int64_t i = 0; i < nvec; ++i)
+        CHECK(seen[size_t(i)] == 1, "reduction visits vector %lld %d times", (long long)i,
+              int(seen[size_t(i)]));
+
+    // ---- elementwise kernels
+    std::fill(seen.begin(), seen.end(), 0);
+    const int64_t stride = pl.apply_blocks * kThreads;
+    if (pl.layout == kNCHW) {
+        const int64_t HWv = pl.HW / V;
+        for (int64_t t0 = 0; t0 < stride; ++t0) {
+            int64_t v = t0;
+            FlatNCHWWalk w;
+            w.init(v < nvec ? v : 0, C, HWv, stride);
+            for (; v < nvec; v += stride) {
+                CHECK(w.c == (v / HWv) % C, "FlatNCHWWalk v=%lld", (long long)v);
+                CHECK(w.c >= 0 && w.c < C, "channel bounds");
+                seen[size_t(v)]++;
+                w.step();
+            }
+        }
+    } else {
+        const int64_t Cv = C / V;
+        if (pl.fixed_col) CHECK(stride % Cv == 0, "fixed channel group needs stride %% Cv == 0");
+        for (int64_t t0 = 0; t0 < stride; ++t0) {
+            if (t0 >= nvec) break;
+            const int64_t c0 = (t0 % Cv) * V;
+            CHECK(c0 + V - 1 < C, "channel group bounds");
+            for (int64_t v = t0; v < nvec; v += stride) {
+                if (pl.fixed_col) CHECK((v % Cv) * V == c0, "fixed channel group");
+                seen[size_t(v)]++;
+            }
+        }
+    }
+    for (int64_t i = 0; i < nvec; ++i)
+        CHECK(seen[size_t(i)] == 1, "elementwise visits vector %lld %d times", (long long)i,
+              int(seen[size_t(i)]));
+}
+
+int main(int argc, char** argv)
+{
+    std::vector<Shape> shapes = {
+        {2, 4, 8, 8, kNCHW, kF32},      {32, 256, 56, 56, kNCHW, kF32},
+        {2, 256, 512, 512, kNHWC, kBF16}, {16, 512, 28, 28, kNCHW, kF32},
+        {64, 2048, 7, 7, kNHWC, kBF16},
+        {4, 6, 16, 20, kNCHW, kF32}, {3, 5, 17, 19, kNCHW, kF32}, {4, 6, 16, 20, kNCHW, kBF16},
+        {3, 5, 17, 19, kNCHW, kBF16}, {3, 24, 9, 11, kNHWC, kF32}, {2, 13, 10, 7, kNHWC, kF32},
+        {2, 200, 12, 12, kNHWC, kF32}, {3, 24, 9, 11, kNHWC, kBF16}, {2, 13, 10, 7, kNHWC, kBF16},
+        {2, 200, 12, 12, kNHWC, kBF16}, {2, 5, 1, 1, kNCHW, kF32}, {1, 1, 300, 301, kNCHW, kF32},
+        {2, 4104, 3, 3, kNHWC, kBF16}, {2, 4104, 3, 3, kNHWC, kF32}, {2, 64, 3, 1, kNCHW, kF32},
+        {3, 8, 1, 1, kNHWC, kBF16}, {8, 32, 28, 28, kNCHW, kF32}, {4, 64, 32, 32, kNHWC, kBF16},
+        {4, 32, 14, 14, kNCHW, kF32}, {8, 512, 7, 7, kNHWC, kBF16}, {4, 64, 16, 16, kNCHW, kF32},
+        {4, 64, 16, 16, kNHWC, kBF16}, {4, 32, 12, 12, kNCHW, kF32}, {4, 256, 12, 12, kNHWC, kBF16},
+        {2, 16, 8, 8, kNCHW, kF32}, {2, 16, 8, 8, kNHWC, kBF16}, {2, 16, 8, 8, kNCHW, kBF16},
+        {2, 16, 8, 8, kNHWC, kF32},
+    };
+    std::mt19937_64 rng(12345);
+    const int n_random = argc > 1 ? std::atoi(argv[1]) : 300;
+    for (int i = 0; i < n_random; ++i) {
+        Shape s;
+        s.N = 1 + rng() % 9; s.C = 1 + rng() % 300; s.H = 1 + rng() % 17; s.W = 1 + rng() % 17;
+        s.layout = int(rng() % 2); s.dtype = int(rng() % 2);
+        if (s.N * s.H * s.W < 2) s.N = 2;
+        shapes.push_back(s);
+    }
+    int checked = 0;
+    for (const Shape& s : shapes) {
+        check_plan(s, false);
+        if (vec_shape_ok(s.C, s.H * s.W, s.layout, s.dtype)) check_plan(s, true);
+        ++checked;
+        if (failures) {
+            std::printf("shape N=%lld C=%lld H=%lld W=%lld layout=%d dtype=%d\n", (long long)s.N,
+                        (long long)s.C, (long long)s.H, (long long)s.W, s.layout, s.dtype);
+            return 1;
+        }
+    }
+    std::printf("OK %d shapes\n", checked);
+    return 0;
+}

@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every entry point include/iabn.h declares, and
+rejects bad arguments before any HIP call (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iabn.h")
+
+iabn = pytest.importorskip("place_batchnorm_activation_amd")
+lib = iabn.lib
+
+OK, INVALID, UNSUPPORTED, WS, MISALIGNED = 0, 1, 2, 3, 4
+A = 0x10000  # a 64 KiB-aligned fake device address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(iabn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "iabn_forward_train" in names and "iabn_backward" in names
+    assert "iabn_forward_eval" in names and "iabn_workspace_size" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert iabn.status_string(0) == "ok"
+    assert "workspace" in iabn.status_string(3)
+    assert iabn.iabn_version() >= 100
+
+
+def test_workspace_size_depends_only_on_shape():
+    a = lib.iabn_workspace_size(32, 256, 56, 56, 0, 0)
+    assert a > 256 * 16
+    assert a == lib.iabn_workspace_size(32, 256, 56, 56, 0, 0)
+    assert lib.iabn_workspace_size(0, 256, 56, 56, 0, 0) == 0
+    assert lib.iabn_workspace_size(2, 0, 4, 4, 0, 0) == 0
+    assert lib.iabn_workspace_size(-1, 4, 4, 4, 0, 0) == 0
+    assert lib.iabn_workspace_size(2, 4, 4, 4, 7, 0) == 0
+    # partial workspace stays small next to the data (a few percent)
+    for (N, C, H, W, lay, dt) in [(32, 256, 56, 56, 0, 0), (2, 256, 512, 512, 1, 1),
+                                  (16, 512, 28, 28, 0, 0), (64, 2048, 7, 7, 1, 1)]:
+        data = N * C * H * W * (4 if dt == 0 else 2)
+        assert lib.iabn_workspace_size(N, C, H, W, lay, dt) < 0.05 * data
+
+
+def _fwd(x=A, N=2, C=3, H=4, W=4, layout=0, dtype=0, g=A, b=A, rm=A, rv=A, sm=A, si=A,
+         act=1, p=0.01, eps=1e-5, mom=0.1, ws=A, wsb=1 << 20):
+    return lib.iabn_forward_train(x, N, C, H, W, layout, dtype, g, b, rm, rv, sm, si, act, p, eps,
+                                  mom, ws, wsb, None)
+
+
+def test_forward_train_validation():
+    assert _fwd(layout=2) == INVALID
+    assert _fwd(dtype=5) == INVALID
+    assert _fwd(N=-1) == INVALID
+    assert _fwd(act=9) == INVALID
+    assert _fwd(p=0.0) == INVALID
+    assert _fwd(p=-0.1) == INVALID
+    assert _fwd(p=float("nan")) == INVALID
+    assert _fwd(act=2, p=-1.0) == INVALID
+    assert _fwd(eps=-1e-5) == INVALID
+    assert _fwd(eps=float("inf")) == INVALID
+    assert _fwd(mom=1.5) == INVALID
+    assert _fwd(mom=-0.1) == INVALID
+    assert _fwd(rm=None) == INVALID             # running stats: both or neither
+    assert _fwd(N=1, H=1, W=1) == INVALID       # m = 1: unbiased variance undefined
+    assert _fwd(x=None) == INVALID
+    assert _fwd(g=None) == INVALID
+    assert _fwd(sm=None) == INVALID
+    assert _fwd(x=A + 2) == MISALIGNED          # fp32 element pointer not 4-byte aligned
+    assert _fwd(g=A + 1) == MISALIGNED
+    assert _fwd(ws=None) == WS
+    assert _fwd(wsb=16) == WS
+    assert _fwd(ws=A + 4) == MISALIGNED
+    # C == 0 is a no-op that succeeds without touching anything
+    assert _fwd(C=0, x=None, g=None, b=None, sm=None, si=None, ws=None) == OK
+
+
+def test_stage_entry_validation():
+    assert lib.iabn_forward_stats(A, 2, 3, 4, 4, 0, 0, A, A, None, None, A, A, -1.0, 0.1, A,
+                                  1 << 20, None) == INVALID
+    assert lib.iabn_forward_apply(A, 2, 3, 4, 4, 0, 0, 1, 0.0, A, 1 << 20, None) == INVALID
+    assert lib.iabn_forward_apply(A, 2, 3, 4, 4, 0, 0, 1, 0.01, None, 0, None) == WS
+    assert lib.iabn_backward_reduce(A, A, 2, 3, 4, 4, 0, 0, A, A, None, A, A, 1, 0.01, A,
+                                    1 << 20, None) == INVALID
+    assert lib.iabn_backward_apply(A, A, A + 64, 2, 3, 4, 4, 0, 0, 1, 0.01, None, 0, None) == INVALID
+
+
+def test_forward_eval_validation():
+    ev = lib.iabn_forward_eval
+    assert ev(A, 2, 3, 4, 4, 0, 0, A, A, A, None, 1, 0.01, 1e-5, None) == INVALID
+    assert ev(A, 2, 3, 4, 4, 0, 1, A, A, A, A, 1, 0.01, -1.0, None) == INVALID
+    assert ev(A + 1, 2, 3, 4, 4, 0, 1, A, A, A, A, 1, 0.01, 1e-5, None) == MISALIGNED
+    # empty tensors are a no-op
+    assert ev(None, 0, 3, 4, 4, 0, 0, None, None, None, None, 1, 0.01, 1e-5, None) == OK
+    assert ev(None, 2, 3, 0, 4, 1, 1, None, None, None, None, 2, 1.0, 1e-5, None) == OK
+
+
+def _bwd(y=A, dy=2 * A, dx=3 * A, N=2, C=3, H=4, W=4, layout=0, dtype=0, g=A, b=A, si=A, dg=A,
+         db=A, act=1, p=0.01, ws=A, wsb=1 << 20):
+    return lib.iabn_backward(y, dy, dx, N, C, H, W, layout, dtype, g, b, si, dg, db, act, p, ws,
+                             wsb, None)
+
+
+def test_backward_validation():
+    assert _bwd(act=1, p=0.0) == INVALID
+    assert _bwd(dx=A) == INVALID                 # dx aliases y
+    assert _bwd(dx=A + 64) == INVALID            # dx overlaps y
+    assert _bwd(dx=2 * A + 64) == INVALID        # dx partly overlaps dy
+    assert _bwd(N=1, H=1, W=1) == INVALID
+    assert _bwd(g=None) == INVALID
+    assert _bwd(si=None) == INVALID
+    assert _bwd(ws=None) == WS
+    assert _bwd(dtype=1, y=A + 1) == MISALIGNED
+    assert _bwd(C=0, y=None, dy=None, dx=None, g=None, b=None, si=None, dg=None, db=None,
+                ws=None) == OK

@@ -1,0 +1,290 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Forward: GPU y / statistics / running statistics vs the oracle on the same x bits.
+Backward: GPU dx / dgamma / dbeta vs the oracle on the GPU's own y bits and
+save_invstd.  Gates: 1e-5 (fp32 storage) and 2e-2 (bf16 storage) on the
+metric of tests/harness.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import harness
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import place_batchnorm_activation_amd as iabn
+
+
+def custom(base: int, N, C, H, W, **kw) -> workloads.Workload:
+    wl = workloads.config(base).with_shape(N, C, H, W)
+    name = "%s_%dx%dx%dx%d" % (wl.name, N, C, H, W)
+    for k, v in kw.items():
+        name += "_%s=%s" % (k, v)
+    return dataclasses.replace(wl, name=name, **kw)
+
+
+def full_check(wl, seed=None, channels=None, dx_over_dy=False):
+    inp = workloads.make_inputs(wl, seed=seed)
+    print("case:", wl.name, wl.layout, wl.dtype, wl.act, wl.act_param, flush=True)
+    run = harness.run_gpu(inp, dx_over_dy=dx_over_dy)
+    ef = harness.check_forward(inp, run, channels)
+    eb = harness.check_backward(inp, run, channels)
+    print("  forward", ef, "\n  backward", eb, flush=True)
+    harness.assert_within(ef, wl.dtype, "forward " + wl.name)
+    harness.assert_within(eb, wl.dtype, "backward " + wl.name)
+    return inp, run
+
+
+# ---------------------------------------------------------------------------
+# small and mid sizes: every layout x dtype x activation, several tiles, ragged tails
+
+def test_config1_tiny():
+    full_check(workloads.config(1))
+
+
+MID = []
+for layout in ("NCHW", "NHWC"):
+    for dtype in ("f32", "bf16"):
+        for act, p in (("leaky_relu", 0.01), ("elu", 1.0), ("identity", 0.0)):
+            base = 4 if act == "elu" else (2 if dtype == "f32" else 3)
+            # vector path shapes and scalar (ragged) path shapes
+            if layout == "NCHW":
+                shapes = [(4, 6, 16, 20), (3, 5, 17, 19)]
+            else:
+                shapes = [(3, 24, 9, 11), (2, 13, 10, 7), (2, 200, 12, 12)]
+            for s in shapes:
+                MID.append(custom(base, *s, layout=layout, dtype=dtype, act=act, act_param=p))
+
+
+@pytest.mark.parametrize("wl", MID, ids=lambda w: w.name)
+def test_mid_sizes(wl):
+    full_check(wl)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at their full sizes; the oracle checks a sample of channels
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_sampled(idx):
+    wl = workloads.config(idx)
+    rng = np.random.default_rng(idx)
+    ch = sorted(set([0, 1, wl.C // 2, wl.C - 1] + list(rng.choice(wl.C, 8, replace=False))))
+    inp, run = full_check(wl, channels=ch)
+    # property that holds at any size: every channel's input gradient sums to zero
+    dx = run.dx.float() if wl.layout == "NCHW" else run.dx.float().permute(0, 3, 1, 2)
+    s = dx.sum(dim=(0, 2, 3)).double().cpu().numpy()
+    a = dx.abs().sum(dim=(0, 2, 3)).double().cpu().numpy()
+    tol = 1e-4 if wl.dtype == "f32" else 2e-2
+    assert np.all(np.abs(s) <= tol * a + 1e-30), np.max(np.abs(s) / a)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+
+EDGE = [
+    custom(2, 2, 5, 1, 1),                                  # m = 2, the minimum
+    custom(2, 1, 1, 300, 301),                               # one channel, long reduction
+    custom(3, 2, 4104, 3, 3, dtype="bf16"),                  # many channels, short rows (NHWC)
+    custom(2, 2, 4104, 3, 3, layout="NHWC"),                 # fp32 NHWC many channels
+    custom(2, 3, 7, 8, 8, eps=0.0),                          # eps = 0
+    custom(4, 3, 7, 9, 9, act_param=0.5),                    # ELU alpha != 1
+    custom(2, 3, 7, 9, 9, act_param=1.0),                    # leaky slope 1 = identity
+    custom(2, 3, 7, 9, 9, act_param=0.3, momentum=0.0),      # momentum 0
+    custom(2, 3, 7, 9, 9, momentum=1.0),                     # momentum 1
+    custom(2, 64, 3, 1, 1),                                  # tiny planes, many channels
+    custom(5, 3, 8, 1, 1),                                   # NHWC with m = 3 rows
+]
+
+
+@pytest.mark.parametrize("wl", EDGE, ids=lambda w: w.name)
+def test_edge_cases(wl):
+    full_check(wl)
+
+
+def test_constant_channel():
+    wl = custom(2, 2, 3, 4, 4)
+    inp = workloads.make_inputs(wl)
+    inp.x[:, 1] = np.float32(2.5)        # variance 0 in channel 1: xhat = 0, y = act(beta)
+    run = harness.run_gpu(inp)
+    harness.assert_within(harness.check_forward(inp, run), "f32", "forward")
+    harness.assert_within(harness.check_backward(inp, run), "f32", "backward")
+
+
+@pytest.mark.parametrize("layout,dtype", [("NCHW", "f32"), ("NHWC", "bf16"), ("NCHW", "bf16"),
+                                          ("NHWC", "f32")])
+def test_misaligned_pointers_take_scalar_path(layout, dtype):
+    """Tensors one element off 16-byte alignment: same results within tolerance."""
+    wl = custom(2 if dtype == "f32" else 3, 2, 16, 8, 8, layout=layout, dtype=dtype)
+    inp = workloads.make_inputs(wl)
+    n = wl.numel
+    tdt = workloads.storage_torch_dtype(dtype)
+    bx = torch.empty(n + 1, dtype=tdt, device="cuda")
+    bdy = torch.empty(n + 1, dtype=tdt, device="cuda")
+    bdx = torch.empty(n + 1, dtype=tdt, device="cuda")
+    x = bx[1:]
+    x.copy_(workloads.to_torch(inp.x, dtype).reshape(-1))
+    dy = bdy[1:]
+    dy.copy_(workloads.to_torch(inp.dy, dtype).reshape(-1))
+    dx = bdx[1:]
+    assert x.data_ptr() % 16 != 0
+    C = wl.C
+    g = torch.from_numpy(inp.gamma).cuda()
+    b = torch.from_numpy(inp.beta).cuda()
+    sm, si = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    dg, db = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    ws = iabn.workspace(wl.N, C, wl.H, wl.W, layout, tdt)
+    iabn.iabn_forward_train(x, wl.N, C, wl.H, wl.W, layout, g, b, None, None, sm, si, wl.act,
+                            wl.act_param, wl.eps, wl.momentum, ws)
+    iabn.iabn_backward(x, dy, dx, wl.N, C, wl.H, wl.W, layout, g, b, si, dg, db, wl.act,
+                       wl.act_param, ws)
+    torch.cuda.synchronize()
+    run = harness.GpuRun(y=x.reshape(harness.storage_shape(wl)),
+                         dx=dx.reshape(harness.storage_shape(wl)), save_mean=sm.cpu().numpy(),
+                         save_invstd=si.cpu().numpy(), running_mean=inp.running_mean,
+                         running_var=inp.running_var, dgamma=dg.cpu().numpy(),
+                         dbeta=db.cpu().numpy())
+    ef = harness.check_forward(inp, run)
+    ef.pop("running_mean")
+    ef.pop("running_var")
+    harness.assert_within(ef, dtype, "forward")
+    harness.assert_within(harness.check_backward(inp, run), dtype, "backward")
+
+
+# ---------------------------------------------------------------------------
+# determinism, aliasing, stage entry points, inference
+
+@pytest.mark.parametrize("wl", [custom(2, 8, 32, 28, 28), custom(3, 4, 64, 32, 32),
+                                custom(4, 4, 32, 14, 14), custom(5, 8, 512, 7, 7)],
+                         ids=lambda w: w.name)
+def test_bitwise_deterministic(wl):
+    inp = workloads.make_inputs(wl)
+    runs = [harness.run_gpu(inp) for _ in range(3)]
+    for r in runs[1:]:
+        assert torch.equal(r.y, runs[0].y)
+        assert torch.equal(r.dx, runs[0].dx)
+        for k in ("save_mean", "save_invstd", "running_mean", "running_var", "dgamma", "dbeta"):
+            assert np.array_equal(getattr(r, k), getattr(runs[0], k)), k
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_dx_in_place_over_dy(idx):
+    wl = workloads.config(idx).with_shape(4, 64, 16, 16)
+    inp = workloads.make_inputs(wl)
+    a = harness.run_gpu(inp)
+    b = harness.run_gpu(inp, dx_over_dy=True)
+    assert torch.equal(a.dx, b.dx)
+    assert np.array_equal(a.dgamma, b.dgamma) and np.array_equal(a.dbeta, b.dbeta)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_stage_entry_points_match_fused_calls(idx):
+    wl = workloads.config(idx).with_shape(4, 32 if idx != 5 else 256, 12, 12)
+    inp = workloads.make_inputs(wl)
+    ref = harness.run_gpu(inp)
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+    x = harness.to_device(inp.x, wl)
+    dy = harness.to_device(inp.dy, wl)
+    g = torch.from_numpy(inp.gamma).cuda()
+    b = torch.from_numpy(inp.beta).cuda()
+    rm = torch.from_numpy(inp.running_mean).cuda()
+    rv = torch.from_numpy(inp.running_var).cuda()
+    sm, si = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    dg, db = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    dx = torch.empty_like(dy)
+    ws = iabn.workspace(N, C, H, W, wl.layout, x.dtype)
+    x0 = x.clone()
+    iabn.iabn_forward_stats(x, N, C, H, W, wl.layout, g, b, rm, rv, sm, si, wl.eps, wl.momentum,
+                            ws)
+    torch.cuda.synchronize()
+    assert torch.equal(x, x0)            # the statistics stage does not write x
+    iabn.iabn_forward_apply(x, N, C, H, W, wl.layout, wl.act, wl.act_param, ws)
+    y0 = x.clone()
+    iabn.iabn_backward_reduce(x, dy, N, C, H, W, wl.layout, g, b, si, dg, db, wl.act,
+                              wl.act_param, ws)
+    iabn.iabn_backward_apply(x, dy, dx, N, C, H, W, wl.layout, wl.act, wl.act_param, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(x, ref.y)
+    assert torch.equal(x, y0)            # the backward never writes y
+    assert torch.equal(dx, ref.dx)
+    assert np.array_equal(sm.cpu().numpy(), ref.save_mean)
+    assert np.array_equal(si.cpu().numpy(), ref.save_invstd)
+    assert np.array_equal(rm.cpu().numpy(), ref.running_mean)
+    assert np.array_equal(dg.cpu().numpy(), ref.dgamma)
+    assert np.array_equal(db.cpu().numpy(), ref.dbeta)
+
+
+def test_backward_uses_only_y():
+    """The same y bits in a fresh buffer (x long gone) give the same gradients."""
+    wl = workloads.config(4).with_shape(4, 16, 10, 10)
+    inp = workloads.make_inputs(wl)
+    ref = harness.run_gpu(inp)
+    y2 = ref.y.clone()
+    dy = harness.to_device(inp.dy, wl)
+    dx = torch.empty_like(dy)
+    C = wl.C
+    g = torch.from_numpy(inp.gamma).cuda()
+    b = torch.from_numpy(inp.beta).cuda()
+    si = torch.from_numpy(ref.save_invstd).cuda()
+    dg, db = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    ws = iabn.workspace(wl.N, C, wl.H, wl.W, wl.layout, y2.dtype)
+    ws.fill_(0xAB)                        # workspace contents on entry do not matter
+    iabn.iabn_backward(y2, dy, dx, wl.N, C, wl.H, wl.W, wl.layout, g, b, si, dg, db, wl.act,
+                       wl.act_param, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, ref.dx)
+    assert np.array_equal(dg.cpu().numpy(), ref.dgamma)
+
+
+EVAL = [custom(2, 3, 8, 9, 9), custom(3, 2, 24, 6, 6), custom(4, 3, 8, 5, 5),
+        custom(5, 2, 40, 3, 3), custom(2, 3, 7, 5, 3, layout="NHWC", act="elu", act_param=0.7),
+        custom(3, 2, 13, 4, 5, dtype="bf16")]
+
+
+@pytest.mark.parametrize("wl", EVAL, ids=lambda w: w.name)
+def test_forward_eval(wl):
+    inp = workloads.make_inputs(wl)
+    rng = np.random.default_rng(1)
+    rm = rng.normal(0, 1, wl.C).astype(np.float32)
+    rv = rng.uniform(0.3, 2.0, wl.C).astype(np.float32)
+    x = harness.to_device(inp.x, wl)
+    iabn.iabn_forward_eval(x, wl.N, wl.C, wl.H, wl.W, wl.layout, torch.from_numpy(inp.gamma).cuda(),
+                           torch.from_numpy(inp.beta).cuda(), torch.from_numpy(rm).cuda(),
+                           torch.from_numpy(rv).cuda(), wl.act, wl.act_param, wl.eps)
+    torch.cuda.synchronize()
+    xf = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    o = oracle.forward_eval(xf, inp.gamma, inp.beta, rm, rv, wl.act, harness.f32(wl.act_param),
+                            harness.f32(wl.eps), storage=wl.dtype)
+    e = harness.rel_err_tensor(harness.to_nchw64(x, wl), o)
+    assert e <= harness.TOL[wl.dtype], e
+
+
+def test_running_stats_are_optional():
+    wl = custom(2, 4, 8, 6, 6)
+    inp = workloads.make_inputs(wl)
+    x = harness.to_device(inp.x, wl)
+    C = wl.C
+    sm, si = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    ws = iabn.workspace(wl.N, C, wl.H, wl.W, wl.layout, x.dtype)
+    iabn.iabn_forward_train(x, wl.N, C, wl.H, wl.W, wl.layout,
+                            torch.from_numpy(inp.gamma).cuda(), torch.from_numpy(inp.beta).cuda(),
+                            None, None, sm, si, wl.act, wl.act_param, wl.eps, wl.momentum, ws)
+    torch.cuda.synchronize()
+    ref = harness.run_gpu(inp, backward=False)
+    assert torch.equal(x, ref.y)
+    assert np.array_equal(si.cpu().numpy(), ref.save_invstd)
+
+
+def test_errors_raise_in_python():
+    wl = custom(2, 2, 4, 4, 4)
+    x = torch.zeros(harness.storage_shape(wl), device="cuda")
+    C = wl.C
+    v = torch.ones(C, device="cuda")
+    with pytest.raises(iabn.IABNError):
+        iabn.iabn_forward_train(x, wl.N, C, wl.H, wl.W, "NCHW", v, v, None, None, v.clone(),
+                                v.clone(), "leaky_relu", 0.01, 1e-5, 0.1, None)
