@@ -1,0 +1,235 @@
+"""Benchmark of the In-Place ABN hot path on one MI355X.
+
+One step = one training forward (statistics + normalise/activate in place) and
+one backward (reductions from y + dx) over one batch of synthetic input already
+resident in HBM, all through the C ABI.
+
+  python bench.py [--steps K] [--warmup W] [--config I] [--gpus 1] [--no-cpu]
+
+Prints ONE JSON line.  value = numel / time-per-step (Gelem/s), measured "cold":
+consecutive steps rotate over buffer sets totalling >= 512 MB, more than the
+256 MB Infinity Cache, so every step reads its tensors from HBM.  The same loop
+on one buffer set is reported as "warm".  Pass-model bytes per step are 8*S
+(S = tensor bytes): forward reads x twice and writes y; backward reads y and dy
+twice and writes dx.
+
+The roofline object is for the dominant kernel (the longest average duration),
+timed with HIP events recorded on the stream the library launches on (torch's
+current stream) around each stage in a second timed loop.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD public figure
+METRIC = "InPlace-ABN fwd+bwd Gelem/s and achieved HBM GB/s (% of MI355X peak)"
+COLD_BYTES = 512 << 20
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("device.hpp", "plan.hpp", "fwd.hip", "bwd.hip"):
+        with open(os.path.join(ROOT, "place_batchnorm_activation_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        table = json.load(fh)
+    ent = table.get("%s@%s" % (kernel, workload))
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp) -> dict:
+    """The fp64 oracle, as it stands, on the host cores: forward + from-y backward."""
+    import oracle
+    import workloads
+    x = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    dy = workloads.from_storage(inp.dy, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    # bounded sample: whole channels, enough for ~10 s of oracle work
+    per_elem_guess = 4e-8 / max(1, oracle.num_threads())
+    ch = int(min(wl.C, max(1, 10.0 / (per_elem_guess * wl.m) / 3)))
+    xs, dys = np.ascontiguousarray(x[:, :ch]), np.ascontiguousarray(dy[:, :ch])
+    g, b = inp.gamma[:ch], inp.beta[:ch]
+    times = []
+    reps = 3
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        f = oracle.forward_train(xs, g, b, wl.act, wl.act_param, wl.eps, wl.momentum,
+                                 inp.running_mean[:ch], inp.running_var[:ch], storage=wl.dtype)
+        oracle.backward_from_y(f["y"], dys, g, b, f["invstd"], wl.act, wl.act_param)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    n = ch * wl.m
+    return {"value": round(n / t / 1e9, 5), "unit": "Gelem/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d channels (all %d elements each) of the same workload, fp64 "
+                      "forward_train + backward_from_y, median of %d runs (%.2f s each)"
+                      % (ch, wl.C, wl.m, reps, t)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload index 1..5 (default 2)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--warm-only", action="store_true", help="one buffer set (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import place_batchnorm_activation_amd as iabn
+    import workloads
+
+    wl = workloads.config(args.config)
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+    inp = workloads.make_inputs(wl)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sshape = (N, C, H, W) if wl.layout == "NCHW" else (N, H, W, C)
+    S = wl.storage_bytes
+    nsets = 1 if args.warm_only else max(2, math.ceil(COLD_BYTES / (3 * S)))
+
+    x0 = workloads.to_torch(inp.x, wl.dtype).reshape(sshape).to(dev)
+    dy0 = workloads.to_torch(inp.dy, wl.dtype).reshape(sshape).to(dev)
+    sets = []
+    for _ in range(nsets):
+        sets.append({"x": x0.clone(), "dy": dy0.clone(), "dx": torch.empty_like(dy0)})
+    warm_set = sets[0]
+    g = torch.from_numpy(inp.gamma).to(dev)
+    b = torch.from_numpy(inp.beta).to(dev)
+    rm = torch.from_numpy(inp.running_mean).to(dev)
+    rv = torch.from_numpy(inp.running_var).to(dev)
+    sm, si = torch.empty(C, device=dev), torch.empty(C, device=dev)
+    dg, db = torch.empty(C, device=dev), torch.empty(C, device=dev)
+    ws = iabn.workspace(N, C, H, W, wl.layout, x0.dtype, dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def stages(s):
+        return [
+            lambda: iabn.iabn_forward_stats(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, sm, si,
+                                            wl.eps, wl.momentum, ws, sp),
+            lambda: iabn.iabn_forward_apply(s["x"], N, C, H, W, wl.layout, wl.act, wl.act_param,
+                                            ws, sp),
+            lambda: iabn.iabn_backward_reduce(s["x"], s["dy"], N, C, H, W, wl.layout, g, b, si,
+                                              dg, db, wl.act, wl.act_param, ws, sp),
+            lambda: iabn.iabn_backward_apply(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout,
+                                             wl.act, wl.act_param, ws, sp),
+        ]
+
+    def step(s):
+        iabn.iabn_forward_train(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, sm, si, wl.act,
+                                wl.act_param, wl.eps, wl.momentum, ws, sp)
+        iabn.iabn_backward(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout, g, b, si, dg, db,
+                           wl.act, wl.act_param, ws, sp)
+
+    def timed(set_list, k):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(k):
+            step(set_list[i % len(set_list)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k        # ms per step
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    print("bench: %s warmup done, %d buffer set(s)" % (wl.name, nsets), file=sys.stderr, flush=True)
+
+    ms_cold = timed(sets, args.steps)
+    ms_warm = timed([warm_set], args.steps)
+
+    # per-stage durations: HIP events on the library's stream around each stage
+    names = ["forward_stats", "forward_apply", "backward_reduce", "backward_apply"]
+    acc = np.zeros(4)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        st = stages(sets[i % nsets])
+        evs[i][0].record(stream)
+        for j, fn in enumerate(st):
+            fn()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for j in range(4):
+            acc[j] += evs[i][j].elapsed_time(evs[i][j + 1])
+    stage_us = {n: round(1e3 * a / args.steps, 3) for n, a in zip(names, acc)}
+    print("bench: stages (us) %s" % stage_us, file=sys.stderr, flush=True)
+
+    # algorithmic bytes per launch of each single-kernel stage
+    stage_bytes = {"forward_apply": 2 * S, "backward_apply": 3 * S}
+    kernel_names = {"forward_apply": "fwd_apply", "backward_apply": "bwd_apply"}
+    dom = max(stage_bytes, key=lambda n: stage_us[n])
+    t_dom = stage_us[dom] * 1e-6
+    achieved = stage_bytes[dom] / t_dom / 1e9
+    traffic = load_traffic(kernel_names[dom], wl.name)
+
+    numel = wl.numel
+    t = ms_cold * 1e-3
+    gbps = 8 * S / t / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(numel / t / 1e9, 4),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_cold, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "N": N, "C": C, "H": H, "W": W, "layout": wl.layout,
+                   "storage": wl.dtype, "act": wl.act, "act_param": wl.act_param,
+                   "parallelism": "single_gpu"},
+        "pass_model_GBps": round(gbps, 1),
+        "pass_model_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "protocol": "cold: %d rotating buffer sets of %.0f MB" % (nsets, 3 * S / 1e6),
+        "warm": {"ms_per_step": round(ms_warm, 5),
+                 "value": round(numel / (ms_warm * 1e-3) / 1e9, 4),
+                 "pass_model_GBps": round(8 * S / (ms_warm * 1e-3) / 1e9, 1)},
+        "stage_us": stage_us,
+        "roofline": {"kernel": kernel_names[dom], "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": stage_bytes[dom],
+                     "avg_launch_us": stage_us[dom]},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

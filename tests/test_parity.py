@@ -34,7 +34,9 @@ def full_check(wl, seed=None, channels=None, dx_over_dy=False):
     print("case:", wl.name, wl.layout, wl.dtype, wl.act, wl.act_param, flush=True)
     run = harness.run_gpu(inp, dx_over_dy=dx_over_dy)
     ef = harness.check_forward(inp, run, channels)
-    eb = harness.check_backward(inp, run, channels)
+    # m = 2: dx is the eps/var-sized remainder of a cancellation (xhat = +-sqrt(v/(v+eps)));
+    # its error is gated against the size of the cancelled terms instead
+    eb = harness.check_backward(inp, run, channels, dx_scale="terms" if wl.m == 2 else "rms")
     print("  forward", ef, "\n  backward", eb, flush=True)
     harness.assert_within(ef, wl.dtype, "forward " + wl.name)
     harness.assert_within(eb, wl.dtype, "backward " + wl.name)
