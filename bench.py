@@ -15,7 +15,10 @@ twice and writes dx.
 
 The roofline object is for the dominant kernel (the longest average duration),
 timed with HIP events recorded on the stream the library launches on (torch's
-current stream) around each stage in a second timed loop.
+current stream) around each single-kernel call in further timed loops over the
+same buffer sets.  Its algorithmic bytes are the pass-model bytes of the work it
+does: 3S for a whole forward, 5S for a whole backward, 2S / 3S for the split
+path's forward / backward elementwise kernels.
 """
 from __future__ import annotations
 
@@ -39,7 +42,7 @@ COLD_BYTES = 512 << 20
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("device.hpp", "plan.hpp", "fwd.hip", "bwd.hip"):
+    for f in ("device.hpp", "plan.hpp", "fused.hpp", "fwd.hip", "bwd.hip", "fused_nchw.hip"):
         with open(os.path.join(ROOT, "place_batchnorm_activation_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -166,31 +169,60 @@ def main() -> int:
     ms_cold = timed(sets, args.steps)
     ms_warm = timed([warm_set], args.steps)
 
-    # per-stage durations: HIP events on the library's stream around each stage
-    names = ["forward_stats", "forward_apply", "backward_reduce", "backward_apply"]
-    acc = np.zeros(4)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        st = stages(sets[i % nsets])
-        evs[i][0].record(stream)
-        for j, fn in enumerate(st):
-            fn()
-            evs[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        for j in range(4):
-            acc[j] += evs[i][j].elapsed_time(evs[i][j + 1])
-    stage_us = {n: round(1e3 * a / args.steps, 3) for n, a in zip(names, acc)}
-    print("bench: stages (us) %s" % stage_us, file=sys.stderr, flush=True)
+    # Per-launch durations: HIP events recorded on the library's stream (torch's
+    # current stream) around each call.  With the channel-resident path each of
+    # iabn_forward_train / iabn_backward is one kernel; with the split path the
+    # single-kernel stages (apply) are timed through the stage entry points.
+    plan = iabn.iabn_describe_plan(N, C, H, W, wl.layout, x0.dtype, wl.act)
+    fused_fwd = plan.split()[0].startswith("forward=channel_resident")
+    fused_bwd = plan.split()[1].startswith("backward=channel_resident")
 
-    # algorithmic bytes per launch of each single-kernel stage
-    stage_bytes = {"forward_apply": 2 * S, "backward_apply": 3 * S}
-    kernel_names = {"forward_apply": "fwd_apply", "backward_apply": "bwd_apply"}
-    dom = max(stage_bytes, key=lambda n: stage_us[n])
-    t_dom = stage_us[dom] * 1e-6
-    achieved = stage_bytes[dom] / t_dom / 1e9
-    traffic = load_traffic(kernel_names[dom], wl.name)
+    def event_loop(calls):
+        acc = np.zeros(len(calls))
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            st = sets[i % nsets]
+            evs[i][0].record(stream)
+            for j, fn in enumerate(calls):
+                fn(st)
+                evs[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            for j in range(len(calls)):
+                acc[j] += evs[i][j].elapsed_time(evs[i][j + 1])
+        return [1e3 * a / args.steps for a in acc]
+
+    call_us = event_loop([
+        lambda s: iabn.iabn_forward_train(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, sm, si,
+                                          wl.act, wl.act_param, wl.eps, wl.momentum, ws, sp),
+        lambda s: iabn.iabn_backward(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout, g, b, si,
+                                     dg, db, wl.act, wl.act_param, ws, sp)])
+    timings = {"forward_train": round(call_us[0], 3), "backward": round(call_us[1], 3)}
+    # single kernels and their pass-model bytes: forward 3S, backward 5S, the split
+    # path's apply kernels 2S and 3S
+    kernels = {}
+    if fused_fwd:
+        kernels["fwd_channel_resident"] = (call_us[0], 3 * S)
+    if fused_bwd:
+        kernels["bwd_channel_resident"] = (call_us[1], 5 * S)
+    if not (fused_fwd and fused_bwd):
+        names = ["forward_stats", "forward_apply", "backward_reduce", "backward_apply"]
+        st_us = event_loop([(lambda s, f=f: f(s)) for f in (lambda s: stages(s)[0](),
+                                                            lambda s: stages(s)[1](),
+                                                            lambda s: stages(s)[2](),
+                                                            lambda s: stages(s)[3]())])
+        timings.update({n: round(u, 3) for n, u in zip(names, st_us)})
+        if not fused_fwd:
+            kernels["fwd_apply"] = (st_us[1], 2 * S)
+        if not fused_bwd:
+            kernels["bwd_apply"] = (st_us[3], 3 * S)
+    print("bench: %s; per-call us %s" % (plan, timings), file=sys.stderr, flush=True)
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    t_dom_us, dom_bytes = kernels[dom]
+    achieved = dom_bytes / (t_dom_us * 1e-6) / 1e9
+    traffic = load_traffic(dom, wl.name)
 
     numel = wl.numel
     t = ms_cold * 1e-3
@@ -217,13 +249,14 @@ def main() -> int:
         "warm": {"ms_per_step": round(ms_warm, 5),
                  "value": round(numel / (ms_warm * 1e-3) / 1e9, 4),
                  "pass_model_GBps": round(8 * S / (ms_warm * 1e-3) / 1e9, 1)},
-        "stage_us": stage_us,
-        "roofline": {"kernel": kernel_names[dom], "bound": "hbm",
+        "plan": plan,
+        "launch_us": timings,
+        "roofline": {"kernel": dom, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": stage_bytes[dom],
-                     "avg_launch_us": stage_us[dom]},
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(t_dom_us, 3)},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, inp)

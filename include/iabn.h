@@ -184,6 +184,17 @@ iabn_status iabn_backward_apply(const void *y, const void *dy, void *dx,
                                 void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* Describes, as a short text, the kernels that iabn_forward_train and
+ * iabn_backward launch for this problem when every tensor pointer is 16-byte
+ * aligned (aligned16 != 0) or not, e.g.
+ *   "forward=channel_resident(512x49) backward=channel_resident(512x49,dy_streamed)".
+ * For logging, benchmarks and tests; it launches nothing.  Writes at most
+ * `len` bytes including the terminating NUL into `buf` and returns the length
+ * of the full description (like snprintf), or -1 for invalid arguments. */
+int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W,
+                       iabn_layout layout, iabn_dtype dtype, iabn_act act,
+                       int aligned16, char *buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,8 @@ lib.iabn_backward.argtypes = [_P, _P, _P] + _SHAPE + [_P, _P, _P, _P, _P, _INT, 
 lib.iabn_backward_reduce.argtypes = [_P, _P] + _SHAPE + [_P, _P, _P, _P, _P, _INT, _F, _P, _SZ,
                                                          _P]
 lib.iabn_backward_apply.argtypes = [_P, _P, _P] + _SHAPE + [_INT, _F, _P, _SZ, _P]
+lib.iabn_describe_plan.argtypes = _SHAPE + [_INT, _INT, ctypes.c_char_p, _SZ]
+lib.iabn_describe_plan.restype = _INT
 for _fn in ("iabn_forward_train", "iabn_forward_stats", "iabn_forward_apply", "iabn_forward_eval",
             "iabn_backward", "iabn_backward_reduce", "iabn_backward_apply"):
     getattr(lib, _fn).restype = _INT
@@ -185,6 +187,18 @@ def iabn_backward_apply(y, dy, dx, N, C, H, W, layout, act, act_param, workspace
     _check("iabn_backward_apply", lib.iabn_backward_apply(
         _ptr(y), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y),
         _code(act, ACTS), act_param, wp, wb, _stream(stream)))
+
+
+def iabn_describe_plan(N, C, H, W, layout, dtype, act, aligned16=True) -> str:
+    """Which kernels iabn_forward_train / iabn_backward launch for this problem."""
+    if isinstance(dtype, torch.dtype):
+        dtype = F32 if dtype == torch.float32 else BF16
+    buf = ctypes.create_string_buffer(256)
+    n = lib.iabn_describe_plan(N, C, H, W, _code(layout, LAYOUTS), dtype, _code(act, ACTS),
+                               1 if aligned16 else 0, buf, 256)
+    if n < 0:
+        raise ValueError("invalid problem description")
+    return buf.value.decode()
 
 
 def shape_of(t: torch.Tensor, layout) -> tuple:

@@ -2,10 +2,12 @@
 // plan selection, and launches on the caller's stream.  Declared in iabn.h.
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <hip/hip_runtime_api.h>
 
+#include "fused.hpp"
 #include "iabn.h"
 #include "launch.hpp"
 #include "plan.hpp"
@@ -52,11 +54,24 @@ iabn_status check_tensor(const void* p, iabn_dtype dtype)
     return aligned(p, dtype == IABN_F32 ? 4 : 2) ? IABN_OK : IABN_ERR_MISALIGNED;
 }
 
+// act < 0: the stage entry points, which always run the split kernels.
 Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
-              bool ptrs16)
+              bool ptrs16, int act = -1)
 {
     const bool vec = ptrs16 && vec_shape_ok(C, H * W, layout, dtype);
-    return make_plan(N, C, H, W, layout, dtype, vec);
+    Plan p = make_plan(N, C, H, W, layout, dtype, vec);
+    if (act >= 0 && p.layout == kNCHW && p.vec && p.numel > 0) {
+        const int64_t vc = p.m / p.V;
+        const int f = fused_fwd_pick(vc);
+        if (f >= 0 && fused_worthwhile(p, fused_fwd_threads(f)) &&
+            !(act == kElu && f > kEluMaxFwdVariant))
+            p.fused_variant = f;
+        const int b = fused_bwd_pick(vc);
+        if (b >= 0 && fused_worthwhile(p, fused_bwd_threads(b)) &&
+            !(act == kElu && b > kEluMaxBwdVariant))
+            p.fused_bwd_variant = b;
+    }
+    return p;
 }
 
 size_t workspace_bytes_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
@@ -201,8 +216,13 @@ iabn_status iabn_forward_train(void* x_inout, int64_t N, int64_t C, int64_t H, i
     IABN_TRY(check_forward_train(x_inout, N, C, H, W, layout, dtype, gamma, beta, running_mean,
                                  running_var, save_mean, save_invstd, eps, momentum));
     if (C == 0) return IABN_OK;
-    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(x_inout, 16));
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(x_inout, 16), act);
     IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
+    if (pl.fused_variant >= 0) {
+        launch_forward_fused_nchw(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
+                                  save_invstd, eps, momentum, act, act_param, stream);
+        return launched();
+    }
     launch_forward_stats(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
                          save_invstd, eps, momentum, workspace, stream);
     launch_forward_apply(pl, x_inout, act, act_param, workspace, stream);
@@ -284,13 +304,58 @@ iabn_status iabn_backward(const void* y, const void* dy, void* dx, int64_t N, in
     IABN_TRY(check_channel_vec(dbeta, true));
     const Plan pr = plan_for(N, C, H, W, layout, dtype, aligned(y, 16) && aligned(dy, 16));
     const Plan pa = plan_for(N, C, H, W, layout, dtype,
-                             aligned(y, 16) && aligned(dy, 16) && aligned(dx, 16));
+                             aligned(y, 16) && aligned(dy, 16) && aligned(dx, 16), act);
     IABN_TRY(check_workspace(workspace, workspace_bytes, pr));
     IABN_TRY(check_workspace(workspace, workspace_bytes, pa));
+    if (pa.fused_bwd_variant >= 0) {
+        launch_backward_fused_nchw(pa, y, dy, dx, gamma, beta, save_invstd, dgamma, dbeta, act,
+                                   act_param, stream);
+        return launched();
+    }
     launch_backward_reduce(pr, y, dy, gamma, beta, save_invstd, dgamma, dbeta, act, act_param,
                            workspace, stream);
     launch_backward_apply(pa, y, dy, dx, act, act_param, workspace, stream);
     return launched();
+}
+
+int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
+                       iabn_dtype dtype, iabn_act act, int aligned16, char* buf, size_t len)
+{
+    if (check_shape(N, C, H, W, layout, dtype) != IABN_OK) return -1;
+    if (act != IABN_ACT_IDENTITY && act != IABN_ACT_LEAKY_RELU && act != IABN_ACT_ELU) return -1;
+    const Plan p = plan_for(N, C, H, W, layout, dtype, aligned16 != 0, act);
+    char fwd[96], bwd[96];
+    if (p.fused_variant >= 0) {
+        int T = 0, NR = 0;
+        switch (p.fused_variant) {
+#define IABN_ROW(ID, T_, NR_) case ID: T = T_; NR = NR_; break;
+            IABN_FUSED_FWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+        default: break;
+        }
+        snprintf(fwd, sizeof fwd, "channel_resident(%dx%d)", T, NR);
+    } else {
+        snprintf(fwd, sizeof fwd, "split(stats:%lldx%d,apply:%lldx%d,%s)",
+                 (long long)p.reduce_blocks, kThreads, (long long)p.apply_blocks, kThreads,
+                 p.vec ? "vec16" : "scalar");
+    }
+    if (p.fused_bwd_variant >= 0) {
+        int T = 0, NR = 0;
+        bool dyr = false;
+        switch (p.fused_bwd_variant) {
+#define IABN_ROW(ID, T_, NR_, DYR_) case ID: T = T_; NR = NR_; dyr = DYR_; break;
+            IABN_FUSED_BWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+        default: break;
+        }
+        snprintf(bwd, sizeof bwd, "channel_resident(%dx%d,%s)", T, NR,
+                 dyr ? "dy_resident" : "dy_streamed");
+    } else {
+        snprintf(bwd, sizeof bwd, "split(reduce:%lldx%d,apply:%lldx%d,%s)",
+                 (long long)p.reduce_blocks, kThreads, (long long)p.apply_blocks, kThreads,
+                 p.vec ? "vec16" : "scalar");
+    }
+    return snprintf(buf, len, "forward=%s backward=%s", fwd, bwd);
 }
 
 }  // extern "C"

@@ -184,6 +184,29 @@ struct ChannelWalk {
     }
 };
 
+// ChannelWalk in 32-bit vector offsets (tensors under 2^28 vectors, 4 GiB).
+struct ChannelWalk32 {
+    uint32_t off, o, hwv, d_off, d_carry, r;
+    __host__ __device__ __forceinline__ void init(uint32_t j, uint32_t c, uint32_t C, uint32_t HWv,
+                                                  uint32_t stride)
+    {
+        const uint32_t n = j / HWv;
+        o = j - n * HWv;
+        hwv = HWv;
+        off = (n * C + c) * HWv + o;
+        const uint32_t q = stride / HWv;
+        r = stride - q * HWv;
+        d_off = q * C * HWv + r;
+        d_carry = C * HWv - HWv;
+    }
+    __host__ __device__ __forceinline__ void step()
+    {
+        o += r;
+        off += d_off;
+        if (o >= hwv) { o -= hwv; off += d_carry; }
+    }
+};
+
 // Walk of a flat NCHW tensor: vector v has channel ((v / HWv) % C).  Advancing v
 // by a fixed stride updates the in-plane offset and the channel with carries.
 struct FlatNCHWWalk {

@@ -1,0 +1,375 @@
+// Channel-resident NCHW kernels: one workgroup owns one channel and keeps its
+// data in VGPRs between the reduction and the elementwise pass, so there are no
+// partials, no finishing launch and no second read of the same bytes.
+//
+// Forward (section 3 of the paperlayer summary of "In-Place Activated BatchNorm
+// for Memory-Optimized Training of DNNs", "Batch Normalization Review" and
+// "INPLACE-ABN"): load the channel, pivot-shifted sums -> Chan merge across the
+// workgroup -> statistics in fp64 -> y = act(((x - K) - d)*s + beta) from the
+// registers, written over x.  HBM traffic: read S, write S.
+//
+// Backward ("INPLACE-ABN" I/II, Appendix): y (and dy when it fits) stay
+// resident; sums of dz and dz*(z - beta) -> per-channel constants -> dx.  When
+// dy does not fit it is streamed twice.  HBM traffic: 3S, or 4S with dy
+// streamed.
+//
+// Thread t of the workgroup owns the channel's 16-byte vectors j = t + k*T,
+// k < NR.  Addresses are 32-bit byte offsets from the uniform tensor base (the
+// plan only picks these kernels for tensors under 4 GiB), one VGPR per vector.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "fused.hpp"
+
+namespace iabn {
+
+template <int DT>
+struct Vec16 { static constexpr int V = DT == kF32 ? 4 : 8; };
+
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4& q, float (&v)[Vec16<DT>::V])
+{
+    if constexpr (DT == kF32) {
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+    } else {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 pack(const float (&v)[Vec16<DT>::V])
+{
+    if constexpr (DT == kF32) {
+        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3]));
+    } else {
+        return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+}
+
+__device__ __forceinline__ uint4 ld16(const void* base, uint32_t off)
+{
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + (off << 4));
+}
+
+__device__ __forceinline__ void st16(void* base, uint32_t off, const uint4& q)
+{
+    *reinterpret_cast<uint4*>(static_cast<char*>(base) + (off << 4)) = q;
+}
+
+// A copy of v the compiler cannot see through: the second pass recomputes its
+// addresses instead of keeping the first pass's offsets alive in VGPRs.
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ float opaquef(float v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Same for a resident vector: its unpacked / transformed values are recomputed in
+// the second pass rather than kept from the first.
+__device__ __forceinline__ uint4 opaque4(uint4 q)
+{
+    asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+    return q;
+}
+
+// Streamed loads are issued in groups of kStreamGroup; the compiler may not hoist
+// loads across the group boundary, which bounds the VGPRs they occupy.
+constexpr int kStreamGroup = 4;
+
+__device__ __forceinline__ void group_fence() { asm volatile("" ::: "memory"); }
+
+// Block-wide Chan merge; every thread returns the workgroup's (n, mean, M2).
+template <int T>
+__device__ __forceinline__ void block_chan(float& n, float& mean, float& m2)
+{
+    constexpr int NW = T / kWave;
+    __shared__ float sh[3][NW];
+    wave_chan(n, mean, m2);
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) { sh[0][wave] = n; sh[1][wave] = mean; sh[2][wave] = m2; }
+    __syncthreads();
+    float tn = sh[0][0], tm = sh[1][0], t2 = sh[2][0];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) chan_merge(tn, tm, t2, sh[0][k], sh[1][k], sh[2][k]);
+    n = tn; mean = tm; m2 = t2;
+}
+
+// Block-wide sums in a fixed order; every thread returns the totals.
+template <int T>
+__device__ __forceinline__ void block_sum2(float& a, float& b)
+{
+    constexpr int NW = T / kWave;
+    __shared__ float sh[2][NW];
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) { sh[0][wave] = a; sh[1][wave] = b; }
+    __syncthreads();
+    float ta = sh[0][0], tb = sh[1][0];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) { ta += sh[0][k]; tb += sh[1][k]; }
+    a = ta; b = tb;
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int ACT, int T, int NR>
+__global__ __launch_bounds__(T) void k_fwd_fused_nchw(
+    void* x, uint32_t C, uint32_t HW, uint32_t m, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* __restrict__ running_mean,
+    float* __restrict__ running_var, float* __restrict__ save_mean,
+    float* __restrict__ save_invstd, float eps, float momentum, float a)
+{
+    constexpr int V = Vec16<DT>::V;
+    const uint32_t c = blockIdx.x;
+    const uint32_t t = threadIdx.x;
+    const uint32_t HWv = HW / V;
+    const uint32_t Vc = m / V;
+    const float K = load_one<DT>(x, int64_t(c) * HW);
+
+    uint4 r[NR];
+    ChannelWalk32 w;
+    w.init(t, c, C, HWv, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        r[k] = (t + k * T < Vc) ? ld16(x, w.off) : make_uint4(0, 0, 0, 0);
+        w.step();
+    }
+
+    float s1[V], s2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { s1[e] = 0.f; s2[e] = 0.f; }
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if (t + k * T < Vc) {
+            float v[V];
+            unpack<DT>(r[k], v);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = v[e] - K;
+                s1[e] += d;
+                s2[e] = fmaf(d, d, s2[e]);
+            }
+            ++cnt;
+        }
+    }
+    float S1 = 0.f, S2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) { S1 += s1[e]; S2 += s2[e]; }
+    float n = float(cnt * V);
+    float mean = cnt ? S1 / n : 0.f;
+    float m2 = cnt ? fmaxf(S2 - S1 * mean, 0.f) : 0.f;
+    block_chan<T>(n, mean, m2);
+
+    // statistics in fp64 (every thread computes the same values)
+    const double var = double(m2) / double(m);
+    const double invstd = 1.0 / sqrt(var + double(eps));
+    const float d = float(mean);
+    const float s = float(double(gamma[c]) * invstd);
+    const float b = beta[c];
+    if (t == 0) {
+        const double mu = double(K) + double(mean);
+        save_mean[c] = float(mu);
+        save_invstd[c] = float(invstd);
+        if (running_mean) {
+            const double mom = double(momentum);
+            running_mean[c] = float((1.0 - mom) * double(running_mean[c]) + mom * mu);
+            running_var[c] = float((1.0 - mom) * double(running_var[c])
+                                   + mom * var * double(m) / double(m - 1));
+        }
+    }
+
+    const uint32_t t2 = opaque(t);
+    w.init(t2, c, C, HWv, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if (t2 + k * T < Vc) {
+            float v[V];
+            unpack<DT>(opaque4(r[k]), v);
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K) - d, s, b), a);
+            st16(x, w.off, pack<DT>(v));
+        }
+        w.step();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// DYR: dy resident as well (3S); otherwise dy is streamed twice (4S).
+template <int DT, int ACT, int T, int NR, bool DYR>
+__global__ __launch_bounds__(T) void k_bwd_fused_nchw(
+    const void* __restrict__ y, const void* dy, void* dx, uint32_t C, uint32_t HW, uint32_t m,
+    const float* __restrict__ gamma, const float* __restrict__ beta,
+    const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
+    float a, float inv_a)
+{
+    constexpr int V = Vec16<DT>::V;
+    const uint32_t c = blockIdx.x;
+    const uint32_t t = threadIdx.x;
+    const uint32_t HWv = HW / V;
+    const uint32_t Vc = m / V;
+    const float bc = beta[c];
+
+    uint4 ry[NR];
+    uint4 rd[DYR ? NR : 1];
+    ChannelWalk32 w;
+    w.init(t, c, C, HWv, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const bool ok = t + k * T < Vc;
+        ry[k] = ok ? ld16(y, w.off) : make_uint4(0, 0, 0, 0);
+        if constexpr (DYR) rd[k] = ok ? ld16(dy, w.off) : make_uint4(0, 0, 0, 0);
+        w.step();
+    }
+    float sdz = 0.f, sdzt = 0.f;
+    const uint32_t t1 = opaque(t);
+    if constexpr (!DYR) w.init(t1, c, C, HWv, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if constexpr (!DYR) if (k % kStreamGroup == 0) group_fence();
+        if (t1 + k * T < Vc) {
+            float vy[V], vd[V];
+            unpack<DT>(ry[k], vy);
+            if constexpr (DYR) unpack<DT>(rd[k], vd);
+            else unpack<DT>(ld16(dy, w.off), vd);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float z, slope;
+                act_invert<ACT>(vy[e], a, inv_a, z, slope);
+                const float dz = slope * vd[e];
+                sdz += dz;
+                sdzt = fmaf(dz, z - bc, sdzt);
+            }
+        }
+        if constexpr (!DYR) w.step();
+    }
+    block_sum2<T>(sdz, sdzt);
+
+    const double g = double(gamma[c]);
+    const double db = double(sdz);
+    const double dg = double(sdzt) / g;
+    if (t == 0) {
+        dbeta[c] = float(db);
+        dgamma[c] = float(dg);
+    }
+    const double A = g * double(invstd[c]);
+    const double md = double(m);
+    const float kA = float(A), kB = float(-A * dg / (md * g)), kC = float(-A * db / md);
+
+    const uint32_t t2 = opaque(t);
+    const float a2 = opaquef(a), ia2 = opaquef(inv_a), bc2 = opaquef(bc);
+    w.init(t2, c, C, HWv, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if constexpr (!DYR) if (k % kStreamGroup == 0) group_fence();
+        if (t2 + k * T < Vc) {
+            float vy[V], vd[V];
+            unpack<DT>(opaque4(ry[k]), vy);
+            if constexpr (DYR) unpack<DT>(opaque4(rd[k]), vd);
+            else unpack<DT>(ld16(dy, w.off), vd);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float z, slope;
+                act_invert<ACT>(vy[e], a2, ia2, z, slope);
+                const float dz = slope * vd[e];
+                vd[e] = fmaf(kA, dz, fmaf(kB, z - bc2, kC));
+            }
+            st16(dx, w.off, pack<DT>(vd));
+        }
+        w.step();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+template <int DT, int ACT>
+static void launch_fwd_da(const Plan& pl, void* x, const float* gamma, const float* beta,
+                          float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                          float a, hipStream_t s)
+{
+    const uint32_t C = uint32_t(pl.C), HW = uint32_t(pl.HW), m = uint32_t(pl.m);
+    switch (pl.fused_variant) {
+#define IABN_FWD_CASE(ID, T, NR)                                                                  \
+    case ID:                                                                                      \
+        hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR>), dim3(C), dim3(T), 0, s, x, C, HW, \
+                           m, gamma, beta, rm, rv, sm, si, eps, mom, a);                          \
+        break;
+        IABN_FUSED_FWD_VARIANTS(IABN_FWD_CASE)
+#undef IABN_FWD_CASE
+    default: break;
+    }
+}
+
+void launch_forward_fused_nchw(const Plan& pl, void* x, const float* gamma, const float* beta,
+                               float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                               int act, float a, hipStream_t s)
+{
+    if (pl.dtype == kF32) {
+        switch (act) {
+        case kLeaky: launch_fwd_da<kF32, kLeaky>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
+        case kElu: launch_fwd_da<kF32, kElu>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
+        default: launch_fwd_da<kF32, kIdentity>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
+        }
+    } else {
+        switch (act) {
+        case kLeaky: launch_fwd_da<kBF16, kLeaky>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
+        case kElu: launch_fwd_da<kBF16, kElu>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
+        default: launch_fwd_da<kBF16, kIdentity>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
+        }
+    }
+}
+
+template <int DT, int ACT>
+static void launch_bwd_da(const Plan& pl, const void* y, const void* dy, void* dx,
+                          const float* gamma, const float* beta, const float* invstd,
+                          float* dgamma, float* dbeta, float a, float ia, hipStream_t s)
+{
+    const uint32_t C = uint32_t(pl.C), HW = uint32_t(pl.HW), m = uint32_t(pl.m);
+    switch (pl.fused_bwd_variant) {
+#define IABN_BWD_CASE(ID, T, NR, DYR)                                                            \
+    case ID:                                                                                     \
+        hipLaunchKernelGGL((k_bwd_fused_nchw<DT, ACT, T, NR, DYR>), dim3(C), dim3(T), 0, s, y,  \
+                           dy, dx, C, HW, m, gamma, beta, invstd, dgamma, dbeta, a, ia);         \
+        break;
+        IABN_FUSED_BWD_VARIANTS(IABN_BWD_CASE)
+#undef IABN_BWD_CASE
+    default: break;
+    }
+}
+
+void launch_backward_fused_nchw(const Plan& pl, const void* y, const void* dy, void* dx,
+                                const float* gamma, const float* beta, const float* invstd,
+                                float* dgamma, float* dbeta, int act, float a, hipStream_t s)
+{
+    const float ia = act == kIdentity ? 1.f : 1.f / a;
+    if (pl.dtype == kF32) {
+        switch (act) {
+        case kLeaky: launch_bwd_da<kF32, kLeaky>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
+        case kElu: launch_bwd_da<kF32, kElu>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
+        default: launch_bwd_da<kF32, kIdentity>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
+        }
+    } else {
+        switch (act) {
+        case kLeaky: launch_bwd_da<kBF16, kLeaky>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
+        case kElu: launch_bwd_da<kBF16, kElu>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
+        default: launch_bwd_da<kBF16, kIdentity>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
+        }
+    }
+}
+
+}  // namespace iabn

@@ -42,6 +42,9 @@ struct Plan {
     // elementwise tiling
     int64_t apply_blocks = 0;
     bool fixed_col = false;  // NHWC: each thread keeps one channel group for the whole walk
+    // channel-resident NCHW kernels (-1: not used for this problem)
+    int fused_variant = -1;
+    int fused_bwd_variant = -1;
     // workspace sections (bytes, 256-aligned)
     size_t off_part_a = 0, off_part_b = 0, off_const = 0, bytes = 0;
 };

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "device.hpp"
+#include "fused.hpp"
 #include "plan.hpp"
 
 using namespace iabn;
@@ -127,6 +128,44 @@ static void check_plan(const Shape& s, bool vec)
     for (int64_t i = 0; i < nvec; ++i)
         CHECK(seen[size_t(i)] == 1, "elementwise visits vector %lld %d times", (long long)i,
               int(seen[size_t(i)]));
+
+    // ---- channel-resident NCHW kernels: every variant that could hold the channel
+    if (pl.layout == kNCHW && pl.vec && numel * pl.esize < (int64_t(1) << 32)) {
+        const int64_t HWv = pl.HW / V, Vc = m / V;
+        struct Var { int T, NR; };
+        std::vector<Var> vars;
+#define IABN_ROW(ID, T, NR) vars.push_back({T, NR});
+        IABN_FUSED_FWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+#define IABN_ROW(ID, T, NR, DYR) vars.push_back({T, NR});
+        IABN_FUSED_BWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+        for (const Var& vv : vars) {
+            if (int64_t(vv.T) * vv.NR < Vc) continue;           // the plan never picks it
+            if (nvec > 20000000 && vv.T * vv.NR > 4 * Vc) continue;  // keep big shapes quick
+            std::fill(seen.begin(), seen.end(), 0);
+            for (int64_t c = 0; c < C; ++c)
+                for (int t = 0; t < vv.T; ++t) {
+                    ChannelWalk32 w;
+                    w.init(uint32_t(t), uint32_t(c), uint32_t(C), uint32_t(HWv), uint32_t(vv.T));
+                    for (int k = 0; k < vv.NR; ++k) {
+                        const int64_t j = t + int64_t(k) * vv.T;
+                        if (j < Vc) {
+                            const int64_t direct = ((j / HWv) * C + c) * HWv + j % HWv;
+                            CHECK(int64_t(w.off) == direct, "ChannelWalk32 c=%lld t=%d k=%d",
+                                  (long long)c, t, k);
+                            CHECK(int64_t(w.off) < nvec, "fused bounds");
+                            CHECK((int64_t(w.off) << 4) < (int64_t(1) << 32), "byte offset");
+                            if (int64_t(w.off) < nvec) seen[size_t(w.off)]++;
+                        }
+                        w.step();
+                    }
+                }
+            for (int64_t i = 0; i < nvec; ++i)
+                CHECK(seen[size_t(i)] == 1, "fused T=%d NR=%d visits %lld %d times", vv.T, vv.NR,
+                      (long long)i, int(seen[size_t(i)]));
+        }
+    }
 }
 
 int main(int argc, char** argv)

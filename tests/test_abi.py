@@ -122,3 +122,21 @@ def test_backward_validation():
     assert _bwd(dtype=1, y=A + 1) == MISALIGNED
     assert _bwd(C=0, y=None, dy=None, dx=None, g=None, b=None, si=None, dg=None, db=None,
                 ws=None) == OK
+
+
+def test_plan_choice_for_the_workloads():
+    """Which kernels each workload runs (host-side plan; no GPU needed)."""
+    d = iabn.iabn_describe_plan
+    assert d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu") == \
+        "forward=channel_resident(512x49) backward=channel_resident(512x49,dy_streamed)"
+    assert d(16, 512, 28, 28, "NCHW", iabn.F32, "elu").startswith(
+        "forward=channel_resident(256x13) backward=channel_resident(256x13,dy_resident)")
+    assert d(2, 4, 8, 8, "NCHW", iabn.F32, "leaky_relu").startswith("forward=channel_resident")
+    assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    # misaligned or ragged planes take the scalar split path
+    assert "scalar" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
+    assert "scalar" in d(3, 5, 17, 19, "NCHW", iabn.F32, "leaky_relu")
+    # ELU never takes the largest variants
+    assert "split" in d(32, 256, 56, 56, "NCHW", iabn.F32, "elu")
+    with pytest.raises(ValueError):
+        d(2, 4, 4, 4, "NCHW", iabn.F32, 9)
