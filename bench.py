@@ -98,6 +98,9 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload index 1..5 (default 2)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--warm-only", action="store_true", help="one buffer set (for profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark: copy a MIB-MiB buffer 5 times (a plain copy "
+                         "kernel of known size, the reference that scales memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported"
@@ -105,6 +108,17 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return 0
+
     import place_batchnorm_activation_amd as iabn
     import workloads
 

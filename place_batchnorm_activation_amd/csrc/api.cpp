@@ -63,13 +63,9 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
     if (act >= 0 && p.layout == kNCHW && p.vec && p.numel > 0) {
         const int64_t vc = p.m / p.V;
         const int f = fused_fwd_pick(vc);
-        if (f >= 0 && fused_worthwhile(p, fused_fwd_threads(f)) &&
-            !(act == kElu && f > kEluMaxFwdVariant))
-            p.fused_variant = f;
+        if (f >= 0 && fused_worthwhile(p, fused_fwd_threads(f))) p.fused_variant = f;
         const int b = fused_bwd_pick(vc);
-        if (b >= 0 && fused_worthwhile(p, fused_bwd_threads(b)) &&
-            !(act == kElu && b > kEluMaxBwdVariant))
-            p.fused_bwd_variant = b;
+        if (b >= 0 && fused_worthwhile(p, fused_bwd_threads(b))) p.fused_bwd_variant = b;
     }
     return p;
 }
@@ -343,7 +339,7 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         int T = 0, NR = 0;
         bool dyr = false;
         switch (p.fused_bwd_variant) {
-#define IABN_ROW(ID, T_, NR_, DYR_) case ID: T = T_; NR = NR_; dyr = DYR_; break;
+#define IABN_ROW(ID, T_, NRV_, NRL_, G_, DYR_) case ID: T = T_; NR = NRV_ + NRL_; dyr = DYR_; break;
             IABN_FUSED_BWD_VARIANTS(IABN_ROW)
 #undef IABN_ROW
         default: break;

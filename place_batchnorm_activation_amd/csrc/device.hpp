@@ -89,11 +89,31 @@ __device__ __forceinline__ float load_one(const void* base, int64_t i)
 // invertible activations.  Forward branches on z > 0; the backward reads the
 // branch off the stored y (y > 0), which agrees with z > 0 for every slope > 0.
 
+// ELU's two transcendentals, on the hardware exp2 / log2 units (v_exp_f32,
+// v_log_f32: about 1 ulp):
+//   exp(z) - 1 = exp2(z*log2(e)) - 1: absolute error ~1e-7 for z <= 0, which is
+//     all the ELU branch needs (|y| <= alpha, errors are judged against the
+//     channel's RMS);
+//   log1p(u), u in (-1, 0]: w = 1 + u rounded, then ln(w) - ((w - 1) - u)/w, the
+//     first-order correction for the rounding of w (Goldberg, "What every
+//     computer scientist should know about floating-point arithmetic", 1991).
+__device__ __forceinline__ float elu_expm1(float z)
+{
+    return __builtin_amdgcn_exp2f(z * 1.44269504088896341f) - 1.f;
+}
+
+__device__ __forceinline__ float elu_log1p(float u)
+{
+    const float w = 1.f + u;
+    return __builtin_amdgcn_logf(w) * 0.693147180559945309f
+           - ((w - 1.f) - u) * __builtin_amdgcn_rcpf(w);
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_forward(float z, float a)
 {
     if constexpr (ACT == kLeaky) return z > 0.f ? z : a * z;
-    else if constexpr (ACT == kElu) return z > 0.f ? z : a * expm1f(z);
+    else if constexpr (ACT == kElu) return z > 0.f ? z : a * elu_expm1(z);
     else return z;
 }
 
@@ -109,7 +129,7 @@ __device__ __forceinline__ void act_invert(float y, float a, float inv_a, float&
     } else if constexpr (ACT == kElu) {
         const bool pos = y > 0.f;
         const float u = fmaxf(y * inv_a, -1.f + 0x1p-24f);
-        z = pos ? y : log1pf(u);
+        z = pos ? y : elu_log1p(u);
         slope = pos ? 1.f : y + a;
     } else {
         z = y;
@@ -118,13 +138,17 @@ __device__ __forceinline__ void act_invert(float y, float a, float inv_a, float&
 }
 
 // ---------------------------------------------------------------------------
-// Chan et al. pairwise update of (count, mean, M2): merge b into a.
+// Chan et al. pairwise update of (count, mean, M2): merge b into a.  The weight
+// nb/(n+nb) takes the hardware reciprocal in fp32 (1 ulp), an exact division in fp64.
+__device__ __forceinline__ float merge_weight(float nb, float nn) { return nb * __builtin_amdgcn_rcpf(nn); }
+__device__ __forceinline__ double merge_weight(double nb, double nn) { return nb / nn; }
+
 template <typename F>
 __device__ __forceinline__ void chan_merge(F& n, F& mean, F& m2, F nb, F mb, F m2b)
 {
     if (nb > F(0)) {
         const F nn = n + nb;
-        const F f = nb / nn;
+        const F f = merge_weight(nb, nn);
         const F d = mb - mean;
         mean = mean + d * f;
         m2 = m2 + m2b + d * d * n * f;

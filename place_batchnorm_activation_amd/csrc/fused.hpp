@@ -22,16 +22,18 @@
     X(6, 512, 32)                  \
     X(7, 512, 49)
 
-// X(id, T, NR, DYR): DYR = dy resident too; otherwise dy is streamed twice
-#define IABN_FUSED_BWD_VARIANTS(X) \
-    X(0, 256, 1, true)             \
-    X(1, 256, 2, true)             \
-    X(2, 256, 4, true)             \
-    X(3, 256, 8, true)             \
-    X(4, 256, 13, true)            \
-    X(5, 512, 16, false)           \
-    X(6, 512, 32, false)           \
-    X(7, 512, 49, false)
+// X(id, T, NRV, NRL, G, DYR).  DYR: y and dy both resident, NRV vectors each in
+// VGPRs (3S of traffic).  Otherwise y is resident, NRV vectors per thread in VGPRs
+// and NRL in LDS, and dy is streamed twice in groups of G (4S).
+#define IABN_FUSED_BWD_VARIANTS(X)   \
+    X(0, 256, 1, 0, 1, true)         \
+    X(1, 256, 2, 0, 1, true)         \
+    X(2, 256, 4, 0, 1, true)         \
+    X(3, 256, 8, 0, 1, true)         \
+    X(4, 256, 13, 0, 1, true)        \
+    X(5, 512, 16, 0, 6, false)       \
+    X(6, 512, 24, 8, 8, false)       \
+    X(7, 512, 33, 16, 8, false)
 
 namespace iabn {
 
@@ -52,7 +54,7 @@ inline int fused_fwd_pick(int64_t vc)
 inline int fused_bwd_pick(int64_t vc)
 {
     static const FusedVariant tbl[] = {
-#define IABN_ROW(ID, T, NR, DYR) {ID, T, NR, DYR},
+#define IABN_ROW(ID, T, NRV, NRL, G, DYR) {ID, T, NRV + NRL, DYR},
         IABN_FUSED_BWD_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     };
@@ -74,7 +76,7 @@ inline int fused_fwd_threads(int id)
 inline int fused_bwd_threads(int id)
 {
     switch (id) {
-#define IABN_ROW(ID, T, NR, DYR) case ID: return T;
+#define IABN_ROW(ID, T, NRV, NRL, G, DYR) case ID: return T;
         IABN_FUSED_BWD_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     default: return 0;
@@ -83,12 +85,6 @@ inline int fused_bwd_threads(int id)
 
 // Whether the channel-resident kernels fill enough of the chip to beat the
 // split path: they run one workgroup per channel.
-// ELU's inverse and forward expand to long inline sequences; with the largest
-// variants the fully unrolled loops exceed the unroller's limit and the resident
-// array would fall back to scratch memory, so ELU stays on the smaller variants.
-constexpr int kEluMaxFwdVariant = 6;
-constexpr int kEluMaxBwdVariant = 4;
-
 inline bool fused_worthwhile(const Plan& p, int threads)
 {
     // 32-bit byte offsets address the tensor

@@ -139,6 +139,11 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     const uint32_t HWv = HW / V;
     const uint32_t Vc = m / V;
     const float K = load_one<DT>(x, int64_t(c) * HW);
+    // per-channel parameters fetched up front, off the critical path
+    const float g_c = gamma[c];
+    const float b = beta[c];
+    float rm_c = 0.f, rv_c = 0.f;
+    if (t == 0 && running_mean) { rm_c = running_mean[c]; rv_c = running_var[c]; }
 
     uint4 r[NR];
     ChannelWalk32 w;
@@ -179,17 +184,15 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     const double var = double(m2) / double(m);
     const double invstd = 1.0 / sqrt(var + double(eps));
     const float d = float(mean);
-    const float s = float(double(gamma[c]) * invstd);
-    const float b = beta[c];
+    const float s = float(double(g_c) * invstd);
     if (t == 0) {
         const double mu = double(K) + double(mean);
         save_mean[c] = float(mu);
         save_invstd[c] = float(invstd);
         if (running_mean) {
             const double mom = double(momentum);
-            running_mean[c] = float((1.0 - mom) * double(running_mean[c]) + mom * mu);
-            running_var[c] = float((1.0 - mom) * double(running_var[c])
-                                   + mom * var * double(m) / double(m - 1));
+            running_mean[c] = float((1.0 - mom) * double(rm_c) + mom * mu);
+            running_var[c] = float((1.0 - mom) * double(rv_c) + mom * var * double(m) / double(m - 1));
         }
     }
 
@@ -223,6 +226,8 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
     const uint32_t HWv = HW / V;
     const uint32_t Vc = m / V;
     const float bc = beta[c];
+    const float g_c = gamma[c];
+    const float is_c = invstd[c];
 
     uint4 ry[NR];
     uint4 rd[DYR ? NR : 1];
@@ -259,14 +264,14 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
     }
     block_sum2<T>(sdz, sdzt);
 
-    const double g = double(gamma[c]);
+    const double g = double(g_c);
     const double db = double(sdz);
     const double dg = double(sdzt) / g;
     if (t == 0) {
         dbeta[c] = float(db);
         dgamma[c] = float(dg);
     }
-    const double A = g * double(invstd[c]);
+    const double A = g * double(is_c);
     const double md = double(m);
     const float kA = float(A), kB = float(-A * dg / (md * g)), kC = float(-A * db / md);
 
@@ -291,6 +296,149 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
             st16(dx, w.off, pack<DT>(vd));
         }
         w.step();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward for channels too large to keep y and dy both on chip: y stays
+// resident (NRV vectors per thread in VGPRs, NRL in LDS) and dy is streamed
+// twice, through a two-group software pipeline: the G loads of the next group
+// are in flight while the current group is consumed.  HBM traffic 4S.
+template <int DT, int ACT, int T, int NRV, int NRL, int G>
+__global__ __launch_bounds__(T) void k_bwd_stream_nchw(
+    const void* __restrict__ y, const void* dy, void* dx, uint32_t C, uint32_t HW, uint32_t m,
+    const float* __restrict__ gamma, const float* __restrict__ beta,
+    const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
+    float a, float inv_a)
+{
+    constexpr int V = Vec16<DT>::V;
+    constexpr int NR = NRV + NRL;
+    constexpr int NG = (NR + G - 1) / G;
+    __shared__ uint4 ly[NRL > 0 ? NRL * T : 1];
+    const uint32_t c = blockIdx.x;
+    const uint32_t t = threadIdx.x;
+    const uint32_t HWv = HW / V;
+    const uint32_t Vc = m / V;
+    const float bc = beta[c];
+    const float g_c = gamma[c];
+    const float is_c = invstd[c];
+
+    // y: registers, then this thread's own LDS slots (read back only by this thread)
+    uint4 ry[NRV];
+    ChannelWalk32 w;
+    w.init(t, c, C, HWv, T);
+#pragma unroll
+    for (int k = 0; k < NRV; ++k) {
+        ry[k] = (t + k * T < Vc) ? ld16(y, w.off) : make_uint4(0, 0, 0, 0);
+        w.step();
+    }
+#pragma unroll
+    for (int k = 0; k < NRL; ++k) {
+        if (t + (NRV + k) * T < Vc) ly[k * T + t] = ld16(y, w.off);
+        w.step();
+    }
+
+    // pass 1: sums over dy streamed in groups of G
+    float sdz = 0.f, sdzt = 0.f;
+    {
+        const uint32_t t1 = opaque(t);
+        ChannelWalk32 wd;
+        wd.init(t1, c, C, HWv, T);
+        uint4 buf[2][G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            buf[0][i] = (i < NR && t1 + i * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+            wd.step();
+        }
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            group_fence();
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int k = (gi + 1) * G + i;
+                if (k < NR) {
+                    buf[(gi + 1) & 1][i] = (t1 + k * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+                    wd.step();
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int k = gi * G + i;
+                if (k < NR && t1 + k * T < Vc) {
+                    float vy[V], vd[V];
+                    unpack<DT>(k < NRV ? ry[k < NRV ? k : 0] : ly[(k >= NRV ? k - NRV : 0) * T + t1], vy);
+                    unpack<DT>(buf[gi & 1][i], vd);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        float z, slope;
+                        act_invert<ACT>(vy[e], a, inv_a, z, slope);
+                        const float dz = slope * vd[e];
+                        sdz += dz;
+                        sdzt = fmaf(dz, z - bc, sdzt);
+                    }
+                }
+            }
+        }
+    }
+    block_sum2<T>(sdz, sdzt);
+
+    const double g = double(g_c);
+    const double db = double(sdz);
+    const double dg = double(sdzt) / g;
+    if (t == 0) {
+        dbeta[c] = float(db);
+        dgamma[c] = float(dg);
+    }
+    const double A = g * double(is_c);
+    const double md = double(m);
+    const float kA = float(A), kB = float(-A * dg / (md * g)), kC = float(-A * db / md);
+
+    // pass 2: dy streamed again, dx written
+    {
+        const uint32_t t2 = opaque(t);
+        const float a2 = opaquef(a), ia2 = opaquef(inv_a), bc2 = opaquef(bc);
+        ChannelWalk32 wd, wx;
+        wd.init(t2, c, C, HWv, T);
+        wx.init(t2, c, C, HWv, T);
+        uint4 buf[2][G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            buf[0][i] = (i < NR && t2 + i * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+            wd.step();
+        }
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            group_fence();
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int k = (gi + 1) * G + i;
+                if (k < NR) {
+                    buf[(gi + 1) & 1][i] = (t2 + k * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+                    wd.step();
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int k = gi * G + i;
+                if (k < NR) {
+                    if (t2 + k * T < Vc) {
+                        float vy[V], vd[V];
+                        unpack<DT>(k < NRV ? opaque4(ry[k < NRV ? k : 0])
+                                           : ly[(k >= NRV ? k - NRV : 0) * T + t2], vy);
+                        unpack<DT>(buf[gi & 1][i], vd);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) {
+                            float z, slope;
+                            act_invert<ACT>(vy[e], a2, ia2, z, slope);
+                            const float dz = slope * vd[e];
+                            vd[e] = fmaf(kA, dz, fmaf(kB, z - bc2, kC));
+                        }
+                        st16(dx, wx.off, pack<DT>(vd));
+                    }
+                    wx.step();
+                }
+            }
+        }
     }
 }
 
@@ -341,10 +489,14 @@ static void launch_bwd_da(const Plan& pl, const void* y, const void* dy, void* d
 {
     const uint32_t C = uint32_t(pl.C), HW = uint32_t(pl.HW), m = uint32_t(pl.m);
     switch (pl.fused_bwd_variant) {
-#define IABN_BWD_CASE(ID, T, NR, DYR)                                                            \
-    case ID:                                                                                     \
-        hipLaunchKernelGGL((k_bwd_fused_nchw<DT, ACT, T, NR, DYR>), dim3(C), dim3(T), 0, s, y,  \
-                           dy, dx, C, HW, m, gamma, beta, invstd, dgamma, dbeta, a, ia);         \
+#define IABN_BWD_CASE(ID, T, NRV, NRL, G, DYR)                                                      \
+    case ID:                                                                                       \
+        if constexpr (DYR)                                                                         \
+            hipLaunchKernelGGL((k_bwd_fused_nchw<DT, ACT, T, NRV, true>), dim3(C), dim3(T), 0, s, \
+                               y, dy, dx, C, HW, m, gamma, beta, invstd, dgamma, dbeta, a, ia);    \
+        else                                                                                       \
+            hipLaunchKernelGGL((k_bwd_stream_nchw<DT, ACT, T, NRV, NRL, G>), dim3(C), dim3(T), 0,  \
+                               s, y, dy, dx, C, HW, m, gamma, beta, invstd, dgamma, dbeta, a, ia); \
         break;
         IABN_FUSED_BWD_VARIANTS(IABN_BWD_CASE)
 #undef IABN_BWD_CASE

@@ -137,7 +137,7 @@ static void check_plan(const Shape& s, bool vec)
 #define IABN_ROW(ID, T, NR) vars.push_back({T, NR});
         IABN_FUSED_FWD_VARIANTS(IABN_ROW)
 #undef IABN_ROW
-#define IABN_ROW(ID, T, NR, DYR) vars.push_back({T, NR});
+#define IABN_ROW(ID, T, NRV, NRL, G, DYR) vars.push_back({T, NRV + NRL});
         IABN_FUSED_BWD_VARIANTS(IABN_ROW)
 #undef IABN_ROW
         for (const Var& vv : vars) {

@@ -129,6 +129,8 @@ def test_plan_choice_for_the_workloads():
     d = iabn.iabn_describe_plan
     assert d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu") == \
         "forward=channel_resident(512x49) backward=channel_resident(512x49,dy_streamed)"
+    assert d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu") == \
+        d(32, 256, 56, 56, "NCHW", iabn.F32, "identity")
     assert d(16, 512, 28, 28, "NCHW", iabn.F32, "elu").startswith(
         "forward=channel_resident(256x13) backward=channel_resident(256x13,dy_resident)")
     assert d(2, 4, 8, 8, "NCHW", iabn.F32, "leaky_relu").startswith("forward=channel_resident")
@@ -136,7 +138,7 @@ def test_plan_choice_for_the_workloads():
     # misaligned or ragged planes take the scalar split path
     assert "scalar" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
     assert "scalar" in d(3, 5, 17, 19, "NCHW", iabn.F32, "leaky_relu")
-    # ELU never takes the largest variants
-    assert "split" in d(32, 256, 56, 56, "NCHW", iabn.F32, "elu")
+    # ELU takes the same channel-resident variants
+    assert "channel_resident(512x49)" in d(32, 256, 56, 56, "NCHW", iabn.F32, "elu")
     with pytest.raises(ValueError):
         d(2, 4, 4, 4, "NCHW", iabn.F32, 9)

@@ -236,8 +236,9 @@ def _variant_shapes():
             m = vc * V                      # elements per channel: N=2, H=1, W=m/2
             base = 2 if dtype == "f32" else 3
             out.append(custom(base, 2, 3, 1, m // 2, layout="NCHW", dtype=dtype))
-        out.append(custom(4, 2, 3, 1, 3300 * V // 2, layout="NCHW", dtype=dtype, act="elu",
-                          act_param=1.0))
+        for vc in (3300, 25000):
+            out.append(custom(4, 2, 3, 1, vc * V // 2, layout="NCHW", dtype=dtype, act="elu",
+                              act_param=1.0))
     return out
 
 
