@@ -8,7 +8,7 @@
 //
 // Three launches:
 //   bwd_reduce_*  one workgroup per (channel tile, partial): sums of dz and dz*t
-//   bwd_finalize  one wave per channel, fixed-order fp64 sums of the partials:
+//   bwd_finalize  16 channels x 64 phases per workgroup, fixed-order fp64 sums:
 //                 dbeta = sum dz, dgamma = (sum dz*t)/gamma, and the constants
 //                 {A = gamma*invstd, B = -A*dgamma/(m*gamma), Cc = -A*dbeta/m, beta}
 //   bwd_apply     dx = A*dz + B*(z - beta) + Cc
@@ -93,17 +93,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
         float t1 = sh[0][0], t2 = sh[1][0];
 #pragma unroll
         for (int k = 1; k < kThreads / kWave; ++k) { t1 += sh[0][k]; t2 += sh[1][k]; }
-        part_dz[c * P + p] = t1;
-        part_dzt[c * P + p] = t2;
+        part_dz[p * C + c] = t1;
+        part_dzt[p * C + c] = t2;
     }
 }
 
 // ---------------------------------------------------------------------------
-// NHWC: workgroup b covers channel slice b % slices and partial b / slices.
+// NHWC: workgroup b covers channel slice b % slices and partial b / slices, i.e.
+// row groups p, p + P, ... of rpi = 256/tpr rows (as the statistics kernel).
 template <int DT, int V, int ACT>
 __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     const void* __restrict__ y, const void* __restrict__ dy, int64_t m, int64_t Cv, int tpr,
-    int64_t slices, int64_t unit, int64_t P, const float* __restrict__ beta, float a,
+    int64_t slices, int64_t groups, int64_t P, const float* __restrict__ beta, float a,
     float inv_a, float* __restrict__ part_dz, float* __restrict__ part_dzt)
 {
     const int64_t b = blockIdx.x;
@@ -114,8 +115,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     const int rpi = kThreads / tpr;
     const int64_t col = sl * tpr + (t - rs * tpr);
     const bool active = col < Cv;
-    const int64_t r1 = dmin(p * unit + unit, m);
-    int64_t r = p * unit + rs;
 
     float bc[V], sdz[V], sdzt[V];
 #pragma unroll
@@ -123,23 +122,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     if (active) {
 #pragma unroll
         for (int e = 0; e < V; ++e) bc[e] = beta[col * V + e];
-        for (; r + (kUnrollB - 1) * rpi < r1; r += kUnrollB * rpi) {
+        int64_t g = p;
+        for (; g + (kUnrollB - 1) * P < groups; g += kUnrollB * P) {
             float vy[kUnrollB][V], vd[kUnrollB][V];
+            bool ok[kUnrollB];
 #pragma unroll
             for (int u = 0; u < kUnrollB; ++u) {
-                const int64_t i = ((r + u * rpi) * Cv + col) * V;
-                load_elems<DT, V>(y, i, vy[u]);
-                load_elems<DT, V>(dy, i, vd[u]);
+                const int64_t r = (g + u * P) * rpi + rs;
+                ok[u] = r < m;
+                if (ok[u]) {
+                    load_elems<DT, V>(y, (r * Cv + col) * V, vy[u]);
+                    load_elems<DT, V>(dy, (r * Cv + col) * V, vd[u]);
+                }
             }
 #pragma unroll
-            for (int u = 0; u < kUnrollB; ++u) accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
+            for (int u = 0; u < kUnrollB; ++u)
+                if (ok[u]) accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
         }
-        for (; r < r1; r += rpi) {
-            float vy[V], vd[V];
-            const int64_t i = (r * Cv + col) * V;
-            load_elems<DT, V>(y, i, vy);
-            load_elems<DT, V>(dy, i, vd);
-            accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+        for (; g < groups; g += P) {
+            const int64_t r = g * rpi + rs;
+            if (r < m) {
+                float vy[V], vd[V];
+                load_elems<DT, V>(y, (r * Cv + col) * V, vy);
+                load_elems<DT, V>(dy, (r * Cv + col) * V, vd);
+                accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+            }
         }
     }
     __shared__ float sh_a[V][kThreads];
@@ -160,43 +167,47 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
         }
     }
     if (rs == 0 && active) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-            const int64_t ch = col * V + e;
-            part_dz[ch * P + p] = sdz[e];
-            part_dzt[ch * P + p] = sdzt[e];
-        }
+        const int64_t base = p * Cv * V + col * V;
+        store_floats<V>(part_dz + base, sdz);
+        store_floats<V>(part_dzt + base, sdzt);
     }
 }
 
 // ---------------------------------------------------------------------------
-// One wave per channel: fixed-order fp64 sums of the P partials.
-__global__ __launch_bounds__(kThreads) void k_bwd_finalize(
+// Finishing the sums: thread t of a 1024-thread workgroup takes channel
+// t % kFinChannels and partials p = t / kFinChannels + k*kFinPhases, adds them in
+// fp64, and the phases are added in a fixed order.
+__global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     int64_t C, int64_t m, int64_t P, const float* __restrict__ part_dz,
     const float* __restrict__ part_dzt, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* __restrict__ invstd,
     float* __restrict__ dgamma, float* __restrict__ dbeta, float4* __restrict__ consts)
 {
-    const int64_t c = int64_t(blockIdx.x) * kFinalizePerBlock + threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    if (c >= C) return;
+    const int cl = threadIdx.x % kFinChannels;
+    const int ph = threadIdx.x / kFinChannels;
+    const int64_t c = int64_t(blockIdx.x) * kFinChannels + cl;
     double s1 = 0.0, s2 = 0.0;
-    for (int64_t p = lane; p < P; p += kWave) {
-        s1 += double(part_dz[c * P + p]);
-        s2 += double(part_dzt[c * P + p]);
+    if (c < C) {
+        for (int64_t p = ph; p < P; p += kFinPhases) {
+            s1 += double(part_dz[p * C + c]);
+            s2 += double(part_dzt[p * C + c]);
+        }
     }
-    s1 = wave_sum(s1);
-    s2 = wave_sum(s2);
-    if (lane == 0) {
-        const double g = double(gamma[c]);
-        const double db = s1;
-        const double dg = s2 / g;
-        dbeta[c] = float(db);
-        dgamma[c] = float(dg);
-        const double A = g * double(invstd[c]);
-        const double md = double(m);
-        consts[c] = make_float4(float(A), float(-A * dg / (md * g)), float(-A * db / md), beta[c]);
-    }
+    __shared__ double sh1[kFinPhases][kFinChannels];
+    __shared__ double sh2[kFinPhases][kFinChannels];
+    sh1[ph][cl] = s1;
+    sh2[ph][cl] = s2;
+    __syncthreads();
+    if (ph != 0 || c >= C) return;
+    for (int k = 1; k < kFinPhases; ++k) { s1 += sh1[k][cl]; s2 += sh2[k][cl]; }
+    const double g = double(gamma[c]);
+    const double db = s1;
+    const double dg = s2 / g;
+    dbeta[c] = float(db);
+    dgamma[c] = float(dg);
+    const double A = g * double(invstd[c]);
+    const double md = double(m);
+    consts[c] = make_float4(float(A), float(-A * dg / (md * g)), float(-A * db / md), beta[c]);
 }
 
 // ---------------------------------------------------------------------------
@@ -347,8 +358,8 @@ void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const
         if (pl.vec) launch_reduce_dv<kBF16, 8>(pl, y, dy, beta, act, a, ia, pa, pb, s);
         else launch_reduce_dv<kBF16, 1>(pl, y, dy, beta, act, a, ia, pa, pb, s);
     }
-    hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinalizePerBlock))),
-                       dim3(kThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta, invstd,
+    hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
+                       dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta, invstd,
                        dgamma, dbeta, consts);
 }
 

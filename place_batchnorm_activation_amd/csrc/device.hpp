@@ -77,6 +77,20 @@ __device__ __forceinline__ void store_elems(void* base, int64_t i, const float (
     }
 }
 
+// V consecutive fp32 values (16-byte aligned when V is a multiple of 4).
+template <int V>
+__device__ __forceinline__ void store_floats(float* p, const float (&v)[V])
+{
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < V; k += 4)
+            *reinterpret_cast<float4*>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) p[k] = v[k];
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ float load_one(const void* base, int64_t i)
 {

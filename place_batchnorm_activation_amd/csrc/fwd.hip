@@ -9,8 +9,8 @@
 // Three launches:
 //   stats_*      one workgroup per (channel tile, partial); streams x once and
 //                writes (mean, M2) of its elements, shifted by a pivot K_c
-//   fwd_finalize one wave per channel; fixed-order Chan merge of the partials in
-//                fp64; statistics, running statistics, and the constants
+//   fwd_finalize the partials of a channel as fp64 shifted sums, added in a fixed
+//                order; statistics, running statistics, and the constants
 //                {K_c, d_c = mean_c - K_c, s_c = gamma_c*invstd_c, beta_c}
 //   fwd_apply    elementwise y = act(((x - K_c) - d_c)*s_c + beta_c), in place
 //
@@ -33,7 +33,7 @@ constexpr int kUnroll = 4;
 template <int DT, int V>
 __global__ __launch_bounds__(kThreads) void k_stats_nchw(
     const void* __restrict__ x, int64_t C, int64_t HW, int64_t m, int64_t unit, int64_t P,
-    float* __restrict__ part_mean, float* __restrict__ part_m2)
+    float* __restrict__ part_mean, float* __restrict__ part_m2, float* __restrict__ count)
 {
     const int64_t b = blockIdx.x;
     const int64_t c = b / P;
@@ -99,31 +99,32 @@ __global__ __launch_bounds__(kThreads) void k_stats_nchw(
         float tn = sh[0][0], tm = sh[1][0], t2 = sh[2][0];
 #pragma unroll
         for (int k = 1; k < kThreads / kWave; ++k) chan_merge(tn, tm, t2, sh[0][k], sh[1][k], sh[2][k]);
-        part_mean[c * P + p] = tm;
-        part_m2[c * P + p] = t2;
+        part_mean[p * C + c] = tm;
+        part_m2[p * C + c] = t2;
+        if (c == 0) count[p] = tn;
     }
 }
 
 // ---------------------------------------------------------------------------
 // NHWC statistics: workgroup b covers channel slice sl = b % slices (tpr vectors
-// of V channels) and partial p = b / slices, i.e. rows [p*unit, min((p+1)*unit, m)).
-// Thread t owns channel vector col = sl*tpr + t % tpr and walks rows t / tpr,
-// t / tpr + 256/tpr, ...; the row slots are then merged by an LDS tree.
+// of V channels) and partial p = b / slices, i.e. row groups p, p + P, p + 2P, ...
+// of rpi = 256/tpr rows.  Thread t owns channel vector col = sl*tpr + t % tpr
+// and row slot t / tpr of every group; the row slots are then merged by an LDS
+// tree.
 template <int DT, int V>
 __global__ __launch_bounds__(kThreads) void k_stats_nhwc(
-    const void* __restrict__ x, int64_t m, int64_t Cv, int tpr, int64_t slices, int64_t unit,
-    int64_t P, float* __restrict__ part_mean, float* __restrict__ part_m2)
+    const void* __restrict__ x, int64_t m, int64_t Cv, int tpr, int64_t slices, int64_t groups,
+    int64_t P, float* __restrict__ part_mean, float* __restrict__ part_m2,
+    float* __restrict__ count)
 {
     const int64_t b = blockIdx.x;
     const int64_t p = b / slices;
     const int64_t sl = b - p * slices;
     const int t = threadIdx.x;
     const int rs = t / tpr;               // row slot
-    const int rpi = kThreads / tpr;       // rows per step
+    const int rpi = kThreads / tpr;       // rows per group
     const int64_t col = sl * tpr + (t - rs * tpr);
     const bool active = col < Cv;
-    const int64_t r1 = dmin(p * unit + unit, m);
-    int64_t r = p * unit + rs;
 
     float K[V];
     float s1[V], s2[V];
@@ -132,30 +133,41 @@ __global__ __launch_bounds__(kThreads) void k_stats_nhwc(
     int cnt = 0;
     if (active) {
         load_elems<DT, V>(x, col * V, K);
-        for (; r + (kUnroll - 1) * rpi < r1; r += kUnroll * rpi) {
+        int64_t g = p;
+        for (; g + (kUnroll - 1) * P < groups; g += kUnroll * P) {
             float v[kUnroll][V];
+            bool ok[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) load_elems<DT, V>(x, ((r + u * rpi) * Cv + col) * V, v[u]);
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t r = (g + u * P) * rpi + rs;
+                ok[u] = r < m;
+                if (ok[u]) load_elems<DT, V>(x, (r * Cv + col) * V, v[u]);
+            }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < kUnroll; ++u) {
+                if (!ok[u]) continue;
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     const float d = v[u][e] - K[e];
                     s1[e] += d;
                     s2[e] = fmaf(d, d, s2[e]);
                 }
-            cnt += kUnroll;
-        }
-        for (; r < r1; r += rpi) {
-            float v[V];
-            load_elems<DT, V>(x, (r * Cv + col) * V, v);
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const float d = v[e] - K[e];
-                s1[e] += d;
-                s2[e] = fmaf(d, d, s2[e]);
+                ++cnt;
             }
-            cnt += 1;
+        }
+        for (; g < groups; g += P) {
+            const int64_t r = g * rpi + rs;
+            if (r < m) {
+                float v[V];
+                load_elems<DT, V>(x, (r * Cv + col) * V, v);
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float d = v[e] - K[e];
+                    s1[e] += d;
+                    s2[e] = fmaf(d, d, s2[e]);
+                }
+                ++cnt;
+            }
         }
     }
     float n = float(cnt);
@@ -192,51 +204,63 @@ __global__ __launch_bounds__(kThreads) void k_stats_nhwc(
         }
     }
     if (rs == 0 && active) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-            const int64_t ch = col * V + e;
-            part_mean[ch * P + p] = mean[e];
-            part_m2[ch * P + p] = m2[e];
-        }
+        const int64_t base = p * Cv * V + col * V;
+        store_floats<V>(part_mean + base, mean);
+        store_floats<V>(part_m2 + base, m2);
     }
+    if (t == 0 && sl == 0) count[p] = n;
 }
 
 // ---------------------------------------------------------------------------
-// One wave per channel: fixed-order Chan merge of the channel's P partials in
-// fp64, then the statistics, the running statistics and the apply constants.
+// Finishing the statistics.  A 1024-thread workgroup covers kFinChannels
+// channels; thread t takes channel t % kFinChannels and partials
+// p = t / kFinChannels + k*kFinPhases.  Each partial (n_p, mean_p, M2_p) becomes
+// the shifted sums n_p*mean_p and M2_p + n_p*mean_p^2, added in fp64 in a fixed
+// order (phases in turn, then partials within a phase); then
+//   mean = S1/m, M2 = S2 - S1*mean, var = M2/m  (all fp64),
+// and the statistics, the running statistics and the apply constants.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_fwd_finalize(
+__global__ __launch_bounds__(kFinThreads) void k_fwd_finalize(
     const void* __restrict__ x, int layout, int64_t C, int64_t HW, int64_t m, int64_t P,
-    int64_t unit, const float* __restrict__ part_mean, const float* __restrict__ part_m2,
-    const float* __restrict__ gamma, const float* __restrict__ beta,
-    float* __restrict__ running_mean, float* __restrict__ running_var,
-    float* __restrict__ save_mean, float* __restrict__ save_invstd,
-    float eps, float momentum, float4* __restrict__ consts)
+    const float* __restrict__ part_mean, const float* __restrict__ part_m2,
+    const float* __restrict__ count, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* __restrict__ running_mean,
+    float* __restrict__ running_var, float* __restrict__ save_mean,
+    float* __restrict__ save_invstd, float eps, float momentum, float4* __restrict__ consts)
 {
-    const int64_t c = int64_t(blockIdx.x) * kFinalizePerBlock + threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    if (c >= C) return;
-    double n = 0.0, mean = 0.0, m2 = 0.0;
-    for (int64_t p = lane; p < P; p += kWave) {
-        const double nb = double(dmin(unit, m - p * unit));
-        chan_merge(n, mean, m2, nb, double(part_mean[c * P + p]), double(part_m2[c * P + p]));
-    }
-    wave_chan(n, mean, m2);
-    if (lane == 0) {
-        const float K = load_one<DT>(x, layout == kNCHW ? c * HW : c);
-        const double var = m2 / double(m);
-        const double invstd = 1.0 / sqrt(var + double(eps));
-        const double mu = double(K) + mean;
-        save_mean[c] = float(mu);
-        save_invstd[c] = float(invstd);
-        if (running_mean) {
-            const double mom = double(momentum);
-            running_mean[c] = float((1.0 - mom) * double(running_mean[c]) + mom * mu);
-            running_var[c] = float((1.0 - mom) * double(running_var[c])
-                                   + mom * var * double(m) / double(m - 1));
+    const int cl = threadIdx.x % kFinChannels;
+    const int ph = threadIdx.x / kFinChannels;
+    const int64_t c = int64_t(blockIdx.x) * kFinChannels + cl;
+    double S1 = 0.0, S2 = 0.0;
+    if (c < C) {
+        for (int64_t p = ph; p < P; p += kFinPhases) {
+            const double n = double(count[p]);
+            const double mu = double(part_mean[p * C + c]);
+            S1 = fma(n, mu, S1);
+            S2 += fma(n * mu, mu, double(part_m2[p * C + c]));
         }
-        consts[c] = make_float4(K, float(mean), float(double(gamma[c]) * invstd), beta[c]);
     }
+    __shared__ double sh1[kFinPhases][kFinChannels];
+    __shared__ double sh2[kFinPhases][kFinChannels];
+    sh1[ph][cl] = S1;
+    sh2[ph][cl] = S2;
+    __syncthreads();
+    if (ph != 0 || c >= C) return;
+    for (int k = 1; k < kFinPhases; ++k) { S1 += sh1[k][cl]; S2 += sh2[k][cl]; }
+    const double mean = S1 / double(m);
+    const double var = fmax(S2 - S1 * mean, 0.0) / double(m);
+    const float K = load_one<DT>(x, layout == kNCHW ? c * HW : c);
+    const double invstd = 1.0 / sqrt(var + double(eps));
+    const double mu = double(K) + mean;
+    save_mean[c] = float(mu);
+    save_invstd[c] = float(invstd);
+    if (running_mean) {
+        const double mom = double(momentum);
+        running_mean[c] = float((1.0 - mom) * double(running_mean[c]) + mom * mu);
+        running_var[c] = float((1.0 - mom) * double(running_var[c])
+                               + mom * var * double(m) / double(m - 1));
+    }
+    consts[c] = make_float4(K, float(mean), float(double(gamma[c]) * invstd), beta[c]);
 }
 
 // ---------------------------------------------------------------------------
@@ -352,14 +376,15 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
 // host launchers
 
 template <int DT, int V>
-static void launch_stats_dv(const Plan& pl, const void* x, float* pa, float* pb, hipStream_t s)
+static void launch_stats_dv(const Plan& pl, const void* x, float* pa, float* pb, float* cnt,
+                            hipStream_t s)
 {
     if (pl.layout == kNCHW)
         hipLaunchKernelGGL((k_stats_nchw<DT, V>), dim3(pl.reduce_blocks), dim3(kThreads), 0, s,
-                           x, pl.C, pl.HW, pl.m, pl.unit, pl.P, pa, pb);
+                           x, pl.C, pl.HW, pl.m, pl.unit, pl.P, pa, pb, cnt);
     else
         hipLaunchKernelGGL((k_stats_nhwc<DT, V>), dim3(pl.reduce_blocks), dim3(kThreads), 0, s,
-                           x, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit, pl.P, pa, pb);
+                           x, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit, pl.P, pa, pb, cnt);
 }
 
 void launch_forward_stats(const Plan& pl, const void* x, const float* gamma, const float* beta,
@@ -370,21 +395,22 @@ void launch_forward_stats(const Plan& pl, const void* x, const float* gamma, con
     float* pa = reinterpret_cast<float*>(wsb + pl.off_part_a);
     float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
     float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
+    float* cnt = reinterpret_cast<float*>(wsb + pl.off_count);
     if (pl.dtype == kF32) {
-        if (pl.vec) launch_stats_dv<kF32, 4>(pl, x, pa, pb, s);
-        else launch_stats_dv<kF32, 1>(pl, x, pa, pb, s);
+        if (pl.vec) launch_stats_dv<kF32, 4>(pl, x, pa, pb, cnt, s);
+        else launch_stats_dv<kF32, 1>(pl, x, pa, pb, cnt, s);
     } else {
-        if (pl.vec) launch_stats_dv<kBF16, 8>(pl, x, pa, pb, s);
-        else launch_stats_dv<kBF16, 1>(pl, x, pa, pb, s);
+        if (pl.vec) launch_stats_dv<kBF16, 8>(pl, x, pa, pb, cnt, s);
+        else launch_stats_dv<kBF16, 1>(pl, x, pa, pb, cnt, s);
     }
-    const dim3 grid(unsigned(ceil_div(pl.C, kFinalizePerBlock)));
+    const dim3 grid(unsigned(ceil_div(pl.C, kFinChannels)));
     if (pl.dtype == kF32)
-        hipLaunchKernelGGL((k_fwd_finalize<kF32>), grid, dim3(kThreads), 0, s, x, pl.layout, pl.C,
-                           pl.HW, pl.m, pl.P, pl.unit, pa, pb, gamma, beta, running_mean,
+        hipLaunchKernelGGL((k_fwd_finalize<kF32>), grid, dim3(kFinThreads), 0, s, x, pl.layout,
+                           pl.C, pl.HW, pl.m, pl.P, pa, pb, cnt, gamma, beta, running_mean,
                            running_var, save_mean, save_invstd, eps, momentum, consts);
     else
-        hipLaunchKernelGGL((k_fwd_finalize<kBF16>), grid, dim3(kThreads), 0, s, x, pl.layout, pl.C,
-                           pl.HW, pl.m, pl.P, pl.unit, pa, pb, gamma, beta, running_mean,
+        hipLaunchKernelGGL((k_fwd_finalize<kBF16>), grid, dim3(kFinThreads), 0, s, x, pl.layout,
+                           pl.C, pl.HW, pl.m, pl.P, pa, pb, cnt, gamma, beta, running_mean,
                            running_var, save_mean, save_invstd, eps, momentum, consts);
 }
 

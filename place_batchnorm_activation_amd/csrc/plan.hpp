@@ -5,14 +5,17 @@
 // same order and the results are bitwise reproducible.
 //
 // Reduction tiling (forward statistics and backward sums).  Every channel's m
-// elements are cut into P "partials" of `unit` elements (the last one ragged):
-//   NCHW: the channel-local index j = n*HW + hw is cut into runs of `unit`; one
-//         workgroup per (channel, partial): grid = C * P.
-//   NHWC: the m rows are cut into runs of `unit` rows; the C channels into
-//         `slices` of `tpr` vectors (tpr threads per row, 256/tpr rows in flight
-//         per workgroup); grid = slices * P, slice index fastest.
-// Each workgroup writes one partial per channel it covers; a finishing kernel
-// combines the P partials of a channel in a fixed order.
+// elements are cut into P "partials":
+//   NCHW: the channel-local index j = n*HW + hw is cut into runs of `unit`
+//         elements (the last one ragged); one workgroup per (channel, partial):
+//         grid = C * P.
+//   NHWC: the C channels are cut into `slices` of `tpr` vectors (tpr threads per
+//         row, rpi = 256/tpr rows per step), the m rows into row groups of rpi
+//         rows; workgroup (slice, p) takes row groups p, p + P, p + 2P, ...:
+//         grid = slices * P, slice index fastest.
+// Each workgroup writes one partial per channel it covers, partial-major
+// (index p*C + c), and its element count; a finishing kernel combines the P
+// partials of a channel in a fixed order.
 #pragma once
 
 #include <stddef.h>
@@ -22,7 +25,10 @@ namespace iabn {
 
 constexpr int kThreads = 256;          // workgroup size of every kernel
 constexpr int kWave = 64;              // CDNA wavefront
-constexpr int kFinalizePerBlock = kThreads / kWave;  // one wave per channel
+// finishing kernels: 1024 threads = kFinChannels channels x kFinPhases phases
+constexpr int kFinThreads = 1024;
+constexpr int kFinChannels = 16;
+constexpr int kFinPhases = kFinThreads / kFinChannels;
 
 enum Layout { kNCHW = 0, kNHWC = 1 };
 enum DType { kF32 = 0, kBF16 = 1 };
@@ -35,7 +41,7 @@ struct Plan {
     int V = 1;           // elements per access
     // reduction tiling
     int64_t P = 1;       // partials per channel
-    int64_t unit = 1;    // NCHW: channel-local elements per partial; NHWC: rows per partial
+    int64_t unit = 1;    // NCHW: channel-local elements per partial; NHWC: row groups
     int tpr = 1;         // NHWC: threads per row
     int64_t slices = 1;  // NHWC: channel slices
     int64_t reduce_blocks = 0;
@@ -46,7 +52,7 @@ struct Plan {
     int fused_variant = -1;
     int fused_bwd_variant = -1;
     // workspace sections (bytes, 256-aligned)
-    size_t off_part_a = 0, off_part_b = 0, off_const = 0, bytes = 0;
+    size_t off_part_a = 0, off_part_b = 0, off_const = 0, off_count = 0, bytes = 0;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -65,6 +71,9 @@ inline int64_t gcd64(int64_t a, int64_t b)
 constexpr int64_t kApplyBlocksMax = 2048;
 // Workgroups a reduction aims for.
 constexpr int64_t kReduceBlocksTarget = 2048;
+// NHWC reductions: fewer, longer-lived workgroups walking row groups with a
+// stride; two per CU.
+constexpr int64_t kNhwcReduceBlocks = 512;
 
 inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, int dtype, bool vec)
 {
@@ -92,24 +101,24 @@ inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, in
         const int64_t p_budget = max64(1, (p.m * p.esize) / 400);
         int tpr = 1;
         while (tpr < cv && tpr < kThreads) tpr <<= 1;
+        auto groups = [&](int t) { return ceil_div(p.m, int64_t(kThreads / t)); };
         auto choose_P = [&](int t) {
-            const int64_t rpi = kThreads / t;               // rows per step of a workgroup
-            const int64_t p_iter = max64(1, p.m / (4 * rpi)); // >= ~4 steps per thread
+            const int64_t p_iter = max64(1, groups(t) / 4);  // >= ~4 row groups per workgroup
             return max64(1, min64(p_budget, p_iter));
         };
         int64_t slices = ceil_div(cv, tpr);
         int64_t P = choose_P(tpr);
         // narrower slices (down to 4 lanes, 64 bytes per row segment) while short of work
-        while (slices * P < kReduceBlocksTarget / 2 && tpr > 4) {
+        while (slices * P < kNhwcReduceBlocks / 2 && tpr > 4) {
             tpr >>= 1;
             slices = ceil_div(cv, tpr);
             P = choose_P(tpr);
         }
-        P = min64(P, max64(1, ceil_div(kReduceBlocksTarget, slices)));
+        P = min64(P, max64(1, ceil_div(kNhwcReduceBlocks, slices)));
         p.tpr = tpr;
         p.slices = slices;
-        p.unit = ceil_div(p.m, P);
-        p.P = ceil_div(p.m, p.unit);
+        p.unit = groups(tpr);                               // row groups in all
+        p.P = min64(P, p.unit);
         p.reduce_blocks = slices * p.P;
     }
 
@@ -133,6 +142,7 @@ inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, in
     p.off_const = off;  off = (size_t)align_up((int64_t)(off + (size_t)C * 16), 256);
     p.off_part_a = off; off = (size_t)align_up((int64_t)(off + part_bytes), 256);
     p.off_part_b = off; off = (size_t)align_up((int64_t)(off + part_bytes), 256);
+    p.off_count = off;  off = (size_t)align_up((int64_t)(off + (size_t)p.P * sizeof(float)), 256);
     p.bytes = off;
     return p;
 }

@@ -36,11 +36,13 @@ static void check_plan(const Shape& s, bool vec)
     if (numel == 0) return;
     CHECK(numel % V == 0, "numel %% V");
     CHECK(pl.P >= 1 && pl.unit >= 1, "P/unit");
-    CHECK(pl.P * pl.unit >= m && (pl.P - 1) * pl.unit < m, "partials cover m exactly");
+    if (pl.layout == kNCHW)
+        CHECK(pl.P * pl.unit >= m && (pl.P - 1) * pl.unit < m, "partials cover m exactly");
     CHECK(pl.reduce_blocks < (int64_t(1) << 31) && pl.apply_blocks < (int64_t(1) << 31), "grid");
     CHECK(pl.off_const == 0 && pl.off_part_a >= size_t(C) * 16, "const section");
     CHECK(pl.off_part_b >= pl.off_part_a + size_t(pl.P * C) * 4, "part a section");
-    CHECK(pl.bytes >= pl.off_part_b + size_t(pl.P * C) * 4, "part b section");
+    CHECK(pl.off_count >= pl.off_part_b + size_t(pl.P * C) * 4, "part b section");
+    CHECK(pl.bytes >= pl.off_count + size_t(pl.P) * 4, "count section");
     CHECK(pl.off_part_a % 256 == 0 && pl.off_part_b % 256 == 0, "alignment");
 
     std::vector<uint8_t> seen(size_t(nvec), 0);
@@ -74,14 +76,18 @@ static void check_plan(const Shape& s, bool vec)
         CHECK(pl.slices * pl.tpr >= Cv, "slices cover the row");
         CHECK(pl.reduce_blocks == pl.slices * pl.P, "NHWC grid");
         const int rpi = kThreads / pl.tpr;
+        CHECK(pl.unit == (m + rpi - 1) / rpi, "row groups");
+        CHECK(pl.P <= pl.unit, "no empty partial");
         for (int64_t b = 0; b < pl.reduce_blocks; ++b) {
             const int64_t p = b / pl.slices, sl = b - p * pl.slices;
-            const int64_t r1 = std::min(p * pl.unit + pl.unit, m);
             for (int t = 0; t < kThreads; ++t) {
                 const int rs = t / pl.tpr;
                 const int64_t col = sl * pl.tpr + (t - rs * pl.tpr);
                 if (col >= Cv) continue;
-                for (int64_t r = p * pl.unit + rs; r < r1; r += rpi) {
+                CHECK(p * C + col * V + V <= pl.P * C, "partial index");
+                for (int64_t g = p; g < pl.unit; g += pl.P) {
+                    const int64_t r = g * rpi + rs;
+                    if (r >= m) continue;
                     const int64_t a = r * Cv + col;
                     CHECK(a >= 0 && a < nvec, "NHWC reduce bounds");
                     if (a >= 0 && a < nvec) seen[size_t(a)]++;
