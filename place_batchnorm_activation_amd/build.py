@@ -21,7 +21,7 @@ ARCH = "gfx950"
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-I" + INCLUDE, "-I" + CSRC,
-]
+] + os.environ.get("IABN_EXTRA_CFLAGS", "").split()
 # Device code: gfx950 only.  Packed fp32 instructions are switched off (they are
 # not needed by this bandwidth-bound code, and plain scalar fp32 is what we test).
 # Code object v5: loadable by the HIP runtime that PyTorch-ROCm ships (the
@@ -43,18 +43,19 @@ def _compile(src: str, verbose: bool) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles every source; returns the library path."""
+def build(verbose: bool = False, out: str = LIB) -> str:
+    """Always recompiles every source; returns the library path.  IABN_EXTRA_CFLAGS
+    (environment) adds compiler flags, e.g. -D overrides of tiling constants."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -23,7 +23,10 @@
 
 namespace iabn {
 
-constexpr int kUnrollB = 4;
+#ifndef IABN_REDUCE_UNROLL
+#define IABN_REDUCE_UNROLL 4
+#endif
+constexpr int kUnrollB = IABN_REDUCE_UNROLL;
 
 template <int ACT, int V>
 __device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy)[V],
@@ -122,30 +125,64 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     if (active) {
 #pragma unroll
         for (int e = 0; e < V; ++e) bc[e] = beta[col * V + e];
-        int64_t g = p;
-        for (; g + (kUnrollB - 1) * P < groups; g += kUnrollB * P) {
-            float vy[kUnrollB][V], vd[kUnrollB][V];
-            bool ok[kUnrollB];
+        if constexpr (V == Raw16<DT>::V) {
+            // software pipeline over complete row groups (branch-free): the next
+            // kUnrollB groups of y and dy load while the current ones are summed;
+            // the rest, at most one ragged group per workgroup, runs checked
+            const int64_t full = m / rpi;
+            const uint4* yv = reinterpret_cast<const uint4*>(y);
+            const uint4* dv = reinterpret_cast<const uint4*>(dy);
+            auto load_set = [&](uint4 (&by)[kUnrollB], uint4 (&bd)[kUnrollB], int64_t g0) {
 #pragma unroll
-            for (int u = 0; u < kUnrollB; ++u) {
-                const int64_t r = (g + u * P) * rpi + rs;
-                ok[u] = r < m;
-                if (ok[u]) {
-                    load_elems<DT, V>(y, (r * Cv + col) * V, vy[u]);
-                    load_elems<DT, V>(dy, (r * Cv + col) * V, vd[u]);
+                for (int u = 0; u < kUnrollB; ++u) {
+                    const int64_t i = ((g0 + u * P) * rpi + rs) * Cv + col;
+                    by[u] = yv[i];
+                    bd[u] = dv[i];
+                }
+            };
+            auto add_set = [&](const uint4 (&by)[kUnrollB], const uint4 (&bd)[kUnrollB]) {
+#pragma unroll
+                for (int u = 0; u < kUnrollB; ++u) {
+                    float vy[V], vd[V];
+                    unpack16<DT>(by[u], vy);
+                    unpack16<DT>(bd[u], vd);
+                    accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+                }
+            };
+            int64_t g = p;
+            if (g + (kUnrollB - 1) * P < full) {
+                uint4 Ay[kUnrollB], Ad[kUnrollB], By[kUnrollB], Bd[kUnrollB];
+                load_set(Ay, Ad, g);
+                for (;;) {
+                    const int64_t g2 = g + kUnrollB * P;
+                    if (g2 + (kUnrollB - 1) * P >= full) { add_set(Ay, Ad); g = g2; break; }
+                    load_set(By, Bd, g2);
+                    add_set(Ay, Ad);
+                    const int64_t g3 = g2 + kUnrollB * P;
+                    if (g3 + (kUnrollB - 1) * P >= full) { add_set(By, Bd); g = g3; break; }
+                    load_set(Ay, Ad, g3);
+                    add_set(By, Bd);
+                    g = g3;
                 }
             }
-#pragma unroll
-            for (int u = 0; u < kUnrollB; ++u)
-                if (ok[u]) accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
-        }
-        for (; g < groups; g += P) {
-            const int64_t r = g * rpi + rs;
-            if (r < m) {
-                float vy[V], vd[V];
-                load_elems<DT, V>(y, (r * Cv + col) * V, vy);
-                load_elems<DT, V>(dy, (r * Cv + col) * V, vd);
-                accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+            for (; g < groups; g += P) {
+                const int64_t r = g * rpi + rs;
+                if (r < m) {
+                    float vy[V], vd[V];
+                    unpack16<DT>(yv[r * Cv + col], vy);
+                    unpack16<DT>(dv[r * Cv + col], vd);
+                    accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+                }
+            }
+        } else {
+            for (int64_t g = p; g < groups; g += P) {
+                const int64_t r = g * rpi + rs;
+                if (r < m) {
+                    float vy[V], vd[V];
+                    load_elems<DT, V>(y, (r * Cv + col) * V, vy);
+                    load_elems<DT, V>(dy, (r * Cv + col) * V, vd);
+                    accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+                }
             }
         }
     }
@@ -250,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nchw(
 #pragma unroll
         for (int u = 0; u < kUnrollB; ++u) {
             dx_one<ACT, V>(vy[u], vd[u], k[u], a, inv_a);
-            store_elems<DT, V>(dx, (v + u * stride) * V, vd[u]);
+            store_out<DT, V>(dx, (v + u * stride) * V, vd[u]);
         }
     }
     for (; v < nvec; v += stride) {
@@ -263,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nchw(
         for (int e = 0; e < V; ++e) k[e] = kc;
         w.step();
         dx_one<ACT, V>(vy, vd, k, a, inv_a);
-        store_elems<DT, V>(dx, v * V, vd);
+        store_out<DT, V>(dx, v * V, vd);
     }
 }
 
@@ -280,6 +317,33 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
         float4 k[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) k[e] = consts[c0 + e];
+        if constexpr (IABN_APPLY_REVERSE) {
+            // walk from the end down: the rows the reduction read last are the
+            // likeliest still to sit in the Infinity Cache
+            const int64_t v0 = v;
+            v = v0 + ((nvec - 1 - v0) / stride) * stride;
+            for (; v - (kUnrollB - 1) * stride >= v0; v -= kUnrollB * stride) {
+                float vy[kUnrollB][V], vd[kUnrollB][V];
+#pragma unroll
+                for (int u = 0; u < kUnrollB; ++u) {
+                    load_elems<DT, V>(y, (v - u * stride) * V, vy[u]);
+                    load_elems<DT, V>(dy, (v - u * stride) * V, vd[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < kUnrollB; ++u) {
+                    dx_one<ACT, V>(vy[u], vd[u], k, a, inv_a);
+                    store_out<DT, V>(dx, (v - u * stride) * V, vd[u]);
+                }
+            }
+            for (; v >= v0; v -= stride) {
+                float vy[V], vd[V];
+                load_elems<DT, V>(y, v * V, vy);
+                load_elems<DT, V>(dy, v * V, vd);
+                dx_one<ACT, V>(vy, vd, k, a, inv_a);
+                store_out<DT, V>(dx, v * V, vd);
+            }
+            return;
+        }
         for (; v + (kUnrollB - 1) * stride < nvec; v += kUnrollB * stride) {
             float vy[kUnrollB][V], vd[kUnrollB][V];
 #pragma unroll
@@ -290,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
 #pragma unroll
             for (int u = 0; u < kUnrollB; ++u) {
                 dx_one<ACT, V>(vy[u], vd[u], k, a, inv_a);
-                store_elems<DT, V>(dx, (v + u * stride) * V, vd[u]);
+                store_out<DT, V>(dx, (v + u * stride) * V, vd[u]);
             }
         }
         for (; v < nvec; v += stride) {
@@ -298,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
             load_elems<DT, V>(y, v * V, vy);
             load_elems<DT, V>(dy, v * V, vd);
             dx_one<ACT, V>(vy, vd, k, a, inv_a);
-            store_elems<DT, V>(dx, v * V, vd);
+            store_out<DT, V>(dx, v * V, vd);
         }
     } else {
         for (; v < nvec; v += stride) {

@@ -61,7 +61,12 @@ __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off)
 
 __device__ __forceinline__ void st16(void* base, uint32_t off, const uint4& q)
 {
-    *reinterpret_cast<uint4*>(static_cast<char*>(base) + (off << 4)) = q;
+    if constexpr (IABN_FUSED_NT_STORE) {
+        const u32x4_t v = {q.x, q.y, q.z, q.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(static_cast<char*>(base) + (off << 4)));
+    } else {
+        *reinterpret_cast<uint4*>(static_cast<char*>(base) + (off << 4)) = q;
+    }
 }
 
 // A copy of v the compiler cannot see through: the second pass recomputes its

@@ -25,7 +25,10 @@
 
 namespace iabn {
 
-constexpr int kUnroll = 4;
+#ifndef IABN_REDUCE_UNROLL
+#define IABN_REDUCE_UNROLL 4
+#endif
+constexpr int kUnroll = IABN_REDUCE_UNROLL;
 
 // ---------------------------------------------------------------------------
 // NCHW statistics: workgroup b covers channel c = b / P, partial p = b % P, i.e.
@@ -110,7 +113,20 @@ __global__ __launch_bounds__(kThreads) void k_stats_nchw(
 // of V channels) and partial p = b / slices, i.e. row groups p, p + P, p + 2P, ...
 // of rpi = 256/tpr rows.  Thread t owns channel vector col = sl*tpr + t % tpr
 // and row slot t / tpr of every group; the row slots are then merged by an LDS
-// tree.
+// tree.  On the 16-byte path the walk is software-pipelined: the next kUnroll
+// row groups are loaded (as raw bits) while the current ones are summed.
+template <int DT, int V>
+__device__ __forceinline__ void stats_add(const float (&v)[V], const float (&K)[V], float (&s1)[V],
+                                          float (&s2)[V])
+{
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const float d = v[e] - K[e];
+        s1[e] += d;
+        s2[e] = fmaf(d, d, s2[e]);
+    }
+}
+
 template <int DT, int V>
 __global__ __launch_bounds__(kThreads) void k_stats_nhwc(
     const void* __restrict__ x, int64_t m, int64_t Cv, int tpr, int64_t slices, int64_t groups,
@@ -133,40 +149,58 @@ __global__ __launch_bounds__(kThreads) void k_stats_nhwc(
     int cnt = 0;
     if (active) {
         load_elems<DT, V>(x, col * V, K);
-        int64_t g = p;
-        for (; g + (kUnroll - 1) * P < groups; g += kUnroll * P) {
-            float v[kUnroll][V];
-            bool ok[kUnroll];
+        if constexpr (V == Raw16<DT>::V) {
+            // complete row groups (every row present) run a branch-free pipeline;
+            // the rest, at most one ragged group per workgroup, runs checked
+            const int64_t full = m / rpi;
+            const uint4* xv = reinterpret_cast<const uint4*>(x);
+            auto load_set = [&](uint4 (&buf)[kUnroll], int64_t g0) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t r = (g + u * P) * rpi + rs;
-                ok[u] = r < m;
-                if (ok[u]) load_elems<DT, V>(x, (r * Cv + col) * V, v[u]);
-            }
+                for (int u = 0; u < kUnroll; ++u) buf[u] = xv[((g0 + u * P) * rpi + rs) * Cv + col];
+            };
+            auto add_set = [&](const uint4 (&buf)[kUnroll]) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                if (!ok[u]) continue;
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const float d = v[u][e] - K[e];
-                    s1[e] += d;
-                    s2[e] = fmaf(d, d, s2[e]);
+                for (int u = 0; u < kUnroll; ++u) {
+                    float v[V];
+                    unpack16<DT>(buf[u], v);
+                    stats_add<DT, V>(v, K, s1, s2);
                 }
-                ++cnt;
-            }
-        }
-        for (; g < groups; g += P) {
-            const int64_t r = g * rpi + rs;
-            if (r < m) {
-                float v[V];
-                load_elems<DT, V>(x, (r * Cv + col) * V, v);
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const float d = v[e] - K[e];
-                    s1[e] += d;
-                    s2[e] = fmaf(d, d, s2[e]);
+                cnt += kUnroll;
+            };
+            int64_t g = p;
+            if (g + (kUnroll - 1) * P < full) {
+                uint4 A[kUnroll], B[kUnroll];
+                load_set(A, g);
+                for (;;) {
+                    const int64_t g2 = g + kUnroll * P;
+                    if (g2 + (kUnroll - 1) * P >= full) { add_set(A); g = g2; break; }
+                    load_set(B, g2);
+                    add_set(A);
+                    const int64_t g3 = g2 + kUnroll * P;
+                    if (g3 + (kUnroll - 1) * P >= full) { add_set(B); g = g3; break; }
+                    load_set(A, g3);
+                    add_set(B);
+                    g = g3;
                 }
-                ++cnt;
+            }
+            for (; g < groups; g += P) {
+                const int64_t r = g * rpi + rs;
+                if (r < m) {
+                    float v[V];
+                    unpack16<DT>(xv[r * Cv + col], v);
+                    stats_add<DT, V>(v, K, s1, s2);
+                    ++cnt;
+                }
+            }
+        } else {
+            for (int64_t g = p; g < groups; g += P) {
+                const int64_t r = g * rpi + rs;
+                if (r < m) {
+                    float v[V];
+                    load_elems<DT, V>(x, (r * Cv + col) * V, v);
+                    stats_add<DT, V>(v, K, s1, s2);
+                    ++cnt;
+                }
             }
         }
     }
@@ -310,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nchw(
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             apply_one<ACT, V>(val[u], k[u], a);
-            store_elems<DT, V>(x, (v + u * stride) * V, val[u]);
+            store_out<DT, V>(x, (v + u * stride) * V, val[u]);
         }
     }
     for (; v < nvec; v += stride) {
@@ -319,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nchw(
         const float4 k = cs.get(w.c);
         w.step();
         apply_one<ACT, V>(val, k, a);
-        store_elems<DT, V>(x, v * V, val);
+        store_out<DT, V>(x, v * V, val);
     }
 }
 
@@ -337,6 +371,33 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
         float4 k[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) k[e] = cs.get(c0 + e);
+        if constexpr (IABN_APPLY_REVERSE) {
+            // walk from the end of the tensor down: the rows the statistics pass read
+            // last are the likeliest still to sit in the Infinity Cache
+            const int64_t v0 = v;
+            v = v0 + ((nvec - 1 - v0) / stride) * stride;
+            for (; v - (kUnroll - 1) * stride >= v0; v -= kUnroll * stride) {
+                float val[kUnroll][V];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) load_elems<DT, V>(x, (v - u * stride) * V, val[u]);
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        val[u][e] = act_forward<ACT>(fmaf((val[u][e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+                    store_out<DT, V>(x, (v - u * stride) * V, val[u]);
+                }
+            }
+            for (; v >= v0; v -= stride) {
+                float val[V];
+                load_elems<DT, V>(x, v * V, val);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    val[e] = act_forward<ACT>(fmaf((val[e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+                store_out<DT, V>(x, v * V, val);
+            }
+            return;
+        }
         for (; v + (kUnroll - 1) * stride < nvec; v += kUnroll * stride) {
             float val[kUnroll][V];
 #pragma unroll
@@ -346,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
 #pragma unroll
                 for (int e = 0; e < V; ++e)
                     val[u][e] = act_forward<ACT>(fmaf((val[u][e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
-                store_elems<DT, V>(x, (v + u * stride) * V, val[u]);
+                store_out<DT, V>(x, (v + u * stride) * V, val[u]);
             }
         }
         for (; v < nvec; v += stride) {
@@ -355,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 val[e] = act_forward<ACT>(fmaf((val[e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
-            store_elems<DT, V>(x, v * V, val);
+            store_out<DT, V>(x, v * V, val);
         }
     } else {
         for (; v < nvec; v += stride) {

@@ -73,7 +73,10 @@ constexpr int64_t kApplyBlocksMax = 2048;
 constexpr int64_t kReduceBlocksTarget = 2048;
 // NHWC reductions: fewer, longer-lived workgroups walking row groups with a
 // stride; two per CU.
-constexpr int64_t kNhwcReduceBlocks = 512;
+#ifndef IABN_NHWC_REDUCE_BLOCKS
+#define IABN_NHWC_REDUCE_BLOCKS 512
+#endif
+constexpr int64_t kNhwcReduceBlocks = IABN_NHWC_REDUCE_BLOCKS;
 
 inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, int dtype, bool vec)
 {
