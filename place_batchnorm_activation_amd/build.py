@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libiabn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["fwd.hip", "bwd.hip", "fused_nchw.hip", "api.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "fused_nchw.hip", "fused_nhwc.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

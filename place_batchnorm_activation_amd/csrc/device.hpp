@@ -312,6 +312,16 @@ struct ChannelWalk32 {
     }
 };
 
+// Slice taken by workgroup b of a slice-resident NHWC launch (one workgroup per
+// slice).  Workgroups are dealt to the 8 XCDs round-robin (b runs on XCD b % 8), so
+// when the slice count divides by 8 each XCD takes a contiguous run of slices:
+// neighbouring slices share cache lines and then meet in one L2.  A permutation of
+// [0, slices).
+__host__ __device__ __forceinline__ uint32_t nhwc_slice_of(uint32_t b, uint32_t slices)
+{
+    return (slices % 8 == 0) ? (b % 8) * (slices / 8) + b / 8 : b;
+}
+
 // Walk of a flat NCHW tensor: vector v has channel ((v / HWv) % C).  Advancing v
 // by a fixed stride updates the in-plane offset and the channel with carries.
 struct FlatNCHWWalk {

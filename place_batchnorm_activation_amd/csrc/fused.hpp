@@ -35,6 +35,25 @@
     X(6, 512, 24, 8, 8, false)       \
     X(7, 512, 33, 16, 8, false)
 
+// Slice-resident NHWC kernels.  X(id, T, LPR, NR): T threads; LPR 16-byte lanes
+// of every row per workgroup (a slice of LPR*V channels); NR rows per thread, so
+// one workgroup holds (T/LPR)*NR rows.  The backward keeps y and dy both resident
+// (8*NR VGPRs of data), which bounds NR at 512 threads.  A -D definition of the
+// macro replaces the table.
+#ifndef IABN_FUSED_NHWC_VARIANTS
+#define IABN_FUSED_NHWC_VARIANTS(X) \
+    X(0, 256, 1, 2)                  \
+    X(1, 256, 1, 4)                  \
+    X(2, 256, 1, 8)                  \
+    X(3, 256, 1, 13)                 \
+    X(4, 512, 1, 13)                 \
+    X(5, 512, 1, 18)                 \
+    X(6, 512, 2, 4)                  \
+    X(7, 512, 2, 8)                  \
+    X(8, 512, 2, 13)                 \
+    X(9, 512, 2, 18)
+#endif
+
 namespace iabn {
 
 struct FusedVariant { int id, T, NR; bool dyr; };
@@ -93,11 +112,50 @@ inline bool fused_worthwhile(const Plan& p, int threads)
     return p.C * threads >= int64_t(256) * 256 || bytes <= (int64_t(4) << 20);
 }
 
+// Slice-resident NHWC variant for a problem, or -1.  Wider slices (LPR = 2: a
+// wave reads 32 bytes of each of 32 rows instead of 16 bytes of 64) coalesce
+// better, so they are preferred while they still give at least 128 workgroups;
+// then the first variant (table order) whose workgroup holds all m rows.  The
+// kernels are taken when the slices fill the chip, or when the tensor is small
+// enough for launch latency to rule.  32-bit vector indices address the tensor.
+inline int fused_nhwc_pick(const Plan& p)
+{
+    if (p.layout != kNHWC || !p.vec || p.numel == 0) return -1;
+    if (p.numel * p.esize >= (int64_t(1) << 32)) return -1;
+    const int64_t cv = p.C / p.V;
+    const int64_t bytes = p.numel * p.esize;
+    struct Row { int id, T, LPR, NR; };
+    static const Row tbl[] = {
+#define IABN_ROW(ID, T, LPR, NR) {ID, T, LPR, NR},
+        IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    };
+    const int want = (cv % 2 == 0 && cv / 2 >= 128) ? 2 : 1;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (const auto& v : tbl) {
+            if ((pass == 0) != (v.LPR == want)) continue;
+            if (cv % v.LPR != 0 || int64_t(v.T / v.LPR) * v.NR < p.m) continue;
+            const int64_t blocks = cv / v.LPR;
+            if (blocks * v.T >= int64_t(256) * 256 || bytes <= (int64_t(4) << 20)) return v.id;
+            return -1;
+        }
+    }
+    return -1;
+}
+
 void launch_forward_fused_nchw(const Plan& pl, void* x, const float* gamma, const float* beta,
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
                                int act, float a, hipStream_t s);
 
 void launch_backward_fused_nchw(const Plan& pl, const void* y, const void* dy, void* dx,
+                                const float* gamma, const float* beta, const float* invstd,
+                                float* dgamma, float* dbeta, int act, float a, hipStream_t s);
+
+void launch_forward_fused_nhwc(const Plan& pl, void* x, const float* gamma, const float* beta,
+                               float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                               int act, float a, hipStream_t s);
+
+void launch_backward_fused_nhwc(const Plan& pl, const void* y, const void* dy, void* dx,
                                 const float* gamma, const float* beta, const float* invstd,
                                 float* dgamma, float* dbeta, int act, float a, hipStream_t s);
 

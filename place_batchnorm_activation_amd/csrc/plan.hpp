@@ -51,6 +51,8 @@ struct Plan {
     // channel-resident NCHW kernels (-1: not used for this problem)
     int fused_variant = -1;
     int fused_bwd_variant = -1;
+    // slice-resident NHWC kernels (-1: not used)
+    int nhwc_variant = -1;
     // workspace sections (bytes, 256-aligned)
     size_t off_part_a = 0, off_part_b = 0, off_const = 0, off_count = 0, bytes = 0;
 };

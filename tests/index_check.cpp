@@ -172,6 +172,48 @@ static void check_plan(const Shape& s, bool vec)
                       (long long)i, int(seen[size_t(i)]));
         }
     }
+
+    // ---- slice-resident NHWC kernels: every variant that could hold the rows
+    if (pl.layout == kNHWC && pl.vec && numel * pl.esize < (int64_t(1) << 32)) {
+        const int64_t cv = C / V;
+        struct Var { int T, LPR, NR; };
+        std::vector<Var> vars;
+#define IABN_ROW(ID, T, LPR, NR) vars.push_back({T, LPR, NR});
+        IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+        for (const Var& vv : vars) {
+            const int64_t rps = vv.T / vv.LPR;
+            if (cv % vv.LPR != 0 || rps * vv.NR < m) continue;  // the plan never picks it
+            const uint32_t slices = uint32_t(cv / vv.LPR);
+            std::fill(seen.begin(), seen.end(), 0);
+            std::vector<int> slice_seen(slices, 0);
+            for (uint32_t b = 0; b < slices; ++b) {
+                const uint32_t sl = nhwc_slice_of(b, slices);
+                CHECK(sl < slices, "slice map bounds");
+                if (sl >= slices) continue;
+                slice_seen[sl]++;
+                for (int t = 0; t < vv.T; ++t) {
+                    const uint32_t lane = uint32_t(t) % uint32_t(vv.LPR), rs = uint32_t(t) / uint32_t(vv.LPR);
+                    const uint32_t col = sl * uint32_t(vv.LPR) + lane;
+                    CHECK(col < cv, "slice column");
+                    for (int k = 0; k < vv.NR; ++k) {
+                        const uint32_t row = rs + uint32_t(k) * uint32_t(rps);
+                        if (row < m) {
+                            const uint32_t idx = row * uint32_t(cv) + col;
+                            CHECK(int64_t(idx) == int64_t(row) * cv + col, "32-bit index");
+                            CHECK(int64_t(idx) < nvec, "slice bounds");
+                            if (int64_t(idx) < nvec) seen[size_t(idx)]++;
+                        }
+                    }
+                }
+            }
+            for (uint32_t q = 0; q < slices; ++q)
+                CHECK(slice_seen[q] == 1, "slice %u taken %d times", q, slice_seen[q]);
+            for (int64_t i = 0; i < nvec; ++i)
+                CHECK(seen[size_t(i)] == 1, "slice T=%d LPR=%d NR=%d visits %lld %d times", vv.T,
+                      vv.LPR, vv.NR, (long long)i, int(seen[size_t(i)]));
+        }
+    }
 }
 
 int main(int argc, char** argv)
@@ -189,7 +231,8 @@ int main(int argc, char** argv)
         {4, 32, 14, 14, kNCHW, kF32}, {8, 512, 7, 7, kNHWC, kBF16}, {4, 64, 16, 16, kNCHW, kF32},
         {4, 64, 16, 16, kNHWC, kBF16}, {4, 32, 12, 12, kNCHW, kF32}, {4, 256, 12, 12, kNHWC, kBF16},
         {2, 16, 8, 8, kNCHW, kF32}, {2, 16, 8, 8, kNHWC, kBF16}, {2, 16, 8, 8, kNCHW, kBF16},
-        {2, 16, 8, 8, kNHWC, kF32},
+        {2, 16, 8, 8, kNHWC, kF32},      {64, 1024, 7, 7, kNHWC, kF32}, {32, 2048, 14, 14, kNHWC, kBF16},
+        {2, 64, 1, 1, kNHWC, kBF16},     {5, 96, 11, 13, kNHWC, kBF16},   {3, 40, 7, 9, kNHWC, kF32},
     };
     std::mt19937_64 rng(12345);
     const int n_random = argc > 1 ? std::atoi(argv[1]) : 300;

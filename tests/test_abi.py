@@ -135,6 +135,12 @@ def test_plan_choice_for_the_workloads():
         "forward=channel_resident(256x13) backward=channel_resident(256x13,dy_resident)")
     assert d(2, 4, 8, 8, "NCHW", iabn.F32, "leaky_relu").startswith("forward=channel_resident")
     assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_resident(512x2x13) backward=slice_resident(512x2x13)"
+    # too many rows for a workgroup to hold: split
+    assert d(2, 16, 80, 80, "NHWC", iabn.F32, "leaky_relu").startswith("forward=split")
+    # few slices on a large tensor: split
+    assert d(16, 16, 28, 28, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
     # misaligned or ragged planes take the scalar split path
     assert "scalar" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
     assert "scalar" in d(3, 5, 17, 19, "NCHW", iabn.F32, "leaky_relu")

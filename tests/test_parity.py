@@ -59,7 +59,9 @@ for layout in ("NCHW", "NHWC"):
             if layout == "NCHW":
                 shapes = [(4, 6, 16, 20), (3, 5, 17, 19)]
             else:
-                shapes = [(3, 24, 9, 11), (2, 13, 10, 7), (2, 200, 12, 12)]
+                # the first three fit the slice-resident kernels; the last has too
+                # many rows for them and takes the split path
+                shapes = [(3, 24, 9, 11), (2, 13, 10, 7), (2, 200, 12, 12), (2, 16, 80, 80)]
             for s in shapes:
                 MID.append(custom(base, *s, layout=layout, dtype=dtype, act=act, act_param=p))
 
@@ -240,6 +242,70 @@ def _variant_shapes():
             out.append(custom(4, 2, 3, 1, vc * V // 2, layout="NCHW", dtype=dtype, act="elu",
                               act_param=1.0))
     return out
+
+
+# every slice-resident NHWC variant, picked through the row count it holds
+# (one lane per row: capacities 512, 1024, 2048, 3328, 6656, 9216 rows), full and
+# ragged; slice counts that divide by 8 (XCD-grouped slice map) and ones that do not
+def _slice_shapes():
+    out = []
+    for dtype, C in (("f32", 96), ("bf16", 256)):
+        base = 2 if dtype == "f32" else 3
+        for N, H, W in ((2, 16, 16), (5, 10, 10), (4, 16, 16), (4, 10, 25), (2, 32, 32),
+                        (5, 20, 20), (4, 25, 33), (4, 32, 52), (3, 40, 50)):
+            out.append(custom(base, N, C, H, W, layout="NHWC", dtype=dtype))
+    out.append(custom(2, 3, 96, 50, 60, layout="NHWC", dtype="f32"))      # 9000 rows
+    out.append(custom(2, 4, 96, 48, 48, layout="NHWC", dtype="f32"))      # 9216 rows
+    out.append(custom(3, 3, 128, 50, 60, layout="NHWC", dtype="bf16"))
+    out.append(custom(3, 4, 128, 48, 48, layout="NHWC", dtype="bf16"))
+    # two lanes per row (vectors per row >= 256): capacities 1024, 2048, 3328, 4608
+    for N, H, W in ((4, 10, 25), (5, 20, 20), (4, 25, 33), (5, 30, 30)):
+        out.append(custom(5, N, 2048, H, W, layout="NHWC", dtype="bf16"))
+    out.append(custom(2, 64, 1024, 7, 7, layout="NHWC", dtype="f32"))
+    out.append(custom(4, 4, 1024, 32, 36, layout="NHWC", dtype="f32", act="elu", act_param=1.0))
+    out.append(custom(3, 4, 48, 25, 33, layout="NHWC", dtype="bf16"))     # 6 slices
+    out.append(custom(2, 2, 20, 7, 9, layout="NHWC", dtype="f32"))        # 5 slices
+    out.append(custom(4, 4, 256, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0))
+    out.append(custom(4, 3, 512, 12, 12, layout="NHWC", dtype="bf16", act="elu", act_param=0.5))
+    out.append(custom(3, 4, 256, 16, 16, layout="NHWC", dtype="bf16", act="identity",
+                      act_param=0.0))
+    return out
+
+
+@pytest.mark.parametrize("wl", _slice_shapes(), ids=lambda w: w.name)
+def test_slice_resident_variants(wl):
+    desc = iabn.iabn_describe_plan(wl.N, wl.C, wl.H, wl.W, wl.layout,
+                                   workloads.storage_torch_dtype(wl.dtype), wl.act)
+    print(desc)
+    assert "slice_resident" in desc
+    full_check(wl)
+
+
+# Channels whose first element -- the pivot of the shifted sums -- lies 8 standard
+# deviations from the mean (alternating sides): the statistics must not lose
+# accuracy to the shift.  One case per kernel family.
+OUTLIER = [custom(2, 4, 32, 16, 16),                                   # NCHW channel-resident
+           custom(2, 3, 5, 17, 19),                                    # NCHW split, scalar
+           custom(3, 4, 256, 25, 33, layout="NHWC", dtype="bf16"),     # NHWC slice-resident
+           custom(2, 4, 96, 25, 33, layout="NHWC", dtype="f32"),
+           custom(2, 2, 16, 80, 80, layout="NHWC", dtype="f32")]       # NHWC split
+
+
+@pytest.mark.parametrize("wl", OUTLIER, ids=lambda w: w.name)
+def test_outlier_pivot(wl):
+    inp = workloads.make_inputs(wl)
+    x = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    mu, sd = x.mean(axis=(0, 2, 3)), x.std(axis=(0, 2, 3))
+    side = np.where(np.arange(wl.C) % 2 == 0, 1.0, -1.0)
+    x[0, :, 0, 0] = mu + side * 8.0 * sd
+    inp = dataclasses.replace(inp, x=workloads.to_storage(x, wl.layout, wl.dtype))
+    print("case:", wl.name, "outlier pivots", flush=True)
+    run = harness.run_gpu(inp)
+    ef = harness.check_forward(inp, run)
+    eb = harness.check_backward(inp, run)
+    print("  forward", ef, "\n  backward", eb, flush=True)
+    harness.assert_within(ef, wl.dtype, "forward " + wl.name)
+    harness.assert_within(eb, wl.dtype, "backward " + wl.name)
 
 
 @pytest.mark.parametrize("wl", _variant_shapes(), ids=lambda w: w.name)
