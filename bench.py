@@ -42,7 +42,8 @@ COLD_BYTES = 512 << 20
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("device.hpp", "plan.hpp", "fused.hpp", "fwd.hip", "bwd.hip", "fused_nchw.hip"):
+    for f in ("device.hpp", "plan.hpp", "fused.hpp", "fwd.hip", "bwd.hip", "fused_nchw.hip",
+              "fused_nhwc.hip"):
         with open(os.path.join(ROOT, "place_batchnorm_activation_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -188,8 +189,11 @@ def main() -> int:
     # iabn_forward_train / iabn_backward is one kernel; with the split path the
     # single-kernel stages (apply) are timed through the stage entry points.
     plan = iabn.iabn_describe_plan(N, C, H, W, wl.layout, x0.dtype, wl.act)
-    fused_fwd = plan.split()[0].startswith("forward=channel_resident")
-    fused_bwd = plan.split()[1].startswith("backward=channel_resident")
+    # kernel family of each pass: channel_resident / slice_resident (one kernel) or split
+    fam_fwd = plan.split()[0].split("=", 1)[1].split("(", 1)[0]
+    fam_bwd = plan.split()[1].split("=", 1)[1].split("(", 1)[0]
+    fused_fwd = fam_fwd != "split"
+    fused_bwd = fam_bwd != "split"
 
     def event_loop(calls):
         acc = np.zeros(len(calls))
@@ -218,9 +222,9 @@ def main() -> int:
     # path's apply kernels 2S and 3S
     kernels = {}
     if fused_fwd:
-        kernels["fwd_channel_resident"] = (call_us[0], 3 * S)
+        kernels["fwd_" + fam_fwd] = (call_us[0], 3 * S)
     if fused_bwd:
-        kernels["bwd_channel_resident"] = (call_us[1], 5 * S)
+        kernels["bwd_" + fam_bwd] = (call_us[1], 5 * S)
     if not (fused_fwd and fused_bwd):
         names = ["forward_stats", "forward_apply", "backward_reduce", "backward_apply"]
         st_us = event_loop([(lambda s, f=f: f(s)) for f in (lambda s: stages(s)[0](),
