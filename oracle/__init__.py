@@ -16,7 +16,7 @@ import numpy as np
 from . import build as _build
 
 ACT = {"identity": 0, "leaky_relu": 1, "elu": 2}
-STORE = {"f64": 0, "f32": 1, "bf16": 2}
+STORE = {"f64": 0, "f32": 1, "bf16": 2, "f16": 3}
 
 _lib = None
 _D = ctypes.POINTER(ctypes.c_double)
@@ -47,6 +47,8 @@ def _load():
                                      ctypes.c_double, ctypes.c_double, _D]
     lib.orc_backward_from_y.argtypes = [_I64, _I64, _I64, _D, _D, _D, _D, _D, ctypes.c_int,
                                         ctypes.c_double, _D, _D, _D, _D]
+    lib.orc_backward_eval.argtypes = [_I64, _I64, _I64, _D, _D, _D, _D, _D, ctypes.c_double,
+                                      ctypes.c_int, ctypes.c_double, _D, _D, _D]
     lib.orc_backward_from_y_form2.argtypes = [_I64, _I64, _I64, _D, _D, _D, _D, _D, ctypes.c_int,
                                               ctypes.c_double, _D, _D, _D]
     lib.orc_backward_from_x.argtypes = [_I64, _I64, _I64, _D, _D, _D, _D, ctypes.c_int,
@@ -54,7 +56,7 @@ def _load():
     lib.orc_round_storage.argtypes = [_D, _I64, ctypes.c_int]
     lib.orc_num_threads.argtypes = []
     for f in (lib.orc_forward_train, lib.orc_forward_eval, lib.orc_backward_from_y,
-              lib.orc_backward_from_y_form2, lib.orc_backward_from_x, lib.orc_round_storage,
+              lib.orc_backward_eval, lib.orc_backward_from_y_form2, lib.orc_backward_from_x, lib.orc_round_storage,
               lib.orc_num_threads):
         f.restype = ctypes.c_int
     _lib = lib
@@ -131,6 +133,21 @@ def backward_from_y(y, dy, gamma, beta, invstd, act="leaky_relu", act_param=0.01
     if want_xhat:
         out["xhat"] = xh
     return out
+
+
+def backward_eval(y, dy, gamma, beta, running_var, act="leaky_relu", act_param=0.01, eps=1e-5):
+    """Backward through the inference forward (frozen running statistics), from
+    the stored y.  Returns dict dx, dgamma, dbeta."""
+    y, dy = _f64(y), _f64(dy)
+    N, C, HW = _shape(y)
+    dx = np.empty_like(y)
+    dg, db = np.empty(C), np.empty(C)
+    rc = _load().orc_backward_eval(N, C, HW, _p(y), _p(dy), _p(_f64(gamma)), _p(_f64(beta)),
+                                   _p(_f64(running_var)), float(eps), ACT[act], float(act_param),
+                                   _p(dx), _p(dg), _p(db))
+    if rc != 0:
+        raise ValueError("oracle backward_eval rejected its arguments")
+    return {"dx": dx, "dgamma": dg, "dbeta": db}
 
 
 def backward_from_y_form2(y, dy, gamma, beta, invstd, act="leaky_relu", act_param=0.01):

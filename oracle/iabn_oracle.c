@@ -42,6 +42,7 @@
 #define ORC_STORE_F64 0
 #define ORC_STORE_F32 1
 #define ORC_STORE_BF16 2
+#define ORC_STORE_F16 3
 
 /* ---------------------------------------------------------------------------
  * Invertible activations (section 3, "INPLACE-ABN": the activation must be
@@ -234,6 +235,43 @@ int orc_backward_from_y(int64_t N, int64_t C, int64_t HW,
 }
 
 /* ---------------------------------------------------------------------------
+ * Backward through the inference forward, with the normalisation statistics
+ * frozen: the running mean and variance are constants of the layer, as in the
+ * "Eval mode" of a pre-trained network being fine-tuned (the "Problem" section
+ * of the page "Efficient ConvBN Blocks for Transfer Learning and Beyond").  It is
+ * the chain rule of orc_forward_eval, taken from the stored output y:
+ *   z = act^-1(y),  dz = act'(z) dy,  xhat = (z - beta_c) / gamma_c,
+ *   dx = gamma_c dz / sqrt(running_var_c + eps),
+ *   dbeta_c = sum dz,  dgamma_c = sum dz xhat.
+ * No term through the batch statistics: here they are not functions of x.
+ */
+int orc_backward_eval(int64_t N, int64_t C, int64_t HW,
+                      const double *y, const double *dy,
+                      const double *gamma, const double *beta, const double *running_var,
+                      double eps, int act, double p,
+                      double *dx, double *dgamma, double *dbeta)
+{
+    if (C < 0 || N < 0 || HW < 0 || !act_valid(act, p) || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        const double k = gamma[c] / sqrt(running_var[c] + eps);
+        double sdz = 0.0, sdzx = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t i = 0; i < HW; ++i) {
+                const double yy = y[AT(n, c, i)];
+                const double z = act_inverse(act, p, yy);
+                const double dz = act_derivative_from_y(act, p, yy) * dy[AT(n, c, i)];
+                sdz += dz;
+                sdzx += dz * (z - beta[c]) / gamma[c];
+                dx[AT(n, c, i)] = k * dz;
+            }
+        dbeta[c] = sdz;
+        dgamma[c] = sdzx;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Form II (section 3, "INPLACE-ABN" II): the gradients written directly in
  * terms of z = act^-1(y), so the affine recovery becomes per-channel constants:
  *   dbeta_c = sum dz,
@@ -331,7 +369,9 @@ int orc_backward_from_x(int64_t N, int64_t C, int64_t HW,
  * value is the exact result rounded to nearest, ties to even.
  *   ORC_STORE_F64: unchanged; ORC_STORE_F32: IEEE binary32;
  *   ORC_STORE_BF16: 8 significant bits, binary32 exponent range, subnormal
- *   quantum 2^-133, overflow to infinity.
+ *   quantum 2^-133, overflow to infinity;
+ *   ORC_STORE_F16: IEEE binary16, 11 significant bits, normal range down to
+ *   2^-14, subnormal quantum 2^-24, largest finite 65504, overflow to infinity.
  */
 static double round_bf16(double v)
 {
@@ -350,12 +390,31 @@ static double round_bf16(double v)
     return r;
 }
 
+static double round_f16(double v)
+{
+    if (!isfinite(v) || v == 0.0) return v;
+    double r;
+    if (fabs(v) < ldexp(1.0, -14)) {
+        r = ldexp(nearbyint(ldexp(v, 24)), -24);
+    } else {
+        int e;
+        const double f = frexp(v, &e);          /* v = f 2^e, 0.5 <= |f| < 1 */
+        r = ldexp(nearbyint(ldexp(f, 11)), e - 11);
+    }
+    if (fabs(r) > 65504.0) r = copysign(INFINITY, v);
+    return r;
+}
+
 int orc_round_storage(double *v, int64_t count, int storage)
 {
     if (storage == ORC_STORE_F64) return 0;
-    if (storage != ORC_STORE_F32 && storage != ORC_STORE_BF16) return -1;
+    if (storage != ORC_STORE_F32 && storage != ORC_STORE_BF16 && storage != ORC_STORE_F16)
+        return -1;
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < count; ++i)
-        v[i] = storage == ORC_STORE_F32 ? (double)(float)v[i] : round_bf16(v[i]);
+    for (int64_t i = 0; i < count; ++i) {
+        if (storage == ORC_STORE_F32) v[i] = (double)(float)v[i];
+        else if (storage == ORC_STORE_BF16) v[i] = round_bf16(v[i]);
+        else v[i] = round_f16(v[i]);
+    }
     return 0;
 }

@@ -8,7 +8,9 @@
   * invariants: mean(xhat) = 0, mean(xhat^2) = v/(v+eps), sum dx = 0 per channel;
   * brute force (pure Python loops) for the statistics on a tiny case;
   * closed form of the running statistics after k steps;
-  * storage rounding against numpy / torch casts.
+  * storage rounding against numpy / torch casts;
+  * the backward with frozen statistics against PyTorch's inference-mode
+    batch_norm + activation under autograd, and against finite differences.
 """
 import dataclasses
 from fractions import Fraction
@@ -114,6 +116,70 @@ def test_eval_forward_matches_torch(act, p):
     z = F.batch_norm(torch.tensor(x), torch.tensor(rm), torch.tensor(rv), torch.tensor(g),
                      torch.tensor(b), training=False, eps=1e-4)
     assert _rel(y, _torch_act(z, act, p).numpy()) < 1e-13
+
+
+EVAL_ACTS = [("leaky_relu", 0.01), ("elu", 1.0), ("elu", 0.5), ("identity", 0.0),
+             ("leaky_relu", 0.2)]
+
+
+def _eval_case(seed=17, shape=(3, 5, 4, 3)):
+    rng = np.random.default_rng(seed)
+    C = shape[1]
+    x = rng.normal(0.3, 2.0, size=shape)
+    dy = rng.normal(size=shape)
+    g = rng.uniform(0.5, 1.5, C) * np.where(np.arange(C) % 2 == 0, 1.0, -1.0)
+    b = rng.normal(0, 0.3, C)
+    rm = rng.normal(0, 1, C)
+    rv = rng.uniform(0.2, 3.0, C)
+    return x, dy, g, b, rm, rv
+
+
+@pytest.mark.parametrize("act,p", EVAL_ACTS)
+def test_eval_backward_matches_torch(act, p):
+    """Frozen statistics: torch's inference-mode batch_norm treats the running
+    statistics as constants, so its autograd is the reference."""
+    x, dy, g, b, rm, rv = _eval_case()
+    eps = 1e-4
+    y = oracle.forward_eval(x, g, b, rm, rv, act, p, eps)
+    bw = oracle.backward_eval(y, dy, g, b, rv, act, p, eps)
+    xt = torch.tensor(x, requires_grad=True)
+    gt = torch.tensor(g, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    z = F.batch_norm(xt, torch.tensor(rm), torch.tensor(rv), gt, bt, training=False, eps=eps)
+    _torch_act(z, act, p).backward(torch.tensor(dy))
+    tol = 1e-9 if act == "elu" else 1e-12
+    assert _rel(bw["dx"], xt.grad.numpy()) < tol
+    assert _rel(bw["dgamma"], gt.grad.numpy()) < tol
+    assert _rel(bw["dbeta"], bt.grad.numpy()) < tol
+
+
+def test_eval_backward_matches_finite_differences():
+    x, dy, g, b, rm, rv = _eval_case(seed=23, shape=(2, 3, 3, 2))
+    act, p, eps = "elu", 0.7, 1e-3
+
+    def loss(xx, gg, bb):
+        return float(np.sum(dy * oracle.forward_eval(xx, gg, bb, rm, rv, act, p, eps)))
+
+    y = oracle.forward_eval(x, g, b, rm, rv, act, p, eps)
+    bw = oracle.backward_eval(y, dy, g, b, rv, act, p, eps)
+    h = 1e-6
+    for i in range(x.size):
+        xp, xm = x.copy(), x.copy()
+        xp.reshape(-1)[i] += h
+        xm.reshape(-1)[i] -= h
+        fd = (loss(xp, g, b) - loss(xm, g, b)) / (2 * h)
+        assert abs(fd - bw["dx"].reshape(-1)[i]) <= 1e-6 * (abs(fd) + 1.0)
+    for c in range(x.shape[1]):
+        gp, gm = g.copy(), g.copy()
+        gp[c] += h
+        gm[c] -= h
+        fd = (loss(x, gp, b) - loss(x, gm, b)) / (2 * h)
+        assert abs(fd - bw["dgamma"][c]) <= 1e-6 * (abs(fd) + 1.0)
+        bp, bm = b.copy(), b.copy()
+        bp[c] += h
+        bm[c] -= h
+        fd = (loss(x, g, bp) - loss(x, g, bm)) / (2 * h)
+        assert abs(fd - bw["dbeta"][c]) <= 1e-6 * (abs(fd) + 1.0)
 
 
 def test_backward_matches_finite_differences():
@@ -321,6 +387,22 @@ def test_round_storage_bf16_matches_torch_on_f32_values():
     # halfway cases round to even
     assert oracle.round_storage(np.array([1.0 + 2 ** -8]), "bf16")[0] == 1.0
     assert oracle.round_storage(np.array([1.0 + 3 * 2 ** -8]), "bf16")[0] == 1.0 + 2 ** -6
+
+
+def test_round_storage_f16_matches_numpy_on_f32_values():
+    """numpy's float32 -> float16 cast rounds to nearest even, with subnormals and
+    overflow to infinity; on float32 inputs one rounding from fp64 is the same."""
+    rng = np.random.default_rng(12)
+    f32 = np.concatenate([
+        (rng.normal(size=4000) * 10.0 ** rng.uniform(-9, 5, 4000)).astype(np.float32),
+        np.array([1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, -(1.0 + 2 ** -11), 2 ** -25, 3 * 2 ** -26,
+                  2 ** -24, 65504.0, 65519.0, 65520.0, -70000.0, 6.1e-5], np.float32)])
+    r = oracle.round_storage(f32.astype(np.float64), "f16")
+    with np.errstate(over="ignore"):
+        ref = f32.astype(np.float16).astype(np.float64)
+    assert np.array_equal(r, ref)
+    assert oracle.round_storage(np.array([1.0 + 2 ** -11]), "f16")[0] == 1.0
+    assert oracle.round_storage(np.array([65520.0]), "f16")[0] == np.inf
 
 
 def test_oracle_rejects_invalid_arguments():

@@ -42,6 +42,17 @@ MUTANTS = {
                          "const double xhat = z / gamma[c];\n                sdz += dz;"),
     "bf16_truncates": ("r = ldexp(nearbyint(ldexp(f, 8)), e - 8);",
                        "r = ldexp(trunc(ldexp(f, 8)), e - 8);"),
+    "eval_backward_drops_slope": ("const double dz = act_derivative_from_y(act, p, yy) * dy[AT(n, c, i)];\n"
+                                  "                sdz += dz;\n                sdzx += dz * (z - beta[c]) / gamma[c];",
+                                  "const double dz = dy[AT(n, c, i)];\n"
+                                  "                sdz += dz;\n                sdzx += dz * (z - beta[c]) / gamma[c];"),
+    "eval_backward_eps_outside_root": ("const double k = gamma[c] / sqrt(running_var[c] + eps);",
+                                       "const double k = gamma[c] / (sqrt(running_var[c]) + eps);"),
+    "eval_backward_keeps_beta": ("sdzx += dz * (z - beta[c]) / gamma[c];",
+                                 "sdzx += dz * z / gamma[c];"),
+    "f16_flushes_subnormals": ("r = ldexp(nearbyint(ldexp(v, 24)), -24);", "r = 0.0 * v;"),
+    "f16_wrong_precision": ("r = ldexp(nearbyint(ldexp(f, 11)), e - 11);",
+                            "r = ldexp(nearbyint(ldexp(f, 10)), e - 10);"),
     "gamma_not_applied": ("const double z = gamma[c] * xhat + beta[c];\n"
                           "                y[AT(n, c, i)] = act_forward(act, p, z);",
                           "const double z = xhat + beta[c];\n"
@@ -63,6 +74,9 @@ def _pin_suite():
         ("running_closed_form", pins.test_running_statistics_closed_form),
         ("bf16_rounding", pins.test_round_storage_bf16_matches_torch_on_f32_values),
         ("eval", lambda: pins.test_eval_forward_matches_torch("elu", 1.0)),
+        ("eval_backward", lambda: pins.test_eval_backward_matches_torch("leaky_relu", 0.2)),
+        ("eval_backward_fd", pins.test_eval_backward_matches_finite_differences),
+        ("f16_rounding", pins.test_round_storage_f16_matches_numpy_on_f32_values),
     ]
     failed = []
     for name, fn in cases:
