@@ -184,6 +184,31 @@ iabn_status iabn_backward_apply(const void *y, const void *dy, void *dx,
                                 void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* Backward through iabn_forward_eval: the running statistics are frozen
+ * constants of the layer, as when a pre-trained network is fine-tuned with its
+ * normalisation statistics fixed (the "Eval mode" in the "Problem" section of
+ * "Efficient ConvBN Blocks for Transfer Learning and Beyond").  The chain rule of
+ * the inference forward, taken from the stored output alone:
+ *   z = act^-1(y), dz = act'(z)*dy (both from y),
+ *   dx = gamma_c * dz / sqrt(running_var_c + eps),
+ *   dbeta_c = sum dz, dgamma_c = sum dz*(z - beta_c)/gamma_c.
+ *   y, dy, dx    as for iabn_backward (dx may be exactly dy)
+ *   gamma, beta, running_var, eps   in: the values iabn_forward_eval used
+ *                (gamma_c != 0, eps >= 0)
+ *   dgamma, dbeta out fp32 [C], both or neither may be NULL; when NULL the sums
+ *                are skipped and only dx is written
+ *   Needs m >= 1.  C == 0 is a no-op.  Workspace as for the forward.
+ * HBM traffic: 3S for dx (read y, dy; write dx), 2S more for the sums. */
+iabn_status iabn_backward_eval(const void *y, const void *dy, void *dx,
+                               int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype,
+                               const float *gamma, const float *beta,
+                               const float *running_var, float eps,
+                               float *dgamma, float *dbeta,
+                               iabn_act act, float act_param,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Describes, as a short text, the kernels that iabn_forward_train and
  * iabn_backward launch for this problem when every tensor pointer is 16-byte
  * aligned (aligned16 != 0) or not, e.g.

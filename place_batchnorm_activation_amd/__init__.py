@@ -58,10 +58,12 @@ lib.iabn_backward.argtypes = [_P, _P, _P] + _SHAPE + [_P, _P, _P, _P, _P, _INT, 
 lib.iabn_backward_reduce.argtypes = [_P, _P] + _SHAPE + [_P, _P, _P, _P, _P, _INT, _F, _P, _SZ,
                                                          _P]
 lib.iabn_backward_apply.argtypes = [_P, _P, _P] + _SHAPE + [_INT, _F, _P, _SZ, _P]
+lib.iabn_backward_eval.argtypes = [_P, _P, _P] + _SHAPE + [_P, _P, _P, _F, _P, _P, _INT, _F, _P,
+                                                           _SZ, _P]
 lib.iabn_describe_plan.argtypes = _SHAPE + [_INT, _INT, ctypes.c_char_p, _SZ]
 lib.iabn_describe_plan.restype = _INT
 for _fn in ("iabn_forward_train", "iabn_forward_stats", "iabn_forward_apply", "iabn_forward_eval",
-            "iabn_backward", "iabn_backward_reduce", "iabn_backward_apply"):
+            "iabn_backward", "iabn_backward_reduce", "iabn_backward_apply", "iabn_backward_eval"):
     getattr(lib, _fn).restype = _INT
 
 
@@ -186,6 +188,15 @@ def iabn_backward_apply(y, dy, dx, N, C, H, W, layout, act, act_param, workspace
     wp, wb = _ws(workspace)
     _check("iabn_backward_apply", lib.iabn_backward_apply(
         _ptr(y), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y),
+        _code(act, ACTS), act_param, wp, wb, _stream(stream)))
+
+
+def iabn_backward_eval(y, dy, dx, N, C, H, W, layout, gamma, beta, running_var, eps, dgamma,
+                       dbeta, act, act_param, workspace, stream=None):
+    wp, wb = _ws(workspace)
+    _check("iabn_backward_eval", lib.iabn_backward_eval(
+        _ptr(y), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y),
+        _ptr(gamma), _ptr(beta), _ptr(running_var), eps, _ptr(dgamma), _ptr(dbeta),
         _code(act, ACTS), act_param, wp, wb, _stream(stream)))
 
 

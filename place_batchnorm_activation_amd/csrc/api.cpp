@@ -325,6 +325,44 @@ iabn_status iabn_backward(const void* y, const void* dy, void* dx, int64_t N, in
     return launched();
 }
 
+iabn_status iabn_backward_eval(const void* y, const void* dy, void* dx, int64_t N, int64_t C,
+                               int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
+                               const float* gamma, const float* beta, const float* running_var,
+                               float eps, float* dgamma, float* dbeta, iabn_act act,
+                               float act_param, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    IABN_TRY(check_shape(N, C, H, W, layout, dtype));
+    IABN_TRY(check_act(act, act_param));
+    if (!(eps >= 0.f) || !isfinite(eps)) return IABN_ERR_INVALID_ARG;
+    if ((dgamma == nullptr) != (dbeta == nullptr)) return IABN_ERR_INVALID_ARG;
+    if (C == 0) return IABN_OK;
+    if (N * H * W < 1) return IABN_ERR_INVALID_ARG;
+    IABN_TRY(check_tensor(y, dtype));
+    IABN_TRY(check_tensor(dy, dtype));
+    IABN_TRY(check_tensor(dx, dtype));
+    const size_t bytes = size_t(N * C * H * W) * (dtype == IABN_F32 ? 4 : 2);
+    if (overlap(dx, y, bytes)) return IABN_ERR_INVALID_ARG;
+    if (dx != dy && overlap(dx, dy, bytes)) return IABN_ERR_INVALID_ARG;
+    IABN_TRY(check_channel_vec(gamma, true));
+    IABN_TRY(check_channel_vec(beta, true));
+    IABN_TRY(check_channel_vec(running_var, true));
+    IABN_TRY(check_channel_vec(dgamma, false));
+    IABN_TRY(check_channel_vec(dbeta, false));
+    const Plan pr = plan_for(N, C, H, W, layout, dtype, aligned(y, 16) && aligned(dy, 16));
+    const Plan pa = plan_for(N, C, H, W, layout, dtype,
+                             aligned(y, 16) && aligned(dy, 16) && aligned(dx, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pr));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pa));
+    if (dgamma)
+        launch_backward_reduce(pr, y, dy, gamma, beta, nullptr, dgamma, dbeta, act, act_param,
+                               workspace, stream, running_var, eps);
+    else
+        launch_eval_consts(pa, gamma, beta, running_var, eps, workspace, stream);
+    launch_backward_apply(pa, y, dy, dx, act, act_param, workspace, stream);
+    return launched();
+}
+
 int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
                        iabn_dtype dtype, iabn_act act, int aligned16, char* buf, size_t len)
 {

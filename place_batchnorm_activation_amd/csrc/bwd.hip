@@ -214,10 +214,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
 // Finishing the sums: thread t of a 1024-thread workgroup takes channel
 // t % kFinChannels and partials p = t / kFinChannels + k*kFinPhases, adds them in
 // fp64, and the phases are added in a fixed order.
+//
+// frozen_var non-null: the statistics are the frozen running ones (the backward
+// through the inference forward), so dx = gamma*dz/sqrt(frozen_var + eps): the
+// constants become {A, 0, 0, beta}, and dgamma, dbeta are the same sums.
 __global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     int64_t C, int64_t m, int64_t P, const float* __restrict__ part_dz,
     const float* __restrict__ part_dzt, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* __restrict__ invstd,
+    const float* __restrict__ frozen_var, float eps,
     float* __restrict__ dgamma, float* __restrict__ dbeta, float4* __restrict__ consts)
 {
     const int cl = threadIdx.x % kFinChannels;
@@ -242,9 +247,26 @@ __global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     const double dg = s2 / g;
     dbeta[c] = float(db);
     dgamma[c] = float(dg);
+    if (frozen_var) {
+        consts[c] = make_float4(float(g / sqrt(double(frozen_var[c]) + double(eps))), 0.f, 0.f,
+                                beta[c]);
+        return;
+    }
     const double A = g * double(invstd[c]);
     const double md = double(m);
     consts[c] = make_float4(float(A), float(-A * dg / (md * g)), float(-A * db / md), beta[c]);
+}
+
+// The dx constants of the backward through the inference forward when dgamma and
+// dbeta are not wanted: {gamma/sqrt(running_var + eps), 0, 0, beta} per channel.
+__global__ __launch_bounds__(kThreads) void k_eval_consts(
+    int64_t C, const float* __restrict__ gamma, const float* __restrict__ beta,
+    const float* __restrict__ running_var, float eps, float4* __restrict__ consts)
+{
+    const int64_t c = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (c >= C) return;
+    consts[c] = make_float4(float(double(gamma[c]) / sqrt(double(running_var[c]) + double(eps))),
+                            0.f, 0.f, beta[c]);
 }
 
 // ---------------------------------------------------------------------------
@@ -408,7 +430,8 @@ static void launch_reduce_dv(const Plan& pl, const void* y, const void* dy, cons
 
 void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const float* gamma,
                             const float* beta, const float* invstd, float* dgamma, float* dbeta,
-                            int act, float a, void* ws, hipStream_t s)
+                            int act, float a, void* ws, hipStream_t s, const float* frozen_var,
+                            float eps)
 {
     char* wsb = static_cast<char*>(ws);
     float* pa = reinterpret_cast<float*>(wsb + pl.off_part_a);
@@ -424,7 +447,15 @@ void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const
     }
     hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
                        dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta, invstd,
-                       dgamma, dbeta, consts);
+                       frozen_var, eps, dgamma, dbeta, consts);
+}
+
+void launch_eval_consts(const Plan& pl, const float* gamma, const float* beta,
+                        const float* running_var, float eps, void* ws, hipStream_t s)
+{
+    float4* consts = reinterpret_cast<float4*>(static_cast<char*>(ws) + pl.off_const);
+    hipLaunchKernelGGL(k_eval_consts, dim3(unsigned(ceil_div(pl.C, kThreads))), dim3(kThreads), 0,
+                       s, pl.C, gamma, beta, running_var, eps, consts);
 }
 
 template <int DT, int V, int ACT>

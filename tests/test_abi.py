@@ -124,6 +124,27 @@ def test_backward_validation():
                 ws=None) == OK
 
 
+def _bev(y=A, dy=2 * A, dx=3 * A, N=2, C=3, H=4, W=4, layout=0, dtype=0, g=A, b=A, rv=A,
+         eps=1e-5, dg=A, db=A, act=1, p=0.01, ws=A, wsb=1 << 20):
+    return lib.iabn_backward_eval(y, dy, dx, N, C, H, W, layout, dtype, g, b, rv, eps, dg, db,
+                                  act, p, ws, wsb, None)
+
+
+def test_backward_eval_validation():
+    assert _bev(act=2, p=-1.0) == INVALID
+    assert _bev(eps=-1e-3) == INVALID
+    assert _bev(eps=float("nan")) == INVALID
+    assert _bev(dg=None) == INVALID             # dgamma and dbeta: both or neither
+    assert _bev(rv=None) == INVALID
+    assert _bev(dx=A) == INVALID                # dx aliases y
+    assert _bev(dx=2 * A + 64) == INVALID       # dx partly overlaps dy
+    assert _bev(N=0) == INVALID                 # m = 0 with channels
+    assert _bev(ws=None) == WS
+    assert _bev(dtype=1, dy=2 * A + 1) == MISALIGNED
+    assert _bev(C=0, y=None, dy=None, dx=None, g=None, b=None, rv=None, dg=None, db=None,
+                ws=None) == OK
+
+
 def test_plan_choice_for_the_workloads():
     """Which kernels each workload runs (host-side plan; no GPU needed)."""
     d = iabn.iabn_describe_plan

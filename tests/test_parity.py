@@ -362,6 +362,57 @@ def test_forward_eval(wl):
     assert e <= harness.TOL[wl.dtype], e
 
 
+# Backward through the inference forward (frozen running statistics): the GPU's
+# own y from iabn_forward_eval, then iabn_backward_eval, against the oracle fed
+# those y bits.  With and without dgamma/dbeta; vector and scalar paths; both
+# layouts and storage dtypes; dx over dy.
+EVAL_BWD = [custom(2, 3, 8, 9, 9), custom(4, 3, 8, 5, 5, act_param=0.7),
+            custom(3, 2, 24, 6, 6, layout="NHWC"),
+            custom(2, 3, 7, 5, 3, layout="NHWC", act="elu", act_param=0.7),
+            custom(3, 2, 13, 4, 5, dtype="bf16", act="identity", act_param=0.0),
+            custom(2, 8, 64, 28, 28), custom(3, 4, 256, 16, 16, layout="NHWC")]
+
+
+@pytest.mark.parametrize("grads", [True, False], ids=["grads", "dx_only"])
+@pytest.mark.parametrize("wl", EVAL_BWD, ids=lambda w: w.name)
+def test_backward_eval(wl, grads):
+    inp = workloads.make_inputs(wl)
+    rng = np.random.default_rng(5)
+    rm = rng.normal(0, 1, wl.C).astype(np.float32)
+    rv = rng.uniform(0.3, 2.0, wl.C).astype(np.float32)
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+    g = torch.from_numpy(inp.gamma).cuda()
+    b = torch.from_numpy(inp.beta).cuda()
+    rvt = torch.from_numpy(rv).cuda()
+    y = harness.to_device(inp.x, wl)
+    iabn.iabn_forward_eval(y, N, C, H, W, wl.layout, g, b, torch.from_numpy(rm).cuda(), rvt,
+                           wl.act, wl.act_param, wl.eps)
+    dy = harness.to_device(inp.dy, wl)
+    dx = torch.empty_like(dy)
+    dg = torch.empty(C, device="cuda") if grads else None
+    db = torch.empty(C, device="cuda") if grads else None
+    ws = iabn.workspace(N, C, H, W, wl.layout, y.dtype)
+    ws.fill_(0xAB)
+    iabn.iabn_backward_eval(y, dy, dx, N, C, H, W, wl.layout, g, b, rvt, wl.eps, dg, db, wl.act,
+                            wl.act_param, ws)
+    # in place over dy gives the same bits
+    dy2 = harness.to_device(inp.dy, wl)
+    iabn.iabn_backward_eval(y, dy2, dy2, N, C, H, W, wl.layout, g, b, rvt, wl.eps, None, None,
+                            wl.act, wl.act_param, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dy2, dx)
+    y64 = harness.to_nchw64(y, wl)
+    dy64 = workloads.from_storage(inp.dy, N, C, H, W, wl.layout, wl.dtype)
+    o = oracle.backward_eval(y64, dy64, inp.gamma, inp.beta, rv, wl.act,
+                             harness.f32(wl.act_param), harness.f32(wl.eps))
+    errs = {"dx": harness.rel_err_tensor(harness.to_nchw64(dx, wl), o["dx"])}
+    if grads:
+        errs["dgamma"] = harness.rel_err_vec(dg.cpu().numpy(), o["dgamma"])
+        errs["dbeta"] = harness.rel_err_vec(db.cpu().numpy(), o["dbeta"])
+    print("case:", wl.name, grads, errs, flush=True)
+    harness.assert_within(errs, wl.dtype, "backward_eval " + wl.name)
+
+
 def test_running_stats_are_optional():
     wl = custom(2, 4, 8, 6, 6)
     inp = workloads.make_inputs(wl)

@@ -16,7 +16,8 @@ Recipe (all configurations):
     gamma magnitude, beta_c, then x, then dy (each only when the recipe uses it);
   * x and dy are drawn in logical NCHW order as fp64, permuted to the storage
     layout, then rounded to the storage dtype (fp32 by numpy's RNE cast; bf16 by
-    round-to-nearest-even on the fp32 bit pattern);
+    round-to-nearest-even on the fp32 bit pattern; fp16 by numpy's RNE cast of
+    the fp32 value);
   * "N(a, b)" means mean a and *variance* b;
   * running statistics start at mean 0, variance 1.
 """
@@ -28,7 +29,7 @@ from typing import Optional
 import numpy as np
 
 LAYOUTS = ("NCHW", "NHWC")
-DTYPES = ("f32", "bf16")
+DTYPES = ("f32", "bf16", "f16")
 ACTS = ("identity", "leaky_relu", "elu")
 
 
@@ -124,7 +125,8 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def to_storage(x_nchw: np.ndarray, layout: str, dtype: str) -> np.ndarray:
-    """fp64 logical-NCHW array -> storage array (float32 or uint16 bf16 bits) in `layout`."""
+    """fp64 logical-NCHW array -> storage array (float32, or uint16 bf16 / fp16 bits)
+    in `layout`."""
     if layout == "NHWC":
         x_nchw = np.transpose(x_nchw, (0, 2, 3, 1))
     f32 = np.ascontiguousarray(x_nchw, dtype=np.float32)
@@ -132,6 +134,9 @@ def to_storage(x_nchw: np.ndarray, layout: str, dtype: str) -> np.ndarray:
         return f32
     if dtype == "bf16":
         return f32_to_bf16_bits(f32)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return f32.astype(np.float16).view(np.uint16)
     raise ValueError(dtype)
 
 
@@ -139,6 +144,8 @@ def from_storage(s: np.ndarray, N: int, C: int, H: int, W: int, layout: str, dty
     """storage array -> fp64 logical-NCHW array (exact upcast)."""
     if dtype == "bf16":
         f = bf16_bits_to_f32(s.reshape(-1))
+    elif dtype == "f16":
+        f = np.ascontiguousarray(s, dtype=np.uint16).reshape(-1).view(np.float16).astype(np.float32)
     else:
         f = np.ascontiguousarray(s, dtype=np.float32).reshape(-1)
     if layout == "NCHW":
@@ -200,9 +207,10 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, with_dy: bool = True) 
 
 
 def storage_torch_dtype(dtype: str):
-    """torch dtype used to hold the storage bits (bf16 bits travel as torch.bfloat16)."""
+    """torch dtype used to hold the storage bits (bf16 bits travel as torch.bfloat16,
+    fp16 bits as torch.float16)."""
     import torch
-    return torch.float32 if dtype == "f32" else torch.bfloat16
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
 
 
 def to_torch(a: np.ndarray, dtype: str):
@@ -210,7 +218,8 @@ def to_torch(a: np.ndarray, dtype: str):
     import torch
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
 
 
 def from_torch(t, dtype: str) -> np.ndarray:
