@@ -52,8 +52,10 @@ typedef enum iabn_status {
 
 typedef enum iabn_layout { IABN_NCHW = 0, IABN_NHWC = 1 } iabn_layout;
 
-/* storage dtype of x / y / dy / dx */
-typedef enum iabn_dtype { IABN_F32 = 0, IABN_BF16 = 1 } iabn_dtype;
+/* Storage dtype of x / y / dy / dx.  Arithmetic is fp32 (statistics finished in
+ * fp64) for every storage dtype; stored results round to nearest even.  fp16
+ * keeps IEEE binary16 subnormals and overflows to infinity. */
+typedef enum iabn_dtype { IABN_F32 = 0, IABN_BF16 = 1, IABN_F16 = 2 } iabn_dtype;
 
 /* Invertible activations (section 3, "INPLACE-ABN"; section 4, "Experimental
  * setup" uses leaky ReLU with slope 0.01).  act_param is the leaky slope

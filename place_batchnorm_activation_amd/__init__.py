@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libiabn.so")
 
 NCHW, NHWC = 0, 1
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 ACT_IDENTITY, ACT_LEAKY_RELU, ACT_ELU = 0, 1, 2
 
 LAYOUTS = {"NCHW": NCHW, "NHWC": NHWC}
@@ -91,12 +91,23 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+_TORCH_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
 def _dtype_code(t) -> int:
-    if t.dtype == torch.float32:
-        return F32
-    if t.dtype == torch.bfloat16:
-        return BF16
-    raise TypeError("storage dtype must be float32 or bfloat16, got %s" % t.dtype)
+    code = _TORCH_DTYPES.get(t.dtype)
+    if code is None:
+        raise TypeError("storage dtype must be float32, bfloat16 or float16, got %s" % t.dtype)
+    return code
+
+
+def _dtype_arg(dtype) -> int:
+    """A storage dtype given as a torch dtype or as the library's code."""
+    if isinstance(dtype, torch.dtype):
+        if dtype not in _TORCH_DTYPES:
+            raise TypeError("storage dtype must be float32, bfloat16 or float16, got %s" % dtype)
+        return _TORCH_DTYPES[dtype]
+    return int(dtype)
 
 
 def _code(v, table):
@@ -117,10 +128,8 @@ def iabn_version() -> int:
 
 
 def iabn_workspace_size(N, C, H, W, layout, dtype) -> int:
-    """dtype: F32/BF16 code or a torch dtype."""
-    if isinstance(dtype, torch.dtype):
-        dtype = F32 if dtype == torch.float32 else BF16
-    return lib.iabn_workspace_size(N, C, H, W, _code(layout, LAYOUTS), dtype)
+    """dtype: F32/BF16/F16 code or a torch dtype."""
+    return lib.iabn_workspace_size(N, C, H, W, _code(layout, LAYOUTS), _dtype_arg(dtype))
 
 
 def workspace(N, C, H, W, layout, dtype, device="cuda") -> torch.Tensor:
@@ -202,10 +211,9 @@ def iabn_backward_eval(y, dy, dx, N, C, H, W, layout, gamma, beta, running_var, 
 
 def iabn_describe_plan(N, C, H, W, layout, dtype, act, aligned16=True) -> str:
     """Which kernels iabn_forward_train / iabn_backward launch for this problem."""
-    if isinstance(dtype, torch.dtype):
-        dtype = F32 if dtype == torch.float32 else BF16
     buf = ctypes.create_string_buffer(256)
-    n = lib.iabn_describe_plan(N, C, H, W, _code(layout, LAYOUTS), dtype, _code(act, ACTS),
+    n = lib.iabn_describe_plan(N, C, H, W, _code(layout, LAYOUTS), _dtype_arg(dtype),
+                               _code(act, ACTS),
                                1 if aligned16 else 0, buf, 256)
     if n < 0:
         raise ValueError("invalid problem description")

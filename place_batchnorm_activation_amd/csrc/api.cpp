@@ -24,7 +24,7 @@ iabn_status check_shape(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout 
                         iabn_dtype dtype)
 {
     if (layout != IABN_NCHW && layout != IABN_NHWC) return IABN_ERR_INVALID_ARG;
-    if (dtype != IABN_F32 && dtype != IABN_BF16) return IABN_ERR_INVALID_ARG;
+    if (dtype != IABN_F32 && dtype != IABN_BF16 && dtype != IABN_F16) return IABN_ERR_INVALID_ARG;
     if (N < 0 || C < 0 || H < 0 || W < 0) return IABN_ERR_INVALID_ARG;
     // keep every index product well inside int64 and every grid inside 2^31 workgroups
     const double numel = double(N) * double(C) * double(H) * double(W);

@@ -438,13 +438,11 @@ void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const
     float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
     float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
     const float ia = act == kIdentity ? 1.f : 1.f / a;
-    if (pl.dtype == kF32) {
-        if (pl.vec) launch_reduce_dv<kF32, 4>(pl, y, dy, beta, act, a, ia, pa, pb, s);
-        else launch_reduce_dv<kF32, 1>(pl, y, dy, beta, act, a, ia, pa, pb, s);
-    } else {
-        if (pl.vec) launch_reduce_dv<kBF16, 8>(pl, y, dy, beta, act, a, ia, pa, pb, s);
-        else launch_reduce_dv<kBF16, 1>(pl, y, dy, beta, act, a, ia, pa, pb, s);
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        constexpr int DT = decltype(d)::value;
+        if (pl.vec) launch_reduce_dv<DT, vec_width(DT)>(pl, y, dy, beta, act, a, ia, pa, pb, s);
+        else launch_reduce_dv<DT, 1>(pl, y, dy, beta, act, a, ia, pa, pb, s);
+    });
     hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
                        dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta, invstd,
                        frozen_var, eps, dgamma, dbeta, consts);
@@ -491,13 +489,11 @@ void launch_backward_apply(const Plan& pl, const void* y, const void* dy, void* 
 {
     const float4* k = reinterpret_cast<const float4*>(static_cast<char*>(ws) + pl.off_const);
     const float ia = act == kIdentity ? 1.f : 1.f / a;
-    if (pl.dtype == kF32) {
-        if (pl.vec) launch_bapply_dv<kF32, 4>(pl, y, dy, dx, k, act, a, ia, s);
-        else launch_bapply_dv<kF32, 1>(pl, y, dy, dx, k, act, a, ia, s);
-    } else {
-        if (pl.vec) launch_bapply_dv<kBF16, 8>(pl, y, dy, dx, k, act, a, ia, s);
-        else launch_bapply_dv<kBF16, 1>(pl, y, dy, dx, k, act, a, ia, s);
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        constexpr int DT = decltype(d)::value;
+        if (pl.vec) launch_bapply_dv<DT, vec_width(DT)>(pl, y, dy, dx, k, act, a, ia, s);
+        else launch_bapply_dv<DT, 1>(pl, y, dy, dx, k, act, a, ia, s);
+    });
 }
 
 }  // namespace iabn

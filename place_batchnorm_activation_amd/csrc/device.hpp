@@ -12,7 +12,83 @@ __device__ __forceinline__ int64_t dmin(int64_t a, int64_t b) { return a < b ? a
 
 // ---------------------------------------------------------------------------
 // storage access: V consecutive elements <-> V floats.
-// fp32: V = 4 (one 128-bit access) or 1.  bf16: V = 8 (one 128-bit access) or 1.
+// fp32: V = 4 (one 128-bit access) or 1.  bf16 and fp16: V = 8 (one 128-bit
+// access) or 1.  Loads widen exactly; stores round to nearest even.
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two 16-bit elements of a 32-bit word (low half first) <-> two floats.
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi)
+{
+    if constexpr (DT == kBF16) {
+        lo = __uint_as_float(w << 16);
+        hi = __uint_as_float(w & 0xffff0000u);
+    } else {
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, w);
+        lo = float(h.x);
+        hi = float(h.y);
+    }
+}
+
+// fp32 -> bf16 (v_cvt_pk_bf16_f32) or fp16 (v_cvt_f16_f32), nearest even; fp16
+// overflows to infinity and keeps its subnormals.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    if constexpr (DT == kBF16) {
+        const bf16x2_t t = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, t);
+    } else {
+        const f16x2_t t = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, t);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float unpack1(uint16_t b)
+{
+    if constexpr (DT == kBF16) return __uint_as_float(uint32_t(b) << 16);
+    else return float(__builtin_bit_cast(_Float16, b));
+}
+
+template <int DT>
+__device__ __forceinline__ uint16_t pack1(float v)
+{
+    if constexpr (DT == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)v);
+    else return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Raw 16-byte vector <-> floats, for loops that keep loads in flight as raw bits.
+template <int DT>
+struct Raw16 { static constexpr int V = DT == kF32 ? 4 : 8; };
+
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4& q, float (&v)[Raw16<DT>::V])
+{
+    if constexpr (DT == kF32) {
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+    } else {
+        unpack2<DT>(q.x, v[0], v[1]);
+        unpack2<DT>(q.y, v[2], v[3]);
+        unpack2<DT>(q.z, v[4], v[5]);
+        unpack2<DT>(q.w, v[6], v[7]);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 pack16(const float (&v)[Raw16<DT>::V])
+{
+    if constexpr (DT == kF32) {
+        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3]));
+    } else {
+        return make_uint4(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]), pack2<DT>(v[4], v[5]),
+                          pack2<DT>(v[6], v[7]));
+    }
+}
 
 template <int DT, int V>
 __device__ __forceinline__ void load_elems(const void* base, int64_t i, float (&v)[V])
@@ -29,27 +105,12 @@ __device__ __forceinline__ void load_elems(const void* base, int64_t i, float (&
     } else {
         const uint16_t* p = static_cast<const uint16_t*>(base) + i;
         if constexpr (V == 8) {
-            const uint4 q = *reinterpret_cast<const uint4*>(p);
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                v[2 * k] = __uint_as_float(w[k] << 16);
-                v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-            }
+            unpack16<DT>(*reinterpret_cast<const uint4*>(p), v);
         } else {
-            static_assert(V == 1, "bf16 access width");
-            v[0] = __uint_as_float(uint32_t(*p) << 16);
+            static_assert(V == 1, "16-bit access width");
+            v[0] = unpack1<DT>(*p);
         }
     }
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// fp32 -> bf16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    const bf16x2_t t = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, t);
 }
 
 template <int DT, int V>
@@ -65,14 +126,9 @@ __device__ __forceinline__ void store_elems(void* base, int64_t i, const float (
     } else {
         uint16_t* p = static_cast<uint16_t*>(base) + i;
         if constexpr (V == 8) {
-            uint4 q;
-            q.x = pack_bf16x2(v[0], v[1]);
-            q.y = pack_bf16x2(v[2], v[3]);
-            q.z = pack_bf16x2(v[4], v[5]);
-            q.w = pack_bf16x2(v[6], v[7]);
-            *reinterpret_cast<uint4*>(p) = q;
+            *reinterpret_cast<uint4*>(p) = pack16<DT>(v);
         } else {
-            *p = __builtin_bit_cast(uint16_t, (__bf16)v[0]);
+            *p = pack1<DT>(v[0]);
         }
     }
 }
@@ -91,26 +147,6 @@ __device__ __forceinline__ void store_floats(float* p, const float (&v)[V])
     }
 }
 
-// Raw 16-byte vector <-> floats, for loops that keep loads in flight as raw bits.
-template <int DT>
-struct Raw16 { static constexpr int V = DT == kF32 ? 4 : 8; };
-
-template <int DT>
-__device__ __forceinline__ void unpack16(const uint4& q, float (&v)[Raw16<DT>::V])
-{
-    if constexpr (DT == kF32) {
-        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
-        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
-    } else {
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = __uint_as_float(w[k] << 16);
-            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-        }
-    }
-}
-
 // Store of V elements with the non-temporal hint (streaming data that is not read
 // again soon); same values as store_elems.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -119,16 +155,10 @@ template <int DT, int V>
 __device__ __forceinline__ void store_elems_nt(void* base, int64_t i, const float (&v)[V])
 {
     if constexpr (V * (DT == kF32 ? 4 : 2) == 16) {
-        u32x4_t q;
-        if constexpr (DT == kF32) {
-            q = u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                        __float_as_uint(v[3])};
-            __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t*>(static_cast<float*>(base) + i));
-        } else {
-            q = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                        pack_bf16x2(v[6], v[7])};
-            __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(base) + i));
-        }
+        const uint4 q = pack16<DT>(v);
+        const u32x4_t w = {q.x, q.y, q.z, q.w};
+        char* p = static_cast<char*>(base) + i * (DT == kF32 ? 4 : 2);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
     } else {
         store_elems<DT, V>(base, i, v);
     }

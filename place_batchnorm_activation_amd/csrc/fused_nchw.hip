@@ -23,37 +23,6 @@
 
 namespace iabn {
 
-template <int DT>
-struct Vec16 { static constexpr int V = DT == kF32 ? 4 : 8; };
-
-template <int DT>
-__device__ __forceinline__ void unpack(const uint4& q, float (&v)[Vec16<DT>::V])
-{
-    if constexpr (DT == kF32) {
-        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
-        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
-    } else {
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = __uint_as_float(w[k] << 16);
-            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-        }
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ uint4 pack(const float (&v)[Vec16<DT>::V])
-{
-    if constexpr (DT == kF32) {
-        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                          __float_as_uint(v[3]));
-    } else {
-        return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    }
-}
-
 __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off)
 {
     return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + (off << 4));
@@ -138,7 +107,7 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     float* __restrict__ running_var, float* __restrict__ save_mean,
     float* __restrict__ save_invstd, float eps, float momentum, float a)
 {
-    constexpr int V = Vec16<DT>::V;
+    constexpr int V = Raw16<DT>::V;
     const uint32_t c = blockIdx.x;
     const uint32_t t = threadIdx.x;
     const uint32_t HWv = HW / V;
@@ -167,7 +136,7 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     for (int k = 0; k < NR; ++k) {
         if (t + k * T < Vc) {
             float v[V];
-            unpack<DT>(r[k], v);
+            unpack16<DT>(r[k], v);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float d = v[e] - K;
@@ -207,10 +176,10 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     for (int k = 0; k < NR; ++k) {
         if (t2 + k * T < Vc) {
             float v[V];
-            unpack<DT>(opaque4(r[k]), v);
+            unpack16<DT>(opaque4(r[k]), v);
 #pragma unroll
             for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K) - d, s, b), a);
-            st16(x, w.off, pack<DT>(v));
+            st16(x, w.off, pack16<DT>(v));
         }
         w.step();
     }
@@ -225,7 +194,7 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
     const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
     float a, float inv_a)
 {
-    constexpr int V = Vec16<DT>::V;
+    constexpr int V = Raw16<DT>::V;
     const uint32_t c = blockIdx.x;
     const uint32_t t = threadIdx.x;
     const uint32_t HWv = HW / V;
@@ -253,9 +222,9 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
         if constexpr (!DYR) if (k % kStreamGroup == 0) group_fence();
         if (t1 + k * T < Vc) {
             float vy[V], vd[V];
-            unpack<DT>(ry[k], vy);
-            if constexpr (DYR) unpack<DT>(rd[k], vd);
-            else unpack<DT>(ld16(dy, w.off), vd);
+            unpack16<DT>(ry[k], vy);
+            if constexpr (DYR) unpack16<DT>(rd[k], vd);
+            else unpack16<DT>(ld16(dy, w.off), vd);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 float z, slope;
@@ -288,9 +257,9 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
         if constexpr (!DYR) if (k % kStreamGroup == 0) group_fence();
         if (t2 + k * T < Vc) {
             float vy[V], vd[V];
-            unpack<DT>(opaque4(ry[k]), vy);
-            if constexpr (DYR) unpack<DT>(opaque4(rd[k]), vd);
-            else unpack<DT>(ld16(dy, w.off), vd);
+            unpack16<DT>(opaque4(ry[k]), vy);
+            if constexpr (DYR) unpack16<DT>(opaque4(rd[k]), vd);
+            else unpack16<DT>(ld16(dy, w.off), vd);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 float z, slope;
@@ -298,7 +267,7 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
                 const float dz = slope * vd[e];
                 vd[e] = fmaf(kA, dz, fmaf(kB, z - bc2, kC));
             }
-            st16(dx, w.off, pack<DT>(vd));
+            st16(dx, w.off, pack16<DT>(vd));
         }
         w.step();
     }
@@ -316,7 +285,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
     const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
     float a, float inv_a)
 {
-    constexpr int V = Vec16<DT>::V;
+    constexpr int V = Raw16<DT>::V;
     constexpr int NR = NRV + NRL;
     constexpr int NG = (NR + G - 1) / G;
     __shared__ uint4 ly[NRL > 0 ? NRL * T : 1];
@@ -371,8 +340,8 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
                 const int k = gi * G + i;
                 if (k < NR && t1 + k * T < Vc) {
                     float vy[V], vd[V];
-                    unpack<DT>(k < NRV ? ry[k < NRV ? k : 0] : ly[(k >= NRV ? k - NRV : 0) * T + t1], vy);
-                    unpack<DT>(buf[gi & 1][i], vd);
+                    unpack16<DT>(k < NRV ? ry[k < NRV ? k : 0] : ly[(k >= NRV ? k - NRV : 0) * T + t1], vy);
+                    unpack16<DT>(buf[gi & 1][i], vd);
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
                         float z, slope;
@@ -428,9 +397,9 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
                 if (k < NR) {
                     if (t2 + k * T < Vc) {
                         float vy[V], vd[V];
-                        unpack<DT>(k < NRV ? opaque4(ry[k < NRV ? k : 0])
+                        unpack16<DT>(k < NRV ? opaque4(ry[k < NRV ? k : 0])
                                            : ly[(k >= NRV ? k - NRV : 0) * T + t2], vy);
-                        unpack<DT>(buf[gi & 1][i], vd);
+                        unpack16<DT>(buf[gi & 1][i], vd);
 #pragma unroll
                         for (int e = 0; e < V; ++e) {
                             float z, slope;
@@ -438,7 +407,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
                             const float dz = slope * vd[e];
                             vd[e] = fmaf(kA, dz, fmaf(kB, z - bc2, kC));
                         }
-                        st16(dx, wx.off, pack<DT>(vd));
+                        st16(dx, wx.off, pack16<DT>(vd));
                     }
                     wx.step();
                 }
@@ -472,19 +441,12 @@ void launch_forward_fused_nchw(const Plan& pl, void* x, const float* gamma, cons
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
                                int act, float a, hipStream_t s)
 {
-    if (pl.dtype == kF32) {
-        switch (act) {
-        case kLeaky: launch_fwd_da<kF32, kLeaky>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        case kElu: launch_fwd_da<kF32, kElu>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        default: launch_fwd_da<kF32, kIdentity>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        }
-    } else {
-        switch (act) {
-        case kLeaky: launch_fwd_da<kBF16, kLeaky>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        case kElu: launch_fwd_da<kBF16, kElu>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        default: launch_fwd_da<kBF16, kIdentity>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        }
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_fwd_da<decltype(d)::value, decltype(ac)::value>(
+                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s);
+        });
+    });
 }
 
 template <int DT, int ACT>
@@ -514,19 +476,12 @@ void launch_backward_fused_nchw(const Plan& pl, const void* y, const void* dy, v
                                 float* dgamma, float* dbeta, int act, float a, hipStream_t s)
 {
     const float ia = act == kIdentity ? 1.f : 1.f / a;
-    if (pl.dtype == kF32) {
-        switch (act) {
-        case kLeaky: launch_bwd_da<kF32, kLeaky>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        case kElu: launch_bwd_da<kF32, kElu>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        default: launch_bwd_da<kF32, kIdentity>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        }
-    } else {
-        switch (act) {
-        case kLeaky: launch_bwd_da<kBF16, kLeaky>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        case kElu: launch_bwd_da<kBF16, kElu>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        default: launch_bwd_da<kBF16, kIdentity>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        }
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_bwd_da<decltype(d)::value, decltype(ac)::value>(
+                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s);
+        });
+    });
 }
 
 }  // namespace iabn

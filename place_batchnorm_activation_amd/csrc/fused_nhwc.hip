@@ -50,18 +50,6 @@ __device__ __forceinline__ void st16_nt(void* base, uint32_t vec, const uint4& q
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(base) + vec);
 }
 
-template <int DT>
-__device__ __forceinline__ uint4 pack16(const float (&v)[Raw16<DT>::V])
-{
-    if constexpr (DT == kF32) {
-        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                          __float_as_uint(v[3]));
-    } else {
-        return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    }
-}
-
 // Workgroup totals over the row slots, stage one: threads t and t' hold the same
 // channels when t % LPR == t' % LPR.  Inside the wave a reduce-scatter butterfly:
 // at xor offset OFF (32, 16, ...) a lane keeps half of its NV values -- the upper
@@ -188,7 +176,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
     const bool fin = t < V * LPR;
     const uint32_t cf = fin ? (s * LPR + t % LPR) * V + t / LPR : 0;
     uint32_t k_bits = DT == kF32 ? static_cast<const uint32_t*>(x)[cf]
-                                 : uint32_t(static_cast<const uint16_t*>(x)[cf]) << 16;
+                                 : uint32_t(static_cast<const uint16_t*>(x)[cf]);
     float g_f = gamma[cf];
     const float* rm_src = running_mean ? running_mean : gamma;
     const float* rv_src = running_mean ? running_var : gamma;
@@ -233,7 +221,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
         const double dm = S1 / md;
         const double var = fmax(S2 - S1 * dm, 0.0) / md;
         const double invstd = 1.0 / sqrt(var + double(eps));
-        const double mu = double(__uint_as_float(k_bits)) + dm;
+        const double mu = double(DT == kF32 ? __uint_as_float(k_bits) : unpack1<DT>(uint16_t(k_bits))) + dm;
         save_mean[cf] = float(mu);
         save_invstd[cf] = float(invstd);
         if (running_mean) {
@@ -393,19 +381,12 @@ void launch_forward_fused_nhwc(const Plan& pl, void* x, const float* gamma, cons
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
                                int act, float a, hipStream_t s)
 {
-    if (pl.dtype == kF32) {
-        switch (act) {
-        case kLeaky: launch_nhwc_fwd_da<kF32, kLeaky>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        case kElu: launch_nhwc_fwd_da<kF32, kElu>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        default: launch_nhwc_fwd_da<kF32, kIdentity>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        }
-    } else {
-        switch (act) {
-        case kLeaky: launch_nhwc_fwd_da<kBF16, kLeaky>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        case kElu: launch_nhwc_fwd_da<kBF16, kElu>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        default: launch_nhwc_fwd_da<kBF16, kIdentity>(pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s); break;
-        }
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_nhwc_fwd_da<decltype(d)::value, decltype(ac)::value>(
+                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s);
+        });
+    });
 }
 
 template <int DT, int ACT>
@@ -431,19 +412,12 @@ void launch_backward_fused_nhwc(const Plan& pl, const void* y, const void* dy, v
                                 float* dgamma, float* dbeta, int act, float a, hipStream_t s)
 {
     const float ia = act == kIdentity ? 1.f : 1.f / a;
-    if (pl.dtype == kF32) {
-        switch (act) {
-        case kLeaky: launch_nhwc_bwd_da<kF32, kLeaky>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        case kElu: launch_nhwc_bwd_da<kF32, kElu>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        default: launch_nhwc_bwd_da<kF32, kIdentity>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        }
-    } else {
-        switch (act) {
-        case kLeaky: launch_nhwc_bwd_da<kBF16, kLeaky>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        case kElu: launch_nhwc_bwd_da<kBF16, kElu>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        default: launch_nhwc_bwd_da<kBF16, kIdentity>(pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s); break;
-        }
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_nhwc_bwd_da<decltype(d)::value, decltype(ac)::value>(
+                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s);
+        });
+    });
 }
 
 }  // namespace iabn

@@ -457,22 +457,15 @@ void launch_forward_stats(const Plan& pl, const void* x, const float* gamma, con
     float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
     float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
     float* cnt = reinterpret_cast<float*>(wsb + pl.off_count);
-    if (pl.dtype == kF32) {
-        if (pl.vec) launch_stats_dv<kF32, 4>(pl, x, pa, pb, cnt, s);
-        else launch_stats_dv<kF32, 1>(pl, x, pa, pb, cnt, s);
-    } else {
-        if (pl.vec) launch_stats_dv<kBF16, 8>(pl, x, pa, pb, cnt, s);
-        else launch_stats_dv<kBF16, 1>(pl, x, pa, pb, cnt, s);
-    }
     const dim3 grid(unsigned(ceil_div(pl.C, kFinChannels)));
-    if (pl.dtype == kF32)
-        hipLaunchKernelGGL((k_fwd_finalize<kF32>), grid, dim3(kFinThreads), 0, s, x, pl.layout,
+    with_dtype(pl.dtype, [&](auto d) {
+        constexpr int DT = decltype(d)::value;
+        if (pl.vec) launch_stats_dv<DT, vec_width(DT)>(pl, x, pa, pb, cnt, s);
+        else launch_stats_dv<DT, 1>(pl, x, pa, pb, cnt, s);
+        hipLaunchKernelGGL((k_fwd_finalize<DT>), grid, dim3(kFinThreads), 0, s, x, pl.layout,
                            pl.C, pl.HW, pl.m, pl.P, pa, pb, cnt, gamma, beta, running_mean,
                            running_var, save_mean, save_invstd, eps, momentum, consts);
-    else
-        hipLaunchKernelGGL((k_fwd_finalize<kBF16>), grid, dim3(kFinThreads), 0, s, x, pl.layout,
-                           pl.C, pl.HW, pl.m, pl.P, pa, pb, cnt, gamma, beta, running_mean,
-                           running_var, save_mean, save_invstd, eps, momentum, consts);
+    });
 }
 
 template <int DT, int V, int ACT, typename CS>
@@ -504,13 +497,11 @@ static void launch_apply_dv(const Plan& pl, void* x, CS cs, int act, float a, hi
 template <typename CS>
 static void launch_apply(const Plan& pl, void* x, CS cs, int act, float a, hipStream_t s)
 {
-    if (pl.dtype == kF32) {
-        if (pl.vec) launch_apply_dv<kF32, 4>(pl, x, cs, act, a, s);
-        else launch_apply_dv<kF32, 1>(pl, x, cs, act, a, s);
-    } else {
-        if (pl.vec) launch_apply_dv<kBF16, 8>(pl, x, cs, act, a, s);
-        else launch_apply_dv<kBF16, 1>(pl, x, cs, act, a, s);
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        constexpr int DT = decltype(d)::value;
+        if (pl.vec) launch_apply_dv<DT, vec_width(DT)>(pl, x, cs, act, a, s);
+        else launch_apply_dv<DT, 1>(pl, x, cs, act, a, s);
+    });
 }
 
 void launch_forward_apply(const Plan& pl, void* x, int act, float a, void* ws, hipStream_t s)

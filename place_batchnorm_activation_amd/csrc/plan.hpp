@@ -21,6 +21,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace iabn {
 
 constexpr int kThreads = 256;          // workgroup size of every kernel
@@ -31,8 +33,35 @@ constexpr int kFinChannels = 16;
 constexpr int kFinPhases = kFinThreads / kFinChannels;
 
 enum Layout { kNCHW = 0, kNHWC = 1 };
-enum DType { kF32 = 0, kBF16 = 1 };
+enum DType { kF32 = 0, kBF16 = 1, kF16 = 2 };
 enum Act { kIdentity = 0, kLeaky = 1, kElu = 2 };
+
+// Host-side dispatch onto compile-time storage dtype and activation: calls f with
+// std::integral_constant<int, value>, so a launcher names its kernel template
+// once for every combination.
+template <class F>
+inline void with_dtype(int dtype, F&& f)
+{
+    switch (dtype) {
+    case kF32: f(std::integral_constant<int, kF32>{}); break;
+    case kBF16: f(std::integral_constant<int, kBF16>{}); break;
+    case kF16: f(std::integral_constant<int, kF16>{}); break;
+    default: break;
+    }
+}
+
+template <class F>
+inline void with_act(int act, F&& f)
+{
+    switch (act) {
+    case kLeaky: f(std::integral_constant<int, kLeaky>{}); break;
+    case kElu: f(std::integral_constant<int, kElu>{}); break;
+    default: f(std::integral_constant<int, kIdentity>{}); break;
+    }
+}
+
+// Elements per 16-byte access.
+constexpr int vec_width(int dtype) { return dtype == kF32 ? 4 : 8; }
 
 struct Plan {
     int64_t N = 0, C = 0, HW = 0, m = 0, numel = 0;

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "iabn.h")
@@ -44,6 +45,10 @@ def test_workspace_size_depends_only_on_shape():
     assert lib.iabn_workspace_size(2, 0, 4, 4, 0, 0) == 0
     assert lib.iabn_workspace_size(-1, 4, 4, 4, 0, 0) == 0
     assert lib.iabn_workspace_size(2, 4, 4, 4, 7, 0) == 0
+    assert lib.iabn_workspace_size(2, 4, 4, 4, 0, 3) == 0          # no dtype 3
+    # fp16 and bf16 storage share every size (16-bit elements)
+    assert lib.iabn_workspace_size(2, 256, 512, 512, 1, 2) == \
+        lib.iabn_workspace_size(2, 256, 512, 512, 1, 1)
     # partial workspace stays small next to the data (a few percent)
     for (N, C, H, W, lay, dt) in [(32, 256, 56, 56, 0, 0), (2, 256, 512, 512, 1, 1),
                                   (16, 512, 28, 28, 0, 0), (64, 2048, 7, 7, 1, 1)]:
@@ -111,6 +116,8 @@ def _bwd(y=A, dy=2 * A, dx=3 * A, N=2, C=3, H=4, W=4, layout=0, dtype=0, g=A, b=
 
 
 def test_backward_validation():
+    assert _bwd(dtype=3) == INVALID
+    assert _bwd(dtype=2, y=A + 1) == MISALIGNED
     assert _bwd(act=1, p=0.0) == INVALID
     assert _bwd(dx=A) == INVALID                 # dx aliases y
     assert _bwd(dx=A + 64) == INVALID            # dx overlaps y
@@ -162,6 +169,10 @@ def test_plan_choice_for_the_workloads():
     assert d(2, 16, 80, 80, "NHWC", iabn.F32, "leaky_relu").startswith("forward=split")
     # few slices on a large tensor: split
     assert d(16, 16, 28, 28, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    # fp16 storage plans exactly as bf16
+    for shape in ((64, 2048, 7, 7, "NHWC"), (2, 256, 512, 512, "NHWC"), (16, 512, 28, 28, "NCHW"),
+                  (32, 256, 56, 56, "NCHW")):
+        assert d(*shape, torch.float16, "leaky_relu") == d(*shape, torch.bfloat16, "leaky_relu")
     # misaligned or ragged planes take the scalar split path
     assert "scalar" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
     assert "scalar" in d(3, 5, 17, 19, "NCHW", iabn.F32, "leaky_relu")

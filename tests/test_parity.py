@@ -52,7 +52,7 @@ def test_config1_tiny():
 
 MID = []
 for layout in ("NCHW", "NHWC"):
-    for dtype in ("f32", "bf16"):
+    for dtype in ("f32", "bf16", "f16"):
         for act, p in (("leaky_relu", 0.01), ("elu", 1.0), ("identity", 0.0)):
             base = 4 if act == "elu" else (2 if dtype == "f32" else 3)
             # vector path shapes and scalar (ragged) path shapes
@@ -241,6 +241,8 @@ def _variant_shapes():
         for vc in (3300, 25000):
             out.append(custom(4, 2, 3, 1, vc * V // 2, layout="NCHW", dtype=dtype, act="elu",
                               act_param=1.0))
+    for vc in (1000, 3300, 16000, 25000):                   # fp16: 8 elements per vector
+        out.append(custom(3, 2, 3, 1, vc * 4, layout="NCHW", dtype="f16"))
     return out
 
 
@@ -264,6 +266,8 @@ def _slice_shapes():
     out.append(custom(2, 64, 1024, 7, 7, layout="NHWC", dtype="f32"))
     out.append(custom(4, 4, 1024, 32, 36, layout="NHWC", dtype="f32", act="elu", act_param=1.0))
     out.append(custom(3, 4, 48, 25, 33, layout="NHWC", dtype="bf16"))     # 6 slices
+    out.append(custom(3, 4, 256, 25, 33, layout="NHWC", dtype="f16"))
+    out.append(custom(5, 4, 2048, 10, 25, layout="NHWC", dtype="f16", act="elu", act_param=1.0))
     out.append(custom(2, 2, 20, 7, 9, layout="NHWC", dtype="f32"))        # 5 slices
     out.append(custom(4, 4, 256, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0))
     out.append(custom(4, 3, 512, 12, 12, layout="NHWC", dtype="bf16", act="elu", act_param=0.5))
@@ -370,7 +374,8 @@ EVAL_BWD = [custom(2, 3, 8, 9, 9), custom(4, 3, 8, 5, 5, act_param=0.7),
             custom(3, 2, 24, 6, 6, layout="NHWC"),
             custom(2, 3, 7, 5, 3, layout="NHWC", act="elu", act_param=0.7),
             custom(3, 2, 13, 4, 5, dtype="bf16", act="identity", act_param=0.0),
-            custom(2, 8, 64, 28, 28), custom(3, 4, 256, 16, 16, layout="NHWC")]
+            custom(2, 8, 64, 28, 28), custom(3, 4, 256, 16, 16, layout="NHWC"),
+            custom(2, 4, 16, 8, 8, dtype="f16", act="elu", act_param=1.0)]
 
 
 @pytest.mark.parametrize("grads", [True, False], ids=["grads", "dx_only"])
@@ -411,6 +416,32 @@ def test_backward_eval(wl, grads):
         errs["dbeta"] = harness.rel_err_vec(db.cpu().numpy(), o["dbeta"])
     print("case:", wl.name, grads, errs, flush=True)
     harness.assert_within(errs, wl.dtype, "backward_eval " + wl.name)
+
+
+@pytest.mark.parametrize("W", [64, 63], ids=["vec", "scalar"])
+def test_f16_storage_rounds_to_nearest_even(W):
+    """fp16 results are rounded to nearest, ties to even, with subnormals and
+    overflow to infinity.  With eps = 0, running stats (0, 1), beta = 0 and the
+    identity activation, the inference forward is y = x*gamma, exact in fp32 for
+    these values, so the one rounding is the storage one and the bits must equal
+    the oracle's binary16 rounding of the exact product."""
+    base = np.array([1.0, 1.0 + 2 ** -10, 1.0 + 3 * 2 ** -10, 2.0 - 2 ** -10, 2 ** -14,
+                     3 * 2 ** -24, 2 ** -24, 1023 * 2 ** -24, 65504.0, -65504.0, 2048.0,
+                     0.5 + 2 ** -11, -(1.0 + 2 ** -10), 60000.0, 0.0, -3 * 2 ** -24])
+    vals = np.resize(base, W)
+    gamma = np.array([1.0 + 2 ** -11, 1.0 - 2 ** -12], np.float32)
+    x64 = np.stack([vals, vals])[None, :, None, :]              # N=1, C=2, H=1, W
+    wl = custom(2, 1, 2, 1, W, dtype="f16", act="identity", act_param=0.0)
+    xs = workloads.to_storage(x64, "NCHW", "f16")
+    assert np.array_equal(workloads.from_storage(xs, 1, 2, 1, W, "NCHW", "f16"), x64)
+    x = harness.to_device(xs, wl)
+    z2 = torch.zeros(2, device="cuda")
+    iabn.iabn_forward_eval(x, 1, 2, 1, W, "NCHW", torch.from_numpy(gamma).cuda(), z2, z2,
+                           torch.ones(2, device="cuda"), "identity", 0.0, 0.0)
+    torch.cuda.synchronize()
+    got = harness.to_nchw64(x, wl)
+    want = oracle.round_storage(x64 * gamma.astype(np.float64)[None, :, None, None], "f16")
+    assert np.array_equal(got, want), (got[0, :, 0, :16], want[0, :, 0, :16])
 
 
 def test_running_stats_are_optional():
