@@ -5,6 +5,7 @@ one backward (reductions from y + dx) over one batch of synthetic input already
 resident in HBM, all through the C ABI.
 
   python bench.py [--steps K] [--warmup W] [--config I] [--gpus 1] [--no-cpu]
+                  [--dtype f32|bf16|f16] [--mode train|frozen]
 
 Prints ONE JSON line.  value = numel / time-per-step (Gelem/s), measured "cold":
 consecutive steps rotate over buffer sets totalling >= 512 MB, more than the
@@ -19,10 +20,16 @@ current stream) around each single-kernel call in further timed loops over the
 same buffer sets.  Its algorithmic bytes are the pass-model bytes of the work it
 does: 3S for a whole forward, 5S for a whole backward, 2S / 3S for the split
 path's forward / backward elementwise kernels.
+
+--dtype stores the workload in another storage dtype.  --mode frozen measures
+the step of a network fine-tuned with frozen normalisation statistics instead:
+iabn_forward_eval (read x, write y: 2S) + iabn_backward_eval with dgamma/dbeta
+(sums 2S + dx 3S), 7S per step.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -91,6 +98,90 @@ def cpu_baseline(wl, inp) -> dict:
                       % (ch, wl.C, wl.m, reps, t)}
 
 
+def run_frozen(args, wl) -> int:
+    """Steps of iabn_forward_eval + iabn_backward_eval (frozen running statistics)."""
+    import torch
+    import place_batchnorm_activation_amd as iabn
+    import workloads
+
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+    inp = workloads.make_inputs(wl)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sshape = (N, C, H, W) if wl.layout == "NCHW" else (N, H, W, C)
+    S = wl.storage_bytes
+    nsets = max(2, math.ceil(COLD_BYTES / (3 * S)))
+    x0 = workloads.to_torch(inp.x, wl.dtype).reshape(sshape).to(dev)
+    dy0 = workloads.to_torch(inp.dy, wl.dtype).reshape(sshape).to(dev)
+    sets = [{"x": x0.clone(), "dy": dy0.clone(), "dx": torch.empty_like(dy0)}
+            for _ in range(nsets)]
+    g = torch.from_numpy(inp.gamma).to(dev)
+    b = torch.from_numpy(inp.beta).to(dev)
+    # frozen statistics with running_var = gamma^2 - eps and running_mean = beta: the
+    # in-place forward then maps x to +-(x - beta) + beta, so repeated steps on a
+    # buffer set keep its values bounded
+    rm = b.clone()
+    rv = torch.from_numpy(np.maximum(inp.gamma.astype(np.float64) ** 2 - wl.eps, 1e-2)
+                          .astype(np.float32)).to(dev)
+    dg, db = torch.empty(C, device=dev), torch.empty(C, device=dev)
+    ws = iabn.workspace(N, C, H, W, wl.layout, x0.dtype, dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def fwd(s):
+        iabn.iabn_forward_eval(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, wl.act, wl.act_param,
+                               wl.eps, sp)
+
+    def bwd(s, grads=True):
+        iabn.iabn_backward_eval(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout, g, b, rv, wl.eps,
+                                dg if grads else None, db if grads else None, wl.act,
+                                wl.act_param, ws, sp)
+
+    def timed(calls, k):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(k):
+            for fn in calls:
+                fn(sets[i % nsets])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k          # us per step
+
+    for i in range(args.warmup):
+        fwd(sets[i % nsets])
+        bwd(sets[i % nsets])
+    us_step = timed([fwd, bwd], args.steps)
+    us_fwd = timed([fwd], args.steps)
+    us_dx = timed([lambda s: bwd(s, grads=False)], args.steps)
+    kernels = {"forward_eval": (us_fwd, 2 * S), "backward_eval_dx": (us_dx, 3 * S)}
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    t_dom, dom_bytes = kernels[dom]
+    achieved = dom_bytes / (t_dom * 1e-6) / 1e9
+    gbps = 7 * S / (us_step * 1e-6) / 1e9
+    out = {
+        "metric": "InPlace-ABN frozen-statistics fwd+bwd Gelem/s",
+        "value": round(wl.numel / (us_step * 1e-6) / 1e9, 4),
+        "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_step * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "N": N, "C": C, "H": H, "W": W, "layout": wl.layout,
+                   "storage": wl.dtype, "act": wl.act, "act_param": wl.act_param,
+                   "mode": "frozen", "parallelism": "single_gpu"},
+        "pass_model_GBps": round(gbps, 1),
+        "pass_model_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "protocol": "cold: %d rotating buffer sets of %.0f MB; 7S per step" % (nsets, 3 * S / 1e6),
+        "launch_us": {"forward_eval": round(us_fwd, 3), "backward_eval_dx_only": round(us_dx, 3),
+                      "step": round(us_step, 3)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(t_dom, 3)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +190,10 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload index 1..5 (default 2)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--warm-only", action="store_true", help="one buffer set (for profiling)")
+    ap.add_argument("--dtype", choices=("f32", "bf16", "f16"), default=None,
+                    help="storage dtype instead of the workload's own")
+    ap.add_argument("--mode", choices=("train", "frozen"), default="train",
+                    help="train: forward_train + backward; frozen: forward_eval + backward_eval")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark: copy a MIB-MiB buffer 5 times (a plain copy "
                          "kernel of known size, the reference that scales memory counters)")
@@ -124,6 +219,10 @@ def main() -> int:
     import workloads
 
     wl = workloads.config(args.config)
+    if args.dtype and args.dtype != wl.dtype:
+        wl = dataclasses.replace(wl, dtype=args.dtype, name="%s_as_%s" % (wl.name, args.dtype))
+    if args.mode == "frozen":
+        return run_frozen(args, wl)
     N, C, H, W = wl.N, wl.C, wl.H, wl.W
     inp = workloads.make_inputs(wl)
     dev = torch.device("cuda", 0)
