@@ -354,12 +354,13 @@ iabn_status iabn_backward_eval(const void* y, const void* dy, void* dx, int64_t 
                              aligned(y, 16) && aligned(dy, 16) && aligned(dx, 16));
     IABN_TRY(check_workspace(workspace, workspace_bytes, pr));
     IABN_TRY(check_workspace(workspace, workspace_bytes, pa));
-    if (dgamma)
-        launch_backward_reduce(pr, y, dy, gamma, beta, nullptr, dgamma, dbeta, act, act_param,
-                               workspace, stream, running_var, eps);
-    else
+    if (dgamma) {
+        launch_backward_eval_grads(pa, y, dy, dx, gamma, beta, running_var, eps, dgamma, dbeta,
+                                   act, act_param, workspace, stream);
+    } else {
         launch_eval_consts(pa, gamma, beta, running_var, eps, workspace, stream);
-    launch_backward_apply(pa, y, dy, dx, act, act_param, workspace, stream);
+        launch_backward_apply(pa, y, dy, dx, act, act_param, workspace, stream);
+    }
     return launched();
 }
 

@@ -43,13 +43,42 @@ __device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy
     }
 }
 
+// The same sums, and dx = A*dz written over dy's values (the backward with frozen
+// statistics, where dx needs no reduction: A = gamma/sqrt(running_var + eps)).
+template <int ACT, int V>
+__device__ __forceinline__ void accumulate_dx(const float (&y)[V], float (&dy)[V],
+                                              const float (&beta)[V], const float (&A)[V],
+                                              float a, float inv_a, float (&sdz)[V],
+                                              float (&sdzt)[V])
+{
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float z, slope;
+        act_invert<ACT>(y[e], a, inv_a, z, slope);
+        const float dz = slope * dy[e];
+        sdz[e] += dz;
+        sdzt[e] = fmaf(dz, z - beta[e], sdzt[e]);
+        dy[e] = A[e] * dz;
+    }
+}
+
+// A = gamma/sqrt(running_var + eps) in fp64, rounded once.
+__device__ __forceinline__ float frozen_scale(const float* gamma, const float* var, float eps,
+                                              int64_t c)
+{
+    return float(double(gamma[c]) / sqrt(double(var[c]) + double(eps)));
+}
+
 // ---------------------------------------------------------------------------
 // NCHW: workgroup b covers channel c = b / P, partial p = b % P.
-template <int DT, int V, int ACT>
+// DX: also writes dx for the backward with frozen statistics (each element of dy
+// is read by the thread that then writes the same element of dx, so dx may be dy).
+template <int DT, int V, int ACT, bool DX>
 __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
-    const void* __restrict__ y, const void* __restrict__ dy, int64_t C, int64_t HW, int64_t m,
+    const void* __restrict__ y, const void* dy, int64_t C, int64_t HW, int64_t m,
     int64_t unit, int64_t P, const float* __restrict__ beta, float a, float inv_a,
-    float* __restrict__ part_dz, float* __restrict__ part_dzt)
+    float* __restrict__ part_dz, float* __restrict__ part_dzt, void* dx,
+    const float* __restrict__ gamma, const float* __restrict__ frozen_var, float eps)
 {
     const int64_t b = blockIdx.x;
     const int64_t c = b / P;
@@ -58,30 +87,46 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
     const int64_t j1 = dmin(p * unit + unit, m) / V;
     int64_t j = p * unit / V + threadIdx.x;
 
-    float bc[V], sdz[V], sdzt[V];
+    float bc[V], sdz[V], sdzt[V], A[V];
     const float bb = beta[c];
+    const float Ac = DX ? frozen_scale(gamma, frozen_var, eps, c) : 0.f;
 #pragma unroll
-    for (int e = 0; e < V; ++e) { bc[e] = bb; sdz[e] = 0.f; sdzt[e] = 0.f; }
+    for (int e = 0; e < V; ++e) { bc[e] = bb; A[e] = Ac; sdz[e] = 0.f; sdzt[e] = 0.f; }
 
     ChannelWalk w;
     w.init(j < j1 ? j : 0, c, C, HWv, kThreads);
     for (; j + (kUnrollB - 1) * kThreads < j1; j += kUnrollB * kThreads) {
         float vy[kUnrollB][V], vd[kUnrollB][V];
+        int64_t ad[kUnrollB];
 #pragma unroll
         for (int u = 0; u < kUnrollB; ++u) {
-            load_elems<DT, V>(y, w.addr * V, vy[u]);
-            load_elems<DT, V>(dy, w.addr * V, vd[u]);
+            ad[u] = w.addr * V;
+            load_elems<DT, V>(y, ad[u], vy[u]);
+            load_elems<DT, V>(dy, ad[u], vd[u]);
             w.step();
         }
 #pragma unroll
-        for (int u = 0; u < kUnrollB; ++u) accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
+        for (int u = 0; u < kUnrollB; ++u) {
+            if constexpr (DX) {
+                accumulate_dx<ACT, V>(vy[u], vd[u], bc, A, a, inv_a, sdz, sdzt);
+                store_out<DT, V>(dx, ad[u], vd[u]);
+            } else {
+                accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
+            }
+        }
     }
     for (; j < j1; j += kThreads) {
         float vy[V], vd[V];
-        load_elems<DT, V>(y, w.addr * V, vy);
-        load_elems<DT, V>(dy, w.addr * V, vd);
+        const int64_t ad = w.addr * V;
+        load_elems<DT, V>(y, ad, vy);
+        load_elems<DT, V>(dy, ad, vd);
         w.step();
-        accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+        if constexpr (DX) {
+            accumulate_dx<ACT, V>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
+            store_out<DT, V>(dx, ad, vd);
+        } else {
+            accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+        }
     }
     float S1 = 0.f, S2 = 0.f;
 #pragma unroll
@@ -104,11 +149,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
 // ---------------------------------------------------------------------------
 // NHWC: workgroup b covers channel slice b % slices and partial b / slices, i.e.
 // row groups p, p + P, ... of rpi = 256/tpr rows (as the statistics kernel).
-template <int DT, int V, int ACT>
+template <int DT, int V, int ACT, bool DX>
 __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
-    const void* __restrict__ y, const void* __restrict__ dy, int64_t m, int64_t Cv, int tpr,
+    const void* __restrict__ y, const void* dy, int64_t m, int64_t Cv, int tpr,
     int64_t slices, int64_t groups, int64_t P, const float* __restrict__ beta, float a,
-    float inv_a, float* __restrict__ part_dz, float* __restrict__ part_dzt)
+    float inv_a, float* __restrict__ part_dz, float* __restrict__ part_dzt, void* dx,
+    const float* __restrict__ gamma, const float* __restrict__ frozen_var, float eps)
 {
     const int64_t b = blockIdx.x;
     const int64_t p = b / slices;
@@ -119,12 +165,24 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     const int64_t col = sl * tpr + (t - rs * tpr);
     const bool active = col < Cv;
 
-    float bc[V], sdz[V], sdzt[V];
+    float bc[V], sdz[V], sdzt[V], A[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) { bc[e] = 0.f; sdz[e] = 0.f; sdzt[e] = 0.f; }
+    for (int e = 0; e < V; ++e) { bc[e] = 0.f; A[e] = 0.f; sdz[e] = 0.f; sdzt[e] = 0.f; }
+    // one element of the reduction; with DX also dx at storage index i (elements)
+    auto one = [&](float (&vy)[V], float (&vd)[V], int64_t i) {
+        if constexpr (DX) {
+            accumulate_dx<ACT, V>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
+            store_out<DT, V>(dx, i, vd);
+        } else {
+            accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+        }
+    };
     if (active) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) bc[e] = beta[col * V + e];
+        for (int e = 0; e < V; ++e) {
+            bc[e] = beta[col * V + e];
+            if constexpr (DX) A[e] = frozen_scale(gamma, frozen_var, eps, col * V + e);
+        }
         if constexpr (V == Raw16<DT>::V) {
             // software pipeline over complete row groups (branch-free): the next
             // kUnrollB groups of y and dy load while the current ones are summed;
@@ -140,13 +198,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                     bd[u] = dv[i];
                 }
             };
-            auto add_set = [&](const uint4 (&by)[kUnrollB], const uint4 (&bd)[kUnrollB]) {
+            auto add_set = [&](const uint4 (&by)[kUnrollB], const uint4 (&bd)[kUnrollB],
+                               int64_t g0) {
 #pragma unroll
                 for (int u = 0; u < kUnrollB; ++u) {
                     float vy[V], vd[V];
                     unpack16<DT>(by[u], vy);
                     unpack16<DT>(bd[u], vd);
-                    accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+                    one(vy, vd, (((g0 + u * P) * rpi + rs) * Cv + col) * V);
                 }
             };
             int64_t g = p;
@@ -155,13 +214,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                 load_set(Ay, Ad, g);
                 for (;;) {
                     const int64_t g2 = g + kUnrollB * P;
-                    if (g2 + (kUnrollB - 1) * P >= full) { add_set(Ay, Ad); g = g2; break; }
+                    if (g2 + (kUnrollB - 1) * P >= full) { add_set(Ay, Ad, g); g = g2; break; }
                     load_set(By, Bd, g2);
-                    add_set(Ay, Ad);
+                    add_set(Ay, Ad, g);
                     const int64_t g3 = g2 + kUnrollB * P;
-                    if (g3 + (kUnrollB - 1) * P >= full) { add_set(By, Bd); g = g3; break; }
+                    if (g3 + (kUnrollB - 1) * P >= full) { add_set(By, Bd, g2); g = g3; break; }
                     load_set(Ay, Ad, g3);
-                    add_set(By, Bd);
+                    add_set(By, Bd, g2);
                     g = g3;
                 }
             }
@@ -171,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                     float vy[V], vd[V];
                     unpack16<DT>(yv[r * Cv + col], vy);
                     unpack16<DT>(dv[r * Cv + col], vd);
-                    accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+                    one(vy, vd, (r * Cv + col) * V);
                 }
             }
         } else {
@@ -181,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                     float vy[V], vd[V];
                     load_elems<DT, V>(y, (r * Cv + col) * V, vy);
                     load_elems<DT, V>(dy, (r * Cv + col) * V, vd);
-                    accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+                    one(vy, vd, (r * Cv + col) * V);
                 }
             }
         }
@@ -404,48 +463,76 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
 // ---------------------------------------------------------------------------
 // host launchers
 
-template <int DT, int V, int ACT>
+// The frozen-statistics arguments (dx, gamma, frozen_var, eps) are used only with DX.
+struct FrozenDx {
+    void* dx = nullptr;
+    const float* gamma = nullptr;
+    const float* var = nullptr;
+    float eps = 0.f;
+};
+
+template <int DT, int V, int ACT, bool DX>
 static void launch_reduce_dva(const Plan& pl, const void* y, const void* dy, const float* beta,
-                              float a, float ia, float* pa, float* pb, hipStream_t s)
+                              float a, float ia, float* pa, float* pb, const FrozenDx& f,
+                              hipStream_t s)
 {
     if (pl.layout == kNCHW)
-        hipLaunchKernelGGL((k_bwd_reduce_nchw<DT, V, ACT>), dim3(pl.reduce_blocks), dim3(kThreads),
-                           0, s, y, dy, pl.C, pl.HW, pl.m, pl.unit, pl.P, beta, a, ia, pa, pb);
+        hipLaunchKernelGGL((k_bwd_reduce_nchw<DT, V, ACT, DX>), dim3(pl.reduce_blocks),
+                           dim3(kThreads), 0, s, y, dy, pl.C, pl.HW, pl.m, pl.unit, pl.P, beta, a,
+                           ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
     else
-        hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT>), dim3(pl.reduce_blocks), dim3(kThreads),
-                           0, s, y, dy, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit, pl.P, beta, a,
-                           ia, pa, pb);
+        hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT, DX>), dim3(pl.reduce_blocks),
+                           dim3(kThreads), 0, s, y, dy, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit,
+                           pl.P, beta, a, ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
 }
 
-template <int DT, int V>
-static void launch_reduce_dv(const Plan& pl, const void* y, const void* dy, const float* beta,
-                             int act, float a, float ia, float* pa, float* pb, hipStream_t s)
+template <bool DX>
+static void launch_reduce(const Plan& pl, const void* y, const void* dy, const float* beta,
+                          int act, float a, float ia, float* pa, float* pb, const FrozenDx& f,
+                          hipStream_t s)
 {
-    switch (act) {
-    case kLeaky: launch_reduce_dva<DT, V, kLeaky>(pl, y, dy, beta, a, ia, pa, pb, s); break;
-    case kElu: launch_reduce_dva<DT, V, kElu>(pl, y, dy, beta, a, ia, pa, pb, s); break;
-    default: launch_reduce_dva<DT, V, kIdentity>(pl, y, dy, beta, a, ia, pa, pb, s); break;
-    }
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            constexpr int DT = decltype(d)::value, ACT = decltype(ac)::value;
+            if (pl.vec)
+                launch_reduce_dva<DT, vec_width(DT), ACT, DX>(pl, y, dy, beta, a, ia, pa, pb, f, s);
+            else
+                launch_reduce_dva<DT, 1, ACT, DX>(pl, y, dy, beta, a, ia, pa, pb, f, s);
+        });
+    });
 }
 
 void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const float* gamma,
                             const float* beta, const float* invstd, float* dgamma, float* dbeta,
-                            int act, float a, void* ws, hipStream_t s, const float* frozen_var,
-                            float eps)
+                            int act, float a, void* ws, hipStream_t s)
 {
     char* wsb = static_cast<char*>(ws);
     float* pa = reinterpret_cast<float*>(wsb + pl.off_part_a);
     float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
     float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
     const float ia = act == kIdentity ? 1.f : 1.f / a;
-    with_dtype(pl.dtype, [&](auto d) {
-        constexpr int DT = decltype(d)::value;
-        if (pl.vec) launch_reduce_dv<DT, vec_width(DT)>(pl, y, dy, beta, act, a, ia, pa, pb, s);
-        else launch_reduce_dv<DT, 1>(pl, y, dy, beta, act, a, ia, pa, pb, s);
-    });
+    launch_reduce<false>(pl, y, dy, beta, act, a, ia, pa, pb, FrozenDx{}, s);
     hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
                        dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta, invstd,
-                       frozen_var, eps, dgamma, dbeta, consts);
+                       static_cast<const float*>(nullptr), 0.f, dgamma, dbeta, consts);
+}
+
+void launch_backward_eval_grads(const Plan& pl, const void* y, const void* dy, void* dx,
+                                const float* gamma, const float* beta, const float* running_var,
+                                float eps, float* dgamma, float* dbeta, int act, float a,
+                                void* ws, hipStream_t s)
+{
+    char* wsb = static_cast<char*>(ws);
+    float* pa = reinterpret_cast<float*>(wsb + pl.off_part_a);
+    float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
+    float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
+    const float ia = act == kIdentity ? 1.f : 1.f / a;
+    launch_reduce<true>(pl, y, dy, beta, act, a, ia, pa, pb, FrozenDx{dx, gamma, running_var, eps},
+                        s);
+    hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
+                       dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta,
+                       static_cast<const float*>(nullptr), running_var, eps, dgamma, dbeta,
+                       consts);
 }
 
 void launch_eval_consts(const Plan& pl, const float* gamma, const float* beta,

@@ -18,12 +18,17 @@ void launch_forward_eval(const Plan& pl, void* x, const float* gamma, const floa
                          const float* rm, const float* rv, float eps, int act, float a,
                          hipStream_t s);
 
-// frozen_var non-null: the backward through the inference forward (statistics
-// frozen at running_var); the finishing kernel then leaves its dx constants.
 void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const float* gamma,
                             const float* beta, const float* invstd, float* dgamma, float* dbeta,
-                            int act, float a, void* ws, hipStream_t s,
-                            const float* frozen_var = nullptr, float eps = 0.f);
+                            int act, float a, void* ws, hipStream_t s);
+
+// Backward through the inference forward with dgamma/dbeta: one pass over y and dy
+// writes dx (it needs no reduction) and the partial sums, then the sums are
+// finished.
+void launch_backward_eval_grads(const Plan& pl, const void* y, const void* dy, void* dx,
+                                const float* gamma, const float* beta, const float* running_var,
+                                float eps, float* dgamma, float* dbeta, int act, float a,
+                                void* ws, hipStream_t s);
 
 // dx constants of the backward through the inference forward, without the sums.
 void launch_eval_consts(const Plan& pl, const float* gamma, const float* beta,

@@ -400,9 +400,11 @@ def test_backward_eval(wl, grads):
     ws.fill_(0xAB)
     iabn.iabn_backward_eval(y, dy, dx, N, C, H, W, wl.layout, g, b, rvt, wl.eps, dg, db, wl.act,
                             wl.act_param, ws)
-    # in place over dy gives the same bits
+    # in place over dy, and the other variant (sums or not), give the same values
     dy2 = harness.to_device(inp.dy, wl)
-    iabn.iabn_backward_eval(y, dy2, dy2, N, C, H, W, wl.layout, g, b, rvt, wl.eps, None, None,
+    dg2 = torch.empty(C, device="cuda") if not grads else None
+    db2 = torch.empty(C, device="cuda") if not grads else None
+    iabn.iabn_backward_eval(y, dy2, dy2, N, C, H, W, wl.layout, g, b, rvt, wl.eps, dg2, db2,
                             wl.act, wl.act_param, ws)
     torch.cuda.synchronize()
     assert torch.equal(dy2, dx)
