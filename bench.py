@@ -25,6 +25,13 @@ path's forward / backward elementwise kernels.
 the step of a network fine-tuned with frozen normalisation statistics instead:
 iabn_forward_eval (read x, write y: 2S) + iabn_backward_eval with dgamma/dbeta
 (read y and dy, write dx in the same pass as the sums: 3S), 5S per step.
+
+--mode block compares, on the workload's tensor, a chain of L layers of
+(1x1 convolution -> normalisation + activation) built with the InPlace-ABN
+autograd module against the same chain with torch's BatchNorm2d + activation:
+forward + backward time per iteration, activation memory held after the
+forward, and peak memory (the pages' claims: less training memory at a small
+compute cost).  The convolutions are torch's (MIOpen) in both chains.
 """
 from __future__ import annotations
 
@@ -185,6 +192,86 @@ def run_frozen(args, wl) -> int:
     return 0
 
 
+def run_block(args, wl) -> int:
+    """InPlace-ABN against BatchNorm2d + activation inside a convolution chain."""
+    import torch
+    import workloads
+    from place_batchnorm_activation_amd.autograd import InPlaceABN
+
+    N, C, H, W, L = wl.N, wl.C, wl.H, wl.W, args.layers
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    dt = workloads.storage_torch_dtype(wl.dtype)
+    fmt = torch.channels_last if wl.layout == "NHWC" else torch.contiguous_format
+    torch.manual_seed(0)
+    convs = [torch.nn.Conv2d(C, C, 1, bias=False).to(dev, dt).to(memory_format=fmt)
+             for _ in range(L)]
+    act = {"leaky_relu": lambda: torch.nn.LeakyReLU(wl.act_param),
+           "elu": lambda: torch.nn.ELU(wl.act_param), "identity": torch.nn.Identity}[wl.act]
+
+    def torch_norm():
+        bn = torch.nn.BatchNorm2d(C, eps=wl.eps, momentum=wl.momentum).to(dev)
+        return torch.nn.Sequential(bn, act())
+
+    chains = {
+        "inplace_abn": [InPlaceABN(C, wl.eps, wl.momentum, wl.act, wl.act_param, device=dev)
+                        for _ in range(L)],
+        "batchnorm2d_act": [torch_norm() for _ in range(L)],
+    }
+    x = torch.randn(N, C, H, W, device=dev, dtype=dt).to(memory_format=fmt).requires_grad_()
+
+    def step(norms):
+        h = x
+        for conv, norm in zip(convs, norms):
+            h = norm(conv(h))
+        h.backward(torch.ones_like(h))
+
+    res = {}
+    S = wl.storage_bytes
+    for name, norms in chains.items():
+        for _ in range(max(2, args.warmup // 5)):
+            step(norms)
+        torch.cuda.synchronize()
+        # memory: activations held after the forward, and the peak of one iteration
+        x.grad = None
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        h = x
+        for conv, norm in zip(convs, norms):
+            h = norm(conv(h))
+        held = torch.cuda.memory_allocated() - base
+        h.backward(torch.ones_like(h))
+        del h
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        k = max(5, args.steps // 20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(k):
+            step(norms)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"ms_per_iter": round(e0.elapsed_time(e1) / k, 4),
+                     "held_after_forward_MB": round(held / 2**20, 1),
+                     "held_tensors_per_layer": round(held / S / L, 2),
+                     "peak_MB": round(peak / 2**20, 1), "iters": k}
+        print("bench: block %s %s" % (name, res[name]), file=sys.stderr, flush=True)
+    a, b = res["inplace_abn"], res["batchnorm2d_act"]
+    out = {
+        "metric": "conv1x1 + norm/act chain: InPlace-ABN vs BatchNorm2d+activation",
+        "config": {"workload": wl.name, "N": N, "C": C, "H": H, "W": W, "layout": wl.layout,
+                   "storage": wl.dtype, "act": wl.act, "act_param": wl.act_param, "layers": L,
+                   "mode": "block"},
+        "data": "synthetic", "n_gpus": 1,
+        "inplace_abn": a, "batchnorm2d_act": b,
+        "time_ratio": round(a["ms_per_iter"] / b["ms_per_iter"], 4),
+        "held_memory_ratio": round(a["held_after_forward_MB"] / b["held_after_forward_MB"], 4),
+        "peak_memory_ratio": round(a["peak_MB"] / b["peak_MB"], 4),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,8 +282,10 @@ def main() -> int:
     ap.add_argument("--warm-only", action="store_true", help="one buffer set (for profiling)")
     ap.add_argument("--dtype", choices=("f32", "bf16", "f16"), default=None,
                     help="storage dtype instead of the workload's own")
-    ap.add_argument("--mode", choices=("train", "frozen"), default="train",
-                    help="train: forward_train + backward; frozen: forward_eval + backward_eval")
+    ap.add_argument("--mode", choices=("train", "frozen", "block"), default="train",
+                    help="train: forward_train + backward; frozen: forward_eval + backward_eval; "
+                         "block: conv + norm/act chain against torch's BatchNorm2d")
+    ap.add_argument("--layers", type=int, default=4, help="layers of the --mode block chain")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark: copy a MIB-MiB buffer 5 times (a plain copy "
                          "kernel of known size, the reference that scales memory counters)")
@@ -226,6 +315,8 @@ def main() -> int:
         wl = dataclasses.replace(wl, dtype=args.dtype, name="%s_as_%s" % (wl.name, args.dtype))
     if args.mode == "frozen":
         return run_frozen(args, wl)
+    if args.mode == "block":
+        return run_block(args, wl)
     N, C, H, W = wl.N, wl.C, wl.H, wl.W
     inp = workloads.make_inputs(wl)
     dev = torch.device("cuda", 0)
