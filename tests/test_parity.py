@@ -246,6 +246,62 @@ def _variant_shapes():
     return out
 
 
+# Tensors beyond 4 GiB: the resident kernels address with 32-bit offsets and must
+# step aside; the split kernels index with 64 bits.  Inputs are drawn on the
+# device; the oracle checks sampled channels (first, middle, last).
+BIG = [custom(2, 8, 16, 2048, 4100),                              # fp32 NCHW, 4.3 GB
+       custom(3, 4, 512, 1024, 1025, layout="NHWC", dtype="bf16")]   # bf16 NHWC, 4.3 GB
+
+
+@pytest.mark.parametrize("wl", BIG, ids=lambda w: w.name)
+def test_beyond_4gib(wl):
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+    assert wl.storage_bytes > 2 ** 32
+    desc = iabn.iabn_describe_plan(N, C, H, W, wl.layout,
+                                   workloads.storage_torch_dtype(wl.dtype), wl.act)
+    assert desc.startswith("forward=split") and "backward=split" in desc, desc
+    inp = workloads.make_device_inputs(wl, seed=4242)
+    chans = [0, C // 2, C - 1]
+    x_ch = [workloads.device_channel(inp.x, wl, c) for c in chans]
+    dy_ch = [workloads.device_channel(inp.dy, wl, c) for c in chans]
+    g = torch.from_numpy(inp.gamma).cuda()
+    b = torch.from_numpy(inp.beta).cuda()
+    rm = torch.from_numpy(inp.running_mean).cuda()
+    rv = torch.from_numpy(inp.running_var).cuda()
+    sm, si = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    dg, db = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    ws = iabn.workspace(N, C, H, W, wl.layout, inp.x.dtype)
+    print("case:", wl.name, desc, flush=True)
+    iabn.iabn_forward_train(inp.x, N, C, H, W, wl.layout, g, b, rm, rv, sm, si, wl.act,
+                            wl.act_param, wl.eps, wl.momentum, ws)
+    iabn.iabn_backward(inp.x, inp.dy, inp.dy, N, C, H, W, wl.layout, g, b, si, dg, db, wl.act,
+                       wl.act_param, ws)           # dx over dy
+    torch.cuda.synchronize()
+    sm, si, dg, db = (t.cpu().numpy() for t in (sm, si, dg, db))
+    ref = {k: [] for k in ("mean", "invstd", "dgamma", "dbeta")}
+    errs = {"y": 0.0, "dx": 0.0}
+    for k, c in enumerate(chans):
+        f = oracle.forward_train(x_ch[k], inp.gamma[c:c + 1], inp.beta[c:c + 1], wl.act,
+                                 harness.f32(wl.act_param), harness.f32(wl.eps),
+                                 storage=wl.dtype)
+        y_gpu = workloads.device_channel(inp.x, wl, c)
+        errs["y"] = max(errs["y"], harness.rel_err_tensor(y_gpu, f["y"]))
+        o = oracle.backward_from_y(y_gpu, dy_ch[k], inp.gamma[c:c + 1], inp.beta[c:c + 1],
+                                   si[c:c + 1].astype(np.float64), wl.act,
+                                   harness.f32(wl.act_param))
+        del y_gpu
+        dx_gpu = workloads.device_channel(inp.dy, wl, c)
+        errs["dx"] = max(errs["dx"], harness.rel_err_tensor(dx_gpu, o["dx"]))
+        for key, src in (("mean", f), ("invstd", f), ("dgamma", o), ("dbeta", o)):
+            ref[key].append(src[key][0])
+    errs["save_mean"] = harness.rel_err_vec(sm[chans], np.array(ref["mean"]))
+    errs["save_invstd"] = harness.rel_err_vec(si[chans], np.array(ref["invstd"]))
+    errs["dgamma"] = harness.rel_err_vec(dg[chans], np.array(ref["dgamma"]))
+    errs["dbeta"] = harness.rel_err_vec(db[chans], np.array(ref["dbeta"]))
+    print("  channels", chans, errs, flush=True)
+    harness.assert_within(errs, wl.dtype, wl.name)
+
+
 # every slice-resident NHWC variant, picked through the row count it holds
 # (one lane per row: capacities 512, 1024, 2048, 3328, 6656, 9216 rows), full and
 # ragged; slice counts that divide by 8 (XCD-grouped slice map) and ones that do not

@@ -206,6 +206,61 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, with_dy: bool = True) 
                   running_mean=np.zeros(C, np.float32), running_var=np.ones(C, np.float32))
 
 
+@dataclasses.dataclass
+class DeviceInputs:
+    """Inputs drawn directly in device memory, for tensors too large to build on the
+    host.  x and dy are torch tensors in the storage layout and dtype; the
+    per-channel vectors are float32 numpy arrays."""
+    wl: Workload
+    x: object
+    dy: object
+    gamma: np.ndarray
+    beta: np.ndarray
+    running_mean: np.ndarray
+    running_var: np.ndarray
+
+
+def make_device_inputs(wl: Workload, seed: int, device="cuda") -> DeviceInputs:
+    """The workload's recipe drawn on the device: per-channel parameters from numpy
+    PCG64(seed) as in make_inputs (same draw order); x and dy from torch's
+    device generator seeded with `seed`, drawn in the storage layout in fp32 and
+    rounded to the storage dtype by torch's (nearest-even) cast."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(seed))
+    r = wl.recipe
+    C = wl.C
+    mu = _draw_vec(rng, r.mu, C)
+    sc = _draw_vec(rng, r.scale, C)
+    sign = (rng.integers(0, 2, size=C) * 2 - 1).astype(np.float64) if r.gamma_signed else np.ones(C)
+    gmag = _draw_vec(rng, r.gamma, C)
+    beta = rng.normal(0.0, np.sqrt(r.beta_var), size=C)
+    shape = (wl.N, C, wl.H, wl.W) if wl.layout == "NCHW" else (wl.N, wl.H, wl.W, C)
+    bshape = (1, C, 1, 1) if wl.layout == "NCHW" else (1, 1, 1, C)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = storage_torch_dtype(wl.dtype)
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    x.mul_(torch.tensor(sc, dtype=torch.float32, device=device).view(bshape))
+    x.add_(torch.tensor(mu, dtype=torch.float32, device=device).view(bshape))
+    x = x.to(dt)
+    dy = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    dy.mul_(float(np.sqrt(r.dy_var)))
+    dy = dy.to(dt)
+    return DeviceInputs(wl=wl, x=x, dy=dy, gamma=(sign * gmag).astype(np.float32),
+                        beta=beta.astype(np.float32), running_mean=np.zeros(C, np.float32),
+                        running_var=np.ones(C, np.float32))
+
+
+def device_channel(t, wl: Workload, c: int) -> np.ndarray:
+    """Channel c of a device storage tensor as an fp64 [N, 1, H, W] host array."""
+    import torch
+    if wl.layout == "NCHW":
+        v = t[:, c:c + 1, :, :]
+    else:
+        v = t[:, :, :, c].unsqueeze(1)
+    return v.to(torch.float32).cpu().numpy().astype(np.float64)
+
+
 def storage_torch_dtype(dtype: str):
     """torch dtype used to hold the storage bits (bf16 bits travel as torch.bfloat16,
     fp16 bits as torch.float16)."""
