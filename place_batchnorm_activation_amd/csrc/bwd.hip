@@ -287,9 +287,29 @@ __global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     const int cl = threadIdx.x % kFinChannels;
     const int ph = threadIdx.x / kFinChannels;
     const int64_t c = int64_t(blockIdx.x) * kFinChannels + cl;
+    // the finishing thread's per-channel inputs, fetched before the sums
+    const bool fin = ph == 0 && c < C;
+    float g_c = 1.f, b_c = 0.f, s_c = 0.f;
+    if (fin) {
+        g_c = gamma[c];
+        b_c = beta[c];
+        s_c = frozen_var ? frozen_var[c] : invstd[c];
+    }
     double s1 = 0.0, s2 = 0.0;
     if (c < C) {
-        for (int64_t p = ph; p < P; p += kFinPhases) {
+        // partials in order, four at a time with their loads issued together
+        int64_t p = ph;
+        for (; p + 3 * kFinPhases < P; p += 4 * kFinPhases) {
+            float a[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = part_dz[(p + u * kFinPhases) * C + c];
+                b[u] = part_dzt[(p + u * kFinPhases) * C + c];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { s1 += double(a[u]); s2 += double(b[u]); }
+        }
+        for (; p < P; p += kFinPhases) {
             s1 += double(part_dz[p * C + c]);
             s2 += double(part_dzt[p * C + c]);
         }
@@ -299,21 +319,20 @@ __global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     sh1[ph][cl] = s1;
     sh2[ph][cl] = s2;
     __syncthreads();
-    if (ph != 0 || c >= C) return;
+    if (!fin) return;
     for (int k = 1; k < kFinPhases; ++k) { s1 += sh1[k][cl]; s2 += sh2[k][cl]; }
-    const double g = double(gamma[c]);
+    const double g = double(g_c);
     const double db = s1;
     const double dg = s2 / g;
     dbeta[c] = float(db);
     dgamma[c] = float(dg);
     if (frozen_var) {
-        consts[c] = make_float4(float(g / sqrt(double(frozen_var[c]) + double(eps))), 0.f, 0.f,
-                                beta[c]);
+        consts[c] = make_float4(float(g / sqrt(double(s_c) + double(eps))), 0.f, 0.f, b_c);
         return;
     }
-    const double A = g * double(invstd[c]);
+    const double A = g * double(s_c);
     const double md = double(m);
-    consts[c] = make_float4(float(A), float(-A * dg / (md * g)), float(-A * db / md), beta[c]);
+    consts[c] = make_float4(float(A), float(-A * dg / (md * g)), float(-A * db / md), b_c);
 }
 
 // The dx constants of the backward through the inference forward when dgamma and

@@ -265,9 +265,37 @@ __global__ __launch_bounds__(kFinThreads) void k_fwd_finalize(
     const int cl = threadIdx.x % kFinChannels;
     const int ph = threadIdx.x / kFinChannels;
     const int64_t c = int64_t(blockIdx.x) * kFinChannels + cl;
+    // the finishing thread's per-channel inputs, fetched before the sums
+    const bool fin = ph == 0 && c < C;
+    float K = 0.f, g_c = 0.f, b_c = 0.f, rm_c = 0.f, rv_c = 0.f;
+    if (fin) {
+        K = load_one<DT>(x, layout == kNCHW ? c * HW : c);
+        g_c = gamma[c];
+        b_c = beta[c];
+        if (running_mean) { rm_c = running_mean[c]; rv_c = running_var[c]; }
+    }
     double S1 = 0.0, S2 = 0.0;
     if (c < C) {
-        for (int64_t p = ph; p < P; p += kFinPhases) {
+        // partials p = ph, ph + kFinPhases, ... in order; four at a time with their
+        // loads issued together
+        int64_t p = ph;
+        for (; p + 3 * kFinPhases < P; p += 4 * kFinPhases) {
+            float n[4], mu[4], m2[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t q = p + u * kFinPhases;
+                n[u] = count[q];
+                mu[u] = part_mean[q * C + c];
+                m2[u] = part_m2[q * C + c];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const double nn = double(n[u]), mm = double(mu[u]);
+                S1 = fma(nn, mm, S1);
+                S2 += fma(nn * mm, mm, double(m2[u]));
+            }
+        }
+        for (; p < P; p += kFinPhases) {
             const double n = double(count[p]);
             const double mu = double(part_mean[p * C + c]);
             S1 = fma(n, mu, S1);
@@ -279,22 +307,20 @@ __global__ __launch_bounds__(kFinThreads) void k_fwd_finalize(
     sh1[ph][cl] = S1;
     sh2[ph][cl] = S2;
     __syncthreads();
-    if (ph != 0 || c >= C) return;
+    if (!fin) return;
     for (int k = 1; k < kFinPhases; ++k) { S1 += sh1[k][cl]; S2 += sh2[k][cl]; }
     const double mean = S1 / double(m);
     const double var = fmax(S2 - S1 * mean, 0.0) / double(m);
-    const float K = load_one<DT>(x, layout == kNCHW ? c * HW : c);
     const double invstd = 1.0 / sqrt(var + double(eps));
     const double mu = double(K) + mean;
     save_mean[c] = float(mu);
     save_invstd[c] = float(invstd);
     if (running_mean) {
         const double mom = double(momentum);
-        running_mean[c] = float((1.0 - mom) * double(running_mean[c]) + mom * mu);
-        running_var[c] = float((1.0 - mom) * double(running_var[c])
-                               + mom * var * double(m) / double(m - 1));
+        running_mean[c] = float((1.0 - mom) * double(rm_c) + mom * mu);
+        running_var[c] = float((1.0 - mom) * double(rv_c) + mom * var * double(m) / double(m - 1));
     }
-    consts[c] = make_float4(K, float(mean), float(double(gamma[c]) * invstd), beta[c]);
+    consts[c] = make_float4(K, float(mean), float(double(g_c) * invstd), b_c);
 }
 
 // ---------------------------------------------------------------------------
