@@ -26,6 +26,9 @@
  *     inside kernels surface at the caller's next synchronisation.
  *   - Results are bitwise deterministic for a given shape, layout, dtype and
  *     pointer alignment: no floating-point atomics, fixed reduction orders.
+ *   - Calls may be captured in a HIP graph (stream capture): they launch
+ *     kernels only, with no allocation, memset, copy or synchronisation, and a
+ *     replay gives the same bits as the eager call.
  *   - Preconditions that are not checked: gamma_c != 0 in the backward (the
  *     affine step must be invertible), finite inputs (NaN propagates), and no
  *     overlap between buffers other than the aliasing each call allows.

@@ -67,7 +67,10 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
         const int b = fused_bwd_pick(vc);
         if (b >= 0 && fused_worthwhile(p, fused_bwd_threads(b))) p.fused_bwd_variant = b;
     }
-    if (act >= 0) p.nhwc_variant = fused_nhwc_pick(p);
+    if (act >= 0) {
+        p.nhwc_variant = fused_nhwc_pick(p);
+        p.scalar_variant = fused_scalar_pick(p);
+    }
     return p;
 }
 
@@ -220,6 +223,12 @@ iabn_status iabn_forward_train(void* x_inout, int64_t N, int64_t C, int64_t H, i
                                   save_invstd, eps, momentum, act, act_param, stream);
         return launched();
     }
+    if (pl.scalar_variant >= 0) {
+        launch_forward_fused_scalar(pl, x_inout, gamma, beta, running_mean, running_var,
+                                    save_mean, save_invstd, eps, momentum, act, act_param,
+                                    stream);
+        return launched();
+    }
     if (pl.nhwc_variant >= 0) {
         launch_forward_fused_nhwc(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
                                   save_invstd, eps, momentum, act, act_param, stream);
@@ -314,6 +323,11 @@ iabn_status iabn_backward(const void* y, const void* dy, void* dx, int64_t N, in
                                    act_param, stream);
         return launched();
     }
+    if (pa.scalar_variant >= 0) {
+        launch_backward_fused_scalar(pa, y, dy, dx, gamma, beta, save_invstd, dgamma, dbeta, act,
+                                     act_param, stream);
+        return launched();
+    }
     if (pa.nhwc_variant >= 0) {
         launch_backward_fused_nhwc(pa, y, dy, dx, gamma, beta, save_invstd, dgamma, dbeta, act,
                                    act_param, stream);
@@ -370,10 +384,16 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
     if (check_shape(N, C, H, W, layout, dtype) != IABN_OK) return -1;
     if (act != IABN_ACT_IDENTITY && act != IABN_ACT_LEAKY_RELU && act != IABN_ACT_ELU) return -1;
     const Plan p = plan_for(N, C, H, W, layout, dtype, aligned16 != 0, act);
-    char fwd[96], bwd[96], nd[48] = "";
+    char fwd[96], bwd[96], nd[48] = "", sd[48] = "";
     switch (p.nhwc_variant) {
 #define IABN_ROW(ID, T, LPR, NR) case ID: snprintf(nd, sizeof nd, "%dx%dx%d", T, LPR, NR); break;
         IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    default: break;
+    }
+    switch (p.scalar_variant) {
+#define IABN_ROW(ID, T, NR) case ID: snprintf(sd, sizeof sd, "%dx%d", T, NR); break;
+        IABN_FUSED_SCALAR_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     default: break;
     }
@@ -386,6 +406,8 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         default: break;
         }
         snprintf(fwd, sizeof fwd, "channel_resident(%dx%d)", T, NR);
+    } else if (p.scalar_variant >= 0) {
+        snprintf(fwd, sizeof fwd, "channel_resident_scalar(%s)", sd);
     } else if (p.nhwc_variant >= 0) {
         snprintf(fwd, sizeof fwd, "slice_resident(%s)", nd);
     } else {
@@ -404,6 +426,8 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         }
         snprintf(bwd, sizeof bwd, "channel_resident(%dx%d,%s)", T, NR,
                  dyr ? "dy_resident" : "dy_streamed");
+    } else if (p.scalar_variant >= 0) {
+        snprintf(bwd, sizeof bwd, "channel_resident_scalar(%s,dy_resident)", sd);
     } else if (p.nhwc_variant >= 0) {
         snprintf(bwd, sizeof bwd, "slice_resident(%s)", nd);
     } else {

@@ -54,6 +54,19 @@
     X(9, 512, 2, 18)
 #endif
 
+// Channel-resident NCHW kernels on single elements, for shapes the 16-byte
+// vectors cannot take (H*W not a multiple of the vector width, e.g. 7x7 maps, or
+// pointers not 16-byte aligned).  X(id, T, NR): NR elements per thread, y and dy
+// both resident in the backward.
+#define IABN_FUSED_SCALAR_VARIANTS(X) \
+    X(0, 256, 2)                       \
+    X(1, 256, 4)                       \
+    X(2, 256, 8)                       \
+    X(3, 256, 16)                      \
+    X(4, 512, 16)                      \
+    X(5, 512, 32)                      \
+    X(6, 512, 48)
+
 namespace iabn {
 
 struct FusedVariant { int id, T, NR; bool dyr; };
@@ -117,7 +130,9 @@ inline bool fused_worthwhile(const Plan& p, int threads)
 // better, so they are preferred while they still give at least 128 workgroups;
 // then the first variant (table order) whose workgroup holds all m rows.  The
 // kernels are taken when the slices fill the chip, or when the tensor is small
-// enough for launch latency to rule.  32-bit vector indices address the tensor.
+// enough for launch latency to rule and each workgroup's rows are few (measured:
+// 32 workgroups of 6272 rows lose to the split path, 64 of 1568 win).  32-bit
+// vector indices address the tensor.
 inline int fused_nhwc_pick(const Plan& p)
 {
     if (p.layout != kNHWC || !p.vec || p.numel == 0) return -1;
@@ -136,9 +151,32 @@ inline int fused_nhwc_pick(const Plan& p)
             if ((pass == 0) != (v.LPR == want)) continue;
             if (cv % v.LPR != 0 || int64_t(v.T / v.LPR) * v.NR < p.m) continue;
             const int64_t blocks = cv / v.LPR;
-            if (blocks * v.T >= int64_t(256) * 256 || bytes <= (int64_t(4) << 20)) return v.id;
+            if (blocks * v.T >= int64_t(256) * 256 || (bytes <= (int64_t(4) << 20) && p.m <= 4096))
+                return v.id;
             return -1;
         }
+    }
+    return -1;
+}
+
+// Scalar channel-resident variant for an NCHW problem off the vector path, or -1:
+// the smallest that holds the channel's m elements, taken on the same terms as
+// the vector kernels (the chip filled, or a tensor under 4 MB).
+inline int fused_scalar_pick(const Plan& p)
+{
+    if (p.layout != kNCHW || p.vec || p.numel == 0) return -1;
+    if (p.numel * p.esize >= (int64_t(1) << 32)) return -1;
+    struct Row { int id, T, NR; };
+    static const Row tbl[] = {
+#define IABN_ROW(ID, T, NR) {ID, T, NR},
+        IABN_FUSED_SCALAR_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    };
+    const int64_t bytes = p.numel * p.esize;
+    for (const auto& v : tbl) {
+        if (int64_t(v.T) * v.NR < p.m) continue;
+        if (p.C * v.T >= int64_t(256) * 256 || bytes <= (int64_t(4) << 20)) return v.id;
+        return -1;
     }
     return -1;
 }
@@ -150,6 +188,14 @@ void launch_forward_fused_nchw(const Plan& pl, void* x, const float* gamma, cons
 void launch_backward_fused_nchw(const Plan& pl, const void* y, const void* dy, void* dx,
                                 const float* gamma, const float* beta, const float* invstd,
                                 float* dgamma, float* dbeta, int act, float a, hipStream_t s);
+
+void launch_forward_fused_scalar(const Plan& pl, void* x, const float* gamma, const float* beta,
+                                 float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                                 int act, float a, hipStream_t s);
+
+void launch_backward_fused_scalar(const Plan& pl, const void* y, const void* dy, void* dx,
+                                  const float* gamma, const float* beta, const float* invstd,
+                                  float* dgamma, float* dbeta, int act, float a, hipStream_t s);
 
 void launch_forward_fused_nhwc(const Plan& pl, void* x, const float* gamma, const float* beta,
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,

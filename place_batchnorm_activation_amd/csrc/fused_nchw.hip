@@ -417,6 +417,168 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
 }
 
 // ---------------------------------------------------------------------------
+// Channel-resident kernels on single elements (planes whose length is not a
+// multiple of the vector width, or pointers off 16-byte alignment).  Thread t
+// owns channel-local elements j = t + k*T, k < NR, walked with ChannelWalk32 in
+// element units; each element's raw bits stay in one VGPR between the passes.
+
+template <int DT>
+__device__ __forceinline__ uint32_t ld_elem(const void* base, uint32_t off)
+{
+    if constexpr (DT == kF32) return static_cast<const uint32_t*>(base)[off];
+    else return static_cast<const uint16_t*>(base)[off];
+}
+
+template <int DT>
+__device__ __forceinline__ float elem_float(uint32_t bits)
+{
+    if constexpr (DT == kF32) return __uint_as_float(bits);
+    else return unpack1<DT>(uint16_t(bits));
+}
+
+template <int DT>
+__device__ __forceinline__ void st_elem(void* base, uint32_t off, float v)
+{
+    if constexpr (DT == kF32) {
+        float* p = static_cast<float*>(base) + off;
+        if constexpr (IABN_FUSED_NT_STORE) __builtin_nontemporal_store(v, p);
+        else *p = v;
+    } else {
+        uint16_t* p = static_cast<uint16_t*>(base) + off;
+        if constexpr (IABN_FUSED_NT_STORE) __builtin_nontemporal_store(pack1<DT>(v), p);
+        else *p = pack1<DT>(v);
+    }
+}
+
+template <int DT, int ACT, int T, int NR>
+__global__ __launch_bounds__(T) void k_fwd_fused_nchw_s(
+    void* x, uint32_t C, uint32_t HW, uint32_t m, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* __restrict__ running_mean,
+    float* __restrict__ running_var, float* __restrict__ save_mean,
+    float* __restrict__ save_invstd, float eps, float momentum, float a)
+{
+    const uint32_t c = blockIdx.x;
+    const uint32_t t = threadIdx.x;
+    const float K = load_one<DT>(x, int64_t(c) * HW);
+    const float g_c = gamma[c];
+    const float b = beta[c];
+    float rm_c = 0.f, rv_c = 0.f;
+    if (t == 0 && running_mean) { rm_c = running_mean[c]; rv_c = running_var[c]; }
+
+    uint32_t r[NR];
+    ChannelWalk32 w;
+    w.init(t, c, C, HW, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        r[k] = (t + k * T < m) ? ld_elem<DT>(x, w.off) : 0u;
+        w.step();
+    }
+    float s1 = 0.f, s2 = 0.f;
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if (t + k * T < m) {
+            const float d = elem_float<DT>(r[k]) - K;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+            ++cnt;
+        }
+    }
+    float n = float(cnt);
+    float mean = cnt ? s1 / n : 0.f;
+    float m2 = cnt ? fmaxf(s2 - s1 * mean, 0.f) : 0.f;
+    block_chan<T>(n, mean, m2);
+
+    const double var = double(m2) / double(m);
+    const double invstd = 1.0 / sqrt(var + double(eps));
+    const float d = float(mean);
+    const float sc = float(double(g_c) * invstd);
+    if (t == 0) {
+        const double mu = double(K) + double(mean);
+        save_mean[c] = float(mu);
+        save_invstd[c] = float(invstd);
+        if (running_mean) {
+            const double mom = double(momentum);
+            running_mean[c] = float((1.0 - mom) * double(rm_c) + mom * mu);
+            running_var[c] = float((1.0 - mom) * double(rv_c) + mom * var * double(m) / double(m - 1));
+        }
+    }
+
+    const uint32_t t2 = opaque(t);
+    w.init(t2, c, C, HW, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if (t2 + k * T < m) {
+            const float v = elem_float<DT>(opaque(r[k]));
+            st_elem<DT>(x, w.off, act_forward<ACT>(fmaf((v - K) - d, sc, b), a));
+        }
+        w.step();
+    }
+}
+
+template <int DT, int ACT, int T, int NR>
+__global__ __launch_bounds__(T) void k_bwd_fused_nchw_s(
+    const void* __restrict__ y, const void* dy, void* dx, uint32_t C, uint32_t HW, uint32_t m,
+    const float* __restrict__ gamma, const float* __restrict__ beta,
+    const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
+    float a, float inv_a)
+{
+    const uint32_t c = blockIdx.x;
+    const uint32_t t = threadIdx.x;
+    const float bc = beta[c];
+    const float g_c = gamma[c];
+    const float is_c = invstd[c];
+
+    uint32_t ry[NR], rd[NR];
+    ChannelWalk32 w;
+    w.init(t, c, C, HW, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const bool ok = t + k * T < m;
+        ry[k] = ok ? ld_elem<DT>(y, w.off) : 0u;
+        rd[k] = ok ? ld_elem<DT>(dy, w.off) : 0u;
+        w.step();
+    }
+    float sdz = 0.f, sdzt = 0.f;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if (t + k * T < m) {
+            float z, slope;
+            act_invert<ACT>(elem_float<DT>(ry[k]), a, inv_a, z, slope);
+            const float dz = slope * elem_float<DT>(rd[k]);
+            sdz += dz;
+            sdzt = fmaf(dz, z - bc, sdzt);
+        }
+    }
+    block_sum2<T>(sdz, sdzt);
+
+    const double g = double(g_c);
+    const double db = double(sdz);
+    const double dg = double(sdzt) / g;
+    if (t == 0) {
+        dbeta[c] = float(db);
+        dgamma[c] = float(dg);
+    }
+    const double A = g * double(is_c);
+    const double md = double(m);
+    const float kA = float(A), kB = float(-A * dg / (md * g)), kC = float(-A * db / md);
+
+    const uint32_t t2 = opaque(t);
+    const float a2 = opaquef(a), ia2 = opaquef(inv_a), bc2 = opaquef(bc);
+    w.init(t2, c, C, HW, T);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if (t2 + k * T < m) {
+            float z, slope;
+            act_invert<ACT>(elem_float<DT>(opaque(ry[k])), a2, ia2, z, slope);
+            const float dz = slope * elem_float<DT>(opaque(rd[k]));
+            st_elem<DT>(dx, w.off, fmaf(kA, dz, fmaf(kB, z - bc2, kC)));
+        }
+        w.step();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 
 template <int DT, int ACT>
@@ -479,6 +641,67 @@ void launch_backward_fused_nchw(const Plan& pl, const void* y, const void* dy, v
     with_dtype(pl.dtype, [&](auto d) {
         with_act(act, [&](auto ac) {
             launch_bwd_da<decltype(d)::value, decltype(ac)::value>(
+                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s);
+        });
+    });
+}
+
+template <int DT, int ACT>
+static void launch_fwd_s_da(const Plan& pl, void* x, const float* gamma, const float* beta,
+                            float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                            float a, hipStream_t s)
+{
+    const uint32_t C = uint32_t(pl.C), HW = uint32_t(pl.HW), m = uint32_t(pl.m);
+    switch (pl.scalar_variant) {
+#define IABN_CASE(ID, T, NR)                                                                      \
+    case ID:                                                                                      \
+        hipLaunchKernelGGL((k_fwd_fused_nchw_s<DT, ACT, T, NR>), dim3(C), dim3(T), 0, s, x, C, HW, \
+                           m, gamma, beta, rm, rv, sm, si, eps, mom, a);                          \
+        break;
+        IABN_FUSED_SCALAR_VARIANTS(IABN_CASE)
+#undef IABN_CASE
+    default: break;
+    }
+}
+
+void launch_forward_fused_scalar(const Plan& pl, void* x, const float* gamma, const float* beta,
+                                 float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                                 int act, float a, hipStream_t s)
+{
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_fwd_s_da<decltype(d)::value, decltype(ac)::value>(
+                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s);
+        });
+    });
+}
+
+template <int DT, int ACT>
+static void launch_bwd_s_da(const Plan& pl, const void* y, const void* dy, void* dx,
+                            const float* gamma, const float* beta, const float* invstd,
+                            float* dgamma, float* dbeta, float a, float ia, hipStream_t s)
+{
+    const uint32_t C = uint32_t(pl.C), HW = uint32_t(pl.HW), m = uint32_t(pl.m);
+    switch (pl.scalar_variant) {
+#define IABN_CASE(ID, T, NR)                                                                      \
+    case ID:                                                                                      \
+        hipLaunchKernelGGL((k_bwd_fused_nchw_s<DT, ACT, T, NR>), dim3(C), dim3(T), 0, s, y, dy, dx, \
+                           C, HW, m, gamma, beta, invstd, dgamma, dbeta, a, ia);                  \
+        break;
+        IABN_FUSED_SCALAR_VARIANTS(IABN_CASE)
+#undef IABN_CASE
+    default: break;
+    }
+}
+
+void launch_backward_fused_scalar(const Plan& pl, const void* y, const void* dy, void* dx,
+                                  const float* gamma, const float* beta, const float* invstd,
+                                  float* dgamma, float* dbeta, int act, float a, hipStream_t s)
+{
+    const float ia = act == kIdentity ? 1.f : 1.f / a;
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_bwd_s_da<decltype(d)::value, decltype(ac)::value>(
                 pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s);
         });
     });

@@ -82,6 +82,8 @@ struct Plan {
     int fused_bwd_variant = -1;
     // slice-resident NHWC kernels (-1: not used)
     int nhwc_variant = -1;
+    // channel-resident NCHW kernels on single elements (-1: not used)
+    int scalar_variant = -1;
     // workspace sections (bytes, 256-aligned)
     size_t off_part_a = 0, off_part_b = 0, off_const = 0, off_count = 0, bytes = 0;
 };

@@ -173,6 +173,41 @@ static void check_plan(const Shape& s, bool vec)
         }
     }
 
+    // ---- channel-resident NCHW kernels on single elements (off the vector path)
+    if (pl.layout == kNCHW && !pl.vec && numel * pl.esize < (int64_t(1) << 32)) {
+        const int64_t HW = pl.HW;
+        struct Var { int T, NR; };
+        std::vector<Var> vars;
+#define IABN_ROW(ID, T, NR) vars.push_back({T, NR});
+        IABN_FUSED_SCALAR_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+        for (const Var& vv : vars) {
+            if (int64_t(vv.T) * vv.NR < m) continue;            // the plan never picks it
+            if (numel > 20000000 && vv.T * vv.NR > 4 * m) continue;
+            std::fill(seen.begin(), seen.end(), 0);
+            for (int64_t c = 0; c < C; ++c)
+                for (int t = 0; t < vv.T; ++t) {
+                    ChannelWalk32 w;
+                    w.init(uint32_t(t), uint32_t(c), uint32_t(C), uint32_t(HW), uint32_t(vv.T));
+                    for (int k = 0; k < vv.NR; ++k) {
+                        const int64_t j = t + int64_t(k) * vv.T;
+                        if (j < m) {
+                            const int64_t direct = ((j / HW) * C + c) * HW + j % HW;
+                            CHECK(int64_t(w.off) == direct, "scalar walk c=%lld t=%d k=%d",
+                                  (long long)c, t, k);
+                            CHECK(int64_t(w.off) < numel, "scalar bounds");
+                            CHECK(int64_t(w.off) * pl.esize < (int64_t(1) << 32), "byte offset");
+                            if (int64_t(w.off) < numel) seen[size_t(w.off)]++;
+                        }
+                        w.step();
+                    }
+                }
+            for (int64_t i = 0; i < numel; ++i)
+                CHECK(seen[size_t(i)] == 1, "scalar T=%d NR=%d visits %lld %d times", vv.T, vv.NR,
+                      (long long)i, int(seen[size_t(i)]));
+        }
+    }
+
     // ---- slice-resident NHWC kernels: every variant that could hold the rows
     if (pl.layout == kNHWC && pl.vec && numel * pl.esize < (int64_t(1) << 32)) {
         const int64_t cv = C / V;
@@ -233,6 +268,7 @@ int main(int argc, char** argv)
         {2, 16, 8, 8, kNCHW, kF32}, {2, 16, 8, 8, kNHWC, kBF16}, {2, 16, 8, 8, kNCHW, kBF16},
         {2, 16, 8, 8, kNHWC, kF32},      {64, 1024, 7, 7, kNHWC, kF32}, {32, 2048, 14, 14, kNHWC, kBF16},
         {2, 64, 1, 1, kNHWC, kBF16},     {5, 96, 11, 13, kNHWC, kBF16},   {3, 40, 7, 9, kNHWC, kF32},
+        {32, 64, 7, 7, kNCHW, kF32},     {500, 3, 7, 7, kNCHW, kBF16},    {10, 5, 7, 7, kNCHW, kF32},
     };
     std::mt19937_64 rng(12345);
     const int n_random = argc > 1 ? std::atoi(argv[1]) : 300;

@@ -173,9 +173,20 @@ def test_plan_choice_for_the_workloads():
     for shape in ((64, 2048, 7, 7, "NHWC"), (2, 256, 512, 512, "NHWC"), (16, 512, 28, 28, "NCHW"),
                   (32, 256, 56, 56, "NCHW")):
         assert d(*shape, torch.float16, "leaky_relu") == d(*shape, torch.bfloat16, "leaky_relu")
-    # misaligned or ragged planes take the scalar split path
-    assert "scalar" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
-    assert "scalar" in d(3, 5, 17, 19, "NCHW", iabn.F32, "leaky_relu")
+    # planes off the vector width (7x7) keep channels resident element by element
+    assert d(32, 2048, 7, 7, "NCHW", iabn.F32, "leaky_relu") == \
+        "forward=channel_resident_scalar(256x8) backward=channel_resident_scalar(256x8,dy_resident)"
+    assert d(3, 5, 17, 19, "NCHW", iabn.F32, "leaky_relu").startswith(
+        "forward=channel_resident_scalar(256x4)")
+    # ... and so do misaligned pointers, up to 24576 elements per channel; beyond
+    # that the scalar split path
+    assert d(32, 512, 7, 7, "NCHW", iabn.F32, "leaky_relu", aligned16=False).startswith(
+        "forward=channel_resident_scalar")
+    assert "split" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
+    assert "scalar)" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
+    # a small NHWC map whose slices would hold many rows on few workgroups: split
+    assert d(32, 256, 14, 14, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    assert d(32, 512, 7, 7, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=slice_resident")
     # ELU takes the same channel-resident variants
     assert "channel_resident(512x49)" in d(32, 256, 56, 56, "NCHW", iabn.F32, "elu")
     with pytest.raises(ValueError):

@@ -21,7 +21,8 @@ CASES = [
     workloads.config(2).with_shape(4, 32, 16, 16),                 # NCHW channel-resident
     workloads.config(5).with_shape(16, 512, 7, 7),                 # NHWC slice-resident
     workloads.config(3).with_shape(2, 32, 96, 96),                 # NHWC split
-    workloads.config(4).with_shape(2, 5, 17, 19),                  # NCHW split, scalar
+    workloads.config(4).with_shape(2, 5, 17, 19),                  # NCHW resident, elements
+    workloads.config(4).with_shape(2, 3, 150, 151),                # NCHW split, scalar
 ]
 
 

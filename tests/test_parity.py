@@ -246,6 +246,31 @@ def _variant_shapes():
     return out
 
 
+# every channel-resident variant on single elements: 7x7 planes (not a multiple
+# of the vector width) with N chosen so that m = 49*N just fits each capacity
+# (512 ... 24576 elements), storage dtypes and activations mixed
+def _scalar_shapes():
+    out = []
+    caps = [(10, "f32"), (20, "bf16"), (41, "f16"), (83, "f32"), (167, "bf16"), (334, "f32"),
+            (501, "f16")]
+    for k, (N, dtype) in enumerate(caps):
+        base = 2 if dtype == "f32" else 3
+        act = ("leaky_relu", "elu", "identity")[k % 3]
+        p = {"leaky_relu": 0.01, "elu": 1.0, "identity": 0.0}[act]
+        out.append(custom(base, N, 3, 7, 7, layout="NCHW", dtype=dtype, act=act, act_param=p))
+    out.append(custom(2, 32, 256, 7, 7))                       # an NCHW 7x7 tail, fp32
+    return out
+
+
+@pytest.mark.parametrize("wl", _scalar_shapes(), ids=lambda w: w.name)
+def test_channel_resident_scalar_variants(wl):
+    desc = iabn.iabn_describe_plan(wl.N, wl.C, wl.H, wl.W, wl.layout,
+                                   workloads.storage_torch_dtype(wl.dtype), wl.act)
+    print(desc)
+    assert "channel_resident_scalar" in desc
+    full_check(wl)
+
+
 # Tensors beyond 4 GiB: the resident kernels address with 32-bit offsets and must
 # step aside; the split kernels index with 64 bits.  Inputs are drawn on the
 # device; the oracle checks sampled channels (first, middle, last).
@@ -307,15 +332,17 @@ def test_beyond_4gib(wl):
 # ragged; slice counts that divide by 8 (XCD-grouped slice map) and ones that do not
 def _slice_shapes():
     out = []
+    # small tensors (up to 4096 rows: the small-tensor rule)
     for dtype, C in (("f32", 96), ("bf16", 256)):
         base = 2 if dtype == "f32" else 3
         for N, H, W in ((2, 16, 16), (5, 10, 10), (4, 16, 16), (4, 10, 25), (2, 32, 32),
-                        (5, 20, 20), (4, 25, 33), (4, 32, 52), (3, 40, 50)):
+                        (5, 20, 20), (4, 25, 33)):
             out.append(custom(base, N, C, H, W, layout="NHWC", dtype=dtype))
-    out.append(custom(2, 3, 96, 50, 60, layout="NHWC", dtype="f32"))      # 9000 rows
-    out.append(custom(2, 4, 96, 48, 48, layout="NHWC", dtype="f32"))      # 9216 rows
-    out.append(custom(3, 3, 128, 50, 60, layout="NHWC", dtype="bf16"))
-    out.append(custom(3, 4, 128, 48, 48, layout="NHWC", dtype="bf16"))
+    # more rows only where the slices fill the chip: 128 slices of 512 threads
+    for dtype, C in (("f32", 512), ("bf16", 1024)):
+        base = 2 if dtype == "f32" else 3
+        for N, H, W in ((4, 32, 52), (3, 40, 50), (3, 50, 60), (4, 48, 48)):   # 6656 ... 9216
+            out.append(custom(base, N, C, H, W, layout="NHWC", dtype=dtype))
     # two lanes per row (vectors per row >= 256): capacities 1024, 2048, 3328, 4608
     for N, H, W in ((4, 10, 25), (5, 20, 20), (4, 25, 33), (5, 30, 30)):
         out.append(custom(5, N, 2048, H, W, layout="NHWC", dtype="bf16"))
@@ -345,7 +372,8 @@ def test_slice_resident_variants(wl):
 # deviations from the mean (alternating sides): the statistics must not lose
 # accuracy to the shift.  One case per kernel family.
 OUTLIER = [custom(2, 4, 32, 16, 16),                                   # NCHW channel-resident
-           custom(2, 3, 5, 17, 19),                                    # NCHW split, scalar
+           custom(2, 3, 5, 17, 19),                                    # NCHW resident, elements
+           custom(2, 1, 3, 157, 163),                                  # NCHW split, scalar
            custom(3, 4, 256, 25, 33, layout="NHWC", dtype="bf16"),     # NHWC slice-resident
            custom(2, 4, 96, 25, 33, layout="NHWC", dtype="f32"),
            custom(2, 2, 16, 80, 80, layout="NHWC", dtype="f32")]       # NHWC split
