@@ -32,6 +32,10 @@ autograd module against the same chain with torch's BatchNorm2d + activation:
 forward + backward time per iteration, activation memory held after the
 forward, and peak memory (the pages' claims: less training memory at a small
 compute cost).  The convolutions are torch's (MIOpen) in both chains.
+
+--mode shapes checks the plan on ResNet-50 activation shapes (N = 32 and a few
+others, NCHW fp32 and NHWC bf16): the cold step with the kernels the plan picks
+against the split kernels (the stage entry points), one JSON line per shape.
 """
 from __future__ import annotations
 
@@ -192,6 +196,81 @@ def run_frozen(args, wl) -> int:
     return 0
 
 
+SHAPES = [(32, 64, 112, 112), (32, 256, 56, 56), (32, 128, 56, 56), (32, 512, 28, 28),
+          (32, 256, 28, 28), (32, 1024, 14, 14), (32, 256, 14, 14), (32, 2048, 7, 7),
+          (32, 512, 7, 7), (8, 512, 28, 28), (8, 1024, 14, 14), (8, 2048, 7, 7),
+          (64, 256, 14, 14)]
+
+
+def run_shapes(args) -> int:
+    """The plan's kernels (forward_train + backward) against the split kernels (the
+    stage entry points) on ResNet-50 activation shapes, cold, one JSON line each."""
+    import torch
+    import place_batchnorm_activation_amd as iabn
+    import workloads
+
+    act, p, eps, mom = "leaky_relu", 0.01, 1e-5, 0.1
+    for layout, dtype in (("NCHW", "f32"), ("NHWC", "bf16")):
+        for (N, C, H, W) in SHAPES:
+            wl = dataclasses.replace(workloads.config(2), N=N, C=C, H=H, W=W, layout=layout,
+                                     dtype=dtype, name="resnet50_%dx%dx%dx%d" % (N, C, H, W))
+            inp = workloads.make_device_inputs(wl, seed=5)
+            S = wl.storage_bytes
+            nsets = max(2, math.ceil(COLD_BYTES / (3 * S)))
+            sets = [{"x": inp.x.clone(), "dy": inp.dy.clone(), "dx": torch.empty_like(inp.dy)}
+                    for _ in range(nsets)]
+            del inp.x, inp.dy
+            g = torch.from_numpy(inp.gamma).cuda()
+            b = torch.from_numpy(inp.beta).cuda()
+            rm, rv = torch.zeros(C, device="cuda"), torch.ones(C, device="cuda")
+            sm, si = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+            dg, db = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+            ws = iabn.workspace(N, C, H, W, layout, sets[0]["x"].dtype)
+
+            def plan_step(s):
+                iabn.iabn_forward_train(s["x"], N, C, H, W, layout, g, b, rm, rv, sm, si, act, p,
+                                        eps, mom, ws)
+                iabn.iabn_backward(s["x"], s["dy"], s["dx"], N, C, H, W, layout, g, b, si, dg,
+                                   db, act, p, ws)
+
+            def split_step(s):
+                iabn.iabn_forward_stats(s["x"], N, C, H, W, layout, g, b, rm, rv, sm, si, eps,
+                                        mom, ws)
+                iabn.iabn_forward_apply(s["x"], N, C, H, W, layout, act, p, ws)
+                iabn.iabn_backward_reduce(s["x"], s["dy"], N, C, H, W, layout, g, b, si, dg, db,
+                                          act, p, ws)
+                iabn.iabn_backward_apply(s["x"], s["dy"], s["dx"], N, C, H, W, layout, act, p,
+                                         ws)
+
+            def timed(fn, k=max(20, args.steps // 4)):
+                for i in range(5):
+                    fn(sets[i % nsets])
+                torch.cuda.synchronize()
+                # a short device-side wait lets the host queue the loop ahead, so that
+                # small shapes are timed on the GPU rather than at Python's launch rate
+                if hasattr(torch.cuda, "_sleep"):
+                    torch.cuda._sleep(50_000_000)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(k):
+                    fn(sets[i % nsets])
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / k
+
+            t_plan, t_split = timed(plan_step), timed(split_step)
+            plan = iabn.iabn_describe_plan(N, C, H, W, layout, sets[0]["x"].dtype, act)
+            print(json.dumps({"mode": "shapes", "layout": layout, "storage": dtype,
+                              "shape": [N, C, H, W], "plan": plan,
+                              "plan_us": round(t_plan, 2), "split_us": round(t_split, 2),
+                              "plan_pass_model_TBps": round(8 * S / t_plan / 1e6, 3)}),
+                  flush=True)
+            del sets
+            torch.cuda.empty_cache()
+    return 0
+
+
 def run_block(args, wl) -> int:
     """InPlace-ABN against BatchNorm2d + activation inside a convolution chain."""
     import torch
@@ -282,9 +361,10 @@ def main() -> int:
     ap.add_argument("--warm-only", action="store_true", help="one buffer set (for profiling)")
     ap.add_argument("--dtype", choices=("f32", "bf16", "f16"), default=None,
                     help="storage dtype instead of the workload's own")
-    ap.add_argument("--mode", choices=("train", "frozen", "block"), default="train",
+    ap.add_argument("--mode", choices=("train", "frozen", "block", "shapes"), default="train",
                     help="train: forward_train + backward; frozen: forward_eval + backward_eval; "
-                         "block: conv + norm/act chain against torch's BatchNorm2d")
+                         "block: conv + norm/act chain against torch's BatchNorm2d; "
+                         "shapes: the plan's kernels against the split ones on ResNet-50 shapes")
     ap.add_argument("--layers", type=int, default=4, help="layers of the --mode block chain")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark: copy a MIB-MiB buffer 5 times (a plain copy "
@@ -317,6 +397,8 @@ def main() -> int:
         return run_frozen(args, wl)
     if args.mode == "block":
         return run_block(args, wl)
+    if args.mode == "shapes":
+        return run_shapes(args)
     N, C, H, W = wl.N, wl.C, wl.H, wl.W
     inp = workloads.make_inputs(wl)
     dev = torch.device("cuda", 0)
