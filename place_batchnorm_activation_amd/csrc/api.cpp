@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include <hip/hip_runtime_api.h>
 
 #include "fused.hpp"
@@ -54,6 +56,39 @@ iabn_status check_tensor(const void* p, iabn_dtype dtype)
     return aligned(p, dtype == IABN_F32 ? 4 : 2) ? IABN_OK : IABN_ERR_MISALIGNED;
 }
 
+// Workspace bytes of the split kernels, whichever of the vector and scalar plans
+// a call takes.
+size_t split_bytes(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
+                   iabn_dtype dtype)
+{
+    const size_t a = make_plan(N, C, H, W, layout, dtype, false).bytes;
+    if (!vec_shape_ok(C, H * W, layout, dtype)) return a;
+    const size_t b = make_plan(N, C, H, W, layout, dtype, true).bytes;
+    return a > b ? a : b;
+}
+
+// Workgroups the current device runs at once with one per CU: its CU count
+// (cached per device).  Without a device (planning only) the MI355X's 256.
+int64_t coresident_grid()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int cus = cache[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0) {
+            (void)hipGetLastError();
+            return 256;
+        }
+        cache[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
 // act < 0: the stage entry points, which always run the split kernels.
 Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
               bool ptrs16, int act = -1)
@@ -68,8 +103,26 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
         if (b >= 0 && fused_worthwhile(p, fused_bwd_threads(b))) p.fused_bwd_variant = b;
     }
     if (act >= 0) {
-        p.nhwc_variant = fused_nhwc_pick(p);
+        const bool nhwc_vec = p.layout == kNHWC && p.vec && p.numel > 0;
+        const NhwcChoice nc = fused_nhwc_pick(p, nhwc_vec ? coresident_grid() : 0);
+        p.nhwc_variant = nc.variant;
+        p.nhwc_group = nc.group;
         p.scalar_variant = fused_scalar_pick(p);
+        if (nc.variant >= 0 && nc.group > 1) {
+            // the exchange goes past every split-kernel section, which other calls
+            // on the same workspace may write
+            p.off_xchg = (size_t)align_up((int64_t)split_bytes(N, C, H, W, layout, dtype), 256);
+            const int64_t lpr = [&] {
+                switch (nc.variant) {
+#define IABN_ROW(ID, T, LPR, NR) case ID: return int64_t(LPR);
+                    IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+                default: return int64_t(1);
+                }
+            }();
+            p.bytes = p.off_xchg + sizeof(uint64_t) *
+                      (size_t)nhwc_exchange_words(C / p.V / lpr, nc.group, C);
+        }
     }
     return p;
 }
@@ -77,9 +130,10 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
 size_t workspace_bytes_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
                            iabn_dtype dtype)
 {
-    const size_t a = make_plan(N, C, H, W, layout, dtype, false).bytes;
+    const size_t a = split_bytes(N, C, H, W, layout, dtype);
     if (!vec_shape_ok(C, H * W, layout, dtype)) return a;
-    const size_t b = make_plan(N, C, H, W, layout, dtype, true).bytes;
+    // the slice-resident NHWC group exchange (act plays no part in its choice)
+    const size_t b = plan_for(N, C, H, W, layout, dtype, true, IABN_ACT_IDENTITY).bytes;
     return a > b ? a : b;
 }
 
@@ -231,7 +285,7 @@ iabn_status iabn_forward_train(void* x_inout, int64_t N, int64_t C, int64_t H, i
     }
     if (pl.nhwc_variant >= 0) {
         launch_forward_fused_nhwc(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
-                                  save_invstd, eps, momentum, act, act_param, stream);
+                                  save_invstd, eps, momentum, act, act_param, workspace, stream);
         return launched();
     }
     launch_forward_stats(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
@@ -330,7 +384,7 @@ iabn_status iabn_backward(const void* y, const void* dy, void* dx, int64_t N, in
     }
     if (pa.nhwc_variant >= 0) {
         launch_backward_fused_nhwc(pa, y, dy, dx, gamma, beta, save_invstd, dgamma, dbeta, act,
-                                   act_param, stream);
+                                   act_param, workspace, stream);
         return launched();
     }
     launch_backward_reduce(pr, y, dy, gamma, beta, save_invstd, dgamma, dbeta, act, act_param,
@@ -390,6 +444,10 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     default: break;
+    }
+    if (p.nhwc_variant >= 0 && p.nhwc_group > 1) {
+        const size_t n = strlen(nd);
+        snprintf(nd + n, sizeof nd - n, ",group%d", p.nhwc_group);
     }
     switch (p.scalar_variant) {
 #define IABN_ROW(ID, T, NR) case ID: snprintf(sd, sizeof sd, "%dx%d", T, NR); break;

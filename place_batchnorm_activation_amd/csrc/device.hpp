@@ -352,6 +352,24 @@ __host__ __device__ __forceinline__ uint32_t nhwc_slice_of(uint32_t b, uint32_t 
     return (slices % 8 == 0) ? (b % 8) * (slices / 8) + b / 8 : b;
 }
 
+// Slice and member of workgroup b when G workgroups share each slice (G == 1:
+// nhwc_slice_of).  With slices % 8 == 0 the G members of a slice are workgroups
+// b, b + 8, ..., so they run on one XCD (one L2), and XCD x takes slices
+// x*(slices/8) onwards.  A bijection of [0, slices*G) onto (slice, member) pairs.
+__host__ __device__ __forceinline__ void nhwc_slice_member(uint32_t b, uint32_t slices,
+                                                           uint32_t G, uint32_t& s,
+                                                           uint32_t& member)
+{
+    if (G == 1) {
+        s = nhwc_slice_of(b, slices);
+        member = 0;
+    } else {
+        const uint32_t j = b / 8;
+        member = j % G;
+        s = (b % 8) * (slices / 8) + j / G;
+    }
+}
+
 // Walk of a flat NCHW tensor: vector v has channel ((v / HWv) % C).  Advancing v
 // by a fixed stride updates the in-plane offset and the channel with carries.
 struct FlatNCHWWalk {

@@ -51,7 +51,10 @@
     X(6, 512, 2, 4)                  \
     X(7, 512, 2, 8)                  \
     X(8, 512, 2, 13)                 \
-    X(9, 512, 2, 18)
+    X(9, 512, 2, 18)                 \
+    X(10, 512, 4, 4)                 \
+    X(11, 512, 4, 7)                 \
+    X(12, 512, 4, 13)
 #endif
 
 // Channel-resident NCHW kernels on single elements, for shapes the 16-byte
@@ -125,18 +128,35 @@ inline bool fused_worthwhile(const Plan& p, int threads)
     return p.C * threads >= int64_t(256) * 256 || bytes <= (int64_t(4) << 20);
 }
 
-// Slice-resident NHWC variant for a problem, or -1.  Wider slices (LPR = 2: a
-// wave reads 32 bytes of each of 32 rows instead of 16 bytes of 64) coalesce
-// better, so they are preferred while they still give at least 128 workgroups;
-// then the first variant (table order) whose workgroup holds all m rows.  The
-// kernels are taken when the slices fill the chip, or when the tensor is small
-// enough for launch latency to rule and each workgroup's rows are few (measured:
-// 32 workgroups of 6272 rows lose to the split path, 64 of 1568 win).  32-bit
-// vector indices address the tensor.
-inline int fused_nhwc_pick(const Plan& p)
+// Slice-resident NHWC plan: variant and group size (variant -1: not used).  A
+// group of G > 1 workgroups shares one slice, each holding a contiguous block of
+// ceil(m/G) rows; the members swap their partial sums through the workspace
+// while all of them stay resident, so the grid must not exceed what the device
+// runs at once (max_grid, one workgroup per CU; 0 forbids groups).
+struct NhwcChoice {
+    int variant = -1;
+    int group = 1;
+};
+
+// Choice, from cold timings of every (variant, G) on ResNet-50 NHWC shapes:
+//  0. A tensor under 4 MB: one lane per row and 256 threads, at most 4 rows per
+//     thread, the smallest group (up to 8) that holds the rows -- on so little
+//     data the count of workgroups, each a CU's load pipeline, matters most.
+//  1. LPR = 4, then 2 (a wave reads LPR*16 contiguous bytes of each row; one
+//     lane per row coalesces poorly): the smallest group whose ceil(m/G) rows fit
+//     a variant of at most 8 rows per thread, else at most 13 (more rows per
+//     thread lengthen each member's load -> reduce -> store round trip more than
+//     extra members cost).  G = 1 here needs the chip filled or a small tensor.
+//  2. One workgroup per slice at any LPR, the chip filled (T*slices >= 256*256)
+//     or a small tensor (under 4 MB with at most 4096 rows), where launch latency
+//     rules.
+// Groups need slices % 8 == 0 (a group's members on one XCD) and a grid within
+// max_grid.  32-bit vector indices address the tensor.
+inline NhwcChoice fused_nhwc_pick(const Plan& p, int64_t max_grid)
 {
-    if (p.layout != kNHWC || !p.vec || p.numel == 0) return -1;
-    if (p.numel * p.esize >= (int64_t(1) << 32)) return -1;
+    NhwcChoice none;
+    if (p.layout != kNHWC || !p.vec || p.numel == 0) return none;
+    if (p.numel * p.esize >= (int64_t(1) << 32)) return none;
     const int64_t cv = p.C / p.V;
     const int64_t bytes = p.numel * p.esize;
     struct Row { int id, T, LPR, NR; };
@@ -145,18 +165,68 @@ inline int fused_nhwc_pick(const Plan& p)
         IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     };
-    const int want = (cv % 2 == 0 && cv / 2 >= 128) ? 2 : 1;
-    for (int pass = 0; pass < 2; ++pass) {
-        for (const auto& v : tbl) {
-            if ((pass == 0) != (v.LPR == want)) continue;
-            if (cv % v.LPR != 0 || int64_t(v.T / v.LPR) * v.NR < p.m) continue;
-            const int64_t blocks = cv / v.LPR;
-            if (blocks * v.T >= int64_t(256) * 256 || (bytes <= (int64_t(4) << 20) && p.m <= 4096))
-                return v.id;
-            return -1;
+    const bool small = bytes <= (int64_t(4) << 20) && p.m <= 4096;
+    auto fills = [&](int64_t grid, int T) { return grid * T >= int64_t(256) * 256; };
+    // the smallest variant of width lpr, at most nr_cap rows per thread, holding rows
+    auto holding = [&](int lpr, int nr_cap, int64_t rows) -> const Row* {
+        const Row* best = nullptr;
+        for (const auto& v : tbl)
+            if (v.LPR == lpr && v.NR <= nr_cap && int64_t(v.T / lpr) * v.NR >= rows &&
+                (!best || int64_t(v.T) * v.NR < int64_t(best->T) * best->NR))
+                best = &v;
+        return best;
+    };
+    // a tensor under 4 MB: as many workgroups as possible, each thread holding at
+    // most 4 rows (one lane per row, 256 threads), groups of at most 8
+    if (bytes <= (int64_t(4) << 20)) {
+        for (int g = 1; g <= 8; g *= 2) {
+            const int64_t grid = cv * g;
+            const int64_t mg = ceil_div(p.m, g);
+            if (g > 1 && (cv % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;
+            const Row* v = holding(1, 4, mg);
+            if (v && v->T == 256) {
+                NhwcChoice c;
+                c.variant = v->id;
+                c.group = g;
+                return c;
+            }
         }
     }
-    return -1;
+    for (int nr_cap : {8, 13}) {
+        for (int lpr : {4, 2}) {
+            if (cv % lpr != 0) continue;
+            const int64_t slices = cv / lpr;
+            for (int g = 1; g <= 16; g *= 2) {
+                const int64_t grid = slices * g;
+                const int64_t mg = ceil_div(p.m, g);
+                if (g > 1 && (slices % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;
+                const Row* v = holding(lpr, nr_cap, mg);
+                if (v && (g > 1 || fills(grid, v->T) || small)) {
+                    NhwcChoice c;
+                    c.variant = v->id;
+                    c.group = g;
+                    return c;
+                }
+            }
+        }
+    }
+    for (int lpr : {2, 1}) {
+        if (cv % lpr != 0) continue;
+        const Row* v = holding(lpr, 1 << 30, p.m);
+        if (v && (fills(cv / lpr, v->T) || small)) {
+            NhwcChoice c;
+            c.variant = v->id;
+            return c;
+        }
+    }
+    return none;
+}
+
+// Workspace words of the group exchange: one epoch per slice (padded to 32
+// words), then per slice, member and channel four tagged words.
+inline int64_t nhwc_exchange_words(int64_t slices, int64_t group, int64_t C)
+{
+    return group > 1 ? align_up(slices, 32) + 4 * group * C : 0;
 }
 
 // Scalar channel-resident variant for an NCHW problem off the vector path, or -1:
@@ -199,10 +269,11 @@ void launch_backward_fused_scalar(const Plan& pl, const void* y, const void* dy,
 
 void launch_forward_fused_nhwc(const Plan& pl, void* x, const float* gamma, const float* beta,
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
-                               int act, float a, hipStream_t s);
+                               int act, float a, void* ws, hipStream_t s);
 
 void launch_backward_fused_nhwc(const Plan& pl, const void* y, const void* dy, void* dx,
                                 const float* gamma, const float* beta, const float* invstd,
-                                float* dgamma, float* dbeta, int act, float a, hipStream_t s);
+                                float* dgamma, float* dbeta, int act, float a, void* ws,
+                                hipStream_t s);
 
 }  // namespace iabn

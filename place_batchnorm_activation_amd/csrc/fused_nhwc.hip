@@ -17,7 +17,31 @@
 // k < NR).  Workgroups are mapped to slices XCD by XCD (nhwc_slice_of), so
 // neighbouring slices -- which share cache lines when a slice is narrower than a
 // line -- meet in one L2.
+//
+// Groups.  When a slice has more rows than one workgroup holds, or one workgroup
+// per slice leaves the chip idle, G workgroups (members) share the slice, member
+// j holding rows [j*mg, min(m, (j+1)*mg)), mg = ceil(m/G).  After its own
+// reduction each member publishes its fp64 per-channel sums in the workspace;
+// the G partials are added in member order (by every member, or for large groups
+// by member 0, which publishes the totals), so every member derives
+// bit-identical statistics.  The grid never
+// exceeds the CU count, so that every member runs at once (the host's choice),
+// and a member waits a bounded time: past it, its statistics become NaN, so a
+// failure shows in every output it writes instead of hanging the device.
+//
+// Exchange protocol (no fences, no reset launch): every word is a relaxed 64-bit
+// atomic {32-bit tag, 32-bit half of an fp64 value}; a partial is accepted when
+// the tags of its words equal the halves of this call's 64-bit token.  The token
+// mixes a per-process salt, the slice and a per-slice epoch that the kernels
+// keep in the workspace: member 0 advances the epoch once every member's sums
+// have arrived (each member read it before publishing), so the next call -- a
+// graph replay too -- uses a fresh token and words left by earlier calls never
+// match.
 #include <hip/hip_runtime.h>
+#include <unistd.h>
+
+#include <chrono>
+#include <random>
 
 #include "device.hpp"
 #include "fused.hpp"
@@ -137,6 +161,165 @@ __device__ __forceinline__ double lds_total(const double (*sh)[kWave], uint32_t 
     return acc;
 }
 
+
+// splitmix64's output mix (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014), a bijection of 64-bit words.
+__device__ __forceinline__ uint64_t mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ uint64_t atomic_ld(const uint64_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_st(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t half)
+{
+    return (uint64_t(tag) << 32) | half;
+}
+
+// Bounded wait of the exchange, in polls (each a round trip to L2 and a sleep):
+// well over a second.
+constexpr uint32_t kMaxPolls = 1u << 21;
+
+// Members per slice at most (the exchange's LDS holds kMaxGroup partials).
+constexpr uint32_t kMaxGroup = 16;
+
+// This member's two fp64 sums of channel ch, as four tagged words.  words: the
+// slice's first word; nch: channels per slice.
+__device__ __forceinline__ void group_publish(uint64_t* words, uint32_t member, uint32_t nch,
+                                              uint32_t ch, uint64_t tok, double s1, double s2)
+{
+    const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
+    const uint64_t b1 = uint64_t(__double_as_longlong(s1)), b2 = uint64_t(__double_as_longlong(s2));
+    uint64_t* w = words + (size_t(member) * nch + ch) * 4;
+    atomic_st(w + 0, tagged(tlo, uint32_t(b1 >> 32)));
+    atomic_st(w + 1, tagged(thi, uint32_t(b1)));
+    atomic_st(w + 2, tagged(tlo, uint32_t(b2 >> 32)));
+    atomic_st(w + 3, tagged(thi, uint32_t(b2)));
+}
+
+// Member j's sums of channel ch, once all four words carry this call's tags
+// (bounded wait; NaN after it).
+__device__ __forceinline__ void group_fetch(const uint64_t* words, uint32_t j, uint32_t nch,
+                                            uint32_t ch, uint64_t tok, double& v1, double& v2)
+{
+    const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
+    const uint64_t* w = words + (size_t(j) * nch + ch) * 4;
+    v1 = v2 = __longlong_as_double(0x7FF8000000000000ll);
+    for (uint32_t poll = 0; poll <= kMaxPolls; ++poll) {
+        const uint64_t w0 = atomic_ld(w + 0), w1 = atomic_ld(w + 1);
+        const uint64_t w2 = atomic_ld(w + 2), w3 = atomic_ld(w + 3);
+        if (uint32_t(w0 >> 32) == tlo && uint32_t(w1 >> 32) == thi &&
+            uint32_t(w2 >> 32) == tlo && uint32_t(w3 >> 32) == thi) {
+            v1 = __longlong_as_double(int64_t((w0 << 32) | uint32_t(w1)));
+            v2 = __longlong_as_double(int64_t((w2 << 32) | uint32_t(w3)));
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+}  // namespace
+
+// Group exchange arguments: the workspace words (epochs, then the tagged sums),
+// the per-process salt, members per slice and rows per member.
+struct SliceGroup {
+    uint64_t* xchg;
+    uint64_t salt;
+    uint32_t G;
+    uint32_t mg;
+};
+
+namespace {
+
+__device__ __forceinline__ uint64_t group_token(const SliceGroup& grp, uint32_t s, uint64_t epoch)
+{
+    return mix64(grp.salt ^ mix64(epoch ^ (uint64_t(s) << 40)));
+}
+
+// First word of slice s's tagged sums (after the epochs, padded to 32 words).
+__device__ __forceinline__ uint64_t* group_words(const SliceGroup& grp, uint32_t s,
+                                                 uint32_t slices, uint32_t nch)
+{
+    return grp.xchg + ((slices + 31u) & ~31u) + size_t(s) * grp.G * nch * 4;
+}
+
+// Groups of at least this many members exchange in two levels.
+constexpr uint32_t kTwoLevelGroup = 16;
+
+// Sums over all members (G > 1), called by every thread of the workgroup: the
+// finishing thread of channel t (t < NCH) passes its member's sums s1, s2 and
+// gets back the sums over members 0..G-1, added in that order, so that every
+// member derives the same bits.
+//  - G < kTwoLevelGroup: each finishing thread publishes and then reads the other
+//    members one after another (measured: reading them with more threads at once
+//    loads the memory system with polls and is slower).
+//  - Larger groups, in two levels: every member but 0 publishes; member 0 reads
+//    them with one thread per (member, channel), adds, and publishes the totals
+//    in its own slot, which the others read.
+template <uint32_t NCH, int T>
+__device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, uint32_t slices,
+                                           uint32_t member, uint64_t tok, bool fin, double& s1,
+                                           double& s2)
+{
+    static_assert(NCH * kMaxGroup <= T, "one thread per (member, channel)");
+    uint64_t* words = group_words(grp, s, slices, NCH);
+    const uint32_t t = threadIdx.x;
+    if (grp.G < kTwoLevelGroup) {
+        if (fin) {
+            group_publish(words, member, NCH, t, tok, s1, s2);
+            double t1 = 0.0, t2 = 0.0;
+            for (uint32_t j = 0; j < grp.G; ++j) {
+                double v1 = s1, v2 = s2;
+                if (j != member) group_fetch(words, j, NCH, t, tok, v1, v2);
+                t1 += v1;
+                t2 += v2;
+            }
+            s1 = t1;
+            s2 = t2;
+        }
+        return;
+    }
+    if (member != 0) {
+        if (fin) {
+            group_publish(words, member, NCH, t, tok, s1, s2);
+            group_fetch(words, 0, NCH, t, tok, s1, s2);
+        }
+        return;
+    }
+    __shared__ double xs[2][kMaxGroup][NCH];
+    if (fin) {
+        xs[0][0][t] = s1;
+        xs[1][0][t] = s2;
+    }
+    const uint32_t j = 1 + t / NCH, ch = t % NCH;
+    if (j < grp.G) {
+        double v1, v2;
+        group_fetch(words, j, NCH, ch, tok, v1, v2);
+        xs[0][j][ch] = v1;
+        xs[1][j][ch] = v2;
+    }
+    __syncthreads();
+    if (fin) {
+        s1 = xs[0][0][t];
+        s2 = xs[1][0][t];
+        for (uint32_t k = 1; k < grp.G; ++k) {
+            s1 += xs[0][k][t];
+            s2 += xs[1][k][t];
+        }
+        group_publish(words, 0, NCH, t, tok, s1, s2);
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -149,26 +332,31 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
     void* x, uint32_t m, uint32_t Cv, const float* __restrict__ gamma,
     const float* __restrict__ beta, float* __restrict__ running_mean,
     float* __restrict__ running_var, float* __restrict__ save_mean,
-    float* __restrict__ save_invstd, float eps, float momentum, float a)
+    float* __restrict__ save_invstd, float eps, float momentum, float a, SliceGroup grp)
 {
     constexpr int V = Raw16<DT>::V;
     constexpr uint32_t RPS = T / LPR;
+    constexpr uint32_t NCH = V * LPR;               // channels per slice
     const uint32_t slices = Cv / LPR;
-    const uint32_t s = nhwc_slice_of(blockIdx.x, slices);
+    uint32_t s, member;
+    nhwc_slice_member(blockIdx.x, slices, grp.G, s, member);
+    const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);   // this member's rows
     const uint32_t t = threadIdx.x;
     const uint32_t lane = t % LPR, rs = t / LPR;
+    const uint32_t rb = r0 + rs;                    // first row of this thread
     const uint32_t col = s * LPR + lane;            // 16-byte vector column of the row
     const uint32_t c0 = col * V;                    // first channel of this thread
     const uint4* xv = reinterpret_cast<const uint4*>(x);
 
-    // pivot K: row 0 of each channel, loaded first since every sum needs it.  Slots
-    // past the last row load row m-1 (no branch); the sums below take K's bits for
-    // them, which add exactly zero.
+    // pivot K: row 0 of each channel (every member's), loaded first since every sum
+    // needs it; member 0 overwrites it only after all members have published sums
+    // taken with it.  Slots past the member's last row load that row (no branch);
+    // the sums below take K's bits for them, which add exactly zero.
     const uint4 kraw = xv[col];
     __builtin_amdgcn_sched_barrier(0);
     uint4 r[NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) r[k] = xv[min(rs + k * RPS, m - 1) * Cv + col];
+    for (int k = 0; k < NR; ++k) r[k] = xv[min(rb + k * RPS, r1 - 1) * Cv + col];
     // Per-channel values for the finishing threads, loaded last (they are needed
     // last) but up front, so that no global load sits between the two barriers:
     // thread t < V*LPR finishes channel cf.  Unconditional loads (the other threads
@@ -184,6 +372,10 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
     float b_c[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) b_c[e] = beta[c0 + e];
+    // the epoch, read by wave 0 alone: thread 0 derives the token from it before
+    // the first barrier and advances it after the exchange
+    uint64_t epoch = 0;
+    if (grp.G > 1 && t < kWave) epoch = atomic_ld(grp.xchg + s);
     // every load above is issued before any of the arithmetic below (a select or a
     // conversion next to a load would make the compiler wait for it there)
     __builtin_amdgcn_sched_barrier(0);
@@ -197,7 +389,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
         float v[V];
-        unpack16<DT>(select16(rs + k * RPS < m, r[k], kraw), v);
+        unpack16<DT>(select16(rb + k * RPS < r1, r[k], kraw), v);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             const float d = v[e] - K[e];
@@ -207,32 +399,42 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
     }
     __shared__ double sh[T / kWave][kWave];
     __shared__ float coef[2][V][LPR];
+    __shared__ uint64_t tok_sh;
     pin_loaded(g_f, rm_f, rv_f);
     asm volatile("" : "+v"(k_bits));
     wave_scatter<LPR, 2 * V>(sums, sh);
+    if (grp.G > 1 && t == 0) tok_sh = group_token(grp, s, epoch);
     __syncthreads();
 
     // statistics in fp64, one thread per channel: d = mean - K, M2 = S2 - S1*d
+    const uint32_t fe = t / LPR, fl = t % LPR;      // finishing thread: channel (fe, fl)
+    double S1 = 0.0, S2 = 0.0;
     if (fin) {
-        const uint32_t e = t / LPR, l = t % LPR;
-        const double S1 = lds_total<T, 2 * V>(sh, e, l);
-        const double S2 = lds_total<T, 2 * V>(sh, V + e, l);
+        S1 = lds_total<T, 2 * V>(sh, fe, fl);
+        S2 = lds_total<T, 2 * V>(sh, V + fe, fl);
+    }
+    if (grp.G > 1) group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, S1, S2);
+    if (fin) {
         const double md = double(m);
         const double dm = S1 / md;
         const double var = fmax(S2 - S1 * dm, 0.0) / md;
         const double invstd = 1.0 / sqrt(var + double(eps));
         const double mu = double(DT == kF32 ? __uint_as_float(k_bits) : unpack1<DT>(uint16_t(k_bits))) + dm;
-        save_mean[cf] = float(mu);
-        save_invstd[cf] = float(invstd);
-        if (running_mean) {
+        if (member == 0) {
+            save_mean[cf] = float(mu);
+            save_invstd[cf] = float(invstd);
+        }
+        if (running_mean && member == 0) {
             const double mom = double(momentum);
             running_mean[cf] = float((1.0 - mom) * double(rm_f) + mom * mu);
             running_var[cf] = float((1.0 - mom) * double(rv_f) + mom * var * md / (md - 1.0));
         }
-        coef[0][e][l] = float(dm);
-        coef[1][e][l] = float(double(g_f) * invstd);
+        coef[0][fe][fl] = float(dm);
+        coef[1][fe][fl] = float(double(g_f) * invstd);
     }
     __syncthreads();
+    // every member has read the epoch (its sums arrived tagged with it): advance it
+    if (grp.G > 1 && member == 0 && t == 0) atomic_st(grp.xchg + s, epoch + 1);
     float d[V], sc[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -240,15 +442,15 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
         sc[e] = coef[1][e][lane];
     }
 
-    const uint32_t rs2 = opaque_u(rs);
+    const uint32_t rb2 = opaque_u(rb);
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        const uint32_t row = rs2 + k * RPS;
+        const uint32_t row = rb2 + k * RPS;
         float v[V];
         unpack16<DT>(opaque_q(r[k]), v);
 #pragma unroll
         for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K[e]) - d[e], sc[e], b_c[e]), a);
-        if (row < m) st16_nt(x, row * Cv + col, pack16<DT>(v));
+        if (row < r1) st16_nt(x, row * Cv + col, pack16<DT>(v));
     }
 }
 
@@ -258,14 +460,18 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
     const void* __restrict__ y, const void* dy, void* dx, uint32_t m, uint32_t Cv,
     const float* __restrict__ gamma, const float* __restrict__ beta,
     const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
-    float a, float inv_a)
+    float a, float inv_a, SliceGroup grp)
 {
     constexpr int V = Raw16<DT>::V;
     constexpr uint32_t RPS = T / LPR;
+    constexpr uint32_t NCH = V * LPR;
     const uint32_t slices = Cv / LPR;
-    const uint32_t s = nhwc_slice_of(blockIdx.x, slices);
+    uint32_t s, member;
+    nhwc_slice_member(blockIdx.x, slices, grp.G, s, member);
+    const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);
     const uint32_t t = threadIdx.x;
     const uint32_t lane = t % LPR, rs = t / LPR;
+    const uint32_t rb = r0 + rs;
     const uint32_t col = s * LPR + lane;
     const uint32_t c0 = col * V;
     const uint4* yv = reinterpret_cast<const uint4*>(y);
@@ -275,13 +481,15 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
     const bool fin = t < V * LPR;
     const uint32_t cf = fin ? (s * LPR + t % LPR) * V + t / LPR : 0;
     float g_f = gamma[cf], i_f = invstd[cf];
+    uint64_t epoch = 0;
+    if (grp.G > 1 && t < kWave) epoch = atomic_ld(grp.xchg + s);
 
-    // slots past the last row load row m-1 (no branch); the sums below take
-    // dy = 0 for them, so dz = 0 adds exactly zero
+    // slots past the member's last row load that row (no branch); the sums below
+    // take dy = 0 for them, so dz = 0 adds exactly zero
     uint4 ry[NR], rd[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        const uint32_t i = min(rs + k * RPS, m - 1) * Cv + col;
+        const uint32_t i = min(rb + k * RPS, r1 - 1) * Cv + col;
         ry[k] = yv[i];
         rd[k] = dv[i];
     }
@@ -298,7 +506,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
     for (int k = 0; k < NR; ++k) {
         float vy[V], vd[V];
         unpack16<DT>(ry[k], vy);
-        unpack16<DT>(select16(rs + k * RPS < m, rd[k], make_uint4(0, 0, 0, 0)), vd);
+        unpack16<DT>(select16(rb + k * RPS < r1, rd[k], make_uint4(0, 0, 0, 0)), vd);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             float z, slope;
@@ -310,25 +518,35 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
     }
     __shared__ double sh[T / kWave][kWave];
     __shared__ float coef[3][V][LPR];
+    __shared__ uint64_t tok_sh;
     pin_loaded(g_f, i_f);
     wave_scatter<LPR, 2 * V>(sums, sh);
+    if (grp.G > 1 && t == 0) tok_sh = group_token(grp, s, epoch);
     __syncthreads();
 
     // per-channel constants in fp64, one thread per channel
+    const uint32_t fe = t / LPR, fl = t % LPR;
+    double db = 0.0, sg = 0.0;
     if (fin) {
-        const uint32_t e = t / LPR, l = t % LPR;
-        const double db = lds_total<T, 2 * V>(sh, e, l);
+        db = lds_total<T, 2 * V>(sh, fe, fl);
+        sg = lds_total<T, 2 * V>(sh, V + fe, fl);
+    }
+    if (grp.G > 1) group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, db, sg);
+    if (fin) {
         const double g = double(g_f);
-        const double dg = lds_total<T, 2 * V>(sh, V + e, l) / g;
-        dbeta[cf] = float(db);
-        dgamma[cf] = float(dg);
+        const double dg = sg / g;
+        if (member == 0) {
+            dbeta[cf] = float(db);
+            dgamma[cf] = float(dg);
+        }
         const double A = g * double(i_f);
         const double md = double(m);
-        coef[0][e][l] = float(A);
-        coef[1][e][l] = float(-A * dg / (md * g));
-        coef[2][e][l] = float(-A * db / md);
+        coef[0][fe][fl] = float(A);
+        coef[1][fe][fl] = float(-A * dg / (md * g));
+        coef[2][fe][fl] = float(-A * db / md);
     }
     __syncthreads();
+    if (grp.G > 1 && member == 0 && t == 0) atomic_st(grp.xchg + s, epoch + 1);
     float kA[V], kB[V], kC[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -337,11 +555,11 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
         kC[e] = coef[2][e][lane];
     }
 
-    const uint32_t rs2 = opaque_u(rs);
+    const uint32_t rb2 = opaque_u(rb);
     const float a2 = opaque_f(a), ia2 = opaque_f(inv_a);
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        const uint32_t row = rs2 + k * RPS;
+        const uint32_t row = rb2 + k * RPS;
         float vy[V], vd[V];
         unpack16<DT>(opaque_q(ry[k]), vy);
         unpack16<DT>(opaque_q(rd[k]), vd);
@@ -352,24 +570,56 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
             const float dz = slope * vd[e];
             vd[e] = fmaf(kA[e], dz, fmaf(kB[e], z - b_c[e], kC[e]));
         }
-        if (row < m) st16_nt(dx, row * Cv + col, pack16<DT>(vd));
+        if (row < r1) st16_nt(dx, row * Cv + col, pack16<DT>(vd));
     }
 }
 
 // ---------------------------------------------------------------------------
 // host side
 
+// The salt of every exchange token of this process: drawn once, so that words a
+// workspace holds from another process or from unrelated data match no token
+// except by a 2^-64 chance.
+static uint64_t process_salt()
+{
+    static const uint64_t salt = [] {
+        uint64_t v = uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+        v ^= uint64_t(getpid()) << 32;
+        try {
+            std::random_device rd;
+            v ^= (uint64_t(rd()) << 32) ^ uint64_t(rd());
+        } catch (...) {
+        }
+        return v ^ reinterpret_cast<uintptr_t>(&v);
+    }();
+    return salt;
+}
+
+static SliceGroup slice_group(const Plan& pl, void* ws)
+{
+    SliceGroup g;
+    g.G = uint32_t(pl.nhwc_group);
+    g.mg = uint32_t(ceil_div(pl.m, pl.nhwc_group));
+    g.xchg = pl.nhwc_group > 1
+                 ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + pl.off_xchg)
+                 : nullptr;
+    g.salt = process_salt();
+    return g;
+}
+
 template <int DT, int ACT>
 static void launch_nhwc_fwd_da(const Plan& pl, void* x, const float* gamma, const float* beta,
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
-                               float a, hipStream_t s)
+                               float a, void* ws, hipStream_t s)
 {
     const uint32_t m = uint32_t(pl.m), Cv = uint32_t(pl.C / pl.V);
+    const SliceGroup grp = slice_group(pl, ws);
     switch (pl.nhwc_variant) {
-#define IABN_CASE(ID, T, LPR, NR)                                                                  \
-    case ID:                                                                                       \
-        hipLaunchKernelGGL((k_fwd_fused_nhwc<DT, ACT, T, LPR, NR>), dim3(Cv / LPR), dim3(T), 0, s, \
-                           x, m, Cv, gamma, beta, rm, rv, sm, si, eps, mom, a);                    \
+#define IABN_CASE(ID, T, LPR, NR)                                                                 \
+    case ID:                                                                                      \
+        hipLaunchKernelGGL((k_fwd_fused_nhwc<DT, ACT, T, LPR, NR>), dim3(Cv / LPR * grp.G),       \
+                           dim3(T), 0, s, x, m, Cv, gamma, beta, rm, rv, sm, si, eps, mom, a,     \
+                           grp);                                                                  \
         break;
         IABN_FUSED_NHWC_VARIANTS(IABN_CASE)
 #undef IABN_CASE
@@ -379,12 +629,12 @@ static void launch_nhwc_fwd_da(const Plan& pl, void* x, const float* gamma, cons
 
 void launch_forward_fused_nhwc(const Plan& pl, void* x, const float* gamma, const float* beta,
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
-                               int act, float a, hipStream_t s)
+                               int act, float a, void* ws, hipStream_t s)
 {
     with_dtype(pl.dtype, [&](auto d) {
         with_act(act, [&](auto ac) {
             launch_nhwc_fwd_da<decltype(d)::value, decltype(ac)::value>(
-                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s);
+                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, ws, s);
         });
     });
 }
@@ -392,14 +642,17 @@ void launch_forward_fused_nhwc(const Plan& pl, void* x, const float* gamma, cons
 template <int DT, int ACT>
 static void launch_nhwc_bwd_da(const Plan& pl, const void* y, const void* dy, void* dx,
                                const float* gamma, const float* beta, const float* invstd,
-                               float* dgamma, float* dbeta, float a, float ia, hipStream_t s)
+                               float* dgamma, float* dbeta, float a, float ia, void* ws,
+                               hipStream_t s)
 {
     const uint32_t m = uint32_t(pl.m), Cv = uint32_t(pl.C / pl.V);
+    const SliceGroup grp = slice_group(pl, ws);
     switch (pl.nhwc_variant) {
-#define IABN_CASE(ID, T, LPR, NR)                                                                  \
-    case ID:                                                                                       \
-        hipLaunchKernelGGL((k_bwd_fused_nhwc<DT, ACT, T, LPR, NR>), dim3(Cv / LPR), dim3(T), 0, s, \
-                           y, dy, dx, m, Cv, gamma, beta, invstd, dgamma, dbeta, a, ia);           \
+#define IABN_CASE(ID, T, LPR, NR)                                                                 \
+    case ID:                                                                                      \
+        hipLaunchKernelGGL((k_bwd_fused_nhwc<DT, ACT, T, LPR, NR>), dim3(Cv / LPR * grp.G),       \
+                           dim3(T), 0, s, y, dy, dx, m, Cv, gamma, beta, invstd, dgamma, dbeta,   \
+                           a, ia, grp);                                                           \
         break;
         IABN_FUSED_NHWC_VARIANTS(IABN_CASE)
 #undef IABN_CASE
@@ -409,13 +662,14 @@ static void launch_nhwc_bwd_da(const Plan& pl, const void* y, const void* dy, vo
 
 void launch_backward_fused_nhwc(const Plan& pl, const void* y, const void* dy, void* dx,
                                 const float* gamma, const float* beta, const float* invstd,
-                                float* dgamma, float* dbeta, int act, float a, hipStream_t s)
+                                float* dgamma, float* dbeta, int act, float a, void* ws,
+                                hipStream_t s)
 {
     const float ia = act == kIdentity ? 1.f : 1.f / a;
     with_dtype(pl.dtype, [&](auto d) {
         with_act(act, [&](auto ac) {
             launch_nhwc_bwd_da<decltype(d)::value, decltype(ac)::value>(
-                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s);
+                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, ws, s);
         });
     });
 }

@@ -80,8 +80,11 @@ struct Plan {
     // channel-resident NCHW kernels (-1: not used for this problem)
     int fused_variant = -1;
     int fused_bwd_variant = -1;
-    // slice-resident NHWC kernels (-1: not used)
+    // slice-resident NHWC kernels (-1: not used), workgroups per slice, and the
+    // workspace section of their exchange (groups only)
     int nhwc_variant = -1;
+    int nhwc_group = 1;
+    size_t off_xchg = 0;
     // channel-resident NCHW kernels on single elements (-1: not used)
     int scalar_variant = -1;
     // workspace sections (bytes, 256-aligned)

@@ -67,8 +67,9 @@ class GpuRun:
 
 
 def run_gpu(inp: workloads.Inputs, backward: bool = True, dx_over_dy: bool = False,
-            device="cuda") -> GpuRun:
-    """Training forward (in place) and backward through the C ABI."""
+            device="cuda", ws=None) -> GpuRun:
+    """Training forward (in place) and backward through the C ABI (ws: a workspace
+    to use instead of a fresh one)."""
     import place_batchnorm_activation_amd as iabn
     wl = inp.wl
     N, C, H, W = wl.N, wl.C, wl.H, wl.W
@@ -79,7 +80,8 @@ def run_gpu(inp: workloads.Inputs, backward: bool = True, dx_over_dy: bool = Fal
     rv = torch.from_numpy(inp.running_var).to(device)
     sm = torch.empty(C, device=device)
     si = torch.empty(C, device=device)
-    ws = iabn.workspace(N, C, H, W, wl.layout, x.dtype, device)
+    if ws is None:
+        ws = iabn.workspace(N, C, H, W, wl.layout, x.dtype, device)
     iabn.iabn_forward_train(x, N, C, H, W, wl.layout, g, b, rm, rv, sm, si, wl.act,
                             wl.act_param, wl.eps, wl.momentum, ws)
     dx = dg = db = None

@@ -6,6 +6,7 @@
 // stays inside its buffer, that the walks agree with the direct index formulas,
 // and that every element is visited exactly once.  Exit status 0 means all held.
 #include <cstdio>
+#include <algorithm>
 #include <cstdlib>
 #include <random>
 #include <vector>
@@ -208,7 +209,8 @@ static void check_plan(const Shape& s, bool vec)
         }
     }
 
-    // ---- slice-resident NHWC kernels: every variant that could hold the rows
+    // ---- slice-resident NHWC kernels: every variant and group size the plan could
+    // take (rows of each member fit; groups: slices % 8 == 0, no empty member)
     if (pl.layout == kNHWC && pl.vec && numel * pl.esize < (int64_t(1) << 32)) {
         const int64_t cv = C / V;
         struct Var { int T, LPR, NR; };
@@ -217,36 +219,73 @@ static void check_plan(const Shape& s, bool vec)
         IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
         for (const Var& vv : vars) {
-            const int64_t rps = vv.T / vv.LPR;
-            if (cv % vv.LPR != 0 || rps * vv.NR < m) continue;  // the plan never picks it
-            const uint32_t slices = uint32_t(cv / vv.LPR);
-            std::fill(seen.begin(), seen.end(), 0);
-            std::vector<int> slice_seen(slices, 0);
-            for (uint32_t b = 0; b < slices; ++b) {
-                const uint32_t sl = nhwc_slice_of(b, slices);
-                CHECK(sl < slices, "slice map bounds");
-                if (sl >= slices) continue;
-                slice_seen[sl]++;
-                for (int t = 0; t < vv.T; ++t) {
-                    const uint32_t lane = uint32_t(t) % uint32_t(vv.LPR), rs = uint32_t(t) / uint32_t(vv.LPR);
-                    const uint32_t col = sl * uint32_t(vv.LPR) + lane;
-                    CHECK(col < cv, "slice column");
-                    for (int k = 0; k < vv.NR; ++k) {
-                        const uint32_t row = rs + uint32_t(k) * uint32_t(rps);
-                        if (row < m) {
-                            const uint32_t idx = row * uint32_t(cv) + col;
-                            CHECK(int64_t(idx) == int64_t(row) * cv + col, "32-bit index");
-                            CHECK(int64_t(idx) < nvec, "slice bounds");
-                            if (int64_t(idx) < nvec) seen[size_t(idx)]++;
+            for (uint32_t G = 1; G <= 16; G *= 2) {
+                const int64_t rps = vv.T / vv.LPR;
+                if (cv % vv.LPR != 0) continue;
+                const uint32_t slices = uint32_t(cv / vv.LPR);
+                const int64_t mg = (m + G - 1) / G;
+                if (rps * vv.NR < mg) continue;                       // never picked
+                if (G > 1 && (slices % 8 != 0 || int64_t(G - 1) * mg >= m)) continue;
+                const int64_t words = nhwc_exchange_words(slices, G, C);
+                const uint32_t nch = uint32_t(V * vv.LPR);
+                std::fill(seen.begin(), seen.end(), 0);
+                std::vector<int> pair_seen(size_t(slices) * G, 0);
+                for (uint32_t b = 0; b < slices * G; ++b) {
+                    uint32_t sl, member;
+                    nhwc_slice_member(b, slices, G, sl, member);
+                    CHECK(sl < slices && member < G, "slice map bounds");
+                    if (sl >= slices || member >= G) continue;
+                    pair_seen[size_t(sl) * G + member]++;
+                    const uint32_t r0 = member * uint32_t(mg);
+                    const uint32_t r1 = std::min(uint32_t(m), r0 + uint32_t(mg));
+                    CHECK(r0 < r1, "member %u of %u has no rows", member, G);
+                    if (G > 1) {
+                        // epoch, and this member's tagged words for every channel
+                        CHECK(int64_t(sl) < ((int64_t(slices) + 31) & ~int64_t(31)), "epoch");
+                        const int64_t w0 = ((int64_t(slices) + 31) & ~int64_t(31)) +
+                                           int64_t(sl) * G * nch * 4;
+                        for (uint32_t j = 0; j < G; ++j)
+                            CHECK(w0 + (int64_t(j) * nch + nch - 1) * 4 + 3 < words,
+                                  "exchange words");
+                    }
+                    for (int t = 0; t < vv.T; ++t) {
+                        const uint32_t lane = uint32_t(t) % uint32_t(vv.LPR);
+                        const uint32_t rb = r0 + uint32_t(t) / uint32_t(vv.LPR);
+                        const uint32_t col = sl * uint32_t(vv.LPR) + lane;
+                        CHECK(col < cv, "slice column");
+                        for (int k = 0; k < vv.NR; ++k) {
+                            const uint32_t row = rb + uint32_t(k) * uint32_t(rps);
+                            // the clamped load stays inside the member's rows
+                            const uint32_t lrow = std::min(row, r1 - 1);
+                            CHECK(lrow >= r0 && int64_t(lrow) * cv + col < nvec, "load bounds");
+                            if (row < r1) {
+                                const uint32_t idx = row * uint32_t(cv) + col;
+                                CHECK(int64_t(idx) == int64_t(row) * cv + col, "32-bit index");
+                                CHECK(int64_t(idx) < nvec, "slice bounds");
+                                if (int64_t(idx) < nvec) seen[size_t(idx)]++;
+                            }
                         }
                     }
                 }
+                for (size_t q = 0; q < pair_seen.size(); ++q)
+                    CHECK(pair_seen[q] == 1, "slice/member %zu taken %d times", q, pair_seen[q]);
+                for (int64_t i = 0; i < nvec; ++i)
+                    CHECK(seen[size_t(i)] == 1, "slice T=%d LPR=%d NR=%d G=%u visits %lld %d times",
+                          vv.T, vv.LPR, vv.NR, G, (long long)i, int(seen[size_t(i)]));
             }
-            for (uint32_t q = 0; q < slices; ++q)
-                CHECK(slice_seen[q] == 1, "slice %u taken %d times", q, slice_seen[q]);
-            for (int64_t i = 0; i < nvec; ++i)
-                CHECK(seen[size_t(i)] == 1, "slice T=%d LPR=%d NR=%d visits %lld %d times", vv.T,
-                      vv.LPR, vv.NR, (long long)i, int(seen[size_t(i)]));
+        }
+        // the plan's own choice obeys the group rules at the MI355X's 256 CUs
+        const NhwcChoice ch = fused_nhwc_pick(pl, 256);
+        if (ch.variant >= 0 && ch.group > 1) {
+            int lpr = 0;
+            switch (ch.variant) {
+#define IABN_ROW(ID, T, LPR, NR) case ID: lpr = LPR; break;
+                IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+            default: break;
+            }
+            CHECK(lpr > 0 && cv % lpr == 0 && (cv / lpr) % 8 == 0, "group slices");
+            CHECK(lpr > 0 && (cv / lpr) * ch.group <= 256, "group grid within the CUs");
         }
     }
 }
@@ -269,6 +308,9 @@ int main(int argc, char** argv)
         {2, 16, 8, 8, kNHWC, kF32},      {64, 1024, 7, 7, kNHWC, kF32}, {32, 2048, 14, 14, kNHWC, kBF16},
         {2, 64, 1, 1, kNHWC, kBF16},     {5, 96, 11, 13, kNHWC, kBF16},   {3, 40, 7, 9, kNHWC, kF32},
         {32, 64, 7, 7, kNCHW, kF32},     {500, 3, 7, 7, kNCHW, kBF16},    {10, 5, 7, 7, kNCHW, kF32},
+        {8, 512, 28, 28, kNHWC, kBF16},  {64, 256, 14, 14, kNHWC, kBF16}, {32, 512, 28, 28, kNHWC, kBF16},
+        {32, 1024, 14, 14, kNHWC, kBF16}, {32, 256, 28, 28, kNHWC, kF32}, {7, 512, 9, 13, kNHWC, kBF16},
+        {3, 1024, 11, 17, kNHWC, kF32},
     };
     std::mt19937_64 rng(12345);
     const int n_random = argc > 1 ? std::atoi(argv[1]) : 300;

@@ -49,6 +49,12 @@ def test_workspace_size_depends_only_on_shape():
     # fp16 and bf16 storage share every size (16-bit elements)
     assert lib.iabn_workspace_size(2, 256, 512, 512, 1, 2) == \
         lib.iabn_workspace_size(2, 256, 512, 512, 1, 1)
+    # a plan whose slices are shared by groups of workgroups holds its exchange past
+    # the split kernels' sections: 8 bytes per epoch (one per slice, padded to 32)
+    # and 4 tagged words per member and channel
+    split = lib.iabn_workspace_size(64, 2048, 7, 7, 1, 1) - 8 * (64 + 4 * 4 * 2048)
+    assert split > 0 and split % 256 == 0
+    assert lib.iabn_workspace_size(64, 2048, 7, 7, 1, 2) == lib.iabn_workspace_size(64, 2048, 7, 7, 1, 1)
     # partial workspace stays small next to the data (a few percent)
     for (N, C, H, W, lay, dt) in [(32, 256, 56, 56, 0, 0), (2, 256, 512, 512, 1, 1),
                                   (16, 512, 28, 28, 0, 0), (64, 2048, 7, 7, 1, 1)]:
@@ -84,6 +90,12 @@ def test_forward_train_validation():
     assert _fwd(g=A + 1) == MISALIGNED
     assert _fwd(ws=None) == WS
     assert _fwd(wsb=16) == WS
+    # a grouped slice-resident plan needs its exchange words: the split kernels'
+    # size alone is refused, before any device call
+    full = lib.iabn_workspace_size(64, 2048, 7, 7, 1, 1)
+    shape = dict(N=64, C=2048, H=7, W=7, layout=1, dtype=1)
+    assert _fwd(wsb=full - 8, **shape) == WS
+    assert _bwd(wsb=full - 8, dy=A + (1 << 26), dx=A + (1 << 27), **shape) == WS
     assert _fwd(ws=A + 4) == MISALIGNED
     # C == 0 is a no-op that succeeds without touching anything
     assert _fwd(C=0, x=None, g=None, b=None, sm=None, si=None, ws=None) == OK
@@ -164,7 +176,7 @@ def test_plan_choice_for_the_workloads():
     assert d(2, 4, 8, 8, "NCHW", iabn.F32, "leaky_relu").startswith("forward=channel_resident")
     assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
     assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_resident(512x2x13) backward=slice_resident(512x2x13)"
+        "forward=slice_resident(512x4x7,group4) backward=slice_resident(512x4x7,group4)"
     # too many rows for a workgroup to hold: split
     assert d(2, 16, 80, 80, "NHWC", iabn.F32, "leaky_relu").startswith("forward=split")
     # few slices on a large tensor: split
@@ -184,9 +196,20 @@ def test_plan_choice_for_the_workloads():
         "forward=channel_resident_scalar")
     assert "split" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
     assert "scalar)" in d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu", aligned16=False)
-    # a small NHWC map whose slices would hold many rows on few workgroups: split
-    assert d(32, 256, 14, 14, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    # NHWC maps with more rows than a workgroup holds share each slice among a
+    # group of workgroups (within the 256 CUs)
+    assert d(32, 1024, 14, 14, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_resident(512x4x7,group8) backward=slice_resident(512x4x7,group8)"
+    assert d(32, 512, 28, 28, "NHWC", iabn.BF16, "leaky_relu").startswith(
+        "forward=slice_resident(512x4x13,group16)")
     assert d(32, 512, 7, 7, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=slice_resident")
+    # tensors under 4 MB: one lane per row, as many workgroups as the CUs take
+    assert d(8, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_resident(256x1x2) backward=slice_resident(256x1x2)"
+    assert d(32, 256, 14, 14, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_resident(256x1x4,group8) backward=slice_resident(256x1x4,group8)"
+    # one lane per row only, with too many rows: split
+    assert d(32, 128, 56, 56, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
     # ELU takes the same channel-resident variants
     assert "channel_resident(512x49)" in d(32, 256, 56, 56, "NCHW", iabn.F32, "elu")
     with pytest.raises(ValueError):

@@ -1,7 +1,8 @@
 """The library's calls inside a captured HIP graph (GPU).
 
 The kernels allocate nothing and issue no memset, so a step can be captured once
-and replayed.  Each test captures a forward + backward on a side stream, then
+and replayed; the slice-resident groups tag their exchange with an epoch kept in
+the workspace, so every replay runs with a fresh token.  Each test captures a forward + backward on a side stream, then
 replays it several times with eager work in between (restoring the in-place
 input and the running statistics) and checks every replay bit for bit against
 the eager run of the same calls.  One case per kernel family.
@@ -20,6 +21,8 @@ pytestmark = pytest.mark.gpu
 CASES = [
     workloads.config(2).with_shape(4, 32, 16, 16),                 # NCHW channel-resident
     workloads.config(5).with_shape(16, 512, 7, 7),                 # NHWC slice-resident
+    workloads.config(3).with_shape(5, 256, 20, 20),                # NHWC slice-resident, group 2
+    workloads.config(3).with_shape(5, 512, 50, 80),                # ... group 16, two levels
     workloads.config(3).with_shape(2, 32, 96, 96),                 # NHWC split
     workloads.config(4).with_shape(2, 5, 17, 19),                  # NCHW resident, elements
     workloads.config(4).with_shape(2, 3, 150, 151),                # NCHW split, scalar

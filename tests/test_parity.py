@@ -164,7 +164,8 @@ def test_misaligned_pointers_take_scalar_path(layout, dtype):
 # determinism, aliasing, stage entry points, inference
 
 @pytest.mark.parametrize("wl", [custom(2, 8, 32, 28, 28), custom(3, 4, 64, 32, 32),
-                                custom(4, 4, 32, 14, 14), custom(5, 8, 512, 7, 7)],
+                                custom(4, 4, 32, 14, 14), custom(5, 8, 512, 7, 7),
+                                custom(3, 5, 256, 40, 60, layout="NHWC", dtype="bf16")],
                          ids=lambda w: w.name)
 def test_bitwise_deterministic(wl):
     inp = workloads.make_inputs(wl)
@@ -327,36 +328,85 @@ def test_beyond_4gib(wl):
     harness.assert_within(errs, wl.dtype, wl.name)
 
 
-# every slice-resident NHWC variant, picked through the row count it holds
-# (one lane per row: capacities 512, 1024, 2048, 3328, 6656, 9216 rows), full and
-# ragged; slice counts that divide by 8 (XCD-grouped slice map) and ones that do not
+# every slice-resident NHWC variant and group sizes 1 to 16, picked through the
+# row count and slice count (the plan is asserted): full and ragged members;
+# slice counts that divide by 8 (XCD-grouped map) and ones that do not
+SLICE_PLANS = [
+    # one lane per row, 256 threads: tensors under 4 MB (groups up to 8) and odd
+    # vector counts per row
+    (custom(2, 1, 8, 7, 7, layout="NHWC", dtype="f32"), "256x1x2"),
+    (custom(2, 2, 20, 7, 9, layout="NHWC", dtype="f32"), "256x1x2"),
+    (custom(2, 1, 8, 40, 13, layout="NHWC", dtype="f32"), "256x1x4"),
+    (custom(2, 1, 64, 80, 13, layout="NHWC", dtype="f32"), "256x1x4,group2"),
+    (custom(3, 2, 128, 80, 13, layout="NHWC", dtype="bf16"), "256x1x4,group4"),
+    (custom(2, 2, 64, 80, 13, layout="NHWC", dtype="f32"), "256x1x4,group4"),
+    (custom(3, 5, 64, 25, 33, layout="NHWC", dtype="f16"), "256x1x4,group8"),
+    (custom(2, 5, 64, 25, 33, layout="NHWC", dtype="f32"), "256x1x4,group8"),
+    (custom(3, 32, 256, 14, 14, layout="NHWC", dtype="bf16"), "256x1x4,group8"),
+    (custom(3, 1, 8, 80, 13, layout="NHWC", dtype="bf16"), "256x1x8"),
+    (custom(2, 5, 44, 20, 20, layout="NHWC", dtype="f32"), "256x1x8"),
+    (custom(3, 2, 8, 80, 13, layout="NHWC", dtype="bf16"), "256x1x13"),
+    (custom(3, 4, 200, 25, 33, layout="NHWC", dtype="bf16"), "256x1x13"),
+    # one lane per row, 512 threads
+    (custom(3, 6, 8, 7, 80, layout="NHWC", dtype="bf16"), "512x1x13"),
+    (custom(5, 3, 1032, 40, 50, layout="NHWC", dtype="bf16"), "512x1x13"),
+    (custom(2, 5, 520, 80, 17, layout="NHWC", dtype="f32"), "512x1x18"),
+    # two lanes per row
+    (custom(2, 1, 1032, 60, 17, layout="NHWC", dtype="f32"), "512x2x4"),
+    (custom(2, 1, 8, 80, 13, layout="NHWC", dtype="f32"), "512x2x8"),
+    (custom(2, 2, 8, 80, 13, layout="NHWC", dtype="f32"), "512x2x13"),
+    (custom(2, 6, 8, 7, 80, layout="NHWC", dtype="f32"), "512x2x18"),
+    (custom(2, 1, 768, 60, 60, layout="NHWC", dtype="f32"), "512x2x8,group2"),
+    (custom(2, 5, 192, 25, 33, layout="NHWC", dtype="f32"), "512x2x8,group4"),
+    (custom(2, 5, 64, 33, 50, layout="NHWC", dtype="f32"), "512x2x8,group8"),
+    (custom(2, 8, 64, 33, 64, layout="NHWC", dtype="f32"), "512x2x8,group16"),
+    (custom(3, 6, 256, 50, 80, layout="NHWC", dtype="bf16"), "512x2x8,group16"),
+    (custom(2, 8, 192, 33, 64, layout="NHWC", dtype="f32"), "512x2x13,group8"),
+    (custom(2, 6, 64, 80, 80, layout="NHWC", dtype="f32"), "512x2x13,group16"),
+    # four lanes per row
+    (custom(2, 1, 2064, 30, 17, layout="NHWC", dtype="f32"), "512x4x4"),
+    (custom(2, 3, 1536, 7, 33, layout="NHWC", dtype="f32"), "512x4x4,group2"),
+    (custom(2, 1, 768, 30, 60, layout="NHWC", dtype="f32"), "512x4x4,group4"),
+    (custom(2, 1, 384, 60, 60, layout="NHWC", dtype="f32"), "512x4x4,group8"),
+    (custom(2, 2, 256, 60, 60, layout="NHWC", dtype="f32"), "512x4x4,group16"),
+    (custom(2, 1, 2048, 40, 13, layout="NHWC", dtype="f32"), "512x4x7"),
+    (custom(2, 1, 768, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group2"),
+    (custom(2, 2, 384, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group4"),
+    (custom(5, 64, 2048, 7, 7, layout="NHWC", dtype="bf16"), "512x4x7,group4"),
+    (custom(2, 5, 256, 25, 33, layout="NHWC", dtype="f32"), "512x4x7,group8"),
+    (custom(2, 5, 128, 33, 50, layout="NHWC", dtype="f32"), "512x4x7,group16"),
+    (custom(2, 2, 1536, 80, 13, layout="NHWC", dtype="f32"), "512x4x13,group2"),
+    (custom(2, 5, 768, 25, 33, layout="NHWC", dtype="f32"), "512x4x13,group4"),
+    (custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"), "512x4x13,group4"),
+    (custom(2, 5, 384, 33, 50, layout="NHWC", dtype="f32"), "512x4x13,group8"),
+    (custom(2, 8, 256, 33, 64, layout="NHWC", dtype="f32"), "512x4x13,group16"),
+    (custom(3, 5, 512, 50, 80, layout="NHWC", dtype="bf16"), "512x4x13,group16"),
+    # other storage types and activations
+    (custom(3, 8, 2048, 10, 25, layout="NHWC", dtype="f16"), "512x4x4,group4"),
+    (custom(5, 8, 2048, 10, 25, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
+     "512x4x4,group4"),
+    (custom(4, 5, 768, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
+     "512x4x13,group4"),
+    (custom(4, 5, 256, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
+     "512x4x7,group8"),
+    (custom(4, 3, 512, 12, 12, layout="NHWC", dtype="bf16", act="elu", act_param=0.5),
+     "256x1x2"),
+    (custom(3, 5, 256, 20, 20, layout="NHWC", dtype="bf16", act="identity", act_param=0.0),
+     "256x1x4,group2"),
+    (custom(2, 2, 256, 60, 60, layout="NHWC", dtype="f32", act="identity", act_param=0.0),
+     "512x4x4,group16"),
+]
+
+
 def _slice_shapes():
-    out = []
-    # small tensors (up to 4096 rows: the small-tensor rule)
-    for dtype, C in (("f32", 96), ("bf16", 256)):
-        base = 2 if dtype == "f32" else 3
-        for N, H, W in ((2, 16, 16), (5, 10, 10), (4, 16, 16), (4, 10, 25), (2, 32, 32),
-                        (5, 20, 20), (4, 25, 33)):
-            out.append(custom(base, N, C, H, W, layout="NHWC", dtype=dtype))
-    # more rows only where the slices fill the chip: 128 slices of 512 threads
-    for dtype, C in (("f32", 512), ("bf16", 1024)):
-        base = 2 if dtype == "f32" else 3
-        for N, H, W in ((4, 32, 52), (3, 40, 50), (3, 50, 60), (4, 48, 48)):   # 6656 ... 9216
-            out.append(custom(base, N, C, H, W, layout="NHWC", dtype=dtype))
-    # two lanes per row (vectors per row >= 256): capacities 1024, 2048, 3328, 4608
-    for N, H, W in ((4, 10, 25), (5, 20, 20), (4, 25, 33), (5, 30, 30)):
-        out.append(custom(5, N, 2048, H, W, layout="NHWC", dtype="bf16"))
-    out.append(custom(2, 64, 1024, 7, 7, layout="NHWC", dtype="f32"))
-    out.append(custom(4, 4, 1024, 32, 36, layout="NHWC", dtype="f32", act="elu", act_param=1.0))
-    out.append(custom(3, 4, 48, 25, 33, layout="NHWC", dtype="bf16"))     # 6 slices
-    out.append(custom(3, 4, 256, 25, 33, layout="NHWC", dtype="f16"))
-    out.append(custom(5, 4, 2048, 10, 25, layout="NHWC", dtype="f16", act="elu", act_param=1.0))
-    out.append(custom(2, 2, 20, 7, 9, layout="NHWC", dtype="f32"))        # 5 slices
-    out.append(custom(4, 4, 256, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0))
-    out.append(custom(4, 3, 512, 12, 12, layout="NHWC", dtype="bf16", act="elu", act_param=0.5))
-    out.append(custom(3, 4, 256, 16, 16, layout="NHWC", dtype="bf16", act="identity",
-                      act_param=0.0))
-    return out
+    return [wl for wl, _ in SLICE_PLANS]
+
+
+@pytest.mark.parametrize("wl,plan", SLICE_PLANS, ids=[w.name for w, _ in SLICE_PLANS])
+def test_slice_resident_plans(wl, plan):
+    desc = iabn.iabn_describe_plan(wl.N, wl.C, wl.H, wl.W, wl.layout,
+                                   workloads.storage_torch_dtype(wl.dtype), wl.act)
+    assert desc == "forward=slice_resident(%s) backward=slice_resident(%s)" % (plan, plan)
 
 
 @pytest.mark.parametrize("wl", _slice_shapes(), ids=lambda w: w.name)
@@ -368,6 +418,40 @@ def test_slice_resident_variants(wl):
     full_check(wl)
 
 
+def _same_run(r, q):
+    assert torch.equal(r.y, q.y) and torch.equal(r.dx, q.dx)
+    for k in ("save_mean", "save_invstd", "running_mean", "running_var", "dgamma", "dbeta"):
+        assert np.array_equal(getattr(r, k), getattr(q, k)), k
+
+
+def test_group_exchange_ignores_workspace_contents():
+    """Groups of workgroups swap partial sums through the workspace in words tagged
+    with a token of the call (a per-slice epoch that the kernels advance): the
+    results must not depend on what the workspace held -- a fill of ones, zeros or
+    random bytes, another shape's exchange, or the same shape's previous call."""
+    a = custom(3, 4, 256, 25, 33, layout="NHWC", dtype="bf16")      # group 4
+    b = custom(3, 5, 256, 40, 60, layout="NHWC", dtype="bf16")      # group 16, two levels
+    dt = workloads.storage_torch_dtype("bf16")
+    size = max(iabn.iabn_workspace_size(w.N, w.C, w.H, w.W, w.layout, dt) for w in (a, b))
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+    ina, inb = workloads.make_inputs(a), workloads.make_inputs(b)
+    ws.fill_(0xFF)
+    first = harness.run_gpu(ina, ws=ws)
+    harness.assert_within(harness.check_forward(ina, first), "bf16", "forward")
+    harness.assert_within(harness.check_backward(ina, first), "bf16", "backward")
+    rb = harness.run_gpu(inb, ws=ws)
+    harness.assert_within(harness.check_forward(inb, rb), "bf16", "forward")
+    harness.assert_within(harness.check_backward(inb, rb), "bf16", "backward")
+    _same_run(harness.run_gpu(ina, ws=ws), first)
+    ws.zero_()
+    _same_run(harness.run_gpu(ina, ws=ws), first)
+    ws.random_(0, 256)
+    _same_run(harness.run_gpu(ina, ws=ws), first)
+    for _ in range(3):
+        _same_run(harness.run_gpu(ina, ws=ws), first)
+    _same_run(harness.run_gpu(ina, dx_over_dy=True, ws=ws), first)
+
+
 # Channels whose first element -- the pivot of the shifted sums -- lies 8 standard
 # deviations from the mean (alternating sides): the statistics must not lose
 # accuracy to the shift.  One case per kernel family.
@@ -375,7 +459,9 @@ OUTLIER = [custom(2, 4, 32, 16, 16),                                   # NCHW ch
            custom(2, 3, 5, 17, 19),                                    # NCHW resident, elements
            custom(2, 1, 3, 157, 163),                                  # NCHW split, scalar
            custom(3, 4, 256, 25, 33, layout="NHWC", dtype="bf16"),     # NHWC slice-resident
-           custom(2, 4, 96, 25, 33, layout="NHWC", dtype="f32"),
+           custom(2, 4, 96, 25, 33, layout="NHWC", dtype="f32"),       # (groups of 4)
+           custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"),    # 4 lanes, group 4
+           custom(2, 8, 256, 33, 64, layout="NHWC", dtype="f32"),      # group 16, two levels
            custom(2, 2, 16, 80, 80, layout="NHWC", dtype="f32")]       # NHWC split
 
 
