@@ -24,8 +24,17 @@
  *     are enqueued on `stream` and return once launched.  The status reports
  *     argument validation (done before any HIP call) and launch errors; faults
  *     inside kernels surface at the caller's next synchronisation.
- *   - Results are bitwise deterministic for a given shape, layout, dtype and
- *     pointer alignment: no floating-point atomics, fixed reduction orders.
+ *   - Results are bitwise deterministic for a given shape, layout, dtype,
+ *     pointer alignment and device CU count: no floating-point atomics, fixed
+ *     reduction orders.
+ *   - Calls that may run at the same time (on different streams) need separate
+ *     workspaces; calls in stream order may share one.
+ *   - NHWC maps with few rows per channel may run a kernel whose workgroups
+ *     exchange partial sums through the workspace while all of them are
+ *     resident (the grid never exceeds the CU count).  Should the device be held
+ *     by other work so long that a partner does not arrive within about a
+ *     second, the waiting workgroup gives up and its statistics, and every
+ *     output computed from them, become NaN instead of the kernel hanging.
  *   - Calls may be captured in a HIP graph (stream capture): they launch
  *     kernels only, with no allocation, memset, copy or synchronisation, and a
  *     replay gives the same bits as the eager call.
@@ -77,10 +86,11 @@ const char *iabn_status_string(iabn_status status);
 int iabn_version(void);
 
 /* Bytes of device workspace that iabn_forward_train, iabn_forward_stats,
- * iabn_backward and iabn_backward_reduce need for this shape (0 for an empty
- * problem).  Depends only on the arguments, never on the device.  One buffer
- * serves forward and backward of the same shape.  Returns 0 for invalid
- * arguments too. */
+ * iabn_backward, iabn_backward_reduce and iabn_backward_eval need for this
+ * shape (0 for an empty problem).  Depends on the arguments and, for NHWC, on
+ * the current device's CU count (which bounds the exchanging kernels' grid).
+ * One buffer serves forward and backward of the same shape.  Returns 0 for
+ * invalid arguments too. */
 size_t iabn_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W,
                            iabn_layout layout, iabn_dtype dtype);
 

@@ -1,8 +1,9 @@
 // Tiling plan for the In-Place ABN kernels (host side).
 //
-// A plan depends only on the shape, layout, dtype and whether the 128-bit vector
-// path applies -- never on the device -- so a given problem always reduces in the
-// same order and the results are bitwise reproducible.
+// A plan depends only on the shape, layout, dtype, whether the 128-bit vector
+// path applies and (the slice-resident NHWC groups) the device's CU count, so a
+// given problem always reduces in the same order on a given device and the
+// results are bitwise reproducible.
 //
 // Reduction tiling (forward statistics and backward sums).  Every channel's m
 // elements are cut into P "partials":
