@@ -228,6 +228,55 @@ __device__ __forceinline__ void group_fetch(const uint64_t* words, uint32_t j, u
     }
 }
 
+// Members kFetchBatch at a time: the sums of channel ch of members j0 .. j0+3
+// (< G; this member's own taken from s1, s2), all four members' words loaded at
+// once on every poll, so that partners that have all published cost one round
+// trip.  NaN for a member not received within the bounded wait.
+constexpr uint32_t kFetchBatch = 4;
+
+__device__ __forceinline__ void group_fetch_batch(const uint64_t* words, uint32_t j0, uint32_t G,
+                                                  uint32_t member, uint32_t nch, uint32_t ch,
+                                                  uint64_t tok, double s1, double s2,
+                                                  double (&v1)[kFetchBatch],
+                                                  double (&v2)[kFetchBatch])
+{
+    const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
+    bool need[kFetchBatch];
+    uint32_t left = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kFetchBatch; ++q) {
+        const uint32_t j = j0 + q;
+        v1[q] = j == member ? s1 : __longlong_as_double(0x7FF8000000000000ll);
+        v2[q] = j == member ? s2 : __longlong_as_double(0x7FF8000000000000ll);
+        need[q] = j < G && j != member;
+        left += need[q] ? 1u : 0u;
+    }
+    for (uint32_t poll = 0; left != 0 && poll <= kMaxPolls; ++poll) {
+        uint64_t w[kFetchBatch][4];
+#pragma unroll
+        for (uint32_t q = 0; q < kFetchBatch; ++q) {
+            if (need[q]) {
+                const uint64_t* src = words + (size_t(j0 + q) * nch + ch) * 4;
+                w[q][0] = atomic_ld(src + 0);
+                w[q][1] = atomic_ld(src + 1);
+                w[q][2] = atomic_ld(src + 2);
+                w[q][3] = atomic_ld(src + 3);
+            }
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < kFetchBatch; ++q) {
+            if (need[q] && uint32_t(w[q][0] >> 32) == tlo && uint32_t(w[q][1] >> 32) == thi &&
+                uint32_t(w[q][2] >> 32) == tlo && uint32_t(w[q][3] >> 32) == thi) {
+                v1[q] = __longlong_as_double(int64_t((w[q][0] << 32) | uint32_t(w[q][1])));
+                v2[q] = __longlong_as_double(int64_t((w[q][2] << 32) | uint32_t(w[q][3])));
+                need[q] = false;
+                --left;
+            }
+        }
+        if (left != 0) __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 }  // namespace
 
 // Group exchange arguments: the workspace words (epochs, then the tagged sums),
@@ -261,8 +310,8 @@ constexpr uint32_t kTwoLevelGroup = 16;
 // gets back the sums over members 0..G-1, added in that order, so that every
 // member derives the same bits.
 //  - G < kTwoLevelGroup: each finishing thread publishes and then reads the other
-//    members one after another (measured: reading them with more threads at once
-//    loads the memory system with polls and is slower).
+//    members, four at a time (measured: reading them with one thread per
+//    (member, channel) loads the memory system with polls and is slower).
 //  - Larger groups, in two levels: every member but 0 publishes; member 0 reads
 //    them with one thread per (member, channel), adds, and publishes the totals
 //    in its own slot, which the others read.
@@ -278,11 +327,16 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
         if (fin) {
             group_publish(words, member, NCH, t, tok, s1, s2);
             double t1 = 0.0, t2 = 0.0;
-            for (uint32_t j = 0; j < grp.G; ++j) {
-                double v1 = s1, v2 = s2;
-                if (j != member) group_fetch(words, j, NCH, t, tok, v1, v2);
-                t1 += v1;
-                t2 += v2;
+            for (uint32_t j0 = 0; j0 < grp.G; j0 += kFetchBatch) {
+                double v1[kFetchBatch], v2[kFetchBatch];
+                group_fetch_batch(words, j0, grp.G, member, NCH, t, tok, s1, s2, v1, v2);
+#pragma unroll
+                for (uint32_t q = 0; q < kFetchBatch; ++q) {
+                    if (j0 + q < grp.G) {
+                        t1 += v1[q];
+                        t2 += v2[q];
+                    }
+                }
             }
             s1 = t1;
             s2 = t2;
