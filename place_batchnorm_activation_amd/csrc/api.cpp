@@ -108,20 +108,34 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
         p.nhwc_variant = nc.variant;
         p.nhwc_group = nc.group;
         p.scalar_variant = fused_scalar_pick(p);
-        if (nc.variant >= 0 && nc.group > 1) {
+        int64_t lpr = 1;
+        if (nc.variant >= 0) {
+            switch (nc.variant) {
+#define IABN_ROW(ID, T, LPR, NR) case ID: lpr = LPR; break;
+                IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+            default: break;
+            }
+        } else if (nhwc_vec) {
+            const NhwcChoice sc = fused_stream_pick(p, coresident_grid());
+            p.stream_variant = sc.variant;
+            if (sc.variant >= 0) {
+                p.nhwc_group = sc.group;
+                if (stream_bwd_worthwhile(p, sc.variant, sc.group)) p.stream_bwd_variant = sc.variant;
+                switch (sc.variant) {
+#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) case ID: lpr = LPR; break;
+                    IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+                default: break;
+                }
+            }
+        }
+        if ((nc.variant >= 0 || p.stream_variant >= 0) && p.nhwc_group > 1) {
             // the exchange goes past every split-kernel section, which other calls
             // on the same workspace may write
             p.off_xchg = (size_t)align_up((int64_t)split_bytes(N, C, H, W, layout, dtype), 256);
-            const int64_t lpr = [&] {
-                switch (nc.variant) {
-#define IABN_ROW(ID, T, LPR, NR) case ID: return int64_t(LPR);
-                    IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
-#undef IABN_ROW
-                default: return int64_t(1);
-                }
-            }();
             p.bytes = p.off_xchg + sizeof(uint64_t) *
-                      (size_t)nhwc_exchange_words(C / p.V / lpr, nc.group, C);
+                      (size_t)nhwc_exchange_words(C / p.V / lpr, p.nhwc_group, C);
         }
     }
     return p;
@@ -288,6 +302,11 @@ iabn_status iabn_forward_train(void* x_inout, int64_t N, int64_t C, int64_t H, i
                                   save_invstd, eps, momentum, act, act_param, workspace, stream);
         return launched();
     }
+    if (pl.stream_variant >= 0) {
+        launch_forward_stream_nhwc(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
+                                   save_invstd, eps, momentum, act, act_param, workspace, stream);
+        return launched();
+    }
     launch_forward_stats(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
                          save_invstd, eps, momentum, workspace, stream);
     launch_forward_apply(pl, x_inout, act, act_param, workspace, stream);
@@ -387,6 +406,11 @@ iabn_status iabn_backward(const void* y, const void* dy, void* dx, int64_t N, in
                                    act_param, workspace, stream);
         return launched();
     }
+    if (pa.stream_bwd_variant >= 0) {
+        launch_backward_stream_nhwc(pa, y, dy, dx, gamma, beta, save_invstd, dgamma, dbeta, act,
+                                    act_param, workspace, stream);
+        return launched();
+    }
     launch_backward_reduce(pr, y, dy, gamma, beta, save_invstd, dgamma, dbeta, act, act_param,
                            workspace, stream);
     launch_backward_apply(pa, y, dy, dx, act, act_param, workspace, stream);
@@ -449,6 +473,17 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         const size_t n = strlen(nd);
         snprintf(nd + n, sizeof nd - n, ",group%d", p.nhwc_group);
     }
+    char sd_f[48] = "", sd_b[48] = "";
+    switch (p.stream_variant) {
+#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB)                                             \
+    case ID:                                                                          \
+        snprintf(sd_f, sizeof sd_f, "%dx%dx%d+%d,group%d", T, LPR, NRF, UF, p.nhwc_group); \
+        snprintf(sd_b, sizeof sd_b, "%dx%dx%d+%d,group%d", T, LPR, NRB, UB, p.nhwc_group); \
+        break;
+        IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    default: break;
+    }
     switch (p.scalar_variant) {
 #define IABN_ROW(ID, T, NR) case ID: snprintf(sd, sizeof sd, "%dx%d", T, NR); break;
         IABN_FUSED_SCALAR_VARIANTS(IABN_ROW)
@@ -468,6 +503,8 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         snprintf(fwd, sizeof fwd, "channel_resident_scalar(%s)", sd);
     } else if (p.nhwc_variant >= 0) {
         snprintf(fwd, sizeof fwd, "slice_resident(%s)", nd);
+    } else if (p.stream_variant >= 0) {
+        snprintf(fwd, sizeof fwd, "slice_streamed(%s)", sd_f);
     } else {
         snprintf(fwd, sizeof fwd, "split(stats:%lldx%d,apply:%lldx%d,%s)",
                  (long long)p.reduce_blocks, kThreads, (long long)p.apply_blocks, kThreads,
@@ -488,6 +525,8 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         snprintf(bwd, sizeof bwd, "channel_resident_scalar(%s,dy_resident)", sd);
     } else if (p.nhwc_variant >= 0) {
         snprintf(bwd, sizeof bwd, "slice_resident(%s)", nd);
+    } else if (p.stream_bwd_variant >= 0) {
+        snprintf(bwd, sizeof bwd, "slice_streamed(%s)", sd_b);
     } else {
         snprintf(bwd, sizeof bwd, "split(reduce:%lldx%d,apply:%lldx%d,%s)",
                  (long long)p.reduce_blocks, kThreads, (long long)p.apply_blocks, kThreads,

@@ -370,6 +370,18 @@ __host__ __device__ __forceinline__ void nhwc_slice_member(uint32_t b, uint32_t 
     }
 }
 
+// Slice and member of workgroup b of a streamed slice launch (G % 8 == 0):
+// XCD x = b % 8 takes members x, x + 8, ... of every slice, so that all slices of
+// one member's rows -- whole 128-byte lines -- meet in one L2.  A bijection of
+// [0, slices*G) onto (slice, member) pairs.
+__host__ __device__ __forceinline__ void nhwc_stream_member(uint32_t b, uint32_t slices,
+                                                            uint32_t& s, uint32_t& member)
+{
+    const uint32_t q = b / 8;
+    s = q % slices;
+    member = b % 8 + 8 * (q / slices);
+}
+
 // Walk of a flat NCHW tensor: vector v has channel ((v / HWv) % C).  Advancing v
 // by a fixed stride updates the in-plane offset and the channel with carries.
 struct FlatNCHWWalk {

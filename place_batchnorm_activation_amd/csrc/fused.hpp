@@ -57,6 +57,16 @@
     X(12, 512, 4, 13)
 #endif
 
+// Streamed slice kernels (NHWC maps too large to hold).  X(id, T, LPR, NRF, UF,
+// NRB, UB): T threads, LPR lanes per row; the forward keeps NRF rows per thread
+// resident and streams the rest UF rows per thread at a time, the backward NRB
+// and UB (y and dy both).
+#ifndef IABN_STREAM_NHWC_VARIANTS
+#define IABN_STREAM_NHWC_VARIANTS(X) \
+    X(0, 512, 4, 28, 4, 14, 2)       \
+    X(1, 512, 2, 28, 4, 14, 2)
+#endif
+
 // Channel-resident NCHW kernels on single elements, for shapes the 16-byte
 // vectors cannot take (H*W not a multiple of the vector width, e.g. 7x7 maps, or
 // pointers not 16-byte aligned).  X(id, T, NR): NR elements per thread, y and dy
@@ -222,6 +232,54 @@ inline NhwcChoice fused_nhwc_pick(const Plan& p, int64_t max_grid)
     return none;
 }
 
+// Streamed slice plan for an NHWC map (variant -1: not used): the widest LPR
+// (4, then 2) whose slices, in groups of a power of two from 8 to 32, make a grid
+// of exactly max_grid workgroups (every CU streams), every member getting rows.
+// Taken where the resident kernels cannot hold the rows.
+inline NhwcChoice fused_stream_pick(const Plan& p, int64_t max_grid)
+{
+    NhwcChoice none;
+    if (p.layout != kNHWC || !p.vec || p.numel == 0) return none;
+    if (p.numel * p.esize >= (int64_t(1) << 32)) return none;
+    const int64_t cv = p.C / p.V;
+    struct Row { int id, T, LPR; };
+    static const Row tbl[] = {
+#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) {ID, T, LPR},
+        IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    };
+    for (int lpr : {4, 2}) {
+        if (cv % lpr != 0) continue;
+        const int64_t slices = cv / lpr;
+        int g = 32;
+        while (g >= 8 && slices * g > max_grid) g /= 2;
+        if (g < 8 || slices * g != max_grid || (g - 1) * ceil_div(p.m, g) >= p.m) continue;
+        for (const auto& v : tbl) {
+            if (v.LPR != lpr) continue;
+            NhwcChoice c;
+            c.variant = v.id;
+            c.group = g;
+            return c;
+        }
+    }
+    return none;
+}
+
+// Whether the streamed backward beats the split one: measured so where at least
+// half of each thread's rows stay resident (y and dy both held); with fewer,
+// re-reading two streams at this kernel's occupancy loses to the split kernels
+// (2x256x512x512 bf16: 313 against 248 us).
+inline bool stream_bwd_worthwhile(const Plan& p, int variant, int group)
+{
+    switch (variant) {
+#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) \
+    case ID: return ceil_div(ceil_div(p.m, group), T / LPR) <= 2 * NRB;
+        IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    default: return false;
+    }
+}
+
 // Workspace words of the group exchange: one epoch per slice (padded to 32
 // words), then per slice, member and channel four tagged words.
 inline int64_t nhwc_exchange_words(int64_t slices, int64_t group, int64_t C)
@@ -275,5 +333,14 @@ void launch_backward_fused_nhwc(const Plan& pl, const void* y, const void* dy, v
                                 const float* gamma, const float* beta, const float* invstd,
                                 float* dgamma, float* dbeta, int act, float a, void* ws,
                                 hipStream_t s);
+
+void launch_forward_stream_nhwc(const Plan& pl, void* x, const float* gamma, const float* beta,
+                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                                int act, float a, void* ws, hipStream_t s);
+
+void launch_backward_stream_nhwc(const Plan& pl, const void* y, const void* dy, void* dx,
+                                 const float* gamma, const float* beta, const float* invstd,
+                                 float* dgamma, float* dbeta, int act, float a, void* ws,
+                                 hipStream_t s);
 
 }  // namespace iabn

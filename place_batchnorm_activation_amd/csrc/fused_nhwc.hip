@@ -68,10 +68,20 @@ __device__ __forceinline__ uint4 opaque_q(uint4 q)
     return q;
 }
 
-__device__ __forceinline__ void st16_nt(void* base, uint32_t vec, const uint4& q)
+// Output store of a slice kernel.  Four lanes per row store 64-byte halves of
+// each 128-byte line: with the non-temporal hint they stream past the caches.
+// Narrower lanes leave 16- or 32-byte pieces from several workgroups in each
+// line, which the L2 should merge before writing back, so they use plain stores
+// (measured, NHWC backward on 256-channel maps: 44 -> 33 us with two lanes; with
+// four lanes plain stores cost 10-20%).
+template <int LPR>
+__device__ __forceinline__ void st16_out(void* base, uint32_t vec, const uint4& q)
 {
     const u32x4_t v = {q.x, q.y, q.z, q.w};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(base) + vec);
+    if constexpr (LPR >= 4)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(base) + vec);
+    else
+        reinterpret_cast<u32x4_t*>(base)[vec] = v;
 }
 
 // Workgroup totals over the row slots, stage one: threads t and t' hold the same
@@ -191,7 +201,7 @@ __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t half)
 constexpr uint32_t kMaxPolls = 1u << 21;
 
 // Members per slice at most (the exchange's LDS holds kMaxGroup partials).
-constexpr uint32_t kMaxGroup = 16;
+constexpr uint32_t kMaxGroup = 32;
 
 // This member's two fp64 sums of channel ch, as four tagged words.  words: the
 // slice's first word; nch: channels per slice.
@@ -313,14 +323,13 @@ constexpr uint32_t kTwoLevelGroup = 16;
 //    members, four at a time (measured: reading them with one thread per
 //    (member, channel) loads the memory system with polls and is slower).
 //  - Larger groups, in two levels: every member but 0 publishes; member 0 reads
-//    them with one thread per (member, channel), adds, and publishes the totals
-//    in its own slot, which the others read.
+//    them, its threads taking the (member, channel) pairs in turn, adds, and
+//    publishes the totals in its own slot, which the others read.
 template <uint32_t NCH, int T>
 __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, uint32_t slices,
                                            uint32_t member, uint64_t tok, bool fin, double& s1,
                                            double& s2)
 {
-    static_assert(NCH * kMaxGroup <= T, "one thread per (member, channel)");
     uint64_t* words = group_words(grp, s, slices, NCH);
     const uint32_t t = threadIdx.x;
     if (grp.G < kTwoLevelGroup) {
@@ -355,8 +364,8 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
         xs[0][0][t] = s1;
         xs[1][0][t] = s2;
     }
-    const uint32_t j = 1 + t / NCH, ch = t % NCH;
-    if (j < grp.G) {
+    for (uint32_t pair = t; pair < (grp.G - 1) * NCH; pair += T) {
+        const uint32_t j = 1 + pair / NCH, ch = pair % NCH;
         double v1, v2;
         group_fetch(words, j, NCH, ch, tok, v1, v2);
         xs[0][j][ch] = v1;
@@ -504,7 +513,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
         unpack16<DT>(opaque_q(r[k]), v);
 #pragma unroll
         for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K[e]) - d[e], sc[e], b_c[e]), a);
-        if (row < r1) st16_nt(x, row * Cv + col, pack16<DT>(v));
+        if (row < r1) st16_out<LPR>(x, row * Cv + col, pack16<DT>(v));
     }
 }
 
@@ -624,7 +633,337 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
             const float dz = slope * vd[e];
             vd[e] = fmaf(kA[e], dz, fmaf(kB[e], z - b_c[e], kC[e]));
         }
-        if (row < r1) st16_nt(dx, row * Cv + col, pack16<DT>(vd));
+        if (row < r1) st16_out<LPR>(dx, row * Cv + col, pack16<DT>(vd));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Streamed slice kernels, for NHWC maps too large to hold: 256 workgroups (one
+// per CU), G of them per slice, mapped member-major to the XCDs
+// (nhwc_stream_member).  A thread keeps its first NR rows in VGPRs and streams
+// the rest in chunks of U rows per thread, two chunks in flight; the second
+// pass re-reads only the streamed rows (newest first) and writes the resident
+// ones from registers.  Traffic: forward (2 + f)S, backward (3 + 2f)S, f the
+// streamed fraction of the rows.
+template <int DT, int ACT, int T, int LPR, int NR, int U>
+__global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
+    void* x, uint32_t m, uint32_t Cv, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* __restrict__ running_mean,
+    float* __restrict__ running_var, float* __restrict__ save_mean,
+    float* __restrict__ save_invstd, float eps, float momentum, float a, SliceGroup grp)
+{
+    constexpr int V = Raw16<DT>::V;
+    constexpr uint32_t RPS = T / LPR;
+    constexpr uint32_t NCH = V * LPR;
+    const uint32_t slices = Cv / LPR;
+    uint32_t s, member;
+    nhwc_stream_member(blockIdx.x, slices, s, member);
+    const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);
+    const uint32_t t = threadIdx.x;
+    const uint32_t lane = t % LPR, rs = t / LPR;
+    const uint32_t rb = r0 + rs;
+    const uint32_t col = s * LPR + lane;
+    const uint32_t c0 = col * V;
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    // rows per thread (uniform bound; rows at or past r1 are masked), streamed
+    // chunks past the NR resident rows
+    const uint32_t nk = (r1 - r0 + RPS - 1) / RPS;
+    const uint32_t nchunk = nk > NR ? (nk - NR + U - 1) / U : 0;
+    auto load_chunk = [&](uint4 (&q)[U], uint32_t c) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) q[u] = xv[min(rb + (NR + c * U + u) * RPS, r1 - 1) * Cv + col];
+    };
+
+    const uint4 kraw = xv[col];
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 r[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) r[k] = xv[min(rb + k * RPS, r1 - 1) * Cv + col];
+    // chunk loads are unconditional, their chunk index clamped (a spare load of
+    // a chunk already read at the ends): no branch in the loops below, so the
+    // compiler waits for exactly the chunk being summed
+    uint4 qa[U], qb[U];
+    load_chunk(qa, 0);
+    const bool fin = t < NCH;
+    const uint32_t cf = fin ? (s * LPR + t % LPR) * V + t / LPR : 0;
+    uint32_t k_bits = DT == kF32 ? static_cast<const uint32_t*>(x)[cf]
+                                 : uint32_t(static_cast<const uint16_t*>(x)[cf]);
+    float g_f = gamma[cf];
+    const float* rm_src = running_mean ? running_mean : gamma;
+    const float* rv_src = running_mean ? running_var : gamma;
+    float rm_f = rm_src[cf], rv_f = rv_src[cf];
+    float b_c[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) b_c[e] = beta[c0 + e];
+    uint64_t epoch = 0;
+    if (t < kWave) epoch = atomic_ld(grp.xchg + s);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float K[V];
+    unpack16<DT>(kraw, K);
+    float sums[2 * V];
+#pragma unroll
+    for (int e = 0; e < 2 * V; ++e) sums[e] = 0.f;
+    auto add = [&](const uint4& q, uint32_t row) {
+        float v[V];
+        unpack16<DT>(select16(row < r1, q, kraw), v);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float d = v[e] - K[e];
+            sums[e] += d;
+            sums[V + e] = fmaf(d, d, sums[V + e]);
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < NR; ++k) add(r[k], rb + k * RPS);
+    // streamed rows: chunk c + 1 loads while chunk c is summed
+    uint32_t c = 0;
+    for (; c + 1 < nchunk; c += 2) {
+        load_chunk(qb, c + 1);
+        __builtin_amdgcn_sched_barrier(0);          // issued before the sums of chunk c
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RPS);
+        load_chunk(qa, min(c + 2, nchunk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(qb[u], rb + (NR + (c + 1) * U + u) * RPS);
+    }
+    if (c < nchunk) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RPS);
+    }
+
+    __shared__ double sh[T / kWave][kWave];
+    __shared__ float coef[2][V][LPR];
+    __shared__ uint64_t tok_sh;
+    pin_loaded(g_f, rm_f, rv_f);
+    asm volatile("" : "+v"(k_bits));
+    wave_scatter<LPR, 2 * V>(sums, sh);
+    if (t == 0) tok_sh = group_token(grp, s, epoch);
+    __syncthreads();
+
+    const uint32_t fe = t / LPR, fl = t % LPR;
+    double S1 = 0.0, S2 = 0.0;
+    if (fin) {
+        S1 = lds_total<T, 2 * V>(sh, fe, fl);
+        S2 = lds_total<T, 2 * V>(sh, V + fe, fl);
+    }
+    group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, S1, S2);
+    if (fin) {
+        const double md = double(m);
+        const double dm = S1 / md;
+        const double var = fmax(S2 - S1 * dm, 0.0) / md;
+        const double invstd = 1.0 / sqrt(var + double(eps));
+        const double mu = double(DT == kF32 ? __uint_as_float(k_bits) : unpack1<DT>(uint16_t(k_bits))) + dm;
+        if (member == 0) {
+            save_mean[cf] = float(mu);
+            save_invstd[cf] = float(invstd);
+            if (running_mean) {
+                const double mom = double(momentum);
+                running_mean[cf] = float((1.0 - mom) * double(rm_f) + mom * mu);
+                running_var[cf] = float((1.0 - mom) * double(rv_f) + mom * var * md / (md - 1.0));
+            }
+        }
+        coef[0][fe][fl] = float(dm);
+        coef[1][fe][fl] = float(double(g_f) * invstd);
+    }
+    __syncthreads();
+    if (member == 0 && t == 0) atomic_st(grp.xchg + s, epoch + 1);
+    float d[V], sc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        d[e] = coef[0][e][lane];
+        sc[e] = coef[1][e][lane];
+    }
+    auto put = [&](const uint4& q, uint32_t row) {
+        float v[V];
+        unpack16<DT>(q, v);
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K[e]) - d[e], sc[e], b_c[e]), a);
+        if (row < r1) st16_out<LPR>(x, row * Cv + col, pack16<DT>(v));
+    };
+
+    // second pass: the last streamed chunks (the likeliest still cached) load
+    // first; the resident rows are written while they are in flight
+    const uint32_t rb2 = opaque_u(rb);
+    load_chunk(qa, nchunk > 0 ? nchunk - 1 : 0);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) put(opaque_q(r[k]), rb2 + k * RPS);
+    uint32_t i = 0;
+    for (; i + 1 < nchunk; i += 2) {
+        const uint32_t cc = nchunk - 1 - i;
+        load_chunk(qb, cc - 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + cc * U + u) * RPS);
+        load_chunk(qa, cc >= 2 ? cc - 2 : 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) put(qb[u], rb2 + (NR + (cc - 1) * U + u) * RPS);
+    }
+    if (i < nchunk) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) put(qa[u], rb2 + NR * RPS + u * RPS);   // chunk 0
+    }
+}
+
+template <int DT, int ACT, int T, int LPR, int NR, int U>
+__global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
+    const void* __restrict__ y, const void* dy, void* dx, uint32_t m, uint32_t Cv,
+    const float* __restrict__ gamma, const float* __restrict__ beta,
+    const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
+    float a, float inv_a, SliceGroup grp)
+{
+    constexpr int V = Raw16<DT>::V;
+    constexpr uint32_t RPS = T / LPR;
+    constexpr uint32_t NCH = V * LPR;
+    const uint32_t slices = Cv / LPR;
+    uint32_t s, member;
+    nhwc_stream_member(blockIdx.x, slices, s, member);
+    const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);
+    const uint32_t t = threadIdx.x;
+    const uint32_t lane = t % LPR, rs = t / LPR;
+    const uint32_t rb = r0 + rs;
+    const uint32_t col = s * LPR + lane;
+    const uint32_t c0 = col * V;
+    const uint4* yv = reinterpret_cast<const uint4*>(y);
+    const uint4* dv = reinterpret_cast<const uint4*>(dy);
+    const uint32_t nk = (r1 - r0 + RPS - 1) / RPS;
+    const uint32_t nchunk = nk > NR ? (nk - NR + U - 1) / U : 0;
+    auto load_chunk = [&](uint4 (&qy)[U], uint4 (&qd)[U], uint32_t c) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i = min(rb + (NR + c * U + u) * RPS, r1 - 1) * Cv + col;
+            qy[u] = yv[i];
+            qd[u] = dv[i];
+        }
+    };
+
+    const bool fin = t < NCH;
+    const uint32_t cf = fin ? (s * LPR + t % LPR) * V + t / LPR : 0;
+    float g_f = gamma[cf], i_f = invstd[cf];
+    uint64_t epoch = 0;
+    if (t < kWave) epoch = atomic_ld(grp.xchg + s);
+    uint4 ry[NR], rd[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const uint32_t i = min(rb + k * RPS, r1 - 1) * Cv + col;
+        ry[k] = yv[i];
+        rd[k] = dv[i];
+    }
+    uint4 ya[U], da[U], yb[U], db_[U];
+    load_chunk(ya, da, 0);                          // unconditional, as in the forward
+    __builtin_amdgcn_sched_barrier(0);
+    float b_c[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) b_c[e] = beta[c0 + e];
+
+    float sums[2 * V];
+#pragma unroll
+    for (int e = 0; e < 2 * V; ++e) sums[e] = 0.f;
+    // rows past r1 take dy = 0: dz = 0 adds exactly zero
+    auto add = [&](const uint4& qy, const uint4& qd, uint32_t row) {
+        float vy[V], vd[V];
+        unpack16<DT>(qy, vy);
+        unpack16<DT>(select16(row < r1, qd, make_uint4(0, 0, 0, 0)), vd);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            float z, slope;
+            act_invert<ACT>(vy[e], a, inv_a, z, slope);
+            const float dz = slope * vd[e];
+            sums[e] += dz;
+            sums[V + e] = fmaf(dz, z - b_c[e], sums[V + e]);
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < NR; ++k) add(ry[k], rd[k], rb + k * RPS);
+    uint32_t c = 0;
+    for (; c + 1 < nchunk; c += 2) {
+        load_chunk(yb, db_, c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RPS);
+        load_chunk(ya, da, min(c + 2, nchunk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(yb[u], db_[u], rb + (NR + (c + 1) * U + u) * RPS);
+    }
+    if (c < nchunk) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RPS);
+    }
+
+    __shared__ double sh[T / kWave][kWave];
+    __shared__ float coef[3][V][LPR];
+    __shared__ uint64_t tok_sh;
+    pin_loaded(g_f, i_f);
+    wave_scatter<LPR, 2 * V>(sums, sh);
+    if (t == 0) tok_sh = group_token(grp, s, epoch);
+    __syncthreads();
+
+    const uint32_t fe = t / LPR, fl = t % LPR;
+    double dbs = 0.0, sg = 0.0;
+    if (fin) {
+        dbs = lds_total<T, 2 * V>(sh, fe, fl);
+        sg = lds_total<T, 2 * V>(sh, V + fe, fl);
+    }
+    group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, dbs, sg);
+    if (fin) {
+        const double g = double(g_f);
+        const double dg = sg / g;
+        if (member == 0) {
+            dbeta[cf] = float(dbs);
+            dgamma[cf] = float(dg);
+        }
+        const double A = g * double(i_f);
+        const double md = double(m);
+        coef[0][fe][fl] = float(A);
+        coef[1][fe][fl] = float(-A * dg / (md * g));
+        coef[2][fe][fl] = float(-A * dbs / md);
+    }
+    __syncthreads();
+    if (member == 0 && t == 0) atomic_st(grp.xchg + s, epoch + 1);
+    float kA[V], kB[V], kC[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        kA[e] = coef[0][e][lane];
+        kB[e] = coef[1][e][lane];
+        kC[e] = coef[2][e][lane];
+    }
+    const float a2 = opaque_f(a), ia2 = opaque_f(inv_a);
+    auto put = [&](const uint4& qy, const uint4& qd, uint32_t row) {
+        float vy[V], vd[V];
+        unpack16<DT>(qy, vy);
+        unpack16<DT>(qd, vd);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            float z, slope;
+            act_invert<ACT>(vy[e], a2, ia2, z, slope);
+            const float dz = slope * vd[e];
+            vd[e] = fmaf(kA[e], dz, fmaf(kB[e], z - b_c[e], kC[e]));
+        }
+        if (row < r1) st16_out<LPR>(dx, row * Cv + col, pack16<DT>(vd));
+    };
+
+    const uint32_t rb2 = opaque_u(rb);
+    load_chunk(ya, da, nchunk > 0 ? nchunk - 1 : 0);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) put(opaque_q(ry[k]), opaque_q(rd[k]), rb2 + k * RPS);
+    uint32_t i = 0;
+    for (; i + 1 < nchunk; i += 2) {
+        const uint32_t cc = nchunk - 1 - i;
+        load_chunk(yb, db_, cc - 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + (NR + cc * U + u) * RPS);
+        load_chunk(ya, da, cc >= 2 ? cc - 2 : 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) put(yb[u], db_[u], rb2 + (NR + (cc - 1) * U + u) * RPS);
+    }
+    if (i < nchunk) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + NR * RPS + u * RPS);   // chunk 0
     }
 }
 
@@ -723,6 +1062,73 @@ void launch_backward_fused_nhwc(const Plan& pl, const void* y, const void* dy, v
     with_dtype(pl.dtype, [&](auto d) {
         with_act(act, [&](auto ac) {
             launch_nhwc_bwd_da<decltype(d)::value, decltype(ac)::value>(
+                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, ws, s);
+        });
+    });
+}
+
+template <int DT, int ACT>
+static void launch_stream_fwd_da(const Plan& pl, void* x, const float* gamma, const float* beta,
+                                 float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                                 float a, void* ws, hipStream_t s)
+{
+    const uint32_t m = uint32_t(pl.m), Cv = uint32_t(pl.C / pl.V);
+    const SliceGroup grp = slice_group(pl, ws);
+    switch (pl.stream_variant) {
+#define IABN_CASE(ID, T, LPR, NRF, UF, NRB, UB)                                                   \
+    case ID:                                                                                      \
+        hipLaunchKernelGGL((k_fwd_stream_nhwc<DT, ACT, T, LPR, NRF, UF>),                         \
+                           dim3(Cv / LPR * grp.G), dim3(T), 0, s, x, m, Cv, gamma, beta, rm, rv,  \
+                           sm, si, eps, mom, a, grp);                                             \
+        break;
+        IABN_STREAM_NHWC_VARIANTS(IABN_CASE)
+#undef IABN_CASE
+    default: break;
+    }
+}
+
+void launch_forward_stream_nhwc(const Plan& pl, void* x, const float* gamma, const float* beta,
+                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
+                                int act, float a, void* ws, hipStream_t s)
+{
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_stream_fwd_da<decltype(d)::value, decltype(ac)::value>(
+                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, ws, s);
+        });
+    });
+}
+
+template <int DT, int ACT>
+static void launch_stream_bwd_da(const Plan& pl, const void* y, const void* dy, void* dx,
+                                 const float* gamma, const float* beta, const float* invstd,
+                                 float* dgamma, float* dbeta, float a, float ia, void* ws,
+                                 hipStream_t s)
+{
+    const uint32_t m = uint32_t(pl.m), Cv = uint32_t(pl.C / pl.V);
+    const SliceGroup grp = slice_group(pl, ws);
+    switch (pl.stream_bwd_variant) {
+#define IABN_CASE(ID, T, LPR, NRF, UF, NRB, UB)                                                   \
+    case ID:                                                                                      \
+        hipLaunchKernelGGL((k_bwd_stream_nhwc<DT, ACT, T, LPR, NRB, UB>),                         \
+                           dim3(Cv / LPR * grp.G), dim3(T), 0, s, y, dy, dx, m, Cv, gamma, beta,  \
+                           invstd, dgamma, dbeta, a, ia, grp);                                    \
+        break;
+        IABN_STREAM_NHWC_VARIANTS(IABN_CASE)
+#undef IABN_CASE
+    default: break;
+    }
+}
+
+void launch_backward_stream_nhwc(const Plan& pl, const void* y, const void* dy, void* dx,
+                                 const float* gamma, const float* beta, const float* invstd,
+                                 float* dgamma, float* dbeta, int act, float a, void* ws,
+                                 hipStream_t s)
+{
+    const float ia = act == kIdentity ? 1.f : 1.f / a;
+    with_dtype(pl.dtype, [&](auto d) {
+        with_act(act, [&](auto ac) {
+            launch_stream_bwd_da<decltype(d)::value, decltype(ac)::value>(
                 pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, ws, s);
         });
     });

@@ -86,6 +86,10 @@ struct Plan {
     int nhwc_variant = -1;
     int nhwc_group = 1;
     size_t off_xchg = 0;
+    // streamed slice kernels, forward and backward (-1: not used; the backward
+    // then takes the split path); their group size is nhwc_group
+    int stream_variant = -1;
+    int stream_bwd_variant = -1;
     // channel-resident NCHW kernels on single elements (-1: not used)
     int scalar_variant = -1;
     // workspace sections (bytes, 256-aligned)

@@ -274,6 +274,59 @@ static void check_plan(const Shape& s, bool vec)
                           vv.T, vv.LPR, vv.NR, G, (long long)i, int(seen[size_t(i)]));
             }
         }
+        // streamed slice kernels: every variant and group size 8..32, the forward's
+        // and the backward's (resident rows, chunk) split
+        struct SVar { int T, LPR, NR, U; };
+        std::vector<SVar> svars;
+#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) svars.push_back({T, LPR, NRF, UF}); svars.push_back({T, LPR, NRB, UB});
+        IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+        for (const SVar& sv : svars) {
+            for (uint32_t G = 8; G <= 32; G *= 2) {
+                if (cv % sv.LPR != 0) continue;
+                const uint32_t slices = uint32_t(cv / sv.LPR);
+                const int64_t mg = (m + G - 1) / G;
+                if (int64_t(G - 1) * mg >= m) continue;
+                const uint32_t RPS = uint32_t(sv.T / sv.LPR);
+                std::fill(seen.begin(), seen.end(), 0);
+                std::vector<int> pair_seen(size_t(slices) * G, 0);
+                for (uint32_t b = 0; b < slices * G; ++b) {
+                    uint32_t sl, member;
+                    nhwc_stream_member(b, slices, sl, member);
+                    CHECK(sl < slices && member < G, "stream map bounds");
+                    if (sl >= slices || member >= G) continue;
+                    CHECK(member % 8 == b % 8, "stream member on XCD b %% 8");
+                    pair_seen[size_t(sl) * G + member]++;
+                    const uint32_t r0 = member * uint32_t(mg);
+                    const uint32_t r1 = std::min(uint32_t(m), r0 + uint32_t(mg));
+                    CHECK(r0 < r1, "stream member %u has no rows", member);
+                    const uint32_t nk = (r1 - r0 + RPS - 1) / RPS;
+                    const uint32_t nchunk = nk > uint32_t(sv.NR) ? (nk - sv.NR + sv.U - 1) / sv.U : 0;
+                    for (int t = 0; t < sv.T; ++t) {
+                        const uint32_t lane = uint32_t(t) % uint32_t(sv.LPR);
+                        const uint32_t rb = r0 + uint32_t(t) / uint32_t(sv.LPR);
+                        const uint32_t col = sl * uint32_t(sv.LPR) + lane;
+                        auto visit = [&](uint32_t row) {
+                            const uint32_t lrow = std::min(row, r1 - 1);
+                            CHECK(int64_t(lrow) * cv + col < nvec, "stream load bounds");
+                            if (row < r1) {
+                                const uint32_t idx = row * uint32_t(cv) + col;
+                                CHECK(int64_t(idx) == int64_t(row) * cv + col, "stream 32-bit index");
+                                if (int64_t(idx) < nvec) seen[size_t(idx)]++;
+                            }
+                        };
+                        for (int k = 0; k < sv.NR; ++k) visit(rb + uint32_t(k) * RPS);
+                        for (uint32_t c = 0; c < nchunk; ++c)
+                            for (int u = 0; u < sv.U; ++u) visit(rb + (uint32_t(sv.NR) + c * sv.U + u) * RPS);
+                    }
+                }
+                for (size_t q = 0; q < pair_seen.size(); ++q)
+                    CHECK(pair_seen[q] == 1, "stream slice/member %zu taken %d times", q, pair_seen[q]);
+                for (int64_t i = 0; i < nvec; ++i)
+                    CHECK(seen[size_t(i)] == 1, "stream T=%d LPR=%d NR=%d U=%d G=%u visits %lld %d times",
+                          sv.T, sv.LPR, sv.NR, sv.U, G, (long long)i, int(seen[size_t(i)]));
+            }
+        }
         // the plan's own choice obeys the group rules at the MI355X's 256 CUs
         const NhwcChoice ch = fused_nhwc_pick(pl, 256);
         if (ch.variant >= 0 && ch.group > 1) {
@@ -310,7 +363,8 @@ int main(int argc, char** argv)
         {32, 64, 7, 7, kNCHW, kF32},     {500, 3, 7, 7, kNCHW, kBF16},    {10, 5, 7, 7, kNCHW, kF32},
         {8, 512, 28, 28, kNHWC, kBF16},  {64, 256, 14, 14, kNHWC, kBF16}, {32, 512, 28, 28, kNHWC, kBF16},
         {32, 1024, 14, 14, kNHWC, kBF16}, {32, 256, 28, 28, kNHWC, kF32}, {7, 512, 9, 13, kNHWC, kBF16},
-        {3, 1024, 11, 17, kNHWC, kF32},
+        {3, 1024, 11, 17, kNHWC, kF32},  {2, 256, 200, 200, kNHWC, kBF16}, {8, 256, 56, 56, kNHWC, kBF16},
+        {5, 128, 99, 101, kNHWC, kF32},   {2, 64, 256, 260, kNHWC, kBF16},
     };
     std::mt19937_64 rng(12345);
     const int n_random = argc > 1 ? std::atoi(argv[1]) : 300;

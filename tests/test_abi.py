@@ -174,7 +174,16 @@ def test_plan_choice_for_the_workloads():
     assert d(16, 512, 28, 28, "NCHW", iabn.F32, "elu").startswith(
         "forward=channel_resident(256x13) backward=channel_resident(256x13,dy_resident)")
     assert d(2, 4, 8, 8, "NCHW", iabn.F32, "leaky_relu").startswith("forward=channel_resident")
-    assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    # a map too large to hold: 256 workgroups in groups of 32 keep part of it in
+    # registers and stream the rest
+    assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_streamed(512x4x28+4,group32) " \
+        "backward=split(reduce:512x256,apply:2048x256,vec16)"
+    # ... the backward too while half its rows stay resident
+    assert d(32, 256, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_streamed(512x4x28+4,group32) backward=slice_streamed(512x4x14+2,group32)"
+    # ... unless its slices cannot fill the chip: split
+    assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
     assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_resident(512x4x7,group4) backward=slice_resident(512x4x7,group4)"
     # too many rows for a workgroup to hold: split
@@ -208,8 +217,9 @@ def test_plan_choice_for_the_workloads():
         "forward=slice_resident(256x1x2) backward=slice_resident(256x1x2)"
     assert d(32, 256, 14, 14, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_resident(256x1x4,group8) backward=slice_resident(256x1x4,group8)"
-    # one lane per row only, with too many rows: split
-    assert d(32, 128, 56, 56, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    # too many rows to hold, 8 slices of two lanes: streamed
+    assert d(32, 128, 56, 56, "NHWC", iabn.BF16, "leaky_relu").startswith(
+        "forward=slice_streamed(512x2x28+4,group32)")
     # ELU takes the same channel-resident variants
     assert "channel_resident(512x49)" in d(32, 256, 56, 56, "NCHW", iabn.F32, "elu")
     with pytest.raises(ValueError):
