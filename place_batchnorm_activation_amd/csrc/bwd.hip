@@ -27,6 +27,11 @@ namespace iabn {
 #define IABN_REDUCE_UNROLL 4
 #endif
 constexpr int kUnrollB = IABN_REDUCE_UNROLL;
+// NHWC reduction: row groups of y and dy in flight per thread, per pipeline stage
+#ifndef IABN_NHWC_REDUCE_UNROLL
+#define IABN_NHWC_REDUCE_UNROLL 8
+#endif
+constexpr int kUnrollN = IABN_NHWC_REDUCE_UNROLL;
 
 template <int ACT, int V>
 __device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy)[V],
@@ -185,23 +190,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
         }
         if constexpr (V == Raw16<DT>::V) {
             // software pipeline over complete row groups (branch-free): the next
-            // kUnrollB groups of y and dy load while the current ones are summed;
+            // kUnrollN groups of y and dy load while the current ones are summed;
             // the rest, at most one ragged group per workgroup, runs checked
             const int64_t full = m / rpi;
             const uint4* yv = reinterpret_cast<const uint4*>(y);
             const uint4* dv = reinterpret_cast<const uint4*>(dy);
-            auto load_set = [&](uint4 (&by)[kUnrollB], uint4 (&bd)[kUnrollB], int64_t g0) {
+            auto load_set = [&](uint4 (&by)[kUnrollN], uint4 (&bd)[kUnrollN], int64_t g0) {
 #pragma unroll
-                for (int u = 0; u < kUnrollB; ++u) {
+                for (int u = 0; u < kUnrollN; ++u) {
                     const int64_t i = ((g0 + u * P) * rpi + rs) * Cv + col;
                     by[u] = yv[i];
                     bd[u] = dv[i];
                 }
             };
-            auto add_set = [&](const uint4 (&by)[kUnrollB], const uint4 (&bd)[kUnrollB],
+            auto add_set = [&](const uint4 (&by)[kUnrollN], const uint4 (&bd)[kUnrollN],
                                int64_t g0) {
 #pragma unroll
-                for (int u = 0; u < kUnrollB; ++u) {
+                for (int u = 0; u < kUnrollN; ++u) {
                     float vy[V], vd[V];
                     unpack16<DT>(by[u], vy);
                     unpack16<DT>(bd[u], vd);
@@ -209,16 +214,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                 }
             };
             int64_t g = p;
-            if (g + (kUnrollB - 1) * P < full) {
-                uint4 Ay[kUnrollB], Ad[kUnrollB], By[kUnrollB], Bd[kUnrollB];
+            if (g + (kUnrollN - 1) * P < full) {
+                uint4 Ay[kUnrollN], Ad[kUnrollN], By[kUnrollN], Bd[kUnrollN];
                 load_set(Ay, Ad, g);
                 for (;;) {
-                    const int64_t g2 = g + kUnrollB * P;
-                    if (g2 + (kUnrollB - 1) * P >= full) { add_set(Ay, Ad, g); g = g2; break; }
+                    const int64_t g2 = g + kUnrollN * P;
+                    if (g2 + (kUnrollN - 1) * P >= full) { add_set(Ay, Ad, g); g = g2; break; }
                     load_set(By, Bd, g2);
                     add_set(Ay, Ad, g);
-                    const int64_t g3 = g2 + kUnrollB * P;
-                    if (g3 + (kUnrollB - 1) * P >= full) { add_set(By, Bd, g2); g = g3; break; }
+                    const int64_t g3 = g2 + kUnrollN * P;
+                    if (g3 + (kUnrollN - 1) * P >= full) { add_set(By, Bd, g2); g = g3; break; }
                     load_set(Ay, Ad, g3);
                     add_set(By, Bd, g2);
                     g = g3;
