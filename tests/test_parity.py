@@ -165,7 +165,8 @@ def test_misaligned_pointers_take_scalar_path(layout, dtype):
 
 @pytest.mark.parametrize("wl", [custom(2, 8, 32, 28, 28), custom(3, 4, 64, 32, 32),
                                 custom(4, 4, 32, 14, 14), custom(5, 8, 512, 7, 7),
-                                custom(3, 5, 256, 40, 60, layout="NHWC", dtype="bf16")],
+                                custom(3, 5, 256, 40, 60, layout="NHWC", dtype="bf16"),
+                                custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16")],
                          ids=lambda w: w.name)
 def test_bitwise_deterministic(wl):
     inp = workloads.make_inputs(wl)
@@ -452,6 +453,21 @@ def test_slice_streamed(wl, fwd, bwd):
                                    workloads.storage_torch_dtype(wl.dtype), wl.act)
     assert desc == "forward=%s backward=%s" % (fwd, bwd)
     full_check(wl)
+
+
+def test_streamed_dx_in_place_and_fresh_workspace():
+    """The streamed kernels (forward streaming, backward streaming) give the same
+    bits with dx written over dy and with a workspace of arbitrary contents."""
+    wl = custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16")
+    inp = workloads.make_inputs(wl)
+    a = harness.run_gpu(inp)
+    b = harness.run_gpu(inp, dx_over_dy=True)
+    assert torch.equal(a.y, b.y) and torch.equal(a.dx, b.dx)
+    ws = iabn.workspace(wl.N, wl.C, wl.H, wl.W, wl.layout, a.y.dtype)
+    ws.random_(0, 256)
+    c = harness.run_gpu(inp, ws=ws)
+    assert torch.equal(a.y, c.y) and torch.equal(a.dx, c.dx)
+    assert np.array_equal(a.dgamma, c.dgamma) and np.array_equal(a.save_invstd, c.save_invstd)
 
 
 def _same_run(r, q):
