@@ -382,6 +382,18 @@ __host__ __device__ __forceinline__ void nhwc_stream_member(uint32_t b, uint32_t
     member = b % 8 + 8 * (q / slices);
 }
 
+// Slice and member of workgroup b of a slice-resident launch: groups of 8 or more
+// members are placed member-major (nhwc_stream_member), so that every line's
+// writers -- the slices of one row range -- share an L2 however narrow the
+// slices; smaller groups slice-major (nhwc_slice_member).
+__host__ __device__ __forceinline__ void nhwc_group_member(uint32_t b, uint32_t slices,
+                                                           uint32_t G, uint32_t& s,
+                                                           uint32_t& member)
+{
+    if (G >= 8) nhwc_stream_member(b, slices, s, member);
+    else nhwc_slice_member(b, slices, G, s, member);
+}
+
 // Walk of a flat NCHW tensor: vector v has channel ((v / HWv) % C).  Advancing v
 // by a fixed stride updates the in-plane offset and the channel with carries.
 struct FlatNCHWWalk {

@@ -149,14 +149,16 @@ struct NhwcChoice {
 };
 
 // Choice, from cold timings of every (variant, G) on ResNet-50 NHWC shapes:
-//  0. A tensor under 4 MB: one lane per row and 256 threads, at most 4 rows per
-//     thread, the smallest group (up to 8) that holds the rows -- on so little
-//     data the count of workgroups, each a CU's load pipeline, matters most.
-//  1. LPR = 4, then 2 (a wave reads LPR*16 contiguous bytes of each row; one
-//     lane per row coalesces poorly): the smallest group whose ceil(m/G) rows fit
-//     a variant of at most 8 rows per thread, else at most 13 (more rows per
-//     thread lengthen each member's load -> reduce -> store round trip more than
-//     extra members cost).  G = 1 here needs the chip filled or a small tensor.
+//  0. A tensor under 4 MB: one lane per row and 256 threads, at most 2 (else 4)
+//     rows per thread, the smallest group (up to 8) that holds the rows -- on so
+//     little data the count of workgroups, each a CU's load pipeline, matters
+//     most.
+//  1. The widest LPR in the table (a wave reads LPR*16 contiguous bytes of each
+//     row; one lane per row coalesces poorly): the smallest group (up to 32)
+//     whose ceil(m/G) rows fit a variant of at most 4 rows per thread, else 8,
+//     else 13 (more rows per thread lengthen each member's load -> reduce ->
+//     store round trip more than extra members cost).  G = 1 here needs the chip
+//     filled or a small tensor.
 //  2. One workgroup per slice at any LPR, the chip filled (T*slices >= 256*256)
 //     or a small tensor (under 4 MB with at most 4096 rows), where launch latency
 //     rules.
@@ -187,26 +189,28 @@ inline NhwcChoice fused_nhwc_pick(const Plan& p, int64_t max_grid)
         return best;
     };
     // a tensor under 4 MB: as many workgroups as possible, each thread holding at
-    // most 4 rows (one lane per row, 256 threads), groups of at most 8
+    // most 2, else 4 rows (one lane per row, 256 threads), groups of at most 8
     if (bytes <= (int64_t(4) << 20)) {
-        for (int g = 1; g <= 8; g *= 2) {
-            const int64_t grid = cv * g;
-            const int64_t mg = ceil_div(p.m, g);
-            if (g > 1 && (cv % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;
-            const Row* v = holding(1, 4, mg);
-            if (v && v->T == 256) {
-                NhwcChoice c;
-                c.variant = v->id;
-                c.group = g;
-                return c;
+        for (int nr_cap : {2, 4}) {
+            for (int g = 1; g <= 8; g *= 2) {
+                const int64_t grid = cv * g;
+                const int64_t mg = ceil_div(p.m, g);
+                if (g > 1 && (cv % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;
+                const Row* v = holding(1, nr_cap, mg);
+                if (v && v->T == 256) {
+                    NhwcChoice c;
+                    c.variant = v->id;
+                    c.group = g;
+                    return c;
+                }
             }
         }
     }
-    for (int nr_cap : {8, 13}) {
-        for (int lpr : {4, 2}) {
+    for (int nr_cap : {4, 8, 13}) {
+        for (int lpr : {8, 4, 2}) {
             if (cv % lpr != 0) continue;
             const int64_t slices = cv / lpr;
-            for (int g = 1; g <= 16; g *= 2) {
+            for (int g = 1; g <= 32; g *= 2) {
                 const int64_t grid = slices * g;
                 const int64_t mg = ceil_div(p.m, g);
                 if (g > 1 && (slices % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;
@@ -232,10 +236,11 @@ inline NhwcChoice fused_nhwc_pick(const Plan& p, int64_t max_grid)
     return none;
 }
 
-// Streamed slice plan for an NHWC map (variant -1: not used): the widest LPR
-// (4, then 2) whose slices, in groups of a power of two from 8 to 32, make a grid
-// of exactly max_grid workgroups (every CU streams), every member getting rows.
-// Taken where the resident kernels cannot hold the rows.
+// Streamed slice plan for an NHWC map (variant -1: not used): the widest LPR of
+// at least 4 (measured: two lanes per row lost to the split path on 64-channel
+// 112x112 maps) whose slices, in groups of a power of two from 8 to 64, make a
+// grid of exactly max_grid workgroups (every CU streams), every member getting
+// rows.  Taken where the resident kernels cannot hold the rows.
 inline NhwcChoice fused_stream_pick(const Plan& p, int64_t max_grid)
 {
     NhwcChoice none;
@@ -248,10 +253,10 @@ inline NhwcChoice fused_stream_pick(const Plan& p, int64_t max_grid)
         IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     };
-    for (int lpr : {4, 2}) {
+    for (int lpr : {8, 4}) {
         if (cv % lpr != 0) continue;
         const int64_t slices = cv / lpr;
-        int g = 32;
+        int g = 64;
         while (g >= 8 && slices * g > max_grid) g /= 2;
         if (g < 8 || slices * g != max_grid || (g - 1) * ceil_div(p.m, g) >= p.m) continue;
         for (const auto& v : tbl) {

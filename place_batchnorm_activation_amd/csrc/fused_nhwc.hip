@@ -86,17 +86,15 @@ __device__ __forceinline__ void st16_out(void* base, uint32_t vec, const uint4& 
 
 // Workgroup totals over the row slots, stage one: threads t and t' hold the same
 // channels when t % LPR == t' % LPR.  Inside the wave a reduce-scatter butterfly:
-// at xor offset OFF (32, 16, ...) a lane keeps half of its NV values -- the upper
-// half when lane & OFF -- and adds the partner's copy of that half, so it sends
-// NV/2 + NV/4 + ... values rather than NV per level.  Once one value is left, the
-// levels down to LPR are plain butterfly sums, in fp64.  Value q of lane position
-// l then sits in lane (q << (6 - log2 NV)) | l of every wave; each lane leaves its
-// value in sh[wave][lane] (the caller waits on the barrier).
+// at xor offset OFF (32, 16, ... down to LPR) a lane keeps half of its values --
+// the upper half when lane & OFF -- and adds the partner's copy of that half, so
+// it sends NV/2 + NV/4 + ... values rather than NV per level.  If one value is
+// left before the levels run out, the rest are plain butterfly sums in fp64; if
+// the levels run out first (NV*LPR > 64), each lane keeps NS = NV*LPR/64 values.
 template <int OFF, int LPR, int N>
-struct ScatterLevels {
-    static constexpr int kEnd = ScatterLevels<OFF / 2, LPR, N / 2>::kEnd;
-    static __device__ __forceinline__ void run(float* a, uint32_t lane)
-    {
+__device__ __forceinline__ void scatter_levels(float* a, uint32_t lane)
+{
+    if constexpr (N > 1 && OFF >= LPR) {
         constexpr int H = N / 2;
         const bool up = (lane & OFF) != 0;
 #pragma unroll
@@ -105,15 +103,17 @@ struct ScatterLevels {
             const float keep = up ? a[i + H] : a[i];
             a[i] = keep + __shfl_xor(send, OFF, kWave);
         }
-        ScatterLevels<OFF / 2, LPR, H>::run(a, lane);
+        scatter_levels<OFF / 2, LPR, H>(a, lane);
     }
-};
+}
 
-template <int OFF, int LPR>
-struct ScatterLevels<OFF, LPR, 1> {
-    static constexpr int kEnd = OFF;             // first plain level
-    static __device__ __forceinline__ void run(float*, uint32_t) {}
-};
+// xor offset at which the scatter stops
+template <int OFF, int LPR, int N>
+constexpr int scatter_end()
+{
+    if constexpr (N > 1 && OFF >= LPR) return scatter_end<OFF / 2, LPR, N / 2>();
+    else return OFF;
+}
 
 template <int OFF, int LPR>
 __device__ __forceinline__ double plain_levels(double a)
@@ -150,27 +150,47 @@ __device__ __forceinline__ uint4 select16(bool ok, const uint4& a, const uint4& 
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
+// Values each lane keeps after the scatter.
 template <int LPR, int NV>
-__device__ __forceinline__ void wave_scatter(float (&v)[NV], double (*sh)[kWave])
+struct ScatterSlots {
+    static constexpr int value = NV * LPR > kWave ? NV * LPR / kWave : 1;
+};
+
+// One wave's share of the LDS the scatter leaves its values in.
+template <int LPR, int NV>
+using ScatterRow = double[ScatterSlots<LPR, NV>::value][kWave];
+
+template <int LPR, int NV>
+__device__ __forceinline__ void wave_scatter(float (&v)[NV], ScatterRow<LPR, NV>* sh)
 {
-    static_assert((1 << ilog2(NV)) == NV && NV * LPR <= kWave, "values per lane position");
+    static_assert((1 << ilog2(NV)) == NV && (1 << ilog2(LPR)) == LPR, "powers of two");
+    constexpr int NS = ScatterSlots<LPR, NV>::value;
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    ScatterLevels<kWave / 2, LPR, NV>::run(v, lane);
-    constexpr int kEnd = ScatterLevels<kWave / 2, LPR, NV>::kEnd;
-    sh[threadIdx.x / kWave][lane] = plain_levels<kEnd, LPR>(double(v[0]));
+    scatter_levels<kWave / 2, LPR, NV>(v, lane);
+    if constexpr (NS == 1) {
+        constexpr int kEnd = scatter_end<kWave / 2, LPR, NV>();
+        sh[threadIdx.x / kWave][0][lane] = plain_levels<kEnd, LPR>(double(v[0]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) sh[threadIdx.x / kWave][j][lane] = double(v[j]);
+    }
 }
 
 // Stage two: the total of value q for lane position l, the waves summed in order.
-template <int T, int NV>
-__device__ __forceinline__ double lds_total(const double (*sh)[kWave], uint32_t q, uint32_t l)
+// One slot per lane: value q sits in lane (q << (6 - log2 NV)) | l.  NS slots:
+// in lane ((q / NS) << log2 LPR) | l, slot q % NS.
+template <int T, int LPR, int NV>
+__device__ __forceinline__ double lds_total(const ScatterRow<LPR, NV>* sh, uint32_t q, uint32_t l)
 {
-    const uint32_t src = (q << (6 - ilog2(NV))) | l;
-    double acc = sh[0][src];
+    constexpr int NS = ScatterSlots<LPR, NV>::value;
+    const uint32_t src = NS == 1 ? (q << (6 - ilog2(NV))) | l
+                                 : ((q / NS) << ilog2(LPR)) | l;
+    const uint32_t slot = NS == 1 ? 0 : q % NS;
+    double acc = sh[0][slot][src];
 #pragma unroll
-    for (int w = 1; w < T / kWave; ++w) acc += sh[w][src];
+    for (int w = 1; w < T / kWave; ++w) acc += sh[w][slot][src];
     return acc;
 }
-
 
 // splitmix64's output mix (Steele, Lea and Flood, "Fast splittable pseudorandom
 // number generators", 2014), a bijection of 64-bit words.
@@ -201,7 +221,7 @@ __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t half)
 constexpr uint32_t kMaxPolls = 1u << 21;
 
 // Members per slice at most (the exchange's LDS holds kMaxGroup partials).
-constexpr uint32_t kMaxGroup = 32;
+constexpr uint32_t kMaxGroup = 64;
 
 // This member's two fp64 sums of channel ch, as four tagged words.  words: the
 // slice's first word; nch: channels per slice.
@@ -238,10 +258,10 @@ __device__ __forceinline__ void group_fetch(const uint64_t* words, uint32_t j, u
     }
 }
 
-// Members kFetchBatch at a time: the sums of channel ch of members j0 .. j0+3
-// (< G; this member's own taken from s1, s2), all four members' words loaded at
-// once on every poll, so that partners that have all published cost one round
-// trip.  NaN for a member not received within the bounded wait.
+// Members kFetchBatch at a time: the sums of channel ch of members j0 ..
+// j0 + kFetchBatch - 1 (< G; this member's own taken from s1, s2), all their
+// words loaded at once on every poll, so that partners that have all published
+// cost one round trip.  NaN for a member not received within the bounded wait.
 constexpr uint32_t kFetchBatch = 4;
 
 __device__ __forceinline__ void group_fetch_batch(const uint64_t* words, uint32_t j0, uint32_t G,
@@ -312,8 +332,10 @@ __device__ __forceinline__ uint64_t* group_words(const SliceGroup& grp, uint32_t
     return grp.xchg + ((slices + 31u) & ~31u) + size_t(s) * grp.G * nch * 4;
 }
 
-// Groups of at least this many members exchange in two levels.
+// Groups of at least this many members exchange in two levels, member 0's
+// threads loading up to kPairBatch (member, channel) pairs at once.
 constexpr uint32_t kTwoLevelGroup = 16;
+constexpr uint32_t kPairBatch = 4;
 
 // Sums over all members (G > 1), called by every thread of the workgroup: the
 // finishing thread of channel t (t < NCH) passes its member's sums s1, s2 and
@@ -323,8 +345,8 @@ constexpr uint32_t kTwoLevelGroup = 16;
 //    members, four at a time (measured: reading them with one thread per
 //    (member, channel) loads the memory system with polls and is slower).
 //  - Larger groups, in two levels: every member but 0 publishes; member 0 reads
-//    them, its threads taking the (member, channel) pairs in turn, adds, and
-//    publishes the totals in its own slot, which the others read.
+//    them, each of its threads loading up to kPairBatch (member, channel) pairs at
+//    once, adds, and publishes the totals in its own slot, which the others read.
 template <uint32_t NCH, int T>
 __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, uint32_t slices,
                                            uint32_t member, uint64_t tok, bool fin, double& s1,
@@ -364,12 +386,49 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
         xs[0][0][t] = s1;
         xs[1][0][t] = s2;
     }
-    for (uint32_t pair = t; pair < (grp.G - 1) * NCH; pair += T) {
-        const uint32_t j = 1 + pair / NCH, ch = pair % NCH;
-        double v1, v2;
-        group_fetch(words, j, NCH, ch, tok, v1, v2);
-        xs[0][j][ch] = v1;
-        xs[1][j][ch] = v2;
+    const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
+    const uint32_t npairs = (grp.G - 1) * NCH;
+    for (uint32_t p0 = 0; p0 < npairs; p0 += kPairBatch * T) {
+        bool need[kPairBatch];
+        uint32_t left = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < kPairBatch; ++q) {
+            const uint32_t pair = p0 + q * T + t;
+            need[q] = pair < npairs;
+            left += need[q] ? 1u : 0u;
+            if (need[q]) {                      // NaN unless received
+                xs[0][1 + pair / NCH][pair % NCH] = __longlong_as_double(0x7FF8000000000000ll);
+                xs[1][1 + pair / NCH][pair % NCH] = __longlong_as_double(0x7FF8000000000000ll);
+            }
+        }
+        for (uint32_t poll = 0; left != 0 && poll <= kMaxPolls; ++poll) {
+            uint64_t w[kPairBatch][4];
+#pragma unroll
+            for (uint32_t q = 0; q < kPairBatch; ++q) {
+                if (need[q]) {
+                    const uint32_t pair = p0 + q * T + t;
+                    const uint64_t* src = words + (size_t(1 + pair / NCH) * NCH + pair % NCH) * 4;
+                    w[q][0] = atomic_ld(src + 0);
+                    w[q][1] = atomic_ld(src + 1);
+                    w[q][2] = atomic_ld(src + 2);
+                    w[q][3] = atomic_ld(src + 3);
+                }
+            }
+#pragma unroll
+            for (uint32_t q = 0; q < kPairBatch; ++q) {
+                if (need[q] && uint32_t(w[q][0] >> 32) == tlo && uint32_t(w[q][1] >> 32) == thi &&
+                    uint32_t(w[q][2] >> 32) == tlo && uint32_t(w[q][3] >> 32) == thi) {
+                    const uint32_t pair = p0 + q * T + t;
+                    xs[0][1 + pair / NCH][pair % NCH] =
+                        __longlong_as_double(int64_t((w[q][0] << 32) | uint32_t(w[q][1])));
+                    xs[1][1 + pair / NCH][pair % NCH] =
+                        __longlong_as_double(int64_t((w[q][2] << 32) | uint32_t(w[q][3])));
+                    need[q] = false;
+                    --left;
+                }
+            }
+            if (left != 0) __builtin_amdgcn_s_sleep(1);
+        }
     }
     __syncthreads();
     if (fin) {
@@ -402,7 +461,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
     constexpr uint32_t NCH = V * LPR;               // channels per slice
     const uint32_t slices = Cv / LPR;
     uint32_t s, member;
-    nhwc_slice_member(blockIdx.x, slices, grp.G, s, member);
+    nhwc_group_member(blockIdx.x, slices, grp.G, s, member);
     const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);   // this member's rows
     const uint32_t t = threadIdx.x;
     const uint32_t lane = t % LPR, rs = t / LPR;
@@ -460,7 +519,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
             sums[V + e] = fmaf(d, d, sums[V + e]);
         }
     }
-    __shared__ double sh[T / kWave][kWave];
+    __shared__ ScatterRow<LPR, 2 * V> sh[T / kWave];
     __shared__ float coef[2][V][LPR];
     __shared__ uint64_t tok_sh;
     pin_loaded(g_f, rm_f, rv_f);
@@ -473,8 +532,8 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
     const uint32_t fe = t / LPR, fl = t % LPR;      // finishing thread: channel (fe, fl)
     double S1 = 0.0, S2 = 0.0;
     if (fin) {
-        S1 = lds_total<T, 2 * V>(sh, fe, fl);
-        S2 = lds_total<T, 2 * V>(sh, V + fe, fl);
+        S1 = lds_total<T, LPR, 2 * V>(sh, fe, fl);
+        S2 = lds_total<T, LPR, 2 * V>(sh, V + fe, fl);
     }
     if (grp.G > 1) group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, S1, S2);
     if (fin) {
@@ -530,7 +589,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
     constexpr uint32_t NCH = V * LPR;
     const uint32_t slices = Cv / LPR;
     uint32_t s, member;
-    nhwc_slice_member(blockIdx.x, slices, grp.G, s, member);
+    nhwc_group_member(blockIdx.x, slices, grp.G, s, member);
     const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);
     const uint32_t t = threadIdx.x;
     const uint32_t lane = t % LPR, rs = t / LPR;
@@ -579,7 +638,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
             sums[V + e] = fmaf(dz, z - b_c[e], sums[V + e]);
         }
     }
-    __shared__ double sh[T / kWave][kWave];
+    __shared__ ScatterRow<LPR, 2 * V> sh[T / kWave];
     __shared__ float coef[3][V][LPR];
     __shared__ uint64_t tok_sh;
     pin_loaded(g_f, i_f);
@@ -591,8 +650,8 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
     const uint32_t fe = t / LPR, fl = t % LPR;
     double db = 0.0, sg = 0.0;
     if (fin) {
-        db = lds_total<T, 2 * V>(sh, fe, fl);
-        sg = lds_total<T, 2 * V>(sh, V + fe, fl);
+        db = lds_total<T, LPR, 2 * V>(sh, fe, fl);
+        sg = lds_total<T, LPR, 2 * V>(sh, V + fe, fl);
     }
     if (grp.G > 1) group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, db, sg);
     if (fin) {
@@ -733,7 +792,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
         for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RPS);
     }
 
-    __shared__ double sh[T / kWave][kWave];
+    __shared__ ScatterRow<LPR, 2 * V> sh[T / kWave];
     __shared__ float coef[2][V][LPR];
     __shared__ uint64_t tok_sh;
     pin_loaded(g_f, rm_f, rv_f);
@@ -745,8 +804,8 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     const uint32_t fe = t / LPR, fl = t % LPR;
     double S1 = 0.0, S2 = 0.0;
     if (fin) {
-        S1 = lds_total<T, 2 * V>(sh, fe, fl);
-        S2 = lds_total<T, 2 * V>(sh, V + fe, fl);
+        S1 = lds_total<T, LPR, 2 * V>(sh, fe, fl);
+        S2 = lds_total<T, LPR, 2 * V>(sh, V + fe, fl);
     }
     group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, S1, S2);
     if (fin) {
@@ -893,7 +952,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
         for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RPS);
     }
 
-    __shared__ double sh[T / kWave][kWave];
+    __shared__ ScatterRow<LPR, 2 * V> sh[T / kWave];
     __shared__ float coef[3][V][LPR];
     __shared__ uint64_t tok_sh;
     pin_loaded(g_f, i_f);
@@ -904,8 +963,8 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
     const uint32_t fe = t / LPR, fl = t % LPR;
     double dbs = 0.0, sg = 0.0;
     if (fin) {
-        dbs = lds_total<T, 2 * V>(sh, fe, fl);
-        sg = lds_total<T, 2 * V>(sh, V + fe, fl);
+        dbs = lds_total<T, LPR, 2 * V>(sh, fe, fl);
+        sg = lds_total<T, LPR, 2 * V>(sh, V + fe, fl);
     }
     group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, dbs, sg);
     if (fin) {

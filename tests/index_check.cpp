@@ -219,7 +219,7 @@ static void check_plan(const Shape& s, bool vec)
         IABN_FUSED_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
         for (const Var& vv : vars) {
-            for (uint32_t G = 1; G <= 16; G *= 2) {
+            for (uint32_t G = 1; G <= 64; G *= 2) {
                 const int64_t rps = vv.T / vv.LPR;
                 if (cv % vv.LPR != 0) continue;
                 const uint32_t slices = uint32_t(cv / vv.LPR);
@@ -232,7 +232,7 @@ static void check_plan(const Shape& s, bool vec)
                 std::vector<int> pair_seen(size_t(slices) * G, 0);
                 for (uint32_t b = 0; b < slices * G; ++b) {
                     uint32_t sl, member;
-                    nhwc_slice_member(b, slices, G, sl, member);
+                    nhwc_group_member(b, slices, G, sl, member);
                     CHECK(sl < slices && member < G, "slice map bounds");
                     if (sl >= slices || member >= G) continue;
                     pair_seen[size_t(sl) * G + member]++;
@@ -282,7 +282,7 @@ static void check_plan(const Shape& s, bool vec)
         IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
         for (const SVar& sv : svars) {
-            for (uint32_t G = 8; G <= 32; G *= 2) {
+            for (uint32_t G = 8; G <= 64; G *= 2) {
                 if (cv % sv.LPR != 0) continue;
                 const uint32_t slices = uint32_t(cv / sv.LPR);
                 const int64_t mg = (m + G - 1) / G;

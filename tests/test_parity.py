@@ -333,15 +333,16 @@ def test_beyond_4gib(wl):
 # row count and slice count (the plan is asserted): full and ragged members;
 # slice counts that divide by 8 (XCD-grouped map) and ones that do not
 SLICE_PLANS = [
-    # one lane per row, 256 threads: tensors under 4 MB (groups up to 8) and odd
-    # vector counts per row
+    # one lane per row, 256 threads: tensors under 4 MB (at most 2, else 4 rows
+    # per thread, groups up to 8) and odd vector counts per row
     (custom(2, 1, 8, 7, 7, layout="NHWC", dtype="f32"), "256x1x2"),
     (custom(2, 2, 20, 7, 9, layout="NHWC", dtype="f32"), "256x1x2"),
+    (custom(2, 1, 64, 40, 13, layout="NHWC", dtype="f32"), "256x1x2,group2"),
+    (custom(3, 1, 64, 80, 13, layout="NHWC", dtype="f16"), "256x1x2,group4"),
+    (custom(2, 2, 64, 80, 13, layout="NHWC", dtype="f32"), "256x1x2,group8"),
     (custom(2, 1, 8, 40, 13, layout="NHWC", dtype="f32"), "256x1x4"),
-    (custom(2, 1, 64, 80, 13, layout="NHWC", dtype="f32"), "256x1x4,group2"),
-    (custom(3, 2, 128, 80, 13, layout="NHWC", dtype="bf16"), "256x1x4,group4"),
-    (custom(2, 2, 64, 80, 13, layout="NHWC", dtype="f32"), "256x1x4,group4"),
-    (custom(3, 5, 64, 25, 33, layout="NHWC", dtype="f16"), "256x1x4,group8"),
+    (custom(2, 1, 384, 80, 13, layout="NHWC", dtype="f32"), "256x1x4,group2"),
+    (custom(2, 2, 192, 80, 13, layout="NHWC", dtype="f32"), "256x1x4,group4"),
     (custom(2, 5, 64, 25, 33, layout="NHWC", dtype="f32"), "256x1x4,group8"),
     (custom(3, 32, 256, 14, 14, layout="NHWC", dtype="bf16"), "256x1x4,group8"),
     (custom(3, 1, 8, 80, 13, layout="NHWC", dtype="bf16"), "256x1x8"),
@@ -354,34 +355,38 @@ SLICE_PLANS = [
     (custom(2, 5, 520, 80, 17, layout="NHWC", dtype="f32"), "512x1x18"),
     # two lanes per row
     (custom(2, 1, 1032, 60, 17, layout="NHWC", dtype="f32"), "512x2x4"),
+    (custom(2, 5, 192, 25, 33, layout="NHWC", dtype="f32"), "512x2x4,group8"),
+    (custom(2, 5, 64, 33, 50, layout="NHWC", dtype="f32"), "512x2x4,group16"),
+    (custom(2, 8, 64, 33, 64, layout="NHWC", dtype="f32"), "512x2x4,group32"),
     (custom(2, 1, 8, 80, 13, layout="NHWC", dtype="f32"), "512x2x8"),
-    (custom(2, 2, 8, 80, 13, layout="NHWC", dtype="f32"), "512x2x13"),
-    (custom(2, 6, 8, 7, 80, layout="NHWC", dtype="f32"), "512x2x18"),
     (custom(2, 1, 768, 60, 60, layout="NHWC", dtype="f32"), "512x2x8,group2"),
-    (custom(2, 5, 192, 25, 33, layout="NHWC", dtype="f32"), "512x2x8,group4"),
-    (custom(2, 5, 64, 33, 50, layout="NHWC", dtype="f32"), "512x2x8,group8"),
-    (custom(2, 8, 64, 33, 64, layout="NHWC", dtype="f32"), "512x2x8,group16"),
-    (custom(3, 6, 256, 50, 80, layout="NHWC", dtype="bf16"), "512x2x8,group16"),
+    (custom(2, 2, 384, 60, 60, layout="NHWC", dtype="f32"), "512x2x8,group4"),
+    (custom(2, 5, 192, 33, 50, layout="NHWC", dtype="f32"), "512x2x8,group8"),
+    (custom(2, 6, 128, 60, 80, layout="NHWC", dtype="f32"), "512x2x8,group16"),
+    (custom(2, 6, 64, 80, 80, layout="NHWC", dtype="f32"), "512x2x8,group32"),
+    (custom(2, 2, 8, 80, 13, layout="NHWC", dtype="f32"), "512x2x13"),
     (custom(2, 8, 192, 33, 64, layout="NHWC", dtype="f32"), "512x2x13,group8"),
-    (custom(2, 6, 64, 80, 80, layout="NHWC", dtype="f32"), "512x2x13,group16"),
+    (custom(2, 6, 8, 7, 80, layout="NHWC", dtype="f32"), "512x2x18"),
     # four lanes per row
     (custom(2, 1, 2064, 30, 17, layout="NHWC", dtype="f32"), "512x4x4"),
     (custom(2, 3, 1536, 7, 33, layout="NHWC", dtype="f32"), "512x4x4,group2"),
-    (custom(2, 1, 768, 30, 60, layout="NHWC", dtype="f32"), "512x4x4,group4"),
-    (custom(2, 1, 384, 60, 60, layout="NHWC", dtype="f32"), "512x4x4,group8"),
-    (custom(2, 2, 256, 60, 60, layout="NHWC", dtype="f32"), "512x4x4,group16"),
-    (custom(2, 1, 2048, 40, 13, layout="NHWC", dtype="f32"), "512x4x7"),
-    (custom(2, 1, 768, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group2"),
-    (custom(2, 2, 384, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group4"),
+    (custom(2, 1, 768, 80, 13, layout="NHWC", dtype="f32"), "512x4x4,group4"),
+    (custom(2, 2, 384, 80, 13, layout="NHWC", dtype="f32"), "512x4x4,group8"),
+    (custom(2, 5, 256, 25, 33, layout="NHWC", dtype="f32"), "512x4x4,group16"),
+    (custom(2, 5, 128, 33, 50, layout="NHWC", dtype="f32"), "512x4x4,group32"),
+    (custom(2, 1, 1536, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group2"),
+    (custom(2, 2, 768, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group4"),
     (custom(5, 64, 2048, 7, 7, layout="NHWC", dtype="bf16"), "512x4x7,group4"),
-    (custom(2, 5, 256, 25, 33, layout="NHWC", dtype="f32"), "512x4x7,group8"),
-    (custom(2, 5, 128, 33, 50, layout="NHWC", dtype="f32"), "512x4x7,group16"),
+    (custom(2, 5, 384, 25, 33, layout="NHWC", dtype="f32"), "512x4x7,group8"),
+    (custom(2, 5, 256, 33, 50, layout="NHWC", dtype="f32"), "512x4x7,group16"),
+    (custom(2, 8, 128, 33, 64, layout="NHWC", dtype="f32"), "512x4x7,group32"),
     (custom(2, 2, 1536, 80, 13, layout="NHWC", dtype="f32"), "512x4x13,group2"),
     (custom(2, 5, 768, 25, 33, layout="NHWC", dtype="f32"), "512x4x13,group4"),
     (custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"), "512x4x13,group4"),
     (custom(2, 5, 384, 33, 50, layout="NHWC", dtype="f32"), "512x4x13,group8"),
     (custom(2, 8, 256, 33, 64, layout="NHWC", dtype="f32"), "512x4x13,group16"),
     (custom(3, 5, 512, 50, 80, layout="NHWC", dtype="bf16"), "512x4x13,group16"),
+    (custom(2, 6, 128, 80, 80, layout="NHWC", dtype="f32"), "512x4x13,group32"),
     # other storage types and activations
     (custom(3, 8, 2048, 10, 25, layout="NHWC", dtype="f16"), "512x4x4,group4"),
     (custom(5, 8, 2048, 10, 25, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
@@ -389,11 +394,11 @@ SLICE_PLANS = [
     (custom(4, 5, 768, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
      "512x4x13,group4"),
     (custom(4, 5, 256, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
-     "512x4x7,group8"),
+     "512x4x4,group16"),
     (custom(4, 3, 512, 12, 12, layout="NHWC", dtype="bf16", act="elu", act_param=0.5),
      "256x1x2"),
     (custom(3, 5, 256, 20, 20, layout="NHWC", dtype="bf16", act="identity", act_param=0.0),
-     "256x1x4,group2"),
+     "256x1x2,group4"),
     (custom(2, 2, 256, 60, 60, layout="NHWC", dtype="f32", act="identity", act_param=0.0),
      "512x4x4,group16"),
 ]
@@ -431,7 +436,7 @@ STREAM_PLANS = [
     (custom(2, 1, 128, 400, 400, layout="NHWC", dtype="f32"),
      "slice_streamed(512x4x28+4,group32)", _SPLIT_BWD),
     (custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x2x28+4,group32)", "slice_streamed(512x2x14+2,group32)"),
+     "slice_streamed(512x4x28+4,group64)", "slice_streamed(512x4x14+2,group64)"),
     (custom(4, 1, 1024, 180, 170, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
      "slice_streamed(512x4x28+4,group8)", "split(reduce:306x256,apply:2048x256,vec16)"),
     (custom(4, 1, 128, 410, 400, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
