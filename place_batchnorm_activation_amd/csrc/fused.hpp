@@ -64,7 +64,7 @@
 #ifndef IABN_STREAM_NHWC_VARIANTS
 #define IABN_STREAM_NHWC_VARIANTS(X) \
     X(0, 512, 4, 28, 4, 14, 2)       \
-    X(1, 512, 2, 28, 4, 14, 2)
+    X(1, 512, 8, 28, 4, 14, 2)
 #endif
 
 // Channel-resident NCHW kernels on single elements, for shapes the 16-byte
@@ -236,11 +236,12 @@ inline NhwcChoice fused_nhwc_pick(const Plan& p, int64_t max_grid)
     return none;
 }
 
-// Streamed slice plan for an NHWC map (variant -1: not used): the widest LPR of
-// at least 4 (measured: two lanes per row lost to the split path on 64-channel
-// 112x112 maps) whose slices, in groups of a power of two from 8 to 64, make a
-// grid of exactly max_grid workgroups (every CU streams), every member getting
-// rows.  Taken where the resident kernels cannot hold the rows.
+// Streamed slice plan for an NHWC map (variant -1: not used): eight lanes per row
+// (each workgroup writes whole 128-byte lines: the 2x256x512x512 forward went from
+// 138 to 128 us), else four (two lost to the split path on 64-channel 112x112
+// maps), whose slices, in groups of a power of two from 8 to 64, make a grid of
+// exactly max_grid workgroups (every CU streams), every member getting rows.
+// Taken where the resident kernels cannot hold the rows.
 inline NhwcChoice fused_stream_pick(const Plan& p, int64_t max_grid)
 {
     NhwcChoice none;

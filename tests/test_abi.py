@@ -174,14 +174,19 @@ def test_plan_choice_for_the_workloads():
     assert d(16, 512, 28, 28, "NCHW", iabn.F32, "elu").startswith(
         "forward=channel_resident(256x13) backward=channel_resident(256x13,dy_resident)")
     assert d(2, 4, 8, 8, "NCHW", iabn.F32, "leaky_relu").startswith("forward=channel_resident")
-    # a map too large to hold: 256 workgroups in groups of 32 keep part of it in
-    # registers and stream the rest
+    # a map too large to hold: 256 workgroups in groups of 64, eight lanes per row,
+    # keep part of it in registers and stream the rest
     assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_streamed(512x4x28+4,group32) " \
+        "forward=slice_streamed(512x8x28+4,group64) " \
         "backward=split(reduce:512x256,apply:2048x256,vec16)"
     # ... the backward too while half its rows stay resident
     assert d(32, 256, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_streamed(512x4x28+4,group32) backward=slice_streamed(512x4x14+2,group32)"
+        "forward=slice_streamed(512x8x28+4,group64) backward=slice_streamed(512x8x14+2,group64)"
+    assert d(4, 2048, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_streamed(512x8x28+4,group8) backward=slice_streamed(512x8x14+2,group8)"
+    # four lanes per row where 16-byte vectors make 16 per pixel
+    assert d(1, 128, 360, 360, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_streamed(512x4x28+4,group64) backward=slice_streamed(512x4x14+2,group64)"
     # ... but not two lanes per row: split
     assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
     assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \

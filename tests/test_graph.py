@@ -23,7 +23,7 @@ CASES = [
     workloads.config(5).with_shape(16, 512, 7, 7),                 # NHWC slice-resident
     workloads.config(3).with_shape(5, 256, 20, 20),                # NHWC slice-resident, group 2
     workloads.config(3).with_shape(5, 512, 50, 80),                # ... group 16, two levels
-    workloads.config(3).with_shape(1, 256, 300, 300),              # streamed, group 32
+    workloads.config(3).with_shape(1, 256, 300, 300),              # streamed, group 64
     workloads.config(3).with_shape(2, 32, 96, 96),                 # NHWC split
     workloads.config(4).with_shape(2, 5, 17, 19),                  # NCHW resident, elements
     workloads.config(4).with_shape(2, 3, 150, 151),                # NCHW split, scalar

@@ -425,30 +425,32 @@ def test_slice_resident_variants(wl):
 
 
 # Streamed slice kernels (NHWC maps too large to hold): 256 workgroups, groups
-# of 8 to 32; threads keep 28 rows (forward) or 14 (backward) resident and
+# of 8 to 64, eight lanes per row (four where 16 vectors make a pixel); threads keep 28 rows (forward) or 14 (backward) resident and
 # stream the rest.  The backward streams only while at least half its rows stay
 # resident (else the split kernels).  Forward cases stream one to three chunks,
 # backward cases up to four.
 _SPLIT_BWD = "split(reduce:512x256,apply:2048x256,vec16)"
 STREAM_PLANS = [
     (custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x4x28+4,group32)", _SPLIT_BWD),
+     "slice_streamed(512x8x28+4,group64)", _SPLIT_BWD),
     (custom(2, 1, 128, 400, 400, layout="NHWC", dtype="f32"),
-     "slice_streamed(512x4x28+4,group32)", _SPLIT_BWD),
+     "slice_streamed(512x8x28+4,group64)", _SPLIT_BWD),
     (custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),
      "slice_streamed(512x4x28+4,group64)", "slice_streamed(512x4x14+2,group64)"),
     (custom(4, 1, 1024, 180, 170, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
-     "slice_streamed(512x4x28+4,group8)", "split(reduce:306x256,apply:2048x256,vec16)"),
-    (custom(4, 1, 128, 410, 400, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
-     "slice_streamed(512x4x28+4,group32)", _SPLIT_BWD),
+     "slice_streamed(512x8x28+4,group16)", "split(reduce:306x256,apply:2048x256,vec16)"),
+    (custom(4, 1, 64, 600, 600, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
+     "slice_streamed(512x4x28+4,group64)", _SPLIT_BWD),
     (custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x4x28+4,group32)", "slice_streamed(512x4x14+2,group32)"),
+     "slice_streamed(512x8x28+4,group64)", "slice_streamed(512x8x14+2,group64)"),
     (custom(2, 1, 128, 300, 310, layout="NHWC", dtype="f32"),
-     "slice_streamed(512x4x28+4,group32)", "slice_streamed(512x4x14+2,group32)"),
+     "slice_streamed(512x8x28+4,group64)", "slice_streamed(512x8x14+2,group64)"),
     (custom(4, 1, 1024, 130, 130, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
-     "slice_streamed(512x4x28+4,group8)", "slice_streamed(512x4x14+2,group8)"),
-    (custom(3, 2, 256, 200, 230, layout="NHWC", dtype="bf16", act="identity", act_param=0.0),
-     "slice_streamed(512x4x28+4,group32)", "slice_streamed(512x4x14+2,group32)"),
+     "slice_streamed(512x8x28+4,group16)", "slice_streamed(512x8x14+2,group16)"),
+    (custom(3, 3, 512, 100, 100, layout="NHWC", dtype="bf16", act="identity", act_param=0.0),
+     "slice_streamed(512x8x28+4,group32)", "slice_streamed(512x8x14+2,group32)"),
+    (custom(3, 1, 2048, 100, 100, layout="NHWC", dtype="bf16"),
+     "slice_streamed(512x8x28+4,group8)", "slice_streamed(512x8x14+2,group8)"),
 ]
 
 
@@ -519,7 +521,8 @@ OUTLIER = [custom(2, 4, 32, 16, 16),                                   # NCHW ch
            custom(2, 4, 96, 25, 33, layout="NHWC", dtype="f32"),       # (groups of 4)
            custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"),    # 4 lanes, group 4
            custom(2, 8, 256, 33, 64, layout="NHWC", dtype="f32"),      # group 16, two levels
-           custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),   # streamed, group 32
+           custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),   # streamed, 8 lanes
+           custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),   # streamed, 4 lanes
            custom(2, 2, 16, 80, 80, layout="NHWC", dtype="f32")]       # NHWC split
 
 
