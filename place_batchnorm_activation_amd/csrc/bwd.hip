@@ -28,8 +28,9 @@ namespace iabn {
 #endif
 constexpr int kUnrollB = IABN_REDUCE_UNROLL;
 // NHWC reduction: row groups of y and dy in flight per thread, per pipeline stage
+// (with one workgroup per CU, 4 ran faster than 8: fewer distinct addresses in flight)
 #ifndef IABN_NHWC_REDUCE_UNROLL
-#define IABN_NHWC_REDUCE_UNROLL 8
+#define IABN_NHWC_REDUCE_UNROLL 4
 #endif
 constexpr int kUnrollN = IABN_NHWC_REDUCE_UNROLL;
 
@@ -505,9 +506,9 @@ static void launch_reduce_dva(const Plan& pl, const void* y, const void* dy, con
                            dim3(kThreads), 0, s, y, dy, pl.C, pl.HW, pl.m, pl.unit, pl.P, beta, a,
                            ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
     else
-        hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT, DX>), dim3(pl.reduce_blocks),
+        hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT, DX>), dim3(pl.reduce_blocks_bwd),
                            dim3(kThreads), 0, s, y, dy, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit,
-                           pl.P, beta, a, ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
+                           pl.P_bwd, beta, a, ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
 }
 
 template <bool DX>
@@ -537,7 +538,7 @@ void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const
     const float ia = act == kIdentity ? 1.f : 1.f / a;
     launch_reduce<false>(pl, y, dy, beta, act, a, ia, pa, pb, FrozenDx{}, s);
     hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
-                       dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta, invstd,
+                       dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P_bwd, pa, pb, gamma, beta, invstd,
                        static_cast<const float*>(nullptr), 0.f, dgamma, dbeta, consts);
 }
 
@@ -554,7 +555,7 @@ void launch_backward_eval_grads(const Plan& pl, const void* y, const void* dy, v
     launch_reduce<true>(pl, y, dy, beta, act, a, ia, pa, pb, FrozenDx{dx, gamma, running_var, eps},
                         s);
     hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
-                       dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P, pa, pb, gamma, beta,
+                       dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P_bwd, pa, pb, gamma, beta,
                        static_cast<const float*>(nullptr), running_var, eps, dgamma, dbeta,
                        consts);
 }

@@ -75,6 +75,9 @@ struct Plan {
     int tpr = 1;         // NHWC: threads per row
     int64_t slices = 1;  // NHWC: channel slices
     int64_t reduce_blocks = 0;
+    // the backward's reduction (NHWC: its own, smaller grid; NCHW: P, reduce_blocks)
+    int64_t P_bwd = 1;
+    int64_t reduce_blocks_bwd = 0;
     // elementwise tiling
     int64_t apply_blocks = 0;
     bool fixed_col = false;  // NHWC: each thread keeps one channel group for the whole walk
@@ -118,6 +121,14 @@ constexpr int64_t kReduceBlocksTarget = 2048;
 #define IABN_NHWC_REDUCE_BLOCKS 512
 #endif
 constexpr int64_t kNhwcReduceBlocks = IABN_NHWC_REDUCE_BLOCKS;
+// The NHWC backward reduction reads y and dy together: one workgroup per CU
+// (each with four row groups of both in flight) keeps the window of addresses
+// in flight narrow, which measured faster than two per CU (2x256x512x512 bf16:
+// 104 against 115 us cold) or more.
+#ifndef IABN_NHWC_BWD_REDUCE_BLOCKS
+#define IABN_NHWC_BWD_REDUCE_BLOCKS 256
+#endif
+constexpr int64_t kNhwcBwdReduceBlocks = IABN_NHWC_BWD_REDUCE_BLOCKS;
 
 inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, int dtype, bool vec)
 {
@@ -139,6 +150,8 @@ inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, in
         p.unit = ceil_div(vc, P) * V;
         p.P = ceil_div(p.m, p.unit);
         p.reduce_blocks = C * p.P;
+        p.P_bwd = p.P;
+        p.reduce_blocks_bwd = p.reduce_blocks;
     } else {
         const int64_t cv = C / V;                            // vectors per row
         // partial traffic (8 B per channel and partial) kept to ~2% of the data
@@ -158,12 +171,15 @@ inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, in
             slices = ceil_div(cv, tpr);
             P = choose_P(tpr);
         }
+        const int64_t P_bwd = min64(P, max64(1, ceil_div(kNhwcBwdReduceBlocks, slices)));
         P = min64(P, max64(1, ceil_div(kNhwcReduceBlocks, slices)));
         p.tpr = tpr;
         p.slices = slices;
         p.unit = groups(tpr);                               // row groups in all
         p.P = min64(P, p.unit);
         p.reduce_blocks = slices * p.P;
+        p.P_bwd = min64(P_bwd, p.unit);
+        p.reduce_blocks_bwd = slices * p.P_bwd;
     }
 
     const int64_t nvec = p.numel / V;
@@ -182,7 +198,7 @@ inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, in
     // that a stage planned for the vector path and one planned for the scalar path
     // (different pointer alignment) agree on where they are.
     size_t off = 0;
-    const size_t part_bytes = (size_t)(p.P * C) * sizeof(float);
+    const size_t part_bytes = (size_t)(max64(p.P, p.P_bwd) * C) * sizeof(float);
     p.off_const = off;  off = (size_t)align_up((int64_t)(off + (size_t)C * 16), 256);
     p.off_part_a = off; off = (size_t)align_up((int64_t)(off + part_bytes), 256);
     p.off_part_b = off; off = (size_t)align_up((int64_t)(off + part_bytes), 256);

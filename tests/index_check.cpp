@@ -41,13 +41,16 @@ static void check_plan(const Shape& s, bool vec)
         CHECK(pl.P * pl.unit >= m && (pl.P - 1) * pl.unit < m, "partials cover m exactly");
     CHECK(pl.reduce_blocks < (int64_t(1) << 31) && pl.apply_blocks < (int64_t(1) << 31), "grid");
     CHECK(pl.off_const == 0 && pl.off_part_a >= size_t(C) * 16, "const section");
-    CHECK(pl.off_part_b >= pl.off_part_a + size_t(pl.P * C) * 4, "part a section");
-    CHECK(pl.off_count >= pl.off_part_b + size_t(pl.P * C) * 4, "part b section");
+    CHECK(pl.P_bwd >= 1 && (pl.layout == kNHWC || pl.P_bwd == pl.P), "backward partials");
+    CHECK(pl.reduce_blocks_bwd < (int64_t(1) << 31), "backward grid");
+    const int64_t Pmax = std::max(pl.P, pl.P_bwd);
+    CHECK(pl.off_part_b >= pl.off_part_a + size_t(Pmax * C) * 4, "part a section");
+    CHECK(pl.off_count >= pl.off_part_b + size_t(Pmax * C) * 4, "part b section");
     CHECK(pl.bytes >= pl.off_count + size_t(pl.P) * 4, "count section");
     CHECK(pl.off_part_a % 256 == 0 && pl.off_part_b % 256 == 0, "alignment");
 
     std::vector<uint8_t> seen(size_t(nvec), 0);
-    // ---- reduction kernels (statistics and backward sums share the tiling)
+    // ---- reduction kernels (the statistics; NCHW backward sums share the tiling)
     if (pl.layout == kNCHW) {
         const int64_t HWv = pl.HW / V;
         CHECK(pl.HW % V == 0 && pl.unit % V == 0, "NCHW vector alignment");
@@ -70,38 +73,48 @@ static void check_plan(const Shape& s, bool vec)
                 }
             }
         }
+        for (int64_t i = 0; i < nvec; ++i)
+            CHECK(seen[size_t(i)] == 1, "reduction visits vector %lld %d times", (long long)i,
+                  int(seen[size_t(i)]));
     } else {
-        const int64_t Cv = C / V;
-        CHECK(C % V == 0, "NHWC vector alignment");
-        CHECK(kThreads % pl.tpr == 0, "tpr divides the workgroup");
-        CHECK(pl.slices * pl.tpr >= Cv, "slices cover the row");
-        CHECK(pl.reduce_blocks == pl.slices * pl.P, "NHWC grid");
-        const int rpi = kThreads / pl.tpr;
-        CHECK(pl.unit == (m + rpi - 1) / rpi, "row groups");
-        CHECK(pl.P <= pl.unit, "no empty partial");
-        for (int64_t b = 0; b < pl.reduce_blocks; ++b) {
-            const int64_t p = b / pl.slices, sl = b - p * pl.slices;
-            for (int t = 0; t < kThreads; ++t) {
-                const int rs = t / pl.tpr;
-                const int64_t col = sl * pl.tpr + (t - rs * pl.tpr);
-                if (col >= Cv) continue;
-                CHECK(p * C + col * V + V <= pl.P * C, "partial index");
-                for (int64_t g = p; g < pl.unit; g += pl.P) {
-                    const int64_t r = g * rpi + rs;
-                    if (r >= m) continue;
-                    const int64_t a = r * Cv + col;
-                    CHECK(a >= 0 && a < nvec, "NHWC reduce bounds");
-                    if (a >= 0 && a < nvec) seen[size_t(a)]++;
+        // the statistics (P partials) and the backward sums (P_bwd) walk the same
+        // row groups with their own grid
+        auto walk = [&](int64_t P, int64_t blocks, const char* what) {
+            std::fill(seen.begin(), seen.end(), 0);
+            const int64_t Cv = C / V;
+            CHECK(C % V == 0, "NHWC vector alignment");
+            CHECK(kThreads % pl.tpr == 0, "tpr divides the workgroup");
+            CHECK(pl.slices * pl.tpr >= Cv, "slices cover the row");
+            CHECK(blocks == pl.slices * P, "NHWC grid (%s)", what);
+            const int rpi = kThreads / pl.tpr;
+            CHECK(pl.unit == (m + rpi - 1) / rpi, "row groups");
+            CHECK(P <= pl.unit, "no empty partial (%s)", what);
+            for (int64_t b = 0; b < blocks; ++b) {
+                const int64_t p = b / pl.slices, sl = b - p * pl.slices;
+                for (int t = 0; t < kThreads; ++t) {
+                    const int rs = t / pl.tpr;
+                    const int64_t col = sl * pl.tpr + (t - rs * pl.tpr);
+                    if (col >= Cv) continue;
+                    CHECK(p * C + col * V + V <= Pmax * C, "partial index (%s)", what);
+                    for (int64_t g = p; g < pl.unit; g += P) {
+                        const int64_t r = g * rpi + rs;
+                        if (r >= m) continue;
+                        const int64_t a = r * Cv + col;
+                        CHECK(a >= 0 && a < nvec, "NHWC reduce bounds (%s)", what);
+                        if (a >= 0 && a < nvec) seen[size_t(a)]++;
+                    }
+                    // LDS tree partners stay inside the workgroup
+                    for (int st = rpi / 2; st >= 1; st >>= 1)
+                        if (rs < st) CHECK(t + st * pl.tpr < kThreads, "LDS partner");
                 }
-                // LDS tree partners stay inside the workgroup
-                for (int st = rpi / 2; st >= 1; st >>= 1)
-                    if (rs < st) CHECK(t + st * pl.tpr < kThreads, "LDS partner");
             }
-        }
+            for (int64_t i = 0; i < nvec; ++i)
+                CHECK(seen[size_t(i)] == 1, "%s visits vector %lld %d times", what,
+                      (long long)i, int(seen[size_t(i)]));
+        };
+        walk(pl.P, pl.reduce_blocks, "statistics");
+        walk(pl.P_bwd, pl.reduce_blocks_bwd, "backward sums");
     }
-    for (int64_t i = 0; i < nvec; ++i)
-        CHECK(seen[size_t(i)] == 1, "reduction visits vector %lld %d times", (long long)i,
-              int(seen[size_t(i)]));
 
     // ---- elementwise kernels
     std::fill(seen.begin(), seen.end(), 0);

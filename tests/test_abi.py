@@ -178,7 +178,7 @@ def test_plan_choice_for_the_workloads():
     # keep part of it in registers and stream the rest
     assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_streamed(512x8x28+4,group64) " \
-        "backward=split(reduce:512x256,apply:2048x256,vec16)"
+        "backward=split(reduce:256x256,apply:2048x256,vec16)"
     # ... the backward too while half its rows stay resident
     assert d(32, 256, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_streamed(512x8x28+4,group64) backward=slice_streamed(512x8x14+2,group64)"
@@ -187,8 +187,10 @@ def test_plan_choice_for_the_workloads():
     # four lanes per row where 16-byte vectors make 16 per pixel
     assert d(1, 128, 360, 360, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_streamed(512x4x28+4,group64) backward=slice_streamed(512x4x14+2,group64)"
-    # ... but not two lanes per row: split
-    assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+    # ... but not two lanes per row: split, the backward sums on one workgroup per CU
+    assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=split(stats:512x256,apply:2048x256,vec16) " \
+        "backward=split(reduce:256x256,apply:2048x256,vec16)"
     assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_resident(512x4x7,group4) backward=slice_resident(512x4x7,group4)"
     # too many rows for a workgroup to hold: split
