@@ -507,7 +507,7 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         snprintf(fwd, sizeof fwd, "slice_streamed(%s)", sd_f);
     } else {
         snprintf(fwd, sizeof fwd, "split(stats:%lldx%d,apply:%lldx%d,%s)",
-                 (long long)p.reduce_blocks, kThreads, (long long)p.apply_blocks, kThreads,
+                 (long long)p.reduce_blocks, kThreads, (long long)apply_grid(p, act), kThreads,
                  p.vec ? "vec16" : "scalar");
     }
     if (p.fused_bwd_variant >= 0) {
@@ -529,7 +529,7 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
         snprintf(bwd, sizeof bwd, "slice_streamed(%s)", sd_b);
     } else {
         snprintf(bwd, sizeof bwd, "split(reduce:%lldx%d,apply:%lldx%d,%s)",
-                 (long long)p.reduce_blocks_bwd, kThreads, (long long)p.apply_blocks, kThreads,
+                 (long long)p.reduce_blocks_bwd, kThreads, (long long)apply_grid(p, act), kThreads,
                  p.vec ? "vec16" : "scalar");
     }
     return snprintf(buf, len, "forward=%s backward=%s", fwd, bwd);

@@ -498,7 +498,7 @@ template <int DT, int V, int ACT, typename CS>
 static void launch_apply_dva(const Plan& pl, void* x, CS cs, float a, hipStream_t s)
 {
     const int64_t nvec = pl.numel / V;
-    const dim3 grid(unsigned(pl.apply_blocks));
+    const dim3 grid(unsigned(apply_grid(pl, ACT)));
     if (pl.layout == kNCHW)
         hipLaunchKernelGGL((k_apply_nchw<DT, V, ACT, CS>), grid, dim3(kThreads), 0, s, x, nvec,
                            pl.C, pl.HW / V, cs, a);

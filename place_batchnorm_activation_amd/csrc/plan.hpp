@@ -80,6 +80,7 @@ struct Plan {
     int64_t reduce_blocks_bwd = 0;
     // elementwise tiling
     int64_t apply_blocks = 0;
+    int64_t apply_blocks_elu = 0;   // the same grid for ELU (more arithmetic to hide)
     bool fixed_col = false;  // NHWC: each thread keeps one channel group for the whole walk
     // channel-resident NCHW kernels (-1: not used for this problem)
     int fused_variant = -1;
@@ -100,6 +101,11 @@ struct Plan {
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// The elementwise grid for an activation.
+inline int64_t apply_grid(const Plan& p, int act)
+{
+    return act == kElu ? p.apply_blocks_elu : p.apply_blocks;
+}
 inline int64_t align_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 inline int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
@@ -110,9 +116,20 @@ inline int64_t gcd64(int64_t a, int64_t b)
     return a;
 }
 
-// Workgroups an elementwise kernel launches: enough to keep every CU busy with
-// several waves while each thread still walks a few vectors.
-constexpr int64_t kApplyBlocksMax = 2048;
+// Workgroups an elementwise kernel launches at most.  Two per CU for leaky ReLU
+// and identity: like the reductions, the elementwise passes stream faster with a
+// narrower window of addresses in flight (the split path's steps on ResNet-50
+// shapes, summed: 1366 us at 512 workgroups, 1413 at 1024, 1452 at 2048).  ELU's
+// transcendentals need more waves to hide them (bf16 NHWC dx pass on
+// 2x256x512x512: 164 us at 2048 workgroups, 185 at 512), so it keeps 2048.
+#ifndef IABN_APPLY_BLOCKS_MAX
+#define IABN_APPLY_BLOCKS_MAX 512
+#endif
+#ifndef IABN_APPLY_BLOCKS_MAX_ELU
+#define IABN_APPLY_BLOCKS_MAX_ELU 2048
+#endif
+constexpr int64_t kApplyBlocksMax = IABN_APPLY_BLOCKS_MAX;
+constexpr int64_t kApplyBlocksMaxElu = IABN_APPLY_BLOCKS_MAX_ELU;
 // Workgroups a reduction aims for.
 constexpr int64_t kReduceBlocksTarget = 2048;
 // NHWC reductions: fewer, longer-lived workgroups walking row groups with a
@@ -184,12 +201,14 @@ inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, in
 
     const int64_t nvec = p.numel / V;
     p.apply_blocks = max64(1, min64(kApplyBlocksMax, ceil_div(nvec, kThreads)));
+    p.apply_blocks_elu = max64(1, min64(kApplyBlocksMaxElu, ceil_div(nvec, kThreads)));
     if (layout == kNHWC) {
         // keep each thread on one channel group: stride (blocks*256) % (C/V) == 0
         const int64_t cv = C / V;
         const int64_t need = cv / gcd64(cv, kThreads);      // blocks must be a multiple of this
-        if (need <= kApplyBlocksMax) {
+        if (need <= min64(kApplyBlocksMax, kApplyBlocksMaxElu)) {
             p.apply_blocks = max64(need, (p.apply_blocks / need) * need);
+            p.apply_blocks_elu = max64(need, (p.apply_blocks_elu / need) * need);
             p.fixed_col = true;
         }
     }

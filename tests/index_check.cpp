@@ -116,38 +116,43 @@ static void check_plan(const Shape& s, bool vec)
         walk(pl.P_bwd, pl.reduce_blocks_bwd, "backward sums");
     }
 
-    // ---- elementwise kernels
-    std::fill(seen.begin(), seen.end(), 0);
-    const int64_t stride = pl.apply_blocks * kThreads;
-    if (pl.layout == kNCHW) {
-        const int64_t HWv = pl.HW / V;
-        for (int64_t t0 = 0; t0 < stride; ++t0) {
-            int64_t v = t0;
-            FlatNCHWWalk w;
-            w.init(v < nvec ? v : 0, C, HWv, stride);
-            for (; v < nvec; v += stride) {
-                CHECK(w.c == (v / HWv) % C, "FlatNCHWWalk v=%lld", (long long)v);
-                CHECK(w.c >= 0 && w.c < C, "channel bounds");
-                seen[size_t(v)]++;
-                w.step();
+    // ---- elementwise kernels (the grid for leaky ReLU and identity, and for ELU)
+    CHECK(pl.apply_blocks_elu < (int64_t(1) << 31), "ELU grid");
+    auto elementwise = [&](int64_t blocks) {
+        std::fill(seen.begin(), seen.end(), 0);
+        const int64_t stride = blocks * kThreads;
+        if (pl.layout == kNCHW) {
+            const int64_t HWv = pl.HW / V;
+            for (int64_t t0 = 0; t0 < stride; ++t0) {
+                int64_t v = t0;
+                FlatNCHWWalk w;
+                w.init(v < nvec ? v : 0, C, HWv, stride);
+                for (; v < nvec; v += stride) {
+                    CHECK(w.c == (v / HWv) % C, "FlatNCHWWalk v=%lld", (long long)v);
+                    CHECK(w.c >= 0 && w.c < C, "channel bounds");
+                    seen[size_t(v)]++;
+                    w.step();
+                }
+            }
+        } else {
+            const int64_t Cv = C / V;
+            if (pl.fixed_col) CHECK(stride % Cv == 0, "fixed channel group needs stride %% Cv == 0");
+            for (int64_t t0 = 0; t0 < stride; ++t0) {
+                if (t0 >= nvec) break;
+                const int64_t c0 = (t0 % Cv) * V;
+                CHECK(c0 + V - 1 < C, "channel group bounds");
+                for (int64_t v = t0; v < nvec; v += stride) {
+                    if (pl.fixed_col) CHECK((v % Cv) * V == c0, "fixed channel group");
+                    seen[size_t(v)]++;
+                }
             }
         }
-    } else {
-        const int64_t Cv = C / V;
-        if (pl.fixed_col) CHECK(stride % Cv == 0, "fixed channel group needs stride %% Cv == 0");
-        for (int64_t t0 = 0; t0 < stride; ++t0) {
-            if (t0 >= nvec) break;
-            const int64_t c0 = (t0 % Cv) * V;
-            CHECK(c0 + V - 1 < C, "channel group bounds");
-            for (int64_t v = t0; v < nvec; v += stride) {
-                if (pl.fixed_col) CHECK((v % Cv) * V == c0, "fixed channel group");
-                seen[size_t(v)]++;
-            }
-        }
-    }
-    for (int64_t i = 0; i < nvec; ++i)
-        CHECK(seen[size_t(i)] == 1, "elementwise visits vector %lld %d times", (long long)i,
-              int(seen[size_t(i)]));
+        for (int64_t i = 0; i < nvec; ++i)
+            CHECK(seen[size_t(i)] == 1, "elementwise visits vector %lld %d times", (long long)i,
+                  int(seen[size_t(i)]));
+    };
+    elementwise(pl.apply_blocks);
+    elementwise(pl.apply_blocks_elu);
 
     // ---- channel-resident NCHW kernels: every variant that could hold the channel
     if (pl.layout == kNCHW && pl.vec && numel * pl.esize < (int64_t(1) << 32)) {

@@ -178,7 +178,7 @@ def test_plan_choice_for_the_workloads():
     # keep part of it in registers and stream the rest
     assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_streamed(512x8x28+4,group64) " \
-        "backward=split(reduce:256x256,apply:2048x256,vec16)"
+        "backward=split(reduce:256x256,apply:512x256,vec16)"
     # ... the backward too while half its rows stay resident
     assert d(32, 256, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_streamed(512x8x28+4,group64) backward=slice_streamed(512x8x14+2,group64)"
@@ -189,8 +189,8 @@ def test_plan_choice_for_the_workloads():
         "forward=slice_streamed(512x4x28+4,group64) backward=slice_streamed(512x4x14+2,group64)"
     # ... but not two lanes per row: split, the backward sums on one workgroup per CU
     assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=split(stats:512x256,apply:2048x256,vec16) " \
-        "backward=split(reduce:256x256,apply:2048x256,vec16)"
+        "forward=split(stats:512x256,apply:512x256,vec16) " \
+        "backward=split(reduce:256x256,apply:512x256,vec16)"
     assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_resident(512x4x7,group4) backward=slice_resident(512x4x7,group4)"
     # too many rows for a workgroup to hold: split

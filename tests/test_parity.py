@@ -429,7 +429,8 @@ def test_slice_resident_variants(wl):
 # stream the rest.  The backward streams only while at least half its rows stay
 # resident (else the split kernels).  Forward cases stream one to three chunks,
 # backward cases up to four.
-_SPLIT_BWD = "split(reduce:256x256,apply:2048x256,vec16)"
+_SPLIT_BWD = "split(reduce:256x256,apply:512x256,vec16)"
+_SPLIT_BWD_ELU = "split(reduce:256x256,apply:2048x256,vec16)"   # ELU: a wider dx grid
 STREAM_PLANS = [
     (custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),
      "slice_streamed(512x8x28+4,group64)", _SPLIT_BWD),
@@ -438,9 +439,9 @@ STREAM_PLANS = [
     (custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),
      "slice_streamed(512x4x28+4,group64)", "slice_streamed(512x4x14+2,group64)"),
     (custom(4, 1, 1024, 180, 170, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
-     "slice_streamed(512x8x28+4,group16)", _SPLIT_BWD),
+     "slice_streamed(512x8x28+4,group16)", _SPLIT_BWD_ELU),
     (custom(4, 1, 64, 600, 600, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
-     "slice_streamed(512x4x28+4,group64)", _SPLIT_BWD),
+     "slice_streamed(512x4x28+4,group64)", _SPLIT_BWD_ELU),
     (custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16"),
      "slice_streamed(512x8x28+4,group64)", "slice_streamed(512x8x14+2,group64)"),
     (custom(2, 1, 128, 300, 310, layout="NHWC", dtype="f32"),
