@@ -131,7 +131,10 @@ inline int64_t gcd64(int64_t a, int64_t b)
 constexpr int64_t kApplyBlocksMax = IABN_APPLY_BLOCKS_MAX;
 constexpr int64_t kApplyBlocksMaxElu = IABN_APPLY_BLOCKS_MAX_ELU;
 // Workgroups a reduction aims for.
-constexpr int64_t kReduceBlocksTarget = 2048;
+#ifndef IABN_REDUCE_BLOCKS_TARGET
+#define IABN_REDUCE_BLOCKS_TARGET 2048
+#endif
+constexpr int64_t kReduceBlocksTarget = IABN_REDUCE_BLOCKS_TARGET;
 // NHWC reductions: fewer, longer-lived workgroups walking row groups with a
 // stride; two per CU.
 #ifndef IABN_NHWC_REDUCE_BLOCKS
