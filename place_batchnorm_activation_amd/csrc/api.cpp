@@ -123,7 +123,7 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
                 p.nhwc_group = sc.group;
                 if (stream_bwd_worthwhile(p, sc.variant, sc.group)) p.stream_bwd_variant = sc.variant;
                 switch (sc.variant) {
-#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) case ID: lpr = LPR; break;
+#define IABN_ROW(ID, T, LPR, NRF, LF, UF, NRB, LB, UB) case ID: lpr = LPR; break;
                     IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
                 default: break;
@@ -475,10 +475,12 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
     }
     char sd_f[48] = "", sd_b[48] = "";
     switch (p.stream_variant) {
-#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB)                                             \
-    case ID:                                                                          \
-        snprintf(sd_f, sizeof sd_f, "%dx%dx%d+%d,group%d", T, LPR, NRF, UF, p.nhwc_group); \
-        snprintf(sd_b, sizeof sd_b, "%dx%dx%d+%d,group%d", T, LPR, NRB, UB, p.nhwc_group); \
+#define IABN_ROW(ID, T, LPR, NRF, LF, UF, NRB, LB, UB)                                   \
+    case ID:                                                                            \
+        snprintf(sd_f, sizeof sd_f, "%dx%dx(%d+%d)+%d,group%d", T, LPR, NRF, LF, UF,       \
+                 p.nhwc_group);                                                         \
+        snprintf(sd_b, sizeof sd_b, "%dx%dx(%d+%d)+%d,group%d", T, LPR, NRB, LB, UB,       \
+                 p.nhwc_group);                                                         \
         break;
         IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW

@@ -57,14 +57,16 @@
     X(12, 512, 4, 13)
 #endif
 
-// Streamed slice kernels (NHWC maps too large to hold).  X(id, T, LPR, NRF, UF,
-// NRB, UB): T threads, LPR lanes per row; the forward keeps NRF rows per thread
-// resident and streams the rest UF rows per thread at a time, the backward NRB
-// and UB (y and dy both).
+// Streamed slice kernels (NHWC maps too large to hold).  X(id, T, LPR, NRF, LF,
+// UF, NRB, LB, UB): T threads, LPR lanes per row; the forward keeps NRF rows per
+// thread in registers and the next LF in LDS, and streams the rest UF rows per
+// thread at a time; the backward likewise with NRB, LB and UB (y and dy both).
+// LF and LB are multiples of UF and UB; the LDS rows take 64 KB, beside up to 72
+// KB for the scatter and the two-level exchange.
 #ifndef IABN_STREAM_NHWC_VARIANTS
-#define IABN_STREAM_NHWC_VARIANTS(X) \
-    X(0, 512, 4, 28, 4, 14, 2)       \
-    X(1, 512, 8, 28, 4, 14, 2)
+#define IABN_STREAM_NHWC_VARIANTS(X)   \
+    X(0, 512, 4, 28, 8, 4, 14, 4, 2)   \
+    X(1, 512, 8, 28, 8, 4, 14, 4, 2)
 #endif
 
 // Channel-resident NCHW kernels on single elements, for shapes the 16-byte
@@ -250,7 +252,7 @@ inline NhwcChoice fused_stream_pick(const Plan& p, int64_t max_grid)
     const int64_t cv = p.C / p.V;
     struct Row { int id, T, LPR; };
     static const Row tbl[] = {
-#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) {ID, T, LPR},
+#define IABN_ROW(ID, T, LPR, NRF, LF, UF, NRB, LB, UB) {ID, T, LPR},
         IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     };
@@ -272,14 +274,14 @@ inline NhwcChoice fused_stream_pick(const Plan& p, int64_t max_grid)
 }
 
 // Whether the streamed backward beats the split one: measured so where at least
-// half of each thread's rows stay resident (y and dy both held); with fewer,
-// re-reading two streams at this kernel's occupancy loses to the split kernels
-// (2x256x512x512 bf16: 313 against 248 us).
+// half of each thread's rows stay on chip (y and dy both held, in registers or
+// LDS); with fewer, re-reading two streams at this kernel's occupancy loses to
+// the split kernels (2x256x512x512 bf16: 313 against 248 us).
 inline bool stream_bwd_worthwhile(const Plan& p, int variant, int group)
 {
     switch (variant) {
-#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) \
-    case ID: return ceil_div(ceil_div(p.m, group), T / LPR) <= 2 * NRB;
+#define IABN_ROW(ID, T, LPR, NRF, LF, UF, NRB, LB, UB) \
+    case ID: return ceil_div(ceil_div(p.m, group), T / LPR) <= 2 * (NRB + LB);
         IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
     default: return false;

@@ -699,12 +699,13 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
 // ---------------------------------------------------------------------------
 // Streamed slice kernels, for NHWC maps too large to hold: 256 workgroups (one
 // per CU), G of them per slice, mapped member-major to the XCDs
-// (nhwc_stream_member).  A thread keeps its first NR rows in VGPRs and streams
-// the rest in chunks of U rows per thread, two chunks in flight; the second
-// pass re-reads only the streamed rows (newest first) and writes the resident
-// ones from registers.  Traffic: forward (2 + f)S, backward (3 + 2f)S, f the
-// streamed fraction of the rows.
-template <int DT, int ACT, int T, int LPR, int NR, int U>
+// (nhwc_stream_member).  A thread keeps its first NR rows in VGPRs, the next NL
+// in LDS (stored there as the first pass streams them), and streams the rest in
+// chunks of U rows per thread, two chunks in flight; the second pass re-reads
+// only the rows held in neither (newest first) and writes the others from
+// registers and LDS.  Traffic: forward (2 + f)S, backward (3 + 2f)S, f the
+// fraction of the rows held in neither.
+template <int DT, int ACT, int T, int LPR, int NR, int NL, int U>
 __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     void* x, uint32_t m, uint32_t Cv, const float* __restrict__ gamma,
     const float* __restrict__ beta, float* __restrict__ running_mean,
@@ -731,6 +732,19 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     auto load_chunk = [&](uint4 (&q)[U], uint32_t c) {
 #pragma unroll
         for (int u = 0; u < U; ++u) q[u] = xv[min(rb + (NR + c * U + u) * RPS, r1 - 1) * Cv + col];
+    };
+    // the first nlc streamed chunks stay in LDS for the second pass (each thread
+    // its own column of slots: 16-byte accesses, no bank conflicts)
+    static_assert(NL % U == 0, "LDS rows are whole chunks");
+    const uint32_t nlc = min(nchunk, uint32_t(NL / U));
+    __shared__ uint4 keep_rows[NL > 0 ? NL : 1][T];
+    auto keep = [&](const uint4 (&q)[U], uint32_t c) {
+        if constexpr (NL > 0) {
+            if (c < nlc) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) keep_rows[c * U + u][t] = q[u];
+            }
+        }
     };
 
     const uint4 kraw = xv[col];
@@ -782,14 +796,17 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
         __builtin_amdgcn_sched_barrier(0);          // issued before the sums of chunk c
 #pragma unroll
         for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RPS);
+        keep(qa, c);
         load_chunk(qa, min(c + 2, nchunk - 1));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) add(qb[u], rb + (NR + (c + 1) * U + u) * RPS);
+        keep(qb, c + 1);
     }
     if (c < nchunk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RPS);
+        keep(qa, c);
     }
 
     __shared__ ScatterRow<LPR, 2 * V> sh[T / kWave];
@@ -843,30 +860,38 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     };
 
     // second pass: the last streamed chunks (the likeliest still cached) load
-    // first; the resident rows are written while they are in flight
+    // first; the resident rows are written while they are in flight; the chunks
+    // kept in LDS come last
     const uint32_t rb2 = opaque_u(rb);
+    const uint32_t ng = nchunk - nlc;               // chunks read again from memory
     load_chunk(qa, nchunk > 0 ? nchunk - 1 : 0);
 #pragma unroll
     for (int k = 0; k < NR; ++k) put(opaque_q(r[k]), rb2 + k * RPS);
     uint32_t i = 0;
-    for (; i + 1 < nchunk; i += 2) {
+    for (; i + 1 < ng; i += 2) {
         const uint32_t cc = nchunk - 1 - i;
         load_chunk(qb, cc - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + cc * U + u) * RPS);
-        load_chunk(qa, cc >= 2 ? cc - 2 : 0);
+        load_chunk(qa, cc >= nlc + 2 ? cc - 2 : nlc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) put(qb[u], rb2 + (NR + (cc - 1) * U + u) * RPS);
     }
-    if (i < nchunk) {
+    if (i < ng) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(qa[u], rb2 + NR * RPS + u * RPS);   // chunk 0
+        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + nlc * U + u) * RPS);   // chunk nlc
+    }
+    if constexpr (NL > 0) {
+        for (uint32_t cc = 0; cc < nlc; ++cc) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) put(keep_rows[cc * U + u][t], rb2 + (NR + cc * U + u) * RPS);
+        }
     }
 }
 
-template <int DT, int ACT, int T, int LPR, int NR, int U>
+template <int DT, int ACT, int T, int LPR, int NR, int NL, int U>
 __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
     const void* __restrict__ y, const void* dy, void* dx, uint32_t m, uint32_t Cv,
     const float* __restrict__ gamma, const float* __restrict__ beta,
@@ -895,6 +920,22 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
             const uint32_t i = min(rb + (NR + c * U + u) * RPS, r1 - 1) * Cv + col;
             qy[u] = yv[i];
             qd[u] = dv[i];
+        }
+    };
+    // the first nlc streamed chunks of y and dy stay in LDS for the second pass
+    static_assert(NL % U == 0, "LDS rows are whole chunks");
+    const uint32_t nlc = min(nchunk, uint32_t(NL / U));
+    __shared__ uint4 keep_y[NL > 0 ? NL : 1][T];
+    __shared__ uint4 keep_d[NL > 0 ? NL : 1][T];
+    auto keep = [&](const uint4 (&qy)[U], const uint4 (&qd)[U], uint32_t c) {
+        if constexpr (NL > 0) {
+            if (c < nlc) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    keep_y[c * U + u][t] = qy[u];
+                    keep_d[c * U + u][t] = qd[u];
+                }
+            }
         }
     };
 
@@ -942,14 +983,17 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RPS);
+        keep(ya, da, c);
         load_chunk(ya, da, min(c + 2, nchunk - 1));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) add(yb[u], db_[u], rb + (NR + (c + 1) * U + u) * RPS);
+        keep(yb, db_, c + 1);
     }
     if (c < nchunk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RPS);
+        keep(ya, da, c);
     }
 
     __shared__ ScatterRow<LPR, 2 * V> sh[T / kWave];
@@ -1005,24 +1049,32 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
     };
 
     const uint32_t rb2 = opaque_u(rb);
+    const uint32_t ng = nchunk - nlc;               // chunks read again from memory
     load_chunk(ya, da, nchunk > 0 ? nchunk - 1 : 0);
 #pragma unroll
     for (int k = 0; k < NR; ++k) put(opaque_q(ry[k]), opaque_q(rd[k]), rb2 + k * RPS);
     uint32_t i = 0;
-    for (; i + 1 < nchunk; i += 2) {
+    for (; i + 1 < ng; i += 2) {
         const uint32_t cc = nchunk - 1 - i;
         load_chunk(yb, db_, cc - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + (NR + cc * U + u) * RPS);
-        load_chunk(ya, da, cc >= 2 ? cc - 2 : 0);
+        load_chunk(ya, da, cc >= nlc + 2 ? cc - 2 : nlc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) put(yb[u], db_[u], rb2 + (NR + (cc - 1) * U + u) * RPS);
     }
-    if (i < nchunk) {
+    if (i < ng) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + NR * RPS + u * RPS);   // chunk 0
+        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + (NR + nlc * U + u) * RPS);   // chunk nlc
+    }
+    if constexpr (NL > 0) {
+        for (uint32_t cc = 0; cc < nlc; ++cc) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                put(keep_y[cc * U + u][t], keep_d[cc * U + u][t], rb2 + (NR + cc * U + u) * RPS);
+        }
     }
 }
 
@@ -1134,9 +1186,9 @@ static void launch_stream_fwd_da(const Plan& pl, void* x, const float* gamma, co
     const uint32_t m = uint32_t(pl.m), Cv = uint32_t(pl.C / pl.V);
     const SliceGroup grp = slice_group(pl, ws);
     switch (pl.stream_variant) {
-#define IABN_CASE(ID, T, LPR, NRF, UF, NRB, UB)                                                   \
+#define IABN_CASE(ID, T, LPR, NRF, LF, UF, NRB, LB, UB)                                           \
     case ID:                                                                                      \
-        hipLaunchKernelGGL((k_fwd_stream_nhwc<DT, ACT, T, LPR, NRF, UF>),                         \
+        hipLaunchKernelGGL((k_fwd_stream_nhwc<DT, ACT, T, LPR, NRF, LF, UF>),                     \
                            dim3(Cv / LPR * grp.G), dim3(T), 0, s, x, m, Cv, gamma, beta, rm, rv,  \
                            sm, si, eps, mom, a, grp);                                             \
         break;
@@ -1167,9 +1219,9 @@ static void launch_stream_bwd_da(const Plan& pl, const void* y, const void* dy, 
     const uint32_t m = uint32_t(pl.m), Cv = uint32_t(pl.C / pl.V);
     const SliceGroup grp = slice_group(pl, ws);
     switch (pl.stream_bwd_variant) {
-#define IABN_CASE(ID, T, LPR, NRF, UF, NRB, UB)                                                   \
+#define IABN_CASE(ID, T, LPR, NRF, LF, UF, NRB, LB, UB)                                           \
     case ID:                                                                                      \
-        hipLaunchKernelGGL((k_bwd_stream_nhwc<DT, ACT, T, LPR, NRB, UB>),                         \
+        hipLaunchKernelGGL((k_bwd_stream_nhwc<DT, ACT, T, LPR, NRB, LB, UB>),                     \
                            dim3(Cv / LPR * grp.G), dim3(T), 0, s, y, dy, dx, m, Cv, gamma, beta,  \
                            invstd, dgamma, dbeta, a, ia, grp);                                    \
         break;

@@ -294,11 +294,18 @@ static void check_plan(const Shape& s, bool vec)
         }
         // streamed slice kernels: every variant and group size 8..32, the forward's
         // and the backward's (resident rows, chunk) split
-        struct SVar { int T, LPR, NR, U; };
+        struct SVar { int T, LPR, NR, L, U, streams; };
         std::vector<SVar> svars;
-#define IABN_ROW(ID, T, LPR, NRF, UF, NRB, UB) svars.push_back({T, LPR, NRF, UF}); svars.push_back({T, LPR, NRB, UB});
+#define IABN_ROW(ID, T, LPR, NRF, LF, UF, NRB, LB, UB) \
+    svars.push_back({T, LPR, NRF, LF, UF, 1}); svars.push_back({T, LPR, NRB, LB, UB, 2});
         IABN_STREAM_NHWC_VARIANTS(IABN_ROW)
 #undef IABN_ROW
+        for (const SVar& sv : svars) {
+            CHECK(sv.L % sv.U == 0, "LDS rows are whole chunks");
+            // the LDS rows (16 B per thread, row and stream) fit 160 KB beside the
+            // scatter rows
+            CHECK(size_t(sv.L) * sv.T * 16 * sv.streams <= size_t(136) * 1024, "LDS rows fit");
+        }
         for (const SVar& sv : svars) {
             for (uint32_t G = 8; G <= 64; G *= 2) {
                 if (cv % sv.LPR != 0) continue;

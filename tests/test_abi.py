@@ -177,16 +177,16 @@ def test_plan_choice_for_the_workloads():
     # a map too large to hold: 256 workgroups in groups of 64, eight lanes per row,
     # keep part of it in registers and stream the rest
     assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_streamed(512x8x28+4,group64) " \
+        "forward=slice_streamed(512x8x(28+8)+4,group64) " \
         "backward=split(reduce:256x256,apply:512x256,vec16)"
     # ... the backward too while half its rows stay resident
     assert d(32, 256, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_streamed(512x8x28+4,group64) backward=slice_streamed(512x8x14+2,group64)"
+        "forward=slice_streamed(512x8x(28+8)+4,group64) backward=slice_streamed(512x8x(14+4)+2,group64)"
     assert d(4, 2048, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_streamed(512x8x28+4,group8) backward=slice_streamed(512x8x14+2,group8)"
+        "forward=slice_streamed(512x8x(28+8)+4,group8) backward=slice_streamed(512x8x(14+4)+2,group8)"
     # four lanes per row where 16-byte vectors make 16 per pixel
     assert d(1, 128, 360, 360, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_streamed(512x4x28+4,group64) backward=slice_streamed(512x4x14+2,group64)"
+        "forward=slice_streamed(512x4x(28+8)+4,group64) backward=slice_streamed(512x4x(14+4)+2,group64)"
     # ... but not two lanes per row: split, the backward sums on one workgroup per CU
     assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=split(stats:512x256,apply:512x256,vec16) " \

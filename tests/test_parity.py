@@ -425,33 +425,38 @@ def test_slice_resident_variants(wl):
 
 
 # Streamed slice kernels (NHWC maps too large to hold): 256 workgroups, groups
-# of 8 to 64, eight lanes per row (four where 16 vectors make a pixel); threads keep 28 rows (forward) or 14 (backward) resident and
+# of 8 to 64, eight lanes per row (four where 16 vectors make a pixel).  Threads
+# keep 28 rows in registers and 8 in LDS (forward) or 14 and 4 (backward) and
 # stream the rest.  The backward streams only while at least half its rows stay
-# resident (else the split kernels).  Forward cases stream one to three chunks,
-# backward cases up to four.
+# on chip (else the split kernels).  The cases cover chunks kept in LDS only
+# (one or two of them) and one to six chunks streamed past them, odd and even.
 _SPLIT_BWD = "split(reduce:256x256,apply:512x256,vec16)"
 _SPLIT_BWD_ELU = "split(reduce:256x256,apply:2048x256,vec16)"   # ELU: a wider dx grid
 STREAM_PLANS = [
     (custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x8x28+4,group64)", _SPLIT_BWD),
+     "slice_streamed(512x8x(28+8)+4,group64)", "slice_streamed(512x8x(14+4)+2,group64)"),
+    (custom(3, 1, 256, 390, 390, layout="NHWC", dtype="bf16"),
+     "slice_streamed(512x8x(28+8)+4,group64)", _SPLIT_BWD),
     (custom(2, 1, 128, 400, 400, layout="NHWC", dtype="f32"),
-     "slice_streamed(512x8x28+4,group64)", _SPLIT_BWD),
+     "slice_streamed(512x8x(28+8)+4,group64)", _SPLIT_BWD),
+    (custom(2, 1, 128, 436, 436, layout="NHWC", dtype="f32"),
+     "slice_streamed(512x8x(28+8)+4,group64)", _SPLIT_BWD),
     (custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x4x28+4,group64)", "slice_streamed(512x4x14+2,group64)"),
+     "slice_streamed(512x4x(28+8)+4,group64)", "slice_streamed(512x4x(14+4)+2,group64)"),
     (custom(4, 1, 1024, 180, 170, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
-     "slice_streamed(512x8x28+4,group16)", _SPLIT_BWD_ELU),
+     "slice_streamed(512x8x(28+8)+4,group16)", "slice_streamed(512x8x(14+4)+2,group16)"),
     (custom(4, 1, 64, 600, 600, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
-     "slice_streamed(512x4x28+4,group64)", _SPLIT_BWD_ELU),
+     "slice_streamed(512x4x(28+8)+4,group64)", _SPLIT_BWD_ELU),
     (custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x8x28+4,group64)", "slice_streamed(512x8x14+2,group64)"),
+     "slice_streamed(512x8x(28+8)+4,group64)", "slice_streamed(512x8x(14+4)+2,group64)"),
     (custom(2, 1, 128, 300, 310, layout="NHWC", dtype="f32"),
-     "slice_streamed(512x8x28+4,group64)", "slice_streamed(512x8x14+2,group64)"),
+     "slice_streamed(512x8x(28+8)+4,group64)", "slice_streamed(512x8x(14+4)+2,group64)"),
     (custom(4, 1, 1024, 130, 130, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
-     "slice_streamed(512x8x28+4,group16)", "slice_streamed(512x8x14+2,group16)"),
+     "slice_streamed(512x8x(28+8)+4,group16)", "slice_streamed(512x8x(14+4)+2,group16)"),
     (custom(3, 3, 512, 100, 100, layout="NHWC", dtype="bf16", act="identity", act_param=0.0),
-     "slice_streamed(512x8x28+4,group32)", "slice_streamed(512x8x14+2,group32)"),
+     "slice_streamed(512x8x(28+8)+4,group32)", "slice_streamed(512x8x(14+4)+2,group32)"),
     (custom(3, 1, 2048, 100, 100, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x8x28+4,group8)", "slice_streamed(512x8x14+2,group8)"),
+     "slice_streamed(512x8x(28+8)+4,group8)", "slice_streamed(512x8x(14+4)+2,group8)"),
 ]
 
 
