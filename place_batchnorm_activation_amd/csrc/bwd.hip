@@ -214,21 +214,24 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                     one(vy, vd, (((g0 + u * P) * rpi + rs) * Cv + col) * V);
                 }
             };
-            int64_t g = p;
-            if (g + (kUnrollN - 1) * P < full) {
+            // sets of kUnrollN complete groups, pipelined as in the statistics
+            const int64_t span = int64_t(kUnrollN) * P;
+            const int64_t first_bad = full - (kUnrollN - 1) * P;
+            const int64_t ns = first_bad > p ? (first_bad - p + span - 1) / span : 0;
+            int64_t g = p + ns * span;
+            if (ns > 0) {
                 uint4 Ay[kUnrollN], Ad[kUnrollN], By[kUnrollN], Bd[kUnrollN];
-                load_set(Ay, Ad, g);
-                for (;;) {
-                    const int64_t g2 = g + kUnrollN * P;
-                    if (g2 + (kUnrollN - 1) * P >= full) { add_set(Ay, Ad, g); g = g2; break; }
-                    load_set(By, Bd, g2);
-                    add_set(Ay, Ad, g);
-                    const int64_t g3 = g2 + kUnrollN * P;
-                    if (g3 + (kUnrollN - 1) * P >= full) { add_set(By, Bd, g2); g = g3; break; }
-                    load_set(Ay, Ad, g3);
-                    add_set(By, Bd, g2);
-                    g = g3;
+                load_set(Ay, Ad, p);
+                int64_t j = 0;
+                for (; j + 1 < ns; j += 2) {
+                    load_set(By, Bd, p + (j + 1) * span);
+                    __builtin_amdgcn_sched_barrier(0);
+                    add_set(Ay, Ad, p + j * span);
+                    load_set(Ay, Ad, p + (j + 2 < ns ? j + 2 : ns - 1) * span);
+                    __builtin_amdgcn_sched_barrier(0);
+                    add_set(By, Bd, p + (j + 1) * span);
                 }
+                if (j < ns) add_set(Ay, Ad, p + j * span);
             }
             for (; g < groups; g += P) {
                 const int64_t r = g * rpi + rs;

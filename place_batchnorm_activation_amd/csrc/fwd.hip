@@ -29,6 +29,11 @@ namespace iabn {
 #define IABN_REDUCE_UNROLL 4
 #endif
 constexpr int kUnroll = IABN_REDUCE_UNROLL;
+// NHWC statistics: row groups in flight per thread and pipeline stage
+#ifndef IABN_NHWC_STATS_UNROLL
+#define IABN_NHWC_STATS_UNROLL 4
+#endif
+constexpr int kUnrollS = IABN_NHWC_STATS_UNROLL;
 
 // ---------------------------------------------------------------------------
 // NCHW statistics: workgroup b covers channel c = b / P, partial p = b % P, i.e.
@@ -154,34 +159,40 @@ __global__ __launch_bounds__(kThreads) void k_stats_nhwc(
             // the rest, at most one ragged group per workgroup, runs checked
             const int64_t full = m / rpi;
             const uint4* xv = reinterpret_cast<const uint4*>(x);
-            auto load_set = [&](uint4 (&buf)[kUnroll], int64_t g0) {
+            auto load_set = [&](uint4 (&buf)[kUnrollS], int64_t g0) {
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) buf[u] = xv[((g0 + u * P) * rpi + rs) * Cv + col];
+                for (int u = 0; u < kUnrollS; ++u) buf[u] = xv[((g0 + u * P) * rpi + rs) * Cv + col];
             };
-            auto add_set = [&](const uint4 (&buf)[kUnroll]) {
+            auto add_set = [&](const uint4 (&buf)[kUnrollS]) {
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
+                for (int u = 0; u < kUnrollS; ++u) {
                     float v[V];
                     unpack16<DT>(buf[u], v);
                     stats_add<DT, V>(v, K, s1, s2);
                 }
-                cnt += kUnroll;
+                cnt += kUnrollS;
             };
-            int64_t g = p;
-            if (g + (kUnroll - 1) * P < full) {
-                uint4 A[kUnroll], B[kUnroll];
-                load_set(A, g);
-                for (;;) {
-                    const int64_t g2 = g + kUnroll * P;
-                    if (g2 + (kUnroll - 1) * P >= full) { add_set(A); g = g2; break; }
-                    load_set(B, g2);
+            // Sets of kUnrollS complete groups, g = p + j*kUnrollS*P for j < ns.  Set
+            // j + 1 loads while set j is summed; the loop has no exit in between
+            // (the last load of an even count is a spare reload of the final set),
+            // so the compiler keeps the two sets in flight together.
+            const int64_t span = int64_t(kUnrollS) * P;
+            const int64_t first_bad = full - (kUnrollS - 1) * P;   // sets starting here are ragged
+            const int64_t ns = first_bad > p ? (first_bad - p + span - 1) / span : 0;
+            int64_t g = p + ns * span;
+            if (ns > 0) {
+                uint4 A[kUnrollS], B[kUnrollS];
+                load_set(A, p);
+                int64_t j = 0;
+                for (; j + 1 < ns; j += 2) {
+                    load_set(B, p + (j + 1) * span);
+                    __builtin_amdgcn_sched_barrier(0);
                     add_set(A);
-                    const int64_t g3 = g2 + kUnroll * P;
-                    if (g3 + (kUnroll - 1) * P >= full) { add_set(B); g = g3; break; }
-                    load_set(A, g3);
+                    load_set(A, p + (j + 2 < ns ? j + 2 : ns - 1) * span);
+                    __builtin_amdgcn_sched_barrier(0);
                     add_set(B);
-                    g = g3;
                 }
+                if (j < ns) add_set(A);
             }
             for (; g < groups; g += P) {
                 const int64_t r = g * rpi + rs;

@@ -135,16 +135,16 @@ constexpr int64_t kApplyBlocksMaxElu = IABN_APPLY_BLOCKS_MAX_ELU;
 #define IABN_REDUCE_BLOCKS_TARGET 2048
 #endif
 constexpr int64_t kReduceBlocksTarget = IABN_REDUCE_BLOCKS_TARGET;
-// NHWC reductions: fewer, longer-lived workgroups walking row groups with a
-// stride; two per CU.
+// NHWC reductions: long-lived workgroups walking row groups with a stride, one
+// per CU, each with four row groups in flight per pipeline stage.  A narrower
+// window of addresses in flight streams faster than two workgroups per CU or
+// deeper stages (2x256x512x512 bf16, cold: statistics 57 against 62 us at 512
+// workgroups; backward sums 104.5 against 115 at 512 x 8 row groups).  The
+// statistics (P) and the backward sums (P_bwd) have a grid each.
 #ifndef IABN_NHWC_REDUCE_BLOCKS
-#define IABN_NHWC_REDUCE_BLOCKS 512
+#define IABN_NHWC_REDUCE_BLOCKS 256
 #endif
 constexpr int64_t kNhwcReduceBlocks = IABN_NHWC_REDUCE_BLOCKS;
-// The NHWC backward reduction reads y and dy together: one workgroup per CU
-// (each with four row groups of both in flight) keeps the window of addresses
-// in flight narrow, which measured faster than two per CU (2x256x512x512 bf16:
-// 104 against 115 us cold) or more.
 #ifndef IABN_NHWC_BWD_REDUCE_BLOCKS
 #define IABN_NHWC_BWD_REDUCE_BLOCKS 256
 #endif

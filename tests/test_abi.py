@@ -189,7 +189,7 @@ def test_plan_choice_for_the_workloads():
         "forward=slice_streamed(512x4x(28+8)+4,group64) backward=slice_streamed(512x4x(14+4)+2,group64)"
     # ... but not two lanes per row: split, the backward sums on one workgroup per CU
     assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=split(stats:512x256,apply:512x256,vec16) " \
+        "forward=split(stats:256x256,apply:512x256,vec16) " \
         "backward=split(reduce:256x256,apply:512x256,vec16)"
     assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_resident(512x4x7,group4) backward=slice_resident(512x4x7,group4)"
