@@ -424,6 +424,24 @@ def test_slice_resident_variants(wl):
     full_check(wl)
 
 
+# NHWC maps the slice kernels cannot take (eight channel vectors a row): the
+# split kernels' two-stage pipelines run several sets a thread.  2x64x300x300
+# bf16: 5 sets of row groups per statistics / sums workgroup and 2 sets of dx
+# vectors per thread, with remainders; 1x32x480x430 fp32: 6 sets and 3.
+SPLIT_PIPELINE = [custom(3, 2, 64, 300, 300, layout="NHWC", dtype="bf16"),
+                  custom(2, 1, 32, 480, 430, layout="NHWC", dtype="f32", act="identity",
+                         act_param=0.0)]
+
+
+@pytest.mark.parametrize("wl", SPLIT_PIPELINE, ids=lambda w: w.name)
+def test_split_pipelines(wl):
+    desc = iabn.iabn_describe_plan(wl.N, wl.C, wl.H, wl.W, wl.layout,
+                                   workloads.storage_torch_dtype(wl.dtype), wl.act)
+    assert desc == ("forward=split(stats:256x256,apply:512x256,vec16) "
+                    "backward=split(reduce:256x256,apply:512x256,vec16)"), desc
+    full_check(wl)
+
+
 # Streamed slice kernels (NHWC maps too large to hold): 256 workgroups, groups
 # of 8 to 64, eight lanes per row (four where 16 vectors make a pixel).  Threads
 # keep 28 rows in registers and 8 in LDS (forward) or 14 and 4 (backward) and
