@@ -14,9 +14,9 @@
 // dz*(z - beta) -> per-channel constants -> dx (3S).
 //
 // Thread t owns lane t % LPR of the slice and rows t / LPR + k*RPS (RPS = T/LPR,
-// k < NR).  Workgroups are mapped to slices XCD by XCD (nhwc_slice_of), so
-// neighbouring slices -- which share cache lines when a slice is narrower than a
-// line -- meet in one L2.
+// k < NR).  Workgroups are mapped to XCDs (nhwc_group_member) so that the
+// workgroups writing one cache line -- neighbouring slices, when a slice is
+// narrower than a line -- meet in one L2.
 //
 // Groups.  When a slice has more rows than one workgroup holds, or one workgroup
 // per slice leaves the chip idle, G workgroups (members) share the slice, member
