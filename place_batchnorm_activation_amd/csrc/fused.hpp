@@ -54,7 +54,9 @@
     X(9, 512, 2, 18)                 \
     X(10, 512, 4, 4)                 \
     X(11, 512, 4, 7)                 \
-    X(12, 512, 4, 13)
+    X(12, 512, 4, 13)                \
+    X(13, 512, 8, 7)                 \
+    X(14, 512, 8, 13)
 #endif
 
 // Streamed slice kernels (NHWC maps too large to hold).  X(id, T, LPR, NRF, LF,
@@ -208,11 +210,18 @@ inline NhwcChoice fused_nhwc_pick(const Plan& p, int64_t max_grid)
             }
         }
     }
+    // Eight lanes per row (whole lines per workgroup) only with 7 or 13 rows a
+    // thread and groups of at most 8: there the backward, whose four-lane stores
+    // leave partial lines (1.38 S written), gains (64x2048x7x7 bf16: 14.3 against
+    // 15.6 us; 128x2048x7x7: 21.8 against 27.5) and the forward holds even; with
+    // 4 rows a thread or the two-level exchange of larger groups it lost (32x2048x7x7:
+    // 10.9 against 10.3; 64x1024x7x7 in groups of 16: 13.6 against 10.8).
     for (int nr_cap : {4, 8, 13}) {
         for (int lpr : {8, 4, 2}) {
             if (cv % lpr != 0) continue;
             const int64_t slices = cv / lpr;
-            for (int g = 1; g <= 32; g *= 2) {
+            const int gmax = lpr == 8 ? 8 : 32;
+            for (int g = 1; g <= gmax; g *= 2) {
                 const int64_t grid = slices * g;
                 const int64_t mg = ceil_div(p.m, g);
                 if (g > 1 && (slices % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;

@@ -51,15 +51,16 @@ def test_workspace_size_depends_only_on_shape():
         lib.iabn_workspace_size(2, 256, 512, 512, 1, 1)
     # a plan whose slices are shared by groups of workgroups holds its exchange past
     # the split kernels' sections: 8 bytes per epoch (one per slice, padded to 32)
-    # and 4 tagged words per member and channel
-    split = lib.iabn_workspace_size(64, 2048, 7, 7, 1, 1) - 8 * (64 + 4 * 4 * 2048)
+    # and 4 tagged words per member and channel (64x2048x7x7: 32 slices of eight
+    # lanes in groups of 8)
+    split = lib.iabn_workspace_size(64, 2048, 7, 7, 1, 1) - 8 * (32 + 4 * 8 * 2048)
     assert split > 0 and split % 256 == 0
     assert lib.iabn_workspace_size(64, 2048, 7, 7, 1, 2) == lib.iabn_workspace_size(64, 2048, 7, 7, 1, 1)
     # partial workspace stays small next to the data (a few percent)
     for (N, C, H, W, lay, dt) in [(32, 256, 56, 56, 0, 0), (2, 256, 512, 512, 1, 1),
                                   (16, 512, 28, 28, 0, 0), (64, 2048, 7, 7, 1, 1)]:
         data = N * C * H * W * (4 if dt == 0 else 2)
-        assert lib.iabn_workspace_size(N, C, H, W, lay, dt) < 0.05 * data
+        assert lib.iabn_workspace_size(N, C, H, W, lay, dt) < 0.08 * data
 
 
 def _fwd(x=A, N=2, C=3, H=4, W=4, layout=0, dtype=0, g=A, b=A, rm=A, rv=A, sm=A, si=A,
@@ -191,8 +192,12 @@ def test_plan_choice_for_the_workloads():
     assert d(32, 64, 112, 112, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=split(stats:256x256,apply:512x256,vec16) " \
         "backward=split(reduce:256x256,apply:512x256,vec16)"
+    # eight lanes per row (whole lines) in groups of 8
     assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
-        "forward=slice_resident(512x4x7,group4) backward=slice_resident(512x4x7,group4)"
+        "forward=slice_resident(512x8x7,group8) backward=slice_resident(512x8x7,group8)"
+    # ... but four lanes where eight would leave 4 rows a thread
+    assert d(32, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
+        "forward=slice_resident(512x4x4,group4) backward=slice_resident(512x4x4,group4)"
     # too many rows for a workgroup to hold: split
     assert d(2, 16, 80, 80, "NHWC", iabn.F32, "leaky_relu").startswith("forward=split")
     # few slices on a large tensor: split

@@ -374,25 +374,29 @@ SLICE_PLANS = [
     (custom(2, 2, 384, 80, 13, layout="NHWC", dtype="f32"), "512x4x4,group8"),
     (custom(2, 5, 256, 25, 33, layout="NHWC", dtype="f32"), "512x4x4,group16"),
     (custom(2, 5, 128, 33, 50, layout="NHWC", dtype="f32"), "512x4x4,group32"),
-    (custom(2, 1, 1536, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group2"),
-    (custom(2, 2, 768, 80, 13, layout="NHWC", dtype="f32"), "512x4x7,group4"),
-    (custom(5, 64, 2048, 7, 7, layout="NHWC", dtype="bf16"), "512x4x7,group4"),
+    (custom(2, 1, 1152, 13, 80, layout="NHWC", dtype="f32"), "512x4x7,group2"),
+    (custom(2, 2, 640, 13, 80, layout="NHWC", dtype="f32"), "512x4x7,group4"),
     (custom(2, 5, 384, 25, 33, layout="NHWC", dtype="f32"), "512x4x7,group8"),
     (custom(2, 5, 256, 33, 50, layout="NHWC", dtype="f32"), "512x4x7,group16"),
     (custom(2, 8, 128, 33, 64, layout="NHWC", dtype="f32"), "512x4x7,group32"),
-    (custom(2, 2, 1536, 80, 13, layout="NHWC", dtype="f32"), "512x4x13,group2"),
-    (custom(2, 5, 768, 25, 33, layout="NHWC", dtype="f32"), "512x4x13,group4"),
-    (custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"), "512x4x13,group4"),
+    (custom(2, 2, 1152, 13, 80, layout="NHWC", dtype="f32"), "512x4x13,group2"),
+    (custom(2, 5, 640, 25, 33, layout="NHWC", dtype="f32"), "512x4x13,group4"),
     (custom(2, 5, 384, 33, 50, layout="NHWC", dtype="f32"), "512x4x13,group8"),
     (custom(2, 8, 256, 33, 64, layout="NHWC", dtype="f32"), "512x4x13,group16"),
     (custom(3, 5, 512, 50, 80, layout="NHWC", dtype="bf16"), "512x4x13,group16"),
     (custom(2, 6, 128, 80, 80, layout="NHWC", dtype="f32"), "512x4x13,group32"),
+    # eight lanes per row (whole lines), 7 or 13 rows a thread, groups of at most 8
+    (custom(2, 1, 1280, 13, 80, layout="NHWC", dtype="f32"), "512x8x7,group4"),
+    (custom(5, 64, 2048, 7, 7, layout="NHWC", dtype="bf16"), "512x8x7,group8"),
+    (custom(2, 2, 1280, 13, 80, layout="NHWC", dtype="f32"), "512x8x13,group4"),
+    (custom(2, 5, 768, 25, 33, layout="NHWC", dtype="f32"), "512x8x13,group8"),
+    (custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"), "512x8x13,group8"),
     # other storage types and activations
     (custom(3, 8, 2048, 10, 25, layout="NHWC", dtype="f16"), "512x4x4,group4"),
     (custom(5, 8, 2048, 10, 25, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
      "512x4x4,group4"),
     (custom(4, 5, 768, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
-     "512x4x13,group4"),
+     "512x8x13,group8"),
     (custom(4, 5, 256, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
      "512x4x4,group16"),
     (custom(4, 3, 512, 12, 12, layout="NHWC", dtype="bf16", act="elu", act_param=0.5),
@@ -543,7 +547,8 @@ OUTLIER = [custom(2, 4, 32, 16, 16),                                   # NCHW ch
            custom(2, 1, 3, 157, 163),                                  # NCHW split, scalar
            custom(3, 4, 256, 25, 33, layout="NHWC", dtype="bf16"),     # NHWC slice-resident
            custom(2, 4, 96, 25, 33, layout="NHWC", dtype="f32"),       # (groups of 4)
-           custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"),    # 4 lanes, group 4
+           custom(3, 5, 2048, 30, 30, layout="NHWC", dtype="bf16"),    # 8 lanes, group 8
+           custom(2, 5, 640, 25, 33, layout="NHWC", dtype="f32"),      # 4 lanes, group 4
            custom(2, 8, 256, 33, 64, layout="NHWC", dtype="f32"),      # group 16, two levels
            custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),   # streamed, 8 lanes
            custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),   # streamed, 4 lanes
