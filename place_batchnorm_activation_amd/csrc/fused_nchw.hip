@@ -203,6 +203,7 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
     const float g_c = gamma[c];
     const float is_c = invstd[c];
 
+    constexpr bool kKeepZ = DYR && DT == kF32;
     uint4 ry[NR];
     uint4 rd[DYR ? NR : 1];
     ChannelWalk32 w;
@@ -232,6 +233,15 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
                 const float dz = slope * vd[e];
                 sdz += dz;
                 sdzt = fmaf(dz, z - bc, sdzt);
+                vy[e] = z;
+                vd[e] = dz;
+            }
+            // fp32 storage with dy resident: z and dz take the places of y and dy,
+            // so the dx pass does not invert the activation again (ELU: a log1p
+            // an element)
+            if constexpr (kKeepZ) {
+                ry[k] = pack16<DT>(vy);
+                rd[k] = pack16<DT>(vd);
             }
         }
         if constexpr (!DYR) w.step();
@@ -262,9 +272,15 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
             else unpack16<DT>(ld16(dy, w.off), vd);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                float z, slope;
-                act_invert<ACT>(vy[e], a2, ia2, z, slope);
-                const float dz = slope * vd[e];
+                float z, dz;
+                if constexpr (kKeepZ) {
+                    z = vy[e];
+                    dz = vd[e];
+                } else {
+                    float slope;
+                    act_invert<ACT>(vy[e], a2, ia2, z, slope);
+                    dz = slope * vd[e];
+                }
                 vd[e] = fmaf(kA, dz, fmaf(kB, z - bc2, kC));
             }
             st16(dx, w.off, pack16<DT>(vd));
@@ -539,6 +555,8 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw_s(
         rd[k] = ok ? ld_elem<DT>(dy, w.off) : 0u;
         w.step();
     }
+    // every element sits in a 32-bit register of its own: z and dz take the
+    // places of y and dy, so the dx pass does not invert the activation again
     float sdz = 0.f, sdzt = 0.f;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
@@ -548,6 +566,8 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw_s(
             const float dz = slope * elem_float<DT>(rd[k]);
             sdz += dz;
             sdzt = fmaf(dz, z - bc, sdzt);
+            ry[k] = __float_as_uint(z);
+            rd[k] = __float_as_uint(dz);
         }
     }
     block_sum2<T>(sdz, sdzt);
@@ -564,14 +584,13 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw_s(
     const float kA = float(A), kB = float(-A * dg / (md * g)), kC = float(-A * db / md);
 
     const uint32_t t2 = opaque(t);
-    const float a2 = opaquef(a), ia2 = opaquef(inv_a), bc2 = opaquef(bc);
+    const float bc2 = opaquef(bc);
     w.init(t2, c, C, HW, T);
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
         if (t2 + k * T < m) {
-            float z, slope;
-            act_invert<ACT>(elem_float<DT>(opaque(ry[k])), a2, ia2, z, slope);
-            const float dz = slope * elem_float<DT>(opaque(rd[k]));
+            const float z = __uint_as_float(opaque(ry[k]));
+            const float dz = __uint_as_float(opaque(rd[k]));
             st_elem<DT>(dx, w.off, fmaf(kA, dz, fmaf(kB, z - bc2, kC)));
         }
         w.step();

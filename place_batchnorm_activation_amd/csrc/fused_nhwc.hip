@@ -624,6 +624,9 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
     float sums[2 * V];
 #pragma unroll
     for (int e = 0; e < 2 * V; ++e) sums[e] = 0.f;
+    // fp32 storage: z and dz take the places of y and dy, so the dx pass does not
+    // invert the activation again (ELU: a log1p an element)
+    constexpr bool kKeepZ = DT == kF32;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
         float vy[V], vd[V];
@@ -636,6 +639,12 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
             const float dz = slope * vd[e];
             sums[e] += dz;
             sums[V + e] = fmaf(dz, z - b_c[e], sums[V + e]);
+            vy[e] = z;
+            vd[e] = dz;
+        }
+        if constexpr (kKeepZ) {
+            ry[k] = pack16<DT>(vy);
+            rd[k] = pack16<DT>(vd);
         }
     }
     __shared__ ScatterRow<LPR, 2 * V> sh[T / kWave];
@@ -687,9 +696,15 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
         unpack16<DT>(opaque_q(rd[k]), vd);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            float z, slope;
-            act_invert<ACT>(vy[e], a2, ia2, z, slope);
-            const float dz = slope * vd[e];
+            float z, dz;
+            if constexpr (kKeepZ) {
+                z = vy[e];
+                dz = vd[e];
+            } else {
+                float slope;
+                act_invert<ACT>(vy[e], a2, ia2, z, slope);
+                dz = slope * vd[e];
+            }
             vd[e] = fmaf(kA[e], dz, fmaf(kB[e], z - b_c[e], kC[e]));
         }
         if (row < r1) st16_out<LPR>(dx, row * Cv + col, pack16<DT>(vd));
