@@ -60,8 +60,8 @@ COLD_BYTES = 512 << 20
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("device.hpp", "plan.hpp", "fused.hpp", "fwd.hip", "bwd.hip", "fused_nchw.hip",
-              "fused_nhwc.hip"):
+    for f in ("device.hpp", "plan.hpp", "fused.hpp", "group.hpp", "fwd.hip", "bwd.hip",
+              "fused_nchw.hip", "fused_nhwc.hip"):
         with open(os.path.join(ROOT, "place_batchnorm_activation_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

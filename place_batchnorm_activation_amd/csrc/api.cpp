@@ -101,6 +101,22 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
         if (f >= 0 && fused_worthwhile(p, fused_fwd_threads(f))) p.fused_variant = f;
         const int b = fused_bwd_pick(vc);
         if (b >= 0 && fused_worthwhile(p, fused_bwd_threads(b))) p.fused_bwd_variant = b;
+        if (p.fused_variant < 0 || p.fused_bwd_variant < 0) {
+            // a channel larger than one workgroup holds, or too few channels to
+            // fill the chip: a group of workgroups per channel
+            const NchwGroupChoice g = fused_nchw_group_pick(p, coresident_grid());
+            if (g.group > 1) {
+                p.fused_variant = g.fwd;
+                p.fused_bwd_variant = g.bwd;
+                p.nchw_group = g.group;
+                // the exchange goes past every split-kernel section, which other
+                // calls on the same workspace may write: one epoch per channel
+                // (padded to 32 words), four tagged words per member and channel
+                p.off_xchg = (size_t)align_up((int64_t)split_bytes(N, C, H, W, layout, dtype), 256);
+                p.bytes = p.off_xchg +
+                          sizeof(uint64_t) * (size_t)nhwc_exchange_words(C, g.group, C);
+            }
+        }
     }
     if (act >= 0) {
         const bool nhwc_vec = p.layout == kNHWC && p.vec && p.numel > 0;
@@ -288,7 +304,7 @@ iabn_status iabn_forward_train(void* x_inout, int64_t N, int64_t C, int64_t H, i
     IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
     if (pl.fused_variant >= 0) {
         launch_forward_fused_nchw(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
-                                  save_invstd, eps, momentum, act, act_param, stream);
+                                  save_invstd, eps, momentum, act, act_param, workspace, stream);
         return launched();
     }
     if (pl.scalar_variant >= 0) {
@@ -393,7 +409,7 @@ iabn_status iabn_backward(const void* y, const void* dy, void* dx, int64_t N, in
     IABN_TRY(check_workspace(workspace, workspace_bytes, pa));
     if (pa.fused_bwd_variant >= 0) {
         launch_backward_fused_nchw(pa, y, dy, dx, gamma, beta, save_invstd, dgamma, dbeta, act,
-                                   act_param, stream);
+                                   act_param, workspace, stream);
         return launched();
     }
     if (pa.scalar_variant >= 0) {
@@ -500,7 +516,10 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
 #undef IABN_ROW
         default: break;
         }
-        snprintf(fwd, sizeof fwd, "channel_resident(%dx%d)", T, NR);
+        if (p.nchw_group > 1)
+            snprintf(fwd, sizeof fwd, "channel_resident(%dx%d,group%d)", T, NR, p.nchw_group);
+        else
+            snprintf(fwd, sizeof fwd, "channel_resident(%dx%d)", T, NR);
     } else if (p.scalar_variant >= 0) {
         snprintf(fwd, sizeof fwd, "channel_resident_scalar(%s)", sd);
     } else if (p.nhwc_variant >= 0) {
@@ -521,8 +540,12 @@ int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout l
 #undef IABN_ROW
         default: break;
         }
-        snprintf(bwd, sizeof bwd, "channel_resident(%dx%d,%s)", T, NR,
-                 dyr ? "dy_resident" : "dy_streamed");
+        if (p.nchw_group > 1)
+            snprintf(bwd, sizeof bwd, "channel_resident(%dx%d,%s,group%d)", T, NR,
+                     dyr ? "dy_resident" : "dy_streamed", p.nchw_group);
+        else
+            snprintf(bwd, sizeof bwd, "channel_resident(%dx%d,%s)", T, NR,
+                     dyr ? "dy_resident" : "dy_streamed");
     } else if (p.scalar_variant >= 0) {
         snprintf(bwd, sizeof bwd, "channel_resident_scalar(%s,dy_resident)", sd);
     } else if (p.nhwc_variant >= 0) {

@@ -132,6 +132,51 @@ inline int fused_bwd_threads(int id)
     }
 }
 
+inline bool fused_bwd_dy_resident(int id)
+{
+    switch (id) {
+#define IABN_ROW(ID, T, NRV, NRL, G, DYR) case ID: return DYR;
+        IABN_FUSED_BWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    default: return false;
+    }
+}
+
+// Channels one workgroup cannot hold, or too few channels to fill the chip: G
+// workgroups (members) share a channel, member j holding its vectors
+// [j*ceil(vc/G), ...), and swap their fp64 sums through the workspace (the
+// exchange of the NHWC groups, one channel a slice).  The largest power of two
+// G (2 to 64) with C*G within max_grid (every member runs at once) whose share
+// fits a forward and a y-resident, dy-streaming backward variant, if the grid
+// then fills the chip (or the tensor is small).  Both passes use that G.
+struct NchwGroupChoice {
+    int fwd = -1, bwd = -1, group = 1;
+};
+
+inline NchwGroupChoice fused_nchw_group_pick(const Plan& p, int64_t max_grid)
+{
+    NchwGroupChoice none;
+    if (p.layout != kNCHW || !p.vec || p.numel == 0) return none;
+    const int64_t bytes = p.numel * p.esize;
+    if (bytes >= (int64_t(1) << 32)) return none;
+    const int64_t vc = p.m / p.V;
+    for (int g = 64; g >= 2; g /= 2) {
+        if (p.C * g > max_grid) continue;
+        const int64_t share = ceil_div(vc, g);
+        if ((g - 1) * share >= vc) continue;        // every member holds vectors
+        const int f = fused_fwd_pick(share), b = fused_bwd_pick(share);
+        if (f < 0 || b < 0 || fused_bwd_dy_resident(b)) continue;
+        const int64_t threads = p.C * g * fused_fwd_threads(f);
+        if (threads < int64_t(256) * 256 && bytes > (int64_t(4) << 20)) return none;
+        NchwGroupChoice c;
+        c.fwd = f;
+        c.bwd = b;
+        c.group = g;
+        return c;
+    }
+    return none;
+}
+
 // Whether the channel-resident kernels fill enough of the chip to beat the
 // split path: they run one workgroup per channel.
 inline bool fused_worthwhile(const Plan& p, int threads)
@@ -328,11 +373,12 @@ inline int fused_scalar_pick(const Plan& p)
 
 void launch_forward_fused_nchw(const Plan& pl, void* x, const float* gamma, const float* beta,
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
-                               int act, float a, hipStream_t s);
+                               int act, float a, void* ws, hipStream_t s);
 
 void launch_backward_fused_nchw(const Plan& pl, const void* y, const void* dy, void* dx,
                                 const float* gamma, const float* beta, const float* invstd,
-                                float* dgamma, float* dbeta, int act, float a, hipStream_t s);
+                                float* dgamma, float* dbeta, int act, float a, void* ws,
+                                hipStream_t s);
 
 void launch_forward_fused_scalar(const Plan& pl, void* x, const float* gamma, const float* beta,
                                  float* rm, float* rv, float* sm, float* si, float eps, float mom,

@@ -20,6 +20,7 @@
 
 #include "device.hpp"
 #include "fused.hpp"
+#include "group.hpp"
 
 namespace iabn {
 
@@ -100,18 +101,24 @@ __device__ __forceinline__ void block_sum2(float& a, float& b)
 }
 
 // ---------------------------------------------------------------------------
-template <int DT, int ACT, int T, int NR>
+template <int DT, int ACT, int T, int NR, bool GRP>
 __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     void* x, uint32_t C, uint32_t HW, uint32_t m, const float* __restrict__ gamma,
     const float* __restrict__ beta, float* __restrict__ running_mean,
     float* __restrict__ running_var, float* __restrict__ save_mean,
-    float* __restrict__ save_invstd, float eps, float momentum, float a)
+    float* __restrict__ save_invstd, float eps, float momentum, float a, SliceGroup grp)
 {
     constexpr int V = Raw16<DT>::V;
-    const uint32_t c = blockIdx.x;
+    // channel and member: with GRP a group of G workgroups shares a channel,
+    // member j holding the channel's vectors [j*mg, min(Vc, (j+1)*mg)); without,
+    // one workgroup holds it all (and the kernel carries no exchange code)
+    const uint32_t c = GRP ? blockIdx.x / grp.G : blockIdx.x;
+    const uint32_t member = GRP ? blockIdx.x - c * grp.G : 0u;
     const uint32_t t = threadIdx.x;
     const uint32_t HWv = HW / V;
     const uint32_t Vc = m / V;
+    const uint32_t v0 = GRP ? member * grp.mg : 0u;
+    const uint32_t v1 = GRP ? min(Vc, v0 + grp.mg) : Vc;
     const float K = load_one<DT>(x, int64_t(c) * HW);
     // per-channel parameters fetched up front, off the critical path
     const float g_c = gamma[c];
@@ -119,12 +126,14 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     float rm_c = 0.f, rv_c = 0.f;
     if (t == 0 && running_mean) { rm_c = running_mean[c]; rv_c = running_var[c]; }
 
+    uint64_t epoch = 0;
+    if (GRP && t == 0) epoch = atomic_ld(grp.xchg + c);
     uint4 r[NR];
     ChannelWalk32 w;
-    w.init(t, c, C, HWv, T);
+    w.init(v0 + t, c, C, HWv, T);
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        r[k] = (t + k * T < Vc) ? ld16(x, w.off) : make_uint4(0, 0, 0, 0);
+        r[k] = (v0 + t + k * T < v1) ? ld16(x, w.off) : make_uint4(0, 0, 0, 0);
         w.step();
     }
 
@@ -134,7 +143,7 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        if (t + k * T < Vc) {
+        if (v0 + t + k * T < v1) {
             float v[V];
             unpack16<DT>(r[k], v);
 #pragma unroll
@@ -152,15 +161,34 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     float n = float(cnt * V);
     float mean = cnt ? S1 / n : 0.f;
     float m2 = cnt ? fmaxf(S2 - S1 * mean, 0.f) : 0.f;
+    __shared__ uint64_t tok_sh;
+    if (GRP && t == 0) tok_sh = group_token(grp, c, epoch);
     block_chan<T>(n, mean, m2);
 
-    // statistics in fp64 (every thread computes the same values)
-    const double var = double(m2) / double(m);
+    // statistics in fp64 (every thread computes the same values).  A group adds
+    // its members' shifted sums, sum(x - K) = n*mean and sum((x - K)^2) = M2 +
+    // n*mean^2, in fp64 and in member order.
+    double dm = double(mean), var = double(m2) / double(m);
+    if constexpr (GRP) {
+        __shared__ double tot_sh[2];
+        double s1 = double(n) * double(mean);
+        double s2 = double(m2) + double(n) * double(mean) * double(mean);
+        group_sums<1, T>(grp, c, C, member, tok_sh, t == 0, s1, s2);
+        if (t == 0) {
+            tot_sh[0] = s1;
+            tot_sh[1] = s2;
+        }
+        __syncthreads();
+        const double md = double(m);
+        dm = tot_sh[0] / md;
+        var = fmax(tot_sh[1] - tot_sh[0] * dm, 0.0) / md;
+        if (member == 0 && t == 0) atomic_st(grp.xchg + c, epoch + 1);
+    }
     const double invstd = 1.0 / sqrt(var + double(eps));
-    const float d = float(mean);
+    const float d = float(dm);
     const float s = float(double(g_c) * invstd);
-    if (t == 0) {
-        const double mu = double(K) + double(mean);
+    if (t == 0 && member == 0) {
+        const double mu = double(K) + dm;
         save_mean[c] = float(mu);
         save_invstd[c] = float(invstd);
         if (running_mean) {
@@ -171,10 +199,10 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
     }
 
     const uint32_t t2 = opaque(t);
-    w.init(t2, c, C, HWv, T);
+    w.init(v0 + t2, c, C, HWv, T);
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        if (t2 + k * T < Vc) {
+        if (v0 + t2 + k * T < v1) {
             float v[V];
             unpack16<DT>(opaque4(r[k]), v);
 #pragma unroll
@@ -294,21 +322,27 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
 // resident (NRV vectors per thread in VGPRs, NRL in LDS) and dy is streamed
 // twice, through a two-group software pipeline: the G loads of the next group
 // are in flight while the current group is consumed.  HBM traffic 4S.
-template <int DT, int ACT, int T, int NRV, int NRL, int G>
+template <int DT, int ACT, int T, int NRV, int NRL, int G, bool GRP>
 __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
     const void* __restrict__ y, const void* dy, void* dx, uint32_t C, uint32_t HW, uint32_t m,
     const float* __restrict__ gamma, const float* __restrict__ beta,
     const float* __restrict__ invstd, float* __restrict__ dgamma, float* __restrict__ dbeta,
-    float a, float inv_a)
+    float a, float inv_a, SliceGroup grp)
 {
     constexpr int V = Raw16<DT>::V;
     constexpr int NR = NRV + NRL;
     constexpr int NG = (NR + G - 1) / G;
     __shared__ uint4 ly[NRL > 0 ? NRL * T : 1];
-    const uint32_t c = blockIdx.x;
+    // channel and member, as in the forward
+    const uint32_t c = GRP ? blockIdx.x / grp.G : blockIdx.x;
+    const uint32_t member = GRP ? blockIdx.x - c * grp.G : 0u;
     const uint32_t t = threadIdx.x;
     const uint32_t HWv = HW / V;
     const uint32_t Vc = m / V;
+    const uint32_t v0 = GRP ? member * grp.mg : 0u;
+    const uint32_t v1 = GRP ? min(Vc, v0 + grp.mg) : Vc;
+    uint64_t epoch = 0;
+    if (GRP && t == 0) epoch = atomic_ld(grp.xchg + c);
     const float bc = beta[c];
     const float g_c = gamma[c];
     const float is_c = invstd[c];
@@ -316,28 +350,28 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
     // y: registers, then this thread's own LDS slots (read back only by this thread)
     uint4 ry[NRV];
     ChannelWalk32 w;
-    w.init(t, c, C, HWv, T);
+    w.init(v0 + t, c, C, HWv, T);
 #pragma unroll
     for (int k = 0; k < NRV; ++k) {
-        ry[k] = (t + k * T < Vc) ? ld16(y, w.off) : make_uint4(0, 0, 0, 0);
+        ry[k] = (v0 + t + k * T < v1) ? ld16(y, w.off) : make_uint4(0, 0, 0, 0);
         w.step();
     }
 #pragma unroll
     for (int k = 0; k < NRL; ++k) {
-        if (t + (NRV + k) * T < Vc) ly[k * T + t] = ld16(y, w.off);
+        if (v0 + t + (NRV + k) * T < v1) ly[k * T + t] = ld16(y, w.off);
         w.step();
     }
 
     // pass 1: sums over dy streamed in groups of G
     float sdz = 0.f, sdzt = 0.f;
     {
-        const uint32_t t1 = opaque(t);
+        const uint32_t t1 = opaque(t), u1 = v0 + t1;   // thread; its first channel vector
         ChannelWalk32 wd;
-        wd.init(t1, c, C, HWv, T);
+        wd.init(u1, c, C, HWv, T);
         uint4 buf[2][G];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            buf[0][i] = (i < NR && t1 + i * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+            buf[0][i] = (i < NR && u1 + i * T < v1) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
             wd.step();
         }
 #pragma unroll
@@ -347,14 +381,14 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
             for (int i = 0; i < G; ++i) {
                 const int k = (gi + 1) * G + i;
                 if (k < NR) {
-                    buf[(gi + 1) & 1][i] = (t1 + k * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+                    buf[(gi + 1) & 1][i] = (u1 + k * T < v1) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
                     wd.step();
                 }
             }
 #pragma unroll
             for (int i = 0; i < G; ++i) {
                 const int k = gi * G + i;
-                if (k < NR && t1 + k * T < Vc) {
+                if (k < NR && u1 + k * T < v1) {
                     float vy[V], vd[V];
                     unpack16<DT>(k < NRV ? ry[k < NRV ? k : 0] : ly[(k >= NRV ? k - NRV : 0) * T + t1], vy);
                     unpack16<DT>(buf[gi & 1][i], vd);
@@ -370,12 +404,28 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
             }
         }
     }
+    __shared__ uint64_t tok_sh;
+    if (GRP && t == 0) tok_sh = group_token(grp, c, epoch);
     block_sum2<T>(sdz, sdzt);
 
+    // a group adds its members' sums in fp64, in member order
+    double sum_dz = double(sdz), sum_dzt = double(sdzt);
+    if constexpr (GRP) {
+        __shared__ double tot_sh[2];
+        group_sums<1, T>(grp, c, C, member, tok_sh, t == 0, sum_dz, sum_dzt);
+        if (t == 0) {
+            tot_sh[0] = sum_dz;
+            tot_sh[1] = sum_dzt;
+        }
+        __syncthreads();
+        sum_dz = tot_sh[0];
+        sum_dzt = tot_sh[1];
+        if (member == 0 && t == 0) atomic_st(grp.xchg + c, epoch + 1);
+    }
     const double g = double(g_c);
-    const double db = double(sdz);
-    const double dg = double(sdzt) / g;
-    if (t == 0) {
+    const double db = sum_dz;
+    const double dg = sum_dzt / g;
+    if (t == 0 && member == 0) {
         dbeta[c] = float(db);
         dgamma[c] = float(dg);
     }
@@ -385,15 +435,15 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
 
     // pass 2: dy streamed again, dx written
     {
-        const uint32_t t2 = opaque(t);
+        const uint32_t t2 = opaque(t), u2 = v0 + t2;
         const float a2 = opaquef(a), ia2 = opaquef(inv_a), bc2 = opaquef(bc);
         ChannelWalk32 wd, wx;
-        wd.init(t2, c, C, HWv, T);
-        wx.init(t2, c, C, HWv, T);
+        wd.init(u2, c, C, HWv, T);
+        wx.init(u2, c, C, HWv, T);
         uint4 buf[2][G];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            buf[0][i] = (i < NR && t2 + i * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+            buf[0][i] = (i < NR && u2 + i * T < v1) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
             wd.step();
         }
 #pragma unroll
@@ -403,7 +453,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
             for (int i = 0; i < G; ++i) {
                 const int k = (gi + 1) * G + i;
                 if (k < NR) {
-                    buf[(gi + 1) & 1][i] = (t2 + k * T < Vc) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
+                    buf[(gi + 1) & 1][i] = (u2 + k * T < v1) ? ld16(dy, wd.off) : make_uint4(0, 0, 0, 0);
                     wd.step();
                 }
             }
@@ -411,7 +461,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
             for (int i = 0; i < G; ++i) {
                 const int k = gi * G + i;
                 if (k < NR) {
-                    if (t2 + k * T < Vc) {
+                    if (u2 + k * T < v1) {
                         float vy[V], vd[V];
                         unpack16<DT>(k < NRV ? opaque4(ry[k < NRV ? k : 0])
                                            : ly[(k >= NRV ? k - NRV : 0) * T + t2], vy);
@@ -600,17 +650,37 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw_s(
 // ---------------------------------------------------------------------------
 // host side
 
+// The group of the channel-resident kernels: G workgroups per channel, mg
+// vectors each (G = 1: the whole channel, no exchange words).
+static SliceGroup channel_group(const Plan& pl, void* ws)
+{
+    SliceGroup g;
+    const int64_t vc = pl.m / pl.V;
+    g.G = uint32_t(pl.nchw_group);
+    g.mg = uint32_t(pl.nchw_group > 1 ? ceil_div(vc, pl.nchw_group) : vc);
+    g.xchg = pl.nchw_group > 1
+                 ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + pl.off_xchg)
+                 : nullptr;
+    g.salt = process_salt();
+    return g;
+}
+
 template <int DT, int ACT>
 static void launch_fwd_da(const Plan& pl, void* x, const float* gamma, const float* beta,
                           float* rm, float* rv, float* sm, float* si, float eps, float mom,
-                          float a, hipStream_t s)
+                          float a, void* ws, hipStream_t s)
 {
     const uint32_t C = uint32_t(pl.C), HW = uint32_t(pl.HW), m = uint32_t(pl.m);
+    const SliceGroup grp = channel_group(pl, ws);
     switch (pl.fused_variant) {
 #define IABN_FWD_CASE(ID, T, NR)                                                                  \
     case ID:                                                                                      \
-        hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR>), dim3(C), dim3(T), 0, s, x, C, HW, \
-                           m, gamma, beta, rm, rv, sm, si, eps, mom, a);                          \
+        if (grp.G > 1)                                                                            \
+            hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, true>), dim3(C * grp.G), dim3(T), \
+                               0, s, x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a, grp); \
+        else                                                                                      \
+            hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, false>), dim3(C), dim3(T), 0, s, \
+                               x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a, grp);       \
         break;
         IABN_FUSED_FWD_VARIANTS(IABN_FWD_CASE)
 #undef IABN_FWD_CASE
@@ -620,12 +690,12 @@ static void launch_fwd_da(const Plan& pl, void* x, const float* gamma, const flo
 
 void launch_forward_fused_nchw(const Plan& pl, void* x, const float* gamma, const float* beta,
                                float* rm, float* rv, float* sm, float* si, float eps, float mom,
-                               int act, float a, hipStream_t s)
+                               int act, float a, void* ws, hipStream_t s)
 {
     with_dtype(pl.dtype, [&](auto d) {
         with_act(act, [&](auto ac) {
             launch_fwd_da<decltype(d)::value, decltype(ac)::value>(
-                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, s);
+                pl, x, gamma, beta, rm, rv, sm, si, eps, mom, a, ws, s);
         });
     });
 }
@@ -633,18 +703,26 @@ void launch_forward_fused_nchw(const Plan& pl, void* x, const float* gamma, cons
 template <int DT, int ACT>
 static void launch_bwd_da(const Plan& pl, const void* y, const void* dy, void* dx,
                           const float* gamma, const float* beta, const float* invstd,
-                          float* dgamma, float* dbeta, float a, float ia, hipStream_t s)
+                          float* dgamma, float* dbeta, float a, float ia, void* ws, hipStream_t s)
 {
     const uint32_t C = uint32_t(pl.C), HW = uint32_t(pl.HW), m = uint32_t(pl.m);
+    const SliceGroup grp = channel_group(pl, ws);
+    const uint32_t grid = C * grp.G;     // (the table's G names its dy stream groups)
+    const bool grouped = grp.G > 1;
     switch (pl.fused_bwd_variant) {
 #define IABN_BWD_CASE(ID, T, NRV, NRL, G, DYR)                                                      \
     case ID:                                                                                       \
         if constexpr (DYR)                                                                         \
             hipLaunchKernelGGL((k_bwd_fused_nchw<DT, ACT, T, NRV, true>), dim3(C), dim3(T), 0, s, \
                                y, dy, dx, C, HW, m, gamma, beta, invstd, dgamma, dbeta, a, ia);    \
+        else if (grouped)                                                                          \
+            hipLaunchKernelGGL((k_bwd_stream_nchw<DT, ACT, T, NRV, NRL, G, true>), dim3(grid),     \
+                               dim3(T), 0, s, y, dy, dx, C, HW, m, gamma, beta, invstd, dgamma,    \
+                               dbeta, a, ia, grp);                                                 \
         else                                                                                       \
-            hipLaunchKernelGGL((k_bwd_stream_nchw<DT, ACT, T, NRV, NRL, G>), dim3(C), dim3(T), 0,  \
-                               s, y, dy, dx, C, HW, m, gamma, beta, invstd, dgamma, dbeta, a, ia); \
+            hipLaunchKernelGGL((k_bwd_stream_nchw<DT, ACT, T, NRV, NRL, G, false>), dim3(C),       \
+                               dim3(T), 0, s, y, dy, dx, C, HW, m, gamma, beta, invstd, dgamma,    \
+                               dbeta, a, ia, grp);                                                 \
         break;
         IABN_FUSED_BWD_VARIANTS(IABN_BWD_CASE)
 #undef IABN_BWD_CASE
@@ -654,13 +732,14 @@ static void launch_bwd_da(const Plan& pl, const void* y, const void* dy, void* d
 
 void launch_backward_fused_nchw(const Plan& pl, const void* y, const void* dy, void* dx,
                                 const float* gamma, const float* beta, const float* invstd,
-                                float* dgamma, float* dbeta, int act, float a, hipStream_t s)
+                                float* dgamma, float* dbeta, int act, float a, void* ws,
+                                hipStream_t s)
 {
     const float ia = act == kIdentity ? 1.f : 1.f / a;
     with_dtype(pl.dtype, [&](auto d) {
         with_act(act, [&](auto ac) {
             launch_bwd_da<decltype(d)::value, decltype(ac)::value>(
-                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, s);
+                pl, y, dy, dx, gamma, beta, invstd, dgamma, dbeta, a, ia, ws, s);
         });
     });
 }

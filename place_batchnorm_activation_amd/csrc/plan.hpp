@@ -85,6 +85,9 @@ struct Plan {
     // channel-resident NCHW kernels (-1: not used for this problem)
     int fused_variant = -1;
     int fused_bwd_variant = -1;
+    // workgroups per channel of those kernels (channels one workgroup cannot
+    // hold); their exchange sits at off_xchg like the NHWC groups'
+    int nchw_group = 1;
     // slice-resident NHWC kernels (-1: not used), workgroups per slice, and the
     // workspace section of their exchange (groups only)
     int nhwc_variant = -1;

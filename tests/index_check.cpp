@@ -192,6 +192,58 @@ static void check_plan(const Shape& s, bool vec)
         }
     }
 
+    // ---- channel-resident NCHW kernels in groups: the group the plan takes at 256
+    // CUs, each member's share walked from its first vector
+    {
+        const NchwGroupChoice gc = fused_nchw_group_pick(pl, 256);
+        if (gc.group > 1) {
+            const int64_t HWv = pl.HW / V, Vc = m / V, G = gc.group;
+            const int64_t share = (Vc + G - 1) / G;
+            CHECK(C * G <= 256, "group grid within the CUs");
+            CHECK((G - 1) * share < Vc, "every member holds vectors");
+            const int64_t words = nhwc_exchange_words(C, G, C);
+            CHECK(((C + 31) / 32) * 32 + (C - 1) * G * 4 + (G - 1) * 4 + 3 < words, "exchange words");
+            for (const int var : {gc.fwd, gc.bwd}) {
+                const int T = var == gc.fwd ? fused_fwd_threads(var) : fused_bwd_threads(var);
+                int NR = 0;
+                if (var == gc.fwd) {
+#define IABN_ROW(ID, T_, NR_) if (ID == var) NR = NR_;
+                    IABN_FUSED_FWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+                } else {
+#define IABN_ROW(ID, T_, NRV, NRL, G_, DYR) if (ID == var) NR = NRV + NRL;
+                    IABN_FUSED_BWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+                }
+                CHECK(int64_t(T) * NR >= share, "variant holds the share");
+                std::fill(seen.begin(), seen.end(), 0);
+                for (int64_t c = 0; c < C; ++c)
+                    for (int64_t j = 0; j < G; ++j) {
+                        const int64_t v0 = j * share, v1 = std::min(Vc, v0 + share);
+                        for (int t = 0; t < T; ++t) {
+                            ChannelWalk32 w;
+                            w.init(uint32_t(v0 + t), uint32_t(c), uint32_t(C), uint32_t(HWv),
+                                   uint32_t(T));
+                            for (int k = 0; k < NR; ++k) {
+                                const int64_t v = v0 + t + int64_t(k) * T;
+                                if (v < v1) {
+                                    const int64_t direct = ((v / HWv) * C + c) * HWv + v % HWv;
+                                    CHECK(int64_t(w.off) == direct, "group walk c=%lld j=%lld t=%d",
+                                          (long long)c, (long long)j, t);
+                                    CHECK((int64_t(w.off) << 4) < (int64_t(1) << 32), "byte offset");
+                                    if (int64_t(w.off) < nvec) seen[size_t(w.off)]++;
+                                }
+                                w.step();
+                            }
+                        }
+                    }
+                for (int64_t i = 0; i < nvec; ++i)
+                    CHECK(seen[size_t(i)] == 1, "grouped T=%d NR=%d G=%lld visits %lld %d times",
+                          T, NR, (long long)G, (long long)i, int(seen[size_t(i)]));
+            }
+        }
+    }
+
     // ---- channel-resident NCHW kernels on single elements (off the vector path)
     if (pl.layout == kNCHW && !pl.vec && numel * pl.esize < (int64_t(1) << 32)) {
         const int64_t HW = pl.HW;
@@ -372,6 +424,8 @@ int main(int argc, char** argv)
 {
     std::vector<Shape> shapes = {
         {2, 4, 8, 8, kNCHW, kF32},      {32, 256, 56, 56, kNCHW, kF32},
+        {32, 64, 112, 112, kNCHW, kF32}, {32, 64, 112, 112, kNCHW, kBF16},
+        {4, 16, 300, 300, kNCHW, kF32}, {3, 16, 100, 97, kNCHW, kF32}, {5, 8, 130, 128, kNCHW, kBF16},
         {2, 256, 512, 512, kNHWC, kBF16}, {16, 512, 28, 28, kNCHW, kF32},
         {64, 2048, 7, 7, kNHWC, kBF16},
         {4, 6, 16, 20, kNCHW, kF32}, {3, 5, 17, 19, kNCHW, kF32}, {4, 6, 16, 20, kNCHW, kBF16},

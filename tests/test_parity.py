@@ -428,6 +428,48 @@ def test_slice_resident_variants(wl):
     full_check(wl)
 
 
+# NCHW channels shared by groups of workgroups (channels one workgroup cannot
+# hold, or too few to fill the chip): every group size from 2 to 64, ragged
+# shares, the two-level exchange from 16 members, every storage type and
+# activation.  (case, forward plan, backward plan)
+CHANNEL_GROUPS = [
+    (custom(2, 3, 64, 97, 100), "512x16,group2", "512x16,dy_streamed,group2"),
+    (custom(3, 8, 64, 80, 84, layout="NCHW", dtype="bf16"), "512x16,group2", "512x16,dy_streamed,group2"),
+    (custom(2, 4, 5, 160, 160), "512x16,group4", "512x16,dy_streamed,group4"),
+    (custom(3, 3, 48, 300, 300, layout="NCHW", dtype="bf16"), "512x32,group4", "512x32,dy_streamed,group4"),
+    (custom(4, 3, 24, 300, 300, act="elu", act_param=1.0), "512x32,group8",
+     "512x32,dy_streamed,group8"),
+    (custom(3, 3, 2, 300, 300, layout="NCHW", dtype="f16"), "512x16,group8", "512x16,dy_streamed,group8"),
+    (custom(2, 3, 2, 300, 300, act="identity", act_param=0.0), "512x16,group16",
+     "512x16,dy_streamed,group16"),
+    (custom(2, 5, 2, 300, 300), "512x16,group32", "512x16,dy_streamed,group32"),
+    (custom(3, 32, 1, 200, 200, layout="NCHW", dtype="bf16"), "512x16,group32", "512x16,dy_streamed,group32"),
+    (custom(2, 32, 2, 200, 200), "512x16,group64", "512x16,dy_streamed,group64"),
+    (custom(2, 32, 64, 112, 112), "512x49,group4", "512x49,dy_streamed,group4"),
+]
+
+
+@pytest.mark.parametrize("wl,fwd,bwd", CHANNEL_GROUPS, ids=[w.name for w, _, _ in CHANNEL_GROUPS])
+def test_channel_groups(wl, fwd, bwd):
+    desc = iabn.iabn_describe_plan(wl.N, wl.C, wl.H, wl.W, wl.layout,
+                                   workloads.storage_torch_dtype(wl.dtype), wl.act)
+    assert desc == "forward=channel_resident(%s) backward=channel_resident(%s)" % (fwd, bwd), desc
+    full_check(wl)
+
+
+def test_channel_groups_ignore_workspace_contents():
+    """A grouped NCHW plan gives the same bits with a workspace of arbitrary
+    contents, twice in a row on one workspace, and with dx over dy."""
+    wl = custom(3, 3, 48, 300, 300, layout="NCHW", dtype="bf16")
+    inp = workloads.make_inputs(wl)
+    first = harness.run_gpu(inp)
+    ws = iabn.workspace(wl.N, wl.C, wl.H, wl.W, wl.layout, first.y.dtype)
+    ws.random_(0, 256)
+    _same_run(harness.run_gpu(inp, ws=ws), first)
+    _same_run(harness.run_gpu(inp, ws=ws), first)
+    _same_run(harness.run_gpu(inp, dx_over_dy=True, ws=ws), first)
+
+
 # NHWC maps the slice kernels cannot take (eight channel vectors a row): the
 # split kernels' two-stage pipelines run several sets a thread.  2x64x300x300
 # bf16: 5 sets of row groups per statistics / sums workgroup and 2 sets of dx
