@@ -21,6 +21,8 @@ pytestmark = pytest.mark.gpu
 CASES = [
     workloads.config(2).with_shape(4, 32, 16, 16),                 # NCHW channel-resident
     workloads.config(4).with_shape(4, 64, 28, 28),                 # ... ELU, z and dz kept
+    workloads.config(2).with_shape(3, 64, 97, 100),                # ... channel groups of 2
+    workloads.config(2).with_shape(3, 2, 300, 300),                # ... of 16, two levels
     workloads.config(5).with_shape(16, 512, 7, 7),                 # NHWC slice-resident, group 2
     workloads.config(3).with_shape(5, 256, 20, 20),                # ... group 4
     workloads.config(5),                                           # ... 8 lanes, group 8
