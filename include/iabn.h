@@ -29,7 +29,8 @@
  *     reduction orders.
  *   - Calls that may run at the same time (on different streams) need separate
  *     workspaces; calls in stream order may share one.
- *   - NHWC maps with few rows per channel may run a kernel whose workgroups
+ *   - NHWC maps, and NCHW maps whose channels are large or few, may run a
+ *     kernel whose workgroups share a slice of channels or one channel and
  *     exchange partial sums through the workspace while all of them are
  *     resident (the grid never exceeds the CU count).  Should the device be held
  *     by other work so long that a partner does not arrive within about a
@@ -87,8 +88,8 @@ int iabn_version(void);
 
 /* Bytes of device workspace that iabn_forward_train, iabn_forward_stats,
  * iabn_backward, iabn_backward_reduce and iabn_backward_eval need for this
- * shape (0 for an empty problem).  Depends on the arguments and, for NHWC, on
- * the current device's CU count (which bounds the exchanging kernels' grid).
+ * shape (0 for an empty problem).  Depends on the arguments and on the current
+ * device's CU count (which bounds the exchanging kernels' grid).
  * One buffer serves forward and backward of the same shape.  Returns 0 for
  * invalid arguments too. */
 size_t iabn_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W,
