@@ -287,7 +287,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
         S1 = lds_total<T, LPR, 2 * V>(sh, fe, fl);
         S2 = lds_total<T, LPR, 2 * V>(sh, V + fe, fl);
     }
-    if (grp.G > 1) group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, S1, S2);
+    if (grp.G > 1) group_sums<NCH, T, 8>(grp, s, slices, member, tok_sh, fin, S1, S2);
     if (fin) {
         const double md = double(m);
         const double dm = S1 / md;
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
         db = lds_total<T, LPR, 2 * V>(sh, fe, fl);
         sg = lds_total<T, LPR, 2 * V>(sh, V + fe, fl);
     }
-    if (grp.G > 1) group_sums<NCH, T>(grp, s, slices, member, tok_sh, fin, db, sg);
+    if (grp.G > 1) group_sums<NCH, T, 8>(grp, s, slices, member, tok_sh, fin, db, sg);
     if (fin) {
         const double g = double(g_f);
         const double dg = sg / g;

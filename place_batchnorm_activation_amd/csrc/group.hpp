@@ -90,23 +90,21 @@ __device__ __forceinline__ void group_fetch(const uint64_t* words, uint32_t j, u
     }
 }
 
-// Members kFetchBatch at a time: the sums of channel ch of members j0 ..
-// j0 + kFetchBatch - 1 (< G; this member's own taken from s1, s2), all their
-// words loaded at once on every poll, so that partners that have all published
-// cost one round trip.  NaN for a member not received within the bounded wait.
-constexpr uint32_t kFetchBatch = 4;
-
+// Members FB at a time: the sums of channel ch of members j0 .. j0 + FB - 1
+// (< G; this member's own taken from s1, s2), all their words loaded at once on
+// every poll, so that partners that have all published cost one round trip.
+// NaN for a member not received within the bounded wait.
+template <uint32_t FB>
 __device__ __forceinline__ void group_fetch_batch(const uint64_t* words, uint32_t j0, uint32_t G,
                                                   uint32_t member, uint32_t nch, uint32_t ch,
                                                   uint64_t tok, double s1, double s2,
-                                                  double (&v1)[kFetchBatch],
-                                                  double (&v2)[kFetchBatch])
+                                                  double (&v1)[FB], double (&v2)[FB])
 {
     const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
-    bool need[kFetchBatch];
+    bool need[FB];
     uint32_t left = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < kFetchBatch; ++q) {
+    for (uint32_t q = 0; q < FB; ++q) {
         const uint32_t j = j0 + q;
         v1[q] = j == member ? s1 : __longlong_as_double(0x7FF8000000000000ll);
         v2[q] = j == member ? s2 : __longlong_as_double(0x7FF8000000000000ll);
@@ -114,9 +112,9 @@ __device__ __forceinline__ void group_fetch_batch(const uint64_t* words, uint32_
         left += need[q] ? 1u : 0u;
     }
     for (uint32_t poll = 0; left != 0 && poll <= kMaxPolls; ++poll) {
-        uint64_t w[kFetchBatch][4];
+        uint64_t w[FB][4];
 #pragma unroll
-        for (uint32_t q = 0; q < kFetchBatch; ++q) {
+        for (uint32_t q = 0; q < FB; ++q) {
             if (need[q]) {
                 const uint64_t* src = words + (size_t(j0 + q) * nch + ch) * 4;
                 w[q][0] = atomic_ld(src + 0);
@@ -126,7 +124,7 @@ __device__ __forceinline__ void group_fetch_batch(const uint64_t* words, uint32_
             }
         }
 #pragma unroll
-        for (uint32_t q = 0; q < kFetchBatch; ++q) {
+        for (uint32_t q = 0; q < FB; ++q) {
             if (need[q] && uint32_t(w[q][0] >> 32) == tlo && uint32_t(w[q][1] >> 32) == thi &&
                 uint32_t(w[q][2] >> 32) == tlo && uint32_t(w[q][3] >> 32) == thi) {
                 v1[q] = __longlong_as_double(int64_t((w[q][0] << 32) | uint32_t(w[q][1])));
@@ -174,12 +172,16 @@ constexpr uint32_t kPairBatch = 4;
 // gets back the sums over members 0..G-1, added in that order, so that every
 // member derives the same bits.
 //  - G < kTwoLevelGroup: each finishing thread publishes and then reads the other
-//    members, four at a time (measured: reading them with one thread per
+//    members, FB at a time (measured: reading them with one thread per
 //    (member, channel) loads the memory system with polls and is slower).
 //  - Larger groups, in two levels: every member but 0 publishes; member 0 reads
 //    them, each of its threads loading up to kPairBatch (member, channel) pairs at
 //    once, adds, and publishes the totals in its own slot, which the others read.
-template <uint32_t NCH, int T>
+// FB: members read per poll in one-level groups.  Eight (every partner of a group
+// of 8 in one round trip) made the slice-resident NHWC kernels 5-7% faster on
+// groups of 8; the other kernels keep four, which left them as fast and their
+// register allocation unchanged.
+template <uint32_t NCH, int T, uint32_t FB = 4>
 __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, uint32_t slices,
                                            uint32_t member, uint64_t tok, bool fin, double& s1,
                                            double& s2)
@@ -190,11 +192,11 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
         if (fin) {
             group_publish(words, member, NCH, t, tok, s1, s2);
             double t1 = 0.0, t2 = 0.0;
-            for (uint32_t j0 = 0; j0 < grp.G; j0 += kFetchBatch) {
-                double v1[kFetchBatch], v2[kFetchBatch];
-                group_fetch_batch(words, j0, grp.G, member, NCH, t, tok, s1, s2, v1, v2);
+            for (uint32_t j0 = 0; j0 < grp.G; j0 += FB) {
+                double v1[FB], v2[FB];
+                group_fetch_batch<FB>(words, j0, grp.G, member, NCH, t, tok, s1, s2, v1, v2);
 #pragma unroll
-                for (uint32_t q = 0; q < kFetchBatch; ++q) {
+                for (uint32_t q = 0; q < FB; ++q) {
                     if (j0 + q < grp.G) {
                         t1 += v1[q];
                         t2 += v2[q];
