@@ -261,23 +261,41 @@ inline NhwcChoice fused_nhwc_pick(const Plan& p, int64_t max_grid)
     // 15.6 us; 128x2048x7x7: 21.8 against 27.5) and the forward holds even; with
     // 4 rows a thread or the two-level exchange of larger groups it lost (32x2048x7x7:
     // 10.9 against 10.3; 64x1024x7x7 in groups of 16: 13.6 against 10.8).
+    // The smallest group of width lpr whose members hold their rows in variants of
+    // at most nr_cap rows per thread (none: variant -1).
+    auto grouped = [&](int lpr, int nr_cap) -> NhwcChoice {
+        NhwcChoice c;
+        if (cv % lpr != 0) return c;
+        const int64_t slices = cv / lpr;
+        const int gmax = lpr == 8 ? 8 : 32;
+        for (int g = 1; g <= gmax; g *= 2) {
+            const int64_t grid = slices * g;
+            const int64_t mg = ceil_div(p.m, g);
+            if (g > 1 && (slices % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;
+            const Row* v = holding(lpr, nr_cap, mg);
+            if (v && (g > 1 || fills(grid, v->T) || small)) {
+                c.variant = v->id;
+                c.group = g;
+                return c;
+            }
+        }
+        return c;
+    };
     for (int nr_cap : {4, 8, 13}) {
         for (int lpr : {8, 4, 2}) {
-            if (cv % lpr != 0) continue;
-            const int64_t slices = cv / lpr;
-            const int gmax = lpr == 8 ? 8 : 32;
-            for (int g = 1; g <= gmax; g *= 2) {
-                const int64_t grid = slices * g;
-                const int64_t mg = ceil_div(p.m, g);
-                if (g > 1 && (slices % 8 != 0 || grid > max_grid || (g - 1) * mg >= p.m)) break;
-                const Row* v = holding(lpr, nr_cap, mg);
-                if (v && (g > 1 || fills(grid, v->T) || small)) {
-                    NhwcChoice c;
-                    c.variant = v->id;
-                    c.group = g;
-                    return c;
-                }
+            NhwcChoice c = grouped(lpr, nr_cap);
+            if (c.variant < 0) continue;
+            // At most 4 rows a thread, where four lanes need the two-level exchange
+            // (groups of 16 or more members), two lanes in a smaller group are faster
+            // (8x512x28x28 bf16: 19.6 against 22.5 us a step in groups of 8 against
+            // 16; 64x256x14x14: 21.5 against 23.5 in 16 against 32).  With more rows
+            // a thread the two-lane backward, whose stores leave quarter lines,
+            // loses (32x512x28x28 at 13 rows: 48.7 against 42.8).
+            if (lpr == 4 && nr_cap == 4 && c.group >= 16) {
+                const NhwcChoice c2 = grouped(2, nr_cap);
+                if (c2.variant >= 0 && c2.group < c.group) return c2;
             }
+            return c;
         }
     }
     for (int lpr : {2, 1}) {

@@ -372,8 +372,8 @@ SLICE_PLANS = [
     (custom(2, 3, 1536, 7, 33, layout="NHWC", dtype="f32"), "512x4x4,group2"),
     (custom(2, 1, 768, 80, 13, layout="NHWC", dtype="f32"), "512x4x4,group4"),
     (custom(2, 2, 384, 80, 13, layout="NHWC", dtype="f32"), "512x4x4,group8"),
-    (custom(2, 5, 256, 25, 33, layout="NHWC", dtype="f32"), "512x4x4,group16"),
-    (custom(2, 5, 128, 33, 50, layout="NHWC", dtype="f32"), "512x4x4,group32"),
+    (custom(2, 5, 256, 25, 33, layout="NHWC", dtype="f32"), "512x2x4,group8"),
+    (custom(2, 5, 128, 33, 50, layout="NHWC", dtype="f32"), "512x2x4,group16"),
     (custom(2, 1, 1152, 13, 80, layout="NHWC", dtype="f32"), "512x4x7,group2"),
     (custom(2, 2, 640, 13, 80, layout="NHWC", dtype="f32"), "512x4x7,group4"),
     (custom(2, 5, 384, 25, 33, layout="NHWC", dtype="f32"), "512x4x7,group8"),
@@ -398,13 +398,13 @@ SLICE_PLANS = [
     (custom(4, 5, 768, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
      "512x8x13,group8"),
     (custom(4, 5, 256, 25, 33, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
-     "512x4x4,group16"),
+     "512x2x4,group8"),
     (custom(4, 3, 512, 12, 12, layout="NHWC", dtype="bf16", act="elu", act_param=0.5),
      "256x1x2"),
     (custom(3, 5, 256, 20, 20, layout="NHWC", dtype="bf16", act="identity", act_param=0.0),
      "256x1x2,group4"),
     (custom(2, 2, 256, 60, 60, layout="NHWC", dtype="f32", act="identity", act_param=0.0),
-     "512x4x4,group16"),
+     "512x2x4,group8"),
 ]
 
 
