@@ -357,6 +357,10 @@ SLICE_PLANS = [
     (custom(2, 1, 1032, 60, 17, layout="NHWC", dtype="f32"), "512x2x4"),
     (custom(2, 5, 192, 25, 33, layout="NHWC", dtype="f32"), "512x2x4,group8"),
     (custom(2, 5, 64, 33, 50, layout="NHWC", dtype="f32"), "512x2x4,group16"),
+    # ResNet-50 maps where two lanes in half the group replace four lanes in
+    # the two-level exchange
+    (custom(3, 8, 512, 28, 28, layout="NHWC", dtype="bf16"), "512x2x4,group8"),
+    (custom(3, 64, 256, 14, 14, layout="NHWC", dtype="bf16"), "512x2x4,group16"),
     (custom(2, 8, 64, 33, 64, layout="NHWC", dtype="f32"), "512x2x4,group32"),
     (custom(2, 1, 8, 80, 13, layout="NHWC", dtype="f32"), "512x2x8"),
     (custom(2, 1, 768, 60, 60, layout="NHWC", dtype="f32"), "512x2x8,group2"),
