@@ -5,21 +5,31 @@ one backward (reductions from y + dx) over one batch of synthetic input already
 resident in HBM, all through the C ABI.
 
   python bench.py [--steps K] [--warmup W] [--config I] [--gpus 1] [--no-cpu]
-                  [--dtype f32|bf16|f16] [--mode train|frozen]
+                  [--dtype f32|bf16|f16] [--mode train|frozen|block|shapes|ckpt]
+
+The default workload is the largest single-GPU one, the 2x256x512x512 bf16 NHWC
+segmentation-scale feature map (leaky ReLU 0.01).
 
 Prints ONE JSON line.  value = numel / time-per-step (Gelem/s), measured "cold":
 consecutive steps rotate over buffer sets totalling >= 512 MB, more than the
 256 MB Infinity Cache, so every step reads its tensors from HBM.  The same loop
-on one buffer set is reported as "warm".  Pass-model bytes per step are 8*S
-(S = tensor bytes): forward reads x twice and writes y; backward reads y and dy
-twice and writes dx.
+on one buffer set is reported as "warm".
+
+Byte models (S = tensor bytes):
+  minimal   forward 2S (read x, write y), backward 3S (read y and dy, write dx):
+            5S per step.  The roofline's "achieved" figure and "min_bytes_GBps"
+            use it: no kernel can move less.
+  pass      forward 3S, backward 5S (each reduction pass re-reads its inputs):
+            8S per step, reported as "pass_model_GBps" only; kernels that keep
+            the tensor on chip between their passes move less than this, so the
+            figure is not a bandwidth.
+  counters  rocprofv3 FETCH_SIZE + WRITE_SIZE of the dominant kernel, calibrated
+            on a plain copy ("roofline.traffic", "roofline.hbm_GBps").
 
 The roofline object is for the dominant kernel (the longest average duration),
 timed with HIP events recorded on the stream the library launches on (torch's
 current stream) around each single-kernel call in further timed loops over the
-same buffer sets.  Its algorithmic bytes are the pass-model bytes of the work it
-does: 3S for a whole forward, 5S for a whole backward, 2S / 3S for the split
-path's forward / backward elementwise kernels.
+same buffer sets.
 
 --dtype stores the workload in another storage dtype.  --mode frozen measures
 the step of a network fine-tuned with frozen normalisation statistics instead:
@@ -81,8 +91,36 @@ def load_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp) -> dict:
-    """The fp64 oracle, as it stands, on the host cores: forward + from-y backward."""
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu's "Model name", from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _rel_err(g: np.ndarray, o: np.ndarray, per_channel: bool) -> float:
+    """max_i |g_i - o_i| / (|o_i| + rms(o)), the RMS over the element's channel
+    (per_channel: [N, C, H, W] arrays) or over the whole vector."""
+    if g.size == 0:
+        return 0.0
+    if per_channel:
+        rms = np.sqrt(np.mean(o * o, axis=(0, 2, 3), keepdims=True))
+    else:
+        rms = np.sqrt(np.mean(o * o))
+    return float(np.max(np.abs(g - o) / (np.abs(o) + rms + 1e-300)))
+
+
+def cpu_baseline(wl, inp, gpu=None) -> dict:
+    """The fp64 oracle, as it stands, on the host cores: forward + from-y backward,
+    timed on a bounded sample of whole channels.  With `gpu` (the outputs of one
+    step of the HIP path on the same input), also the largest error of each
+    output on those channels against the oracle: the forward on the same x bits,
+    the backward on the GPU's own y bits and save_invstd."""
     import oracle
     import workloads
     x = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
@@ -91,22 +129,39 @@ def cpu_baseline(wl, inp) -> dict:
     per_elem_guess = 4e-8 / max(1, oracle.num_threads())
     ch = int(min(wl.C, max(1, 10.0 / (per_elem_guess * wl.m) / 3)))
     xs, dys = np.ascontiguousarray(x[:, :ch]), np.ascontiguousarray(dy[:, :ch])
+    del x, dy
     g, b = inp.gamma[:ch], inp.beta[:ch]
+    f32 = lambda v: float(np.float32(v))               # the scalars the library receives
+    a, eps, mom = f32(wl.act_param), f32(wl.eps), f32(wl.momentum)
     times = []
     reps = 3
     for _ in range(reps):
         t0 = time.perf_counter()
-        f = oracle.forward_train(xs, g, b, wl.act, wl.act_param, wl.eps, wl.momentum,
-                                 inp.running_mean[:ch], inp.running_var[:ch], storage=wl.dtype)
-        oracle.backward_from_y(f["y"], dys, g, b, f["invstd"], wl.act, wl.act_param)
+        f = oracle.forward_train(xs, g, b, wl.act, a, eps, mom, inp.running_mean[:ch],
+                                 inp.running_var[:ch], storage=wl.dtype)
+        oracle.backward_from_y(f["y"], dys, g, b, f["invstd"], wl.act, a)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     n = ch * wl.m
-    return {"value": round(n / t / 1e9, 5), "unit": "Gelem/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%d of %d channels (all %d elements each) of the same workload, fp64 "
-                      "forward_train + backward_from_y, median of %d runs (%.2f s each)"
-                      % (ch, wl.C, wl.m, reps, t)}
+    out = {"value": round(n / t / 1e9, 5), "unit": "Gelem/s", "cores": oracle.num_threads(),
+           "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": "%d of %d channels (all %d elements each) of the same workload, fp64 "
+                     "forward_train + backward_from_y, median of %d runs (%.2f s each)"
+                     % (ch, wl.C, wl.m, reps, t)}
+    if gpu is not None:
+        y = gpu["y"][:, :ch]
+        err = {"y": _rel_err(y, f["y"], True)}
+        for k, ok in (("save_mean", "mean"), ("save_invstd", "invstd"),
+                      ("running_mean", "running_mean"), ("running_var", "running_var")):
+            err[k] = _rel_err(gpu[k][:ch].astype(np.float64), f[ok], False)
+        o = oracle.backward_from_y(np.ascontiguousarray(y), dys, g, b,
+                                   gpu["save_invstd"][:ch].astype(np.float64), wl.act, a)
+        err["dx"] = _rel_err(gpu["dx"][:, :ch], o["dx"], True)
+        err["dgamma"] = _rel_err(gpu["dgamma"][:ch].astype(np.float64), o["dgamma"], False)
+        err["dbeta"] = _rel_err(gpu["dbeta"][:ch].astype(np.float64), o["dbeta"], False)
+        out["max_rel_err"] = {k: float("%.3g" % v) for k, v in err.items()}
+        out["max_rel_err_channels"] = ch
+    return out
 
 
 def run_frozen(args, wl) -> int:
@@ -356,7 +411,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload index 1..5 (default 2)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload index 1..5 (default 3, the largest)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--warm-only", action="store_true", help="one buffer set (for profiling)")
     ap.add_argument("--dtype", choices=("f32", "bf16", "f16"), default=None,
@@ -399,6 +455,23 @@ def main() -> int:
         return run_block(args, wl)
     if args.mode == "shapes":
         return run_shapes(args)
+    return run_train(args, wl)
+
+
+# Minimal bytes of one launch of each single-kernel call, in units of S: a
+# forward reads x and writes y, a backward reads y and dy and writes dx; the
+# split path's elementwise kernels do the same.  The pass model charges a
+# forward 3S and a backward 5S (its reductions re-read their inputs).
+MIN_S = {"fwd": 2, "bwd": 3, "fwd_apply": 2, "bwd_apply": 3}
+PASS_S = {"fwd": 3, "bwd": 5, "fwd_apply": 2, "bwd_apply": 3}
+
+
+def run_train(args, wl) -> int:
+    """Steps of iabn_forward_train + iabn_backward (the training hot path)."""
+    import torch
+    import place_batchnorm_activation_amd as iabn
+    import workloads
+
     N, C, H, W = wl.N, wl.C, wl.H, wl.W
     inp = workloads.make_inputs(wl)
     dev = torch.device("cuda", 0)
@@ -423,23 +496,17 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
-    def stages(s):
-        return [
-            lambda: iabn.iabn_forward_stats(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, sm, si,
-                                            wl.eps, wl.momentum, ws, sp),
-            lambda: iabn.iabn_forward_apply(s["x"], N, C, H, W, wl.layout, wl.act, wl.act_param,
-                                            ws, sp),
-            lambda: iabn.iabn_backward_reduce(s["x"], s["dy"], N, C, H, W, wl.layout, g, b, si,
-                                              dg, db, wl.act, wl.act_param, ws, sp),
-            lambda: iabn.iabn_backward_apply(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout,
-                                             wl.act, wl.act_param, ws, sp),
-        ]
-
-    def step(s):
+    def fwd(s):
         iabn.iabn_forward_train(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, sm, si, wl.act,
                                 wl.act_param, wl.eps, wl.momentum, ws, sp)
+
+    def bwd(s):
         iabn.iabn_backward(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout, g, b, si, dg, db,
                            wl.act, wl.act_param, ws, sp)
+
+    def step(s):
+        fwd(s)
+        bwd(s)
 
     def timed(set_list, k):
         torch.cuda.synchronize()
@@ -460,11 +527,10 @@ def main() -> int:
     ms_warm = timed([warm_set], args.steps)
 
     # Per-launch durations: HIP events recorded on the library's stream (torch's
-    # current stream) around each call.  With the channel-resident path each of
-    # iabn_forward_train / iabn_backward is one kernel; with the split path the
-    # single-kernel stages (apply) are timed through the stage entry points.
+    # current stream) around each call.  A fused pass is one kernel; with the split
+    # path the single-kernel stages (the elementwise kernels) are timed through the
+    # stage entry points.
     plan = iabn.iabn_describe_plan(N, C, H, W, wl.layout, x0.dtype, wl.act)
-    # kernel family of each pass: channel_resident / slice_resident (one kernel) or split
     fam_fwd = plan.split()[0].split("=", 1)[1].split("(", 1)[0]
     fam_bwd = plan.split()[1].split("=", 1)[1].split("(", 1)[0]
     fused_fwd = fam_fwd != "split"
@@ -485,41 +551,61 @@ def main() -> int:
         for i in range(args.steps):
             for j in range(len(calls)):
                 acc[j] += evs[i][j].elapsed_time(evs[i][j + 1])
-        return [1e3 * a / args.steps for a in acc]
+        return [float(1e3 * a / args.steps) for a in acc]
 
-    call_us = event_loop([
-        lambda s: iabn.iabn_forward_train(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, sm, si,
-                                          wl.act, wl.act_param, wl.eps, wl.momentum, ws, sp),
-        lambda s: iabn.iabn_backward(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout, g, b, si,
-                                     dg, db, wl.act, wl.act_param, ws, sp)])
+    call_us = event_loop([fwd, bwd])
     timings = {"forward_train": round(call_us[0], 3), "backward": round(call_us[1], 3)}
-    # single kernels and their pass-model bytes: forward 3S, backward 5S, the split
-    # path's apply kernels 2S and 3S
-    kernels = {}
+    kernels = {}             # name -> (avg us, kind in MIN_S)
     if fused_fwd:
-        kernels["fwd_" + fam_fwd] = (call_us[0], 3 * S)
+        kernels["fwd_" + fam_fwd] = (call_us[0], "fwd")
     if fused_bwd:
-        kernels["bwd_" + fam_bwd] = (call_us[1], 5 * S)
+        kernels["bwd_" + fam_bwd] = (call_us[1], "bwd")
     if not (fused_fwd and fused_bwd):
+        st_us = event_loop([
+            lambda s: iabn.iabn_forward_stats(s["x"], N, C, H, W, wl.layout, g, b, rm, rv, sm,
+                                              si, wl.eps, wl.momentum, ws, sp),
+            lambda s: iabn.iabn_forward_apply(s["x"], N, C, H, W, wl.layout, wl.act,
+                                              wl.act_param, ws, sp),
+            lambda s: iabn.iabn_backward_reduce(s["x"], s["dy"], N, C, H, W, wl.layout, g, b, si,
+                                                dg, db, wl.act, wl.act_param, ws, sp),
+            lambda s: iabn.iabn_backward_apply(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout,
+                                               wl.act, wl.act_param, ws, sp)])
         names = ["forward_stats", "forward_apply", "backward_reduce", "backward_apply"]
-        st_us = event_loop([(lambda s, f=f: f(s)) for f in (lambda s: stages(s)[0](),
-                                                            lambda s: stages(s)[1](),
-                                                            lambda s: stages(s)[2](),
-                                                            lambda s: stages(s)[3]())])
         timings.update({n: round(u, 3) for n, u in zip(names, st_us)})
         if not fused_fwd:
-            kernels["fwd_apply"] = (st_us[1], 2 * S)
+            kernels["fwd_apply"] = (st_us[1], "fwd_apply")
         if not fused_bwd:
-            kernels["bwd_apply"] = (st_us[3], 3 * S)
+            kernels["bwd_apply"] = (st_us[3], "bwd_apply")
     print("bench: %s; per-call us %s" % (plan, timings), file=sys.stderr, flush=True)
     dom = max(kernels, key=lambda k: kernels[k][0])
-    t_dom_us, dom_bytes = kernels[dom]
+    t_dom_us, kind = kernels[dom]
+    dom_bytes = MIN_S[kind] * S
     achieved = dom_bytes / (t_dom_us * 1e-6) / 1e9
     traffic = load_traffic(dom, wl.name)
 
+    # One step on the original input, twice from the same state: the outputs the
+    # oracle is compared with, and run-to-run bitwise determinism.
+    def reference_step():
+        s = {"x": x0.clone(), "dy": dy0.clone(), "dx": torch.empty_like(dy0)}
+        rm1 = torch.from_numpy(inp.running_mean).to(dev)
+        rv1 = torch.from_numpy(inp.running_var).to(dev)
+        sm1, si1 = torch.empty(C, device=dev), torch.empty(C, device=dev)
+        dg1, db1 = torch.empty(C, device=dev), torch.empty(C, device=dev)
+        iabn.iabn_forward_train(s["x"], N, C, H, W, wl.layout, g, b, rm1, rv1, sm1, si1, wl.act,
+                                wl.act_param, wl.eps, wl.momentum, ws, sp)
+        iabn.iabn_backward(s["x"], s["dy"], s["dx"], N, C, H, W, wl.layout, g, b, si1, dg1, db1,
+                           wl.act, wl.act_param, ws, sp)
+        torch.cuda.synchronize()
+        return {"y": s["x"], "dx": s["dx"], "save_mean": sm1, "save_invstd": si1,
+                "running_mean": rm1, "running_var": rv1, "dgamma": dg1, "dbeta": db1}
+
+    del sets
+    r0, r1 = reference_step(), reference_step()
+    deterministic = all(torch.equal(r0[k], r1[k]) for k in r0)
+    del r1
+
     numel = wl.numel
     t = ms_cold * 1e-3
-    gbps = 8 * S / t / 1e9
     out = {
         "metric": METRIC,
         "value": round(numel / t / 1e9, 4),
@@ -536,23 +622,38 @@ def main() -> int:
         "config": {"workload": wl.name, "N": N, "C": C, "H": H, "W": W, "layout": wl.layout,
                    "storage": wl.dtype, "act": wl.act, "act_param": wl.act_param,
                    "parallelism": "single_gpu"},
-        "pass_model_GBps": round(gbps, 1),
-        "pass_model_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "min_bytes_GBps": round(5 * S / t / 1e9, 1),
+        "min_bytes_frac_of_peak": round(5 * S / t / 1e9 / HBM_PEAK_GBPS, 4),
+        "pass_model_GBps": round(8 * S / t / 1e9, 1),
         "protocol": "cold: %d rotating buffer sets of %.0f MB" % (nsets, 3 * S / 1e6),
         "warm": {"ms_per_step": round(ms_warm, 5),
                  "value": round(numel / (ms_warm * 1e-3) / 1e9, 4),
-                 "pass_model_GBps": round(8 * S / (ms_warm * 1e-3) / 1e9, 1)},
+                 "min_bytes_GBps": round(5 * S / (ms_warm * 1e-3) / 1e9, 1)},
+        "deterministic": bool(deterministic),
         "plan": plan,
         "launch_us": timings,
         "roofline": {"kernel": dom, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
+                     "hbm_GBps": (round(traffic / (t_dom_us * 1e-6) / 1e9, 1)
+                                  if traffic else None),
+                     "hbm_frac": (round(traffic / (t_dom_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                                  if traffic else None),
                      "algorithmic_bytes_per_launch": dom_bytes,
+                     "pass_model_bytes_per_launch": PASS_S[kind] * S,
                      "avg_launch_us": round(t_dom_us, 3)},
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(wl, inp)
+        host = {}
+        for k, v in r0.items():
+            if v.dim() == 1:
+                host[k] = v.cpu().numpy()
+            else:
+                host[k] = workloads.from_storage(workloads.from_torch(v, wl.dtype), N, C, H, W,
+                                                 wl.layout, wl.dtype)
+        del r0
+        out["cpu_baseline"] = cpu_baseline(wl, inp, host)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -49,9 +49,37 @@ def to_device(a: np.ndarray, wl: workloads.Workload, device="cuda") -> torch.Ten
     return workloads.to_torch(a, wl.dtype).reshape(storage_shape(wl)).to(device)
 
 
-def to_nchw64(t: torch.Tensor, wl: workloads.Workload) -> np.ndarray:
-    return workloads.from_storage(workloads.from_torch(t, wl.dtype), wl.N, wl.C, wl.H, wl.W,
+def to_nchw64(t: torch.Tensor, wl: workloads.Workload, sel=None) -> np.ndarray:
+    """A storage tensor (any device) -> fp64 logical-NCHW host array; with `sel` (a
+    slice or index list of channels) only those channels are moved and widened."""
+    if sel is None:
+        return workloads.from_storage(workloads.from_torch(t, wl.dtype), wl.N, wl.C, wl.H, wl.W,
+                                      wl.layout, wl.dtype)
+    idx = _channel_index(sel, wl.C)
+    if wl.layout == "NCHW":
+        part = t[:, idx]
+    else:
+        part = t[..., idx]
+    return workloads.from_storage(workloads.from_torch(part, wl.dtype), wl.N, len(idx), wl.H,
+                                  wl.W, wl.layout, wl.dtype)
+
+
+def storage_channels(a: np.ndarray, wl: workloads.Workload, sel=None) -> np.ndarray:
+    """A host storage array (wl.layout) -> fp64 logical-NCHW array of the channels in
+    `sel` (all when None), widened exactly."""
+    if sel is None:
+        return workloads.from_storage(a, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    idx = _channel_index(sel, wl.C)
+    a = a.reshape(storage_shape(wl))
+    part = a[:, idx] if wl.layout == "NCHW" else a[..., idx]
+    return workloads.from_storage(np.ascontiguousarray(part), wl.N, len(idx), wl.H, wl.W,
                                   wl.layout, wl.dtype)
+
+
+def _channel_index(sel, C: int):
+    if isinstance(sel, slice):
+        return list(range(C))[sel]
+    return [int(c) for c in np.asarray(sel).reshape(-1)]
 
 
 @dataclasses.dataclass
@@ -102,14 +130,15 @@ def run_gpu(inp: workloads.Inputs, backward: bool = True, dx_over_dy: bool = Fal
 def check_forward(inp: workloads.Inputs, run: GpuRun, channels=None) -> dict:
     """Forward errors against the oracle on the same x bits (optionally a channel subset)."""
     wl = inp.wl
-    x = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
-    y = to_nchw64(run.y, wl)
-    sel = slice(None) if channels is None else np.asarray(channels)
-    f = oracle.forward_train(x[:, sel], inp.gamma[sel], inp.beta[sel], wl.act, f32(wl.act_param),
+    x = storage_channels(inp.x, wl, channels)
+    y = to_nchw64(run.y, wl, channels)
+    sel = slice(None) if channels is None else np.asarray(_channel_index(channels, wl.C))
+    f = oracle.forward_train(x, inp.gamma[sel], inp.beta[sel], wl.act, f32(wl.act_param),
                              f32(wl.eps), f32(wl.momentum), inp.running_mean[sel],
                              inp.running_var[sel], storage=wl.dtype)
+    del x
     return {
-        "y": rel_err_tensor(y[:, sel], f["y"]),
+        "y": rel_err_tensor(y, f["y"]),
         "save_mean": rel_err_vec(run.save_mean[sel], f["mean"]),
         "save_invstd": rel_err_vec(run.save_invstd[sel], f["invstd"]),
         "running_mean": rel_err_vec(run.running_mean[sel], f["running_mean"]),
@@ -135,24 +164,61 @@ def check_backward(inp: workloads.Inputs, run: GpuRun, channels=None,
     cancellation of those terms (m = 2: xhat^2 = v/(v+eps) ~ 1), where no fp32
     evaluation can carry relative accuracy in dx itself."""
     wl = inp.wl
-    y = to_nchw64(run.y, wl)
-    dy = workloads.from_storage(inp.dy, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
-    dx = to_nchw64(run.dx, wl)
-    sel = slice(None) if channels is None else np.asarray(channels)
-    o = oracle.backward_from_y(y[:, sel], dy[:, sel], inp.gamma[sel], inp.beta[sel],
+    y = to_nchw64(run.y, wl, channels)
+    dy = storage_channels(inp.dy, wl, channels)
+    dx = to_nchw64(run.dx, wl, channels)
+    sel = slice(None) if channels is None else np.asarray(_channel_index(channels, wl.C))
+    o = oracle.backward_from_y(y, dy, inp.gamma[sel], inp.beta[sel],
                                run.save_invstd[sel].astype(np.float64), wl.act, f32(wl.act_param))
     if dx_scale == "terms":
         A = (inp.gamma[sel].astype(np.float64) * run.save_invstd[sel])[None, :, None, None]
-        dz = _slope_from_y(y[:, sel], wl.act, f32(wl.act_param)) * dy[:, sel]
+        dz = _slope_from_y(y, wl.act, f32(wl.act_param)) * dy
         terms = np.sqrt(np.mean((A * dz) ** 2, axis=(0, 2, 3), keepdims=True))
-        e_dx = float(np.max(np.abs(dx[:, sel] - o["dx"]) / (np.abs(o["dx"]) + terms + 1e-300)))
+        e_dx = float(np.max(np.abs(dx - o["dx"]) / (np.abs(o["dx"]) + terms + 1e-300)))
     else:
-        e_dx = rel_err_tensor(dx[:, sel], o["dx"])
+        e_dx = rel_err_tensor(dx, o["dx"])
     return {
         "dx": e_dx,
         "dgamma": rel_err_vec(run.dgamma[sel], o["dgamma"]),
         "dbeta": rel_err_vec(run.dbeta[sel], o["dbeta"]),
     }
+
+
+def check_all_channels(inp: workloads.Inputs, run: GpuRun, block: int) -> dict:
+    """Forward and backward errors over every element and channel, `block` channels
+    at a time (bounds host memory on large tensors).  y and dx errors use each
+    channel's own RMS as in check_forward / check_backward; the per-channel vectors
+    are gathered over all C channels first and compared with the RMS over all C."""
+    wl = inp.wl
+    a = f32(wl.act_param)
+    err = {"y": 0.0, "dx": 0.0}
+    ref = {k: [] for k in ("mean", "invstd", "running_mean", "running_var", "dgamma", "dbeta")}
+    for c0 in range(0, wl.C, block):
+        sel = slice(c0, min(wl.C, c0 + block))
+        x = storage_channels(inp.x, wl, sel)
+        f = oracle.forward_train(x, inp.gamma[sel], inp.beta[sel], wl.act, a, f32(wl.eps),
+                                 f32(wl.momentum), inp.running_mean[sel], inp.running_var[sel],
+                                 storage=wl.dtype)
+        del x
+        y = to_nchw64(run.y, wl, sel)
+        err["y"] = max(err["y"], rel_err_tensor(y, f["y"]))
+        dy = storage_channels(inp.dy, wl, sel)
+        o = oracle.backward_from_y(y, dy, inp.gamma[sel], inp.beta[sel],
+                                   run.save_invstd[sel].astype(np.float64), wl.act, a)
+        del y, dy
+        err["dx"] = max(err["dx"], rel_err_tensor(to_nchw64(run.dx, wl, sel), o["dx"]))
+        for k in ("mean", "invstd", "running_mean", "running_var"):
+            ref[k].append(f[k])
+        ref["dgamma"].append(o["dgamma"])
+        ref["dbeta"].append(o["dbeta"])
+    ref = {k: np.concatenate(v) for k, v in ref.items()}
+    err["save_mean"] = rel_err_vec(run.save_mean, ref["mean"])
+    err["save_invstd"] = rel_err_vec(run.save_invstd, ref["invstd"])
+    err["running_mean"] = rel_err_vec(run.running_mean, ref["running_mean"])
+    err["running_var"] = rel_err_vec(run.running_var, ref["running_var"])
+    err["dgamma"] = rel_err_vec(run.dgamma, ref["dgamma"])
+    err["dbeta"] = rel_err_vec(run.dbeta, ref["dbeta"])
+    return err
 
 
 def assert_within(errs: dict, dtype: str, what: str = "") -> None:

@@ -72,14 +72,21 @@ def test_mid_sizes(wl):
 
 
 # ---------------------------------------------------------------------------
-# the five workloads at their full sizes; the oracle checks a sample of channels
+# the five workloads at their full sizes, every element and channel against the
+# oracle (the 268 MB segmentation map 32 channels at a time, to bound host memory)
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_full_size_sampled(idx):
+def test_full_size_every_channel(idx):
     wl = workloads.config(idx)
-    rng = np.random.default_rng(idx)
-    ch = sorted(set([0, 1, wl.C // 2, wl.C - 1] + list(rng.choice(wl.C, 8, replace=False))))
-    inp, run = full_check(wl, channels=ch)
+    inp = workloads.make_inputs(wl)
+    print("case:", wl.name, iabn.iabn_describe_plan(wl.N, wl.C, wl.H, wl.W, wl.layout,
+                                                     workloads.storage_torch_dtype(wl.dtype),
+                                                     wl.act), flush=True)
+    run = harness.run_gpu(inp)
+    block = 32 if wl.storage_bytes > (128 << 20) else wl.C
+    errs = harness.check_all_channels(inp, run, block)
+    print("  ", errs, flush=True)
+    harness.assert_within(errs, wl.dtype, wl.name)
     # property that holds at any size: every channel's input gradient sums to zero
     dx = run.dx.float() if wl.layout == "NCHW" else run.dx.float().permute(0, 3, 1, 2)
     s = dx.sum(dim=(0, 2, 3)).double().cpu().numpy()
@@ -166,7 +173,12 @@ def test_misaligned_pointers_take_scalar_path(layout, dtype):
 @pytest.mark.parametrize("wl", [custom(2, 8, 32, 28, 28), custom(3, 4, 64, 32, 32),
                                 custom(4, 4, 32, 14, 14), custom(5, 8, 512, 7, 7),
                                 custom(3, 5, 256, 40, 60, layout="NHWC", dtype="bf16"),
-                                custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16")],
+                                custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16"),
+                                # the four full-size workloads in the kernels they plan:
+                                # channel-resident NCHW, streamed slice forward + split
+                                # backward, dy-resident NCHW ELU, eight-lane groups of 8
+                                workloads.config(2), workloads.config(3), workloads.config(4),
+                                workloads.config(5)],
                          ids=lambda w: w.name)
 def test_bitwise_deterministic(wl):
     inp = workloads.make_inputs(wl)
