@@ -20,8 +20,10 @@
  *     per-channel finishing steps in fp64.
  *   - m = N*H*W is the reduction length of one channel.
  *   - The caller owns every buffer, including the workspace.  The library never
- *     allocates, frees or synchronises; it is stateless and reentrant.  Calls
- *     are enqueued on `stream` and return once launched.  The status reports
+ *     allocates or frees, and the compute entry points never synchronise: they
+ *     are reentrant and keep no state besides one process-wide setting
+ *     (iabn_set_grouped_kernels).  Only iabn_workspace_status synchronises.
+ *     Calls are enqueued on `stream` and return once launched.  The status reports
  *     argument validation (done before any HIP call) and launch errors; faults
  *     inside kernels surface at the caller's next synchronisation.
  *   - Results are bitwise deterministic for a given shape, layout, dtype,
@@ -35,7 +37,12 @@
  *     resident (the grid never exceeds the CU count).  Should the device be held
  *     by other work so long that a partner does not arrive within about a
  *     second, the waiting workgroup gives up and its statistics, and every
- *     output computed from them, become NaN instead of the kernel hanging.
+ *     output computed from them, become NaN instead of the kernel hanging; it
+ *     also records the timeout in the workspace, which iabn_workspace_status
+ *     reports.  Callers that share the device with long-running work on other
+ *     streams can switch these kernels off (iabn_set_grouped_kernels, or the
+ *     environment variable IABN_GROUPED_KERNELS=0): every call then takes
+ *     kernels whose workgroups never wait on one another.
  *   - Calls may be captured in a HIP graph (stream capture): they launch
  *     kernels only, with no allocation, memset, copy or synchronisation, and a
  *     replay gives the same bits as the eager call.
@@ -85,6 +92,32 @@ const char *iabn_status_string(iabn_status status);
 
 /* Library ABI version: major*10000 + minor*100 + patch. */
 int iabn_version(void);
+
+/* Process-wide switch of the kernels whose workgroups wait on one another
+ * (the exchanging kernels described above).  enabled = 1 allows them (the
+ * default unless the environment variable IABN_GROUPED_KERNELS is "0" when the
+ * library first plans a call), 0 forbids them: NHWC maps then take one
+ * workgroup per slice of channels or the split kernels, NCHW maps one
+ * workgroup per channel or the split kernels, with results equal within the
+ * parity tolerances (the reduction order differs).  enabled < 0 changes
+ * nothing.  Returns the setting in force before the call.  Calls planned
+ * after it follow the new setting; iabn_workspace_size does not depend on it.
+ * This is the only state the library keeps across calls besides per-device
+ * caches of the CU count. */
+int iabn_set_grouped_kernels(int enabled);
+
+/* Reads the exchange status word that every workspace carries in its first
+ * 256 bytes: *timed_out = 1 if an exchanging kernel that used this workspace
+ * gave up waiting for a partner (its outputs then hold NaN) since the word was
+ * last cleared, else 0.  clear != 0 resets the word after reading it.  Unlike
+ * every other entry point this one synchronises `stream` (it copies the word
+ * to the host); call it after the work to check, not inside graph capture.
+ * A workspace whose contents were never written by the library reads as 0
+ * (the recorded value is one fixed 64-bit pattern).
+ * Errors: IABN_ERR_INVALID_ARG (timed_out NULL), IABN_ERR_WORKSPACE (NULL or
+ * under 256 bytes), IABN_ERR_MISALIGNED, IABN_ERR_HIP (copy failed). */
+iabn_status iabn_workspace_status(void *workspace, size_t workspace_bytes, int clear,
+                                  int *timed_out, hipStream_t stream);
 
 /* Bytes of device workspace that iabn_forward_train, iabn_forward_stats,
  * iabn_backward, iabn_backward_reduce and iabn_backward_eval need for this
@@ -144,7 +177,11 @@ iabn_status iabn_forward_apply(void *x_inout,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
-/* Inference forward, in place, with the running statistics:
+/* Inference forward, in place, with the running statistics: section 3, "Batch
+ * Normalization Review" normalises with the minibatch statistics in training;
+ * at inference the pages state no rule, and the usual one is taken, the
+ * running estimates that iabn_forward_train keeps (momentum update, unbiased
+ * variance) standing in for the batch statistics:
  *   y = act(gamma_c * (x - running_mean_c) / sqrt(running_var_c + eps) + beta_c)
  * written over x.  All per-channel inputs are fp32 [C] and required.  Needs no
  * workspace.  An empty tensor (any extent 0) is a no-op. */

@@ -60,6 +60,10 @@ lib.iabn_backward_reduce.argtypes = [_P, _P] + _SHAPE + [_P, _P, _P, _P, _P, _IN
 lib.iabn_backward_apply.argtypes = [_P, _P, _P] + _SHAPE + [_INT, _F, _P, _SZ, _P]
 lib.iabn_backward_eval.argtypes = [_P, _P, _P] + _SHAPE + [_P, _P, _P, _F, _P, _P, _INT, _F, _P,
                                                            _SZ, _P]
+lib.iabn_set_grouped_kernels.argtypes = [_INT]
+lib.iabn_set_grouped_kernels.restype = _INT
+lib.iabn_workspace_status.argtypes = [_P, _SZ, _INT, ctypes.POINTER(_INT), _P]
+lib.iabn_workspace_status.restype = _INT
 lib.iabn_describe_plan.argtypes = _SHAPE + [_INT, _INT, ctypes.c_char_p, _SZ]
 lib.iabn_describe_plan.restype = _INT
 for _fn in ("iabn_forward_train", "iabn_forward_stats", "iabn_forward_apply", "iabn_forward_eval",
@@ -127,14 +131,47 @@ def iabn_version() -> int:
     return lib.iabn_version()
 
 
+class ExchangeTimeout(RuntimeError):
+    """A kernel whose workgroups exchange partial sums gave up waiting for a
+    partner: the outputs of the calls since the workspace was last checked may
+    hold NaN."""
+
+
+def iabn_set_grouped_kernels(enabled: Optional[bool] = None) -> bool:
+    """Allow (True) or forbid (False) the kernels whose workgroups wait on one
+    another, process-wide; None only reads the setting.  Returns the previous
+    setting."""
+    return bool(lib.iabn_set_grouped_kernels(-1 if enabled is None else int(bool(enabled))))
+
+
+def iabn_workspace_status(ws, clear: bool = True, stream=None) -> bool:
+    """Whether a wait of an exchanging kernel ran out on this workspace since the
+    word was last cleared (synchronises the stream)."""
+    flag = _INT(0)
+    _check("iabn_workspace_status",
+           lib.iabn_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), int(clear),
+                                     ctypes.byref(flag), _stream(stream)))
+    return bool(flag.value)
+
+
+def check_workspace(ws, stream=None) -> None:
+    """Raise ExchangeTimeout if an exchanging kernel timed out on this workspace
+    (reads and clears the word; synchronises the stream)."""
+    if iabn_workspace_status(ws, True, stream):
+        raise ExchangeTimeout("a grouped kernel gave up waiting for a partner workgroup; "
+                              "outputs since the last check may hold NaN "
+                              "(iabn_set_grouped_kernels(False) avoids these kernels)")
+
+
 def iabn_workspace_size(N, C, H, W, layout, dtype) -> int:
     """dtype: F32/BF16/F16 code or a torch dtype."""
     return lib.iabn_workspace_size(N, C, H, W, _code(layout, LAYOUTS), _dtype_arg(dtype))
 
 
 def workspace(N, C, H, W, layout, dtype, device="cuda") -> torch.Tensor:
-    """A workspace tensor of the size the library asks for (at least 16 bytes)."""
-    n = max(16, iabn_workspace_size(N, C, H, W, layout, dtype))
+    """A workspace tensor of the size the library asks for (at least its 256-byte
+    header)."""
+    n = max(256, iabn_workspace_size(N, C, H, W, layout, dtype))
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 

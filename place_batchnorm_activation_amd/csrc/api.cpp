@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -89,10 +90,35 @@ int64_t coresident_grid()
     return cus;
 }
 
-// act < 0: the stage entry points, which always run the split kernels.
-Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
-              bool ptrs16, int act = -1)
+// Whether plans may take the kernels whose workgroups wait on one another (the
+// NCHW channel groups, the NHWC slice groups and the streamed slice kernels):
+// iabn_set_grouped_kernels, initially on unless the environment variable
+// IABN_GROUPED_KERNELS is "0".
+std::atomic<int> g_grouped{-1};
+
+bool grouped_allowed()
 {
+    int v = g_grouped.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = getenv("IABN_GROUPED_KERNELS");
+        v = (e && e[0] == '0' && e[1] == '\0') ? 0 : 1;
+        int expect = -1;
+        g_grouped.compare_exchange_strong(expect, v, std::memory_order_relaxed);
+        v = g_grouped.load(std::memory_order_relaxed);
+    }
+    return v != 0;
+}
+
+// act < 0: the stage entry points, which always run the split kernels.
+// allow_groups: whether grouped kernels may be planned (by default the
+// process-wide setting; the workspace size always plans them, so that one
+// workspace serves either setting).
+Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
+              bool ptrs16, int act = -1, int allow_groups = -1)
+{
+    // the grid a grouped kernel may span: the device's CU count, or 0 (no groups)
+    const bool groups = allow_groups < 0 ? grouped_allowed() : allow_groups != 0;
+    auto group_grid = [&]() -> int64_t { return groups ? coresident_grid() : 0; };
     const bool vec = ptrs16 && vec_shape_ok(C, H * W, layout, dtype);
     Plan p = make_plan(N, C, H, W, layout, dtype, vec);
     if (act >= 0 && p.layout == kNCHW && p.vec && p.numel > 0) {
@@ -104,7 +130,7 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
         if (p.fused_variant < 0 || p.fused_bwd_variant < 0) {
             // a channel larger than one workgroup holds, or too few channels to
             // fill the chip: a group of workgroups per channel
-            const NchwGroupChoice g = fused_nchw_group_pick(p, coresident_grid());
+            const NchwGroupChoice g = fused_nchw_group_pick(p, group_grid());
             if (g.group > 1) {
                 p.fused_variant = g.fwd;
                 p.fused_bwd_variant = g.bwd;
@@ -120,7 +146,7 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
     }
     if (act >= 0) {
         const bool nhwc_vec = p.layout == kNHWC && p.vec && p.numel > 0;
-        const NhwcChoice nc = fused_nhwc_pick(p, nhwc_vec ? coresident_grid() : 0);
+        const NhwcChoice nc = fused_nhwc_pick(p, nhwc_vec ? group_grid() : 0);
         p.nhwc_variant = nc.variant;
         p.nhwc_group = nc.group;
         p.scalar_variant = fused_scalar_pick(p);
@@ -133,7 +159,7 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
             default: break;
             }
         } else if (nhwc_vec) {
-            const NhwcChoice sc = fused_stream_pick(p, coresident_grid());
+            const NhwcChoice sc = fused_stream_pick(p, group_grid());
             p.stream_variant = sc.variant;
             if (sc.variant >= 0) {
                 p.nhwc_group = sc.group;
@@ -162,8 +188,9 @@ size_t workspace_bytes_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layo
 {
     const size_t a = split_bytes(N, C, H, W, layout, dtype);
     if (!vec_shape_ok(C, H * W, layout, dtype)) return a;
-    // the slice-resident NHWC group exchange (act plays no part in its choice)
-    const size_t b = plan_for(N, C, H, W, layout, dtype, true, IABN_ACT_IDENTITY).bytes;
+    // the group exchange (act plays no part in its choice), planned whatever the
+    // process-wide setting of grouped kernels
+    const size_t b = plan_for(N, C, H, W, layout, dtype, true, IABN_ACT_IDENTITY, 1).bytes;
     return a > b ? a : b;
 }
 
@@ -247,7 +274,35 @@ const char* iabn_status_string(iabn_status status)
     }
 }
 
-int iabn_version(void) { return 100; }
+int iabn_version(void) { return 200; }
+
+int iabn_set_grouped_kernels(int enabled)
+{
+    const int prev = grouped_allowed() ? 1 : 0;
+    if (enabled >= 0) g_grouped.store(enabled ? 1 : 0, std::memory_order_relaxed);
+    return prev;
+}
+
+iabn_status iabn_workspace_status(void* workspace, size_t workspace_bytes, int clear,
+                                  int* timed_out, hipStream_t stream)
+{
+    if (!timed_out) return IABN_ERR_INVALID_ARG;
+    *timed_out = 0;
+    if (!workspace || workspace_bytes < kWsHeaderBytes) return IABN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return IABN_ERR_MISALIGNED;
+    uint64_t word = 0;
+    if (hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return IABN_ERR_HIP;
+    *timed_out = word == kExchangeTimeout ? 1 : 0;
+    if (clear && *timed_out) {
+        if (hipMemsetAsync(workspace, 0, sizeof word, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return IABN_ERR_HIP;
+    }
+    return IABN_OK;
+}
 
 size_t iabn_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
                            iabn_dtype dtype)

@@ -875,6 +875,7 @@ static SliceGroup slice_group(const Plan& pl, void* ws)
                  ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + pl.off_xchg)
                  : nullptr;
     g.salt = process_salt();
+    g.status = static_cast<uint64_t*>(ws);      // the workspace header's status word
     return g;
 }
 

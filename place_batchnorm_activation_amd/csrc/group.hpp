@@ -10,12 +10,15 @@
 // publishing), so the next call -- a graph replay too -- uses a fresh token and
 // words left by earlier calls never match.  The members must run at once (the
 // host keeps the grid within the CU count); each wait is bounded, and past it
-// the sums become NaN instead of the device hanging.
+// the sums become NaN instead of the device hanging, and the workspace's status
+// word records the timeout for the host to query.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+
+#include "plan.hpp"
 
 namespace iabn {
 
@@ -52,6 +55,12 @@ __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t half)
 // well over a second.
 constexpr uint32_t kMaxPolls = 1u << 21;
 
+// A wait ran out: the workspace's status word (null: none to set) records it.
+__device__ __forceinline__ void group_timed_out(uint64_t* status)
+{
+    if (status) atomic_st(status, kExchangeTimeout);
+}
+
 // Members per slice at most (the exchange's LDS holds kMaxGroup partials).
 constexpr uint32_t kMaxGroup = 64;
 
@@ -70,9 +79,10 @@ __device__ __forceinline__ void group_publish(uint64_t* words, uint32_t member, 
 }
 
 // Member j's sums of channel ch, once all four words carry this call's tags
-// (bounded wait; NaN after it).
+// (bounded wait; NaN after it, and the timeout recorded in *status).
 __device__ __forceinline__ void group_fetch(const uint64_t* words, uint32_t j, uint32_t nch,
-                                            uint32_t ch, uint64_t tok, double& v1, double& v2)
+                                            uint32_t ch, uint64_t tok, double& v1, double& v2,
+                                            uint64_t* status)
 {
     const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
     const uint64_t* w = words + (size_t(j) * nch + ch) * 4;
@@ -88,17 +98,19 @@ __device__ __forceinline__ void group_fetch(const uint64_t* words, uint32_t j, u
         }
         __builtin_amdgcn_s_sleep(1);
     }
+    group_timed_out(status);
 }
 
 // Members FB at a time: the sums of channel ch of members j0 .. j0 + FB - 1
 // (< G; this member's own taken from s1, s2), all their words loaded at once on
 // every poll, so that partners that have all published cost one round trip.
-// NaN for a member not received within the bounded wait.
+// NaN for a member not received within the bounded wait (recorded in *status).
 template <uint32_t FB>
 __device__ __forceinline__ void group_fetch_batch(const uint64_t* words, uint32_t j0, uint32_t G,
                                                   uint32_t member, uint32_t nch, uint32_t ch,
                                                   uint64_t tok, double s1, double s2,
-                                                  double (&v1)[FB], double (&v2)[FB])
+                                                  double (&v1)[FB], double (&v2)[FB],
+                                                  uint64_t* status)
 {
     const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
     bool need[FB];
@@ -135,17 +147,20 @@ __device__ __forceinline__ void group_fetch_batch(const uint64_t* words, uint32_
         }
         if (left != 0) __builtin_amdgcn_s_sleep(1);
     }
+    if (left != 0) group_timed_out(status);
 }
 
 }  // namespace
 
 // Group exchange arguments: the workspace words (epochs, then the tagged sums),
-// the per-process salt, members per slice and rows per member.
+// the per-process salt, members per slice, rows per member, and the workspace's
+// status word (where a wait that runs out is recorded; null: not recorded).
 struct SliceGroup {
     uint64_t* xchg;
     uint64_t salt;
     uint32_t G;
     uint32_t mg;
+    uint64_t* status = nullptr;
 };
 
 namespace {
@@ -194,7 +209,8 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
             double t1 = 0.0, t2 = 0.0;
             for (uint32_t j0 = 0; j0 < grp.G; j0 += FB) {
                 double v1[FB], v2[FB];
-                group_fetch_batch<FB>(words, j0, grp.G, member, NCH, t, tok, s1, s2, v1, v2);
+                group_fetch_batch<FB>(words, j0, grp.G, member, NCH, t, tok, s1, s2, v1, v2,
+                                       grp.status);
 #pragma unroll
                 for (uint32_t q = 0; q < FB; ++q) {
                     if (j0 + q < grp.G) {
@@ -211,7 +227,7 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
     if (member != 0) {
         if (fin) {
             group_publish(words, member, NCH, t, tok, s1, s2);
-            group_fetch(words, 0, NCH, t, tok, s1, s2);
+            group_fetch(words, 0, NCH, t, tok, s1, s2, grp.status);
         }
         return;
     }
@@ -263,6 +279,7 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
             }
             if (left != 0) __builtin_amdgcn_s_sleep(1);
         }
+        if (left != 0) group_timed_out(grp.status);
     }
     __syncthreads();
     if (fin) {

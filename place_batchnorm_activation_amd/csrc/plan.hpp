@@ -64,6 +64,13 @@ inline void with_act(int act, F&& f)
 // Elements per 16-byte access.
 constexpr int vec_width(int dtype) { return dtype == kF32 ? 4 : 8; }
 
+// Every workspace starts with a header of this many bytes.  Its first 8 bytes
+// are the exchange status word: a group member whose bounded wait for a partner
+// runs out stores kExchangeTimeout there (group.hpp), and the word keeps it
+// until the caller clears it (iabn_workspace_status).
+constexpr size_t kWsHeaderBytes = 256;
+constexpr uint64_t kExchangeTimeout = 0x69616E6254494D45ull;   // any other value: none
+
 struct Plan {
     int64_t N = 0, C = 0, HW = 0, m = 0, numel = 0;
     int layout = 0, dtype = 0, esize = 4;
@@ -100,7 +107,7 @@ struct Plan {
     // channel-resident NCHW kernels on single elements (-1: not used)
     int scalar_variant = -1;
     // workspace sections (bytes, 256-aligned)
-    size_t off_part_a = 0, off_part_b = 0, off_const = 0, off_count = 0, bytes = 0;
+    size_t off_part_a = 0, off_part_b = 0, off_const = kWsHeaderBytes, off_count = 0, bytes = 0;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -219,10 +226,11 @@ inline Plan make_plan(int64_t N, int64_t C, int64_t H, int64_t W, int layout, in
         }
     }
 
-    // The constants come first, at an offset that does not depend on the plan, so
-    // that a stage planned for the vector path and one planned for the scalar path
-    // (different pointer alignment) agree on where they are.
-    size_t off = 0;
+    // The header comes first (the exchange status word), then the constants, at
+    // offsets that do not depend on the plan, so that a stage planned for the
+    // vector path and one planned for the scalar path (different pointer
+    // alignment) agree on where they are.
+    size_t off = kWsHeaderBytes;
     const size_t part_bytes = (size_t)(max64(p.P, p.P_bwd) * C) * sizeof(float);
     p.off_const = off;  off = (size_t)align_up((int64_t)(off + (size_t)C * 16), 256);
     p.off_part_a = off; off = (size_t)align_up((int64_t)(off + part_bytes), 256);

@@ -9,7 +9,9 @@
 //  2. a partial whose four words are not all tagged with this call's token (a
 //     torn or stale one) is not taken; once completed, it is;
 //  3. a member that never publishes turns the others' sums into NaN after the
-//     bounded wait, instead of a hang.
+//     bounded wait, instead of a hang, and the waiting members record the
+//     timeout in the workspace's status word; calls where every member arrives
+//     leave the word as it was.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -69,7 +71,9 @@ static void run_calls(uint32_t G, uint32_t slices, int calls, uint64_t garbage_s
     std::vector<uint64_t> ws(words_needed(slices, G));
     std::mt19937_64 rng(garbage_seed);
     for (auto& w : ws) w = rng();                   // whatever the workspace held
-    SliceGroup grp{ws.data(), process_salt(), G, 1};
+    uint64_t status = rng();
+    const uint64_t status0 = status;
+    SliceGroup grp{ws.data(), process_salt(), G, 1, &status};
     for (int k = 0; k < calls; ++k) {
         std::vector<double> o1(slices * G), o2(slices * G);
         std::vector<std::thread> th;
@@ -91,6 +95,7 @@ static void run_calls(uint32_t G, uint32_t slices, int calls, uint64_t garbage_s
             }
         }
     }
+    CHECK(status == status0, "G=%u: status word changed without a timeout", G);
 }
 
 // A partner whose words carry this call's tag on words 0-1 only: not taken until
@@ -99,7 +104,8 @@ static void torn_partial()
 {
     const uint32_t G = 2, slices = 1;
     std::vector<uint64_t> ws(words_needed(slices, G), 0);
-    SliceGroup grp{ws.data(), process_salt(), G, 1};
+    uint64_t status = 0;
+    SliceGroup grp{ws.data(), process_salt(), G, 1, &status};
     const uint64_t tok = group_token(grp, 0, 0);
     uint64_t* words = group_words(grp, 0, slices, 1);
     const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
@@ -111,18 +117,20 @@ static void torn_partial()
     w[2] = tagged(tlo ^ 1u, uint32_t(b2 >> 32));    // stale tags
     w[3] = tagged(thi ^ 1u, uint32_t(b2));
     double r1 = 0, r2 = 0;
-    std::thread reader([&] { group_fetch(words, 1, 1, 0, tok, r1, r2); });
+    std::thread reader([&] { group_fetch(words, 1, 1, 0, tok, r1, r2, &status); });
     std::this_thread::sleep_for(std::chrono::milliseconds(20));
     __hip_atomic_store(w + 2, tagged(tlo, uint32_t(b2 >> 32)), __ATOMIC_RELAXED, 0);
     __hip_atomic_store(w + 3, tagged(thi, uint32_t(b2)), __ATOMIC_RELAXED, 0);
     reader.join();
     CHECK(r1 == v1 && r2 == v2, "torn partial: got (%g, %g), expected (%g, %g)", r1, r2, v1, v2);
+    CHECK(status == 0, "torn partial completed: status word set");
 
     // the same torn words, never completed: NaN after the bounded wait
     w[2] = tagged(tlo ^ 1u, uint32_t(b2 >> 32));
     w[3] = tagged(thi ^ 1u, uint32_t(b2));
-    group_fetch(words, 1, 1, 0, tok, r1, r2);
+    group_fetch(words, 1, 1, 0, tok, r1, r2, &status);
     CHECK(std::isnan(r1) && std::isnan(r2), "torn partial never completed: got (%g, %g)", r1, r2);
+    CHECK(status == kExchangeTimeout, "torn partial never completed: status word not set");
 }
 
 // Member `absent` never runs: the members that wait on it end with NaN.
@@ -130,7 +138,8 @@ static void absent_member(uint32_t G, uint32_t absent)
 {
     const uint32_t slices = 1;
     std::vector<uint64_t> ws(words_needed(slices, G), 0);
-    SliceGroup grp{ws.data(), process_salt(), G, 1};
+    uint64_t status = 0;
+    SliceGroup grp{ws.data(), process_salt(), G, 1, &status};
     std::vector<double> o1(G, 0.0), o2(G, 0.0);
     std::vector<std::thread> th;
     for (uint32_t j = 0; j < G; ++j)
@@ -142,6 +151,8 @@ static void absent_member(uint32_t G, uint32_t absent)
         CHECK(std::isnan(o1[j]) && std::isnan(o2[j]), "G=%u absent %u: member %u got (%g, %g), expected NaN", G,
               absent, j, o1[j], o2[j]);
     }
+    CHECK(status == kExchangeTimeout, "G=%u absent %u: status word not set (%llx)", G, absent,
+          (unsigned long long)status);
 }
 
 int main()

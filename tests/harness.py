@@ -122,6 +122,8 @@ def run_gpu(inp: workloads.Inputs, backward: bool = True, dx_over_dy: bool = Fal
                            wl.act_param, ws)
         dg, db = dgt.cpu().numpy(), dbt.cpu().numpy()
     torch.cuda.synchronize()
+    # no exchanging kernel gave up waiting for a partner (reads and clears the word)
+    assert not iabn.iabn_workspace_status(ws), "exchange timeout recorded in the workspace"
     return GpuRun(y=x, dx=dx, save_mean=sm.cpu().numpy(), save_invstd=si.cpu().numpy(),
                   running_mean=rm.cpu().numpy(), running_var=rv.cpu().numpy(), dgamma=dg,
                   dbeta=db)

@@ -40,7 +40,7 @@ static void check_plan(const Shape& s, bool vec)
     if (pl.layout == kNCHW)
         CHECK(pl.P * pl.unit >= m && (pl.P - 1) * pl.unit < m, "partials cover m exactly");
     CHECK(pl.reduce_blocks < (int64_t(1) << 31) && pl.apply_blocks < (int64_t(1) << 31), "grid");
-    CHECK(pl.off_const == 0 && pl.off_part_a >= size_t(C) * 16, "const section");
+    CHECK(pl.off_const == kWsHeaderBytes && pl.off_part_a >= kWsHeaderBytes + size_t(C) * 16, "const section");
     CHECK(pl.P_bwd >= 1 && (pl.layout == kNHWC || pl.P_bwd == pl.P), "backward partials");
     CHECK(pl.reduce_blocks_bwd < (int64_t(1) << 31), "backward grid");
     const int64_t Pmax = std::max(pl.P, pl.P_bwd);

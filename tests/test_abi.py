@@ -235,3 +235,47 @@ def test_plan_choice_for_the_workloads():
     assert "channel_resident(512x49)" in d(32, 256, 56, 56, "NCHW", iabn.F32, "elu")
     with pytest.raises(ValueError):
         d(2, 4, 4, 4, "NCHW", iabn.F32, 9)
+
+
+def test_grouped_kernels_can_be_switched_off():
+    """With the grouped kernels forbidden, no plan has workgroups that wait on one
+    another, and the workspace size does not change (host-side plan only)."""
+    d = iabn.iabn_describe_plan
+    shapes = [(64, 2048, 7, 7, "NHWC", iabn.BF16), (2, 256, 512, 512, "NHWC", iabn.BF16),
+              (32, 1024, 14, 14, "NHWC", iabn.BF16), (32, 256, 56, 56, "NHWC", iabn.BF16),
+              (32, 64, 112, 112, "NCHW", iabn.F32), (16, 512, 28, 28, "NCHW", iabn.F32),
+              (32, 256, 56, 56, "NCHW", iabn.F32)]
+    sizes = [lib.iabn_workspace_size(N, C, H, W, 0 if lay == "NCHW" else 1, dt)
+             for (N, C, H, W, lay, dt) in shapes]
+    before = iabn.iabn_set_grouped_kernels(None)
+    try:
+        assert iabn.iabn_set_grouped_kernels(True) == before
+        assert "group" in d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu")
+        assert "group" in d(32, 64, 112, 112, "NCHW", iabn.F32, "leaky_relu")
+        assert iabn.iabn_set_grouped_kernels(False) is True
+        assert iabn.iabn_set_grouped_kernels(None) is False
+        for (N, C, H, W, lay, dt) in shapes:
+            plan = d(N, C, H, W, lay, dt, "leaky_relu")
+            assert "group" not in plan and "slice_streamed" not in plan, plan
+        # the tail map keeps its slices on chip, one workgroup per slice
+        assert d(64, 2048, 7, 7, "NHWC", iabn.BF16, "leaky_relu") == \
+            "forward=slice_resident(512x2x13) backward=slice_resident(512x2x13)"
+        assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu").startswith("forward=split")
+        # channels a workgroup holds stay resident without groups
+        assert d(32, 256, 56, 56, "NCHW", iabn.F32, "leaky_relu") == \
+            "forward=channel_resident(512x49) backward=channel_resident(512x49,dy_streamed)"
+        for (N, C, H, W, lay, dt), n in zip(shapes, sizes):
+            assert lib.iabn_workspace_size(N, C, H, W, 0 if lay == "NCHW" else 1, dt) == n
+    finally:
+        iabn.iabn_set_grouped_kernels(before)
+    assert iabn.iabn_set_grouped_kernels(None) == before
+
+
+def test_workspace_status_validation():
+    flag = ctypes.c_int(7)
+    assert lib.iabn_workspace_status(A, 1 << 20, 0, None, None) == INVALID
+    assert lib.iabn_workspace_status(None, 1 << 20, 0, ctypes.byref(flag), None) == WS
+    assert flag.value == 0
+    assert lib.iabn_workspace_status(A, 255, 0, ctypes.byref(flag), None) == WS
+    assert lib.iabn_workspace_status(A + 8, 1 << 20, 0, ctypes.byref(flag), None) == MISALIGNED
+

@@ -2,7 +2,7 @@
 against the library's own group.hpp, with one host thread per workgroup, and runs
 it -- member-order sums in one- and two-level groups over many calls on one
 workspace, torn and stale partials rejected, and NaN instead of a hang when a
-member never publishes."""
+member never publishes, with the timeout recorded in the workspace's status word."""
 import os
 import subprocess
 
