@@ -262,6 +262,33 @@ iabn_status iabn_backward_eval(const void *y, const void *dy, void *dx,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the training
+ * forward exactly as iabn_forward_train, with the same arguments, results and
+ * errors, but no workspace argument.  Its workspace is a static device array of
+ * IABN_NOALLOC_SCRATCH_BYTES bytes inside the library, one per device, held from
+ * the library's load until the process ends; the call allocates nothing.
+ *   - Shapes whose iabn_workspace_size exceeds the array are rejected with
+ *     IABN_ERR_WORKSPACE before any HIP call (use iabn_forward_train).
+ *   - Every call on a device shares that device's array: calls that may overlap
+ *     on one device (different streams, or several host threads) race and give
+ *     wrong results.  Calls in stream order are safe; the array keeps the last
+ *     call's contents, which no call needs cleared.
+ *   - A timeout of the exchanging kernels is recorded in the array, where
+ *     iabn_workspace_status cannot reach it; callers that share the device with
+ *     long-running work switch those kernels off (iabn_set_grouped_kernels).
+ *   - The first call on a device looks up the array's device address (a HIP
+ *     runtime query, no allocation); capture a graph after one eager call. */
+#define IABN_NOALLOC_SCRATCH_BYTES (8u << 20)
+iabn_status iabn_forward_train_noalloc(void *x_inout,
+                                       int64_t N, int64_t C, int64_t H, int64_t W,
+                                       iabn_layout layout, iabn_dtype dtype,
+                                       const float *gamma, const float *beta,
+                                       float *running_mean, float *running_var,
+                                       float *save_mean, float *save_invstd,
+                                       iabn_act act, float act_param, float eps, float momentum,
+                                       hipStream_t stream);
+
 /* Describes, as a short text, the kernels that iabn_forward_train and
  * iabn_backward launch for this problem when every tensor pointer is 16-byte
  * aligned (aligned16 != 0) or not, e.g.

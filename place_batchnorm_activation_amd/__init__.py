@@ -51,6 +51,8 @@ lib.iabn_workspace_size.restype = _SZ
 _SHAPE = [_I64, _I64, _I64, _I64, _INT, _INT]
 lib.iabn_forward_train.argtypes = [_P] + _SHAPE + [_P, _P, _P, _P, _P, _P, _INT, _F, _F, _F, _P,
                                                    _SZ, _P]
+lib.iabn_forward_train_noalloc.argtypes = [_P] + _SHAPE + [_P, _P, _P, _P, _P, _P, _INT, _F, _F,
+                                                           _F, _P]
 lib.iabn_forward_stats.argtypes = [_P] + _SHAPE + [_P, _P, _P, _P, _P, _P, _F, _F, _P, _SZ, _P]
 lib.iabn_forward_apply.argtypes = [_P] + _SHAPE + [_INT, _F, _P, _SZ, _P]
 lib.iabn_forward_eval.argtypes = [_P] + _SHAPE + [_P, _P, _P, _P, _INT, _F, _F, _P]
@@ -66,7 +68,7 @@ lib.iabn_workspace_status.argtypes = [_P, _SZ, _INT, ctypes.POINTER(_INT), _P]
 lib.iabn_workspace_status.restype = _INT
 lib.iabn_describe_plan.argtypes = _SHAPE + [_INT, _INT, ctypes.c_char_p, _SZ]
 lib.iabn_describe_plan.restype = _INT
-for _fn in ("iabn_forward_train", "iabn_forward_stats", "iabn_forward_apply", "iabn_forward_eval",
+for _fn in ("iabn_forward_train", "iabn_forward_train_noalloc", "iabn_forward_stats", "iabn_forward_apply", "iabn_forward_eval",
             "iabn_backward", "iabn_backward_reduce", "iabn_backward_apply", "iabn_backward_eval"):
     getattr(lib, _fn).restype = _INT
 
@@ -186,6 +188,19 @@ def iabn_forward_train(x, N, C, H, W, layout, gamma, beta, running_mean, running
         _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma), _ptr(beta),
         _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_invstd),
         _code(act, ACTS), act_param, eps, momentum, wp, wb, _stream(stream)))
+
+
+def iabn_forward_train_noalloc(x, N, C, H, W, layout, gamma, beta, running_mean, running_var,
+                               save_mean, save_invstd, act, act_param, eps, momentum, stream=None):
+    """iabn_forward_train with the library's static per-device scratch as workspace
+    (no allocation; shapes within IABN_NOALLOC_SCRATCH_BYTES of workspace)."""
+    _check("iabn_forward_train_noalloc", lib.iabn_forward_train_noalloc(
+        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma), _ptr(beta),
+        _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_invstd),
+        _code(act, ACTS), act_param, eps, momentum, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def iabn_forward_stats(x, N, C, H, W, layout, gamma, beta, running_mean, running_var, save_mean,

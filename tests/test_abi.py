@@ -279,3 +279,24 @@ def test_workspace_status_validation():
     assert lib.iabn_workspace_status(A, 255, 0, ctypes.byref(flag), None) == WS
     assert lib.iabn_workspace_status(A + 8, 1 << 20, 0, ctypes.byref(flag), None) == MISALIGNED
 
+
+def test_noalloc_forward_rejects_shapes_beyond_its_scratch():
+    """The no-allocation forward rejects, before any HIP call, a shape whose
+    workspace exceeds its static scratch, and validates like iabn_forward_train."""
+    big = (1, 1 << 20, 16, 16)                    # NHWC bf16: 24 MiB of workspace
+    assert lib.iabn_workspace_size(*big, 1, 1) > iabn.NOALLOC_SCRATCH_BYTES
+    assert lib.iabn_forward_train_noalloc(A, *big, 1, 1, A, A, A, A, A, A, 1, 0.01, 1e-5, 0.1,
+                                          None) == WS
+    assert lib.iabn_workspace_size(64, 2048, 7, 7, 1, 1) <= iabn.NOALLOC_SCRATCH_BYTES
+    assert lib.iabn_workspace_size(2, 256, 512, 512, 1, 1) <= iabn.NOALLOC_SCRATCH_BYTES
+    # argument errors as for iabn_forward_train, before any HIP call
+    assert lib.iabn_forward_train_noalloc(A, 2, 3, 4, 4, 0, 0, A, A, A, A, A, A, 1, 0.0, 1e-5,
+                                          0.1, None) == INVALID
+    assert lib.iabn_forward_train_noalloc(A, 2, 3, 4, 4, 0, 0, None, A, A, A, A, A, 1, 0.01, 1e-5,
+                                          0.1, None) == INVALID
+    assert lib.iabn_forward_train_noalloc(A, 1, 3, 1, 1, 0, 0, A, A, A, A, A, A, 1, 0.01, 1e-5,
+                                          0.1, None) == INVALID           # m = 1
+    assert lib.iabn_forward_train_noalloc(A + 2, 2, 3, 4, 4, 0, 0, A, A, A, A, A, A, 1, 0.01,
+                                          1e-5, 0.1, None) == MISALIGNED
+    assert lib.iabn_forward_train_noalloc(None, 2, 0, 4, 4, 0, 0, None, None, None, None, None,
+                                          None, 1, 0.01, 1e-5, 0.1, None) == OK
