@@ -132,6 +132,19 @@ inline int fused_bwd_threads(int id)
     }
 }
 
+// The largest group a forward variant may run in: variants holding more than 32
+// vectors a thread compile only the one-level exchange (fused_nchw.hip,
+// kFwdTwoLevel), so their groups stay under the two-level size of 16.
+inline int fused_fwd_group_max(int id)
+{
+    switch (id) {
+#define IABN_ROW(ID, T, NR) case ID: return NR > 32 ? 15 : 64;
+        IABN_FUSED_FWD_VARIANTS(IABN_ROW)
+#undef IABN_ROW
+    default: return 0;
+    }
+}
+
 inline bool fused_bwd_dy_resident(int id)
 {
     switch (id) {
@@ -147,8 +160,9 @@ inline bool fused_bwd_dy_resident(int id)
 // [j*ceil(vc/G), ...), and swap their fp64 sums through the workspace (the
 // exchange of the NHWC groups, one channel a slice).  The largest power of two
 // G (2 to 64) with C*G within max_grid (every member runs at once) whose share
-// fits a forward and a y-resident, dy-streaming backward variant, if the grid
-// then fills the chip (or the tensor is small).  Both passes use that G.
+// fits a forward and a y-resident, dy-streaming backward variant (and a group
+// size the forward variant allows), if the grid then fills the chip (or the
+// tensor is small).  Both passes use that G.
 struct NchwGroupChoice {
     int fwd = -1, bwd = -1, group = 1;
 };
@@ -165,7 +179,7 @@ inline NchwGroupChoice fused_nchw_group_pick(const Plan& p, int64_t max_grid)
         const int64_t share = ceil_div(vc, g);
         if ((g - 1) * share >= vc) continue;        // every member holds vectors
         const int f = fused_fwd_pick(share), b = fused_bwd_pick(share);
-        if (f < 0 || b < 0 || fused_bwd_dy_resident(b)) continue;
+        if (f < 0 || b < 0 || fused_bwd_dy_resident(b) || g > fused_fwd_group_max(f)) continue;
         const int64_t threads = p.C * g * fused_fwd_threads(f);
         if (threads < int64_t(256) * 256 && bytes > (int64_t(4) << 20)) return none;
         NchwGroupChoice c;

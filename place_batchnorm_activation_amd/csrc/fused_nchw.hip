@@ -100,6 +100,13 @@ __device__ __forceinline__ void block_sum2(float& a, float& b)
     a = ta; b = tb;
 }
 
+// A grouped forward whose share takes nearly all the registers (49 vectors a
+// thread) compiles only the one-level exchange: with the two-level path in, it
+// spilled about 24 VGPRs around the exchange.  The plan never gives it a group
+// of kTwoLevelGroup members or more (fused_nchw_group_pick).
+template <int NR>
+constexpr bool kFwdTwoLevel = NR <= 32;
+
 // ---------------------------------------------------------------------------
 template <int DT, int ACT, int T, int NR, bool GRP>
 __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
@@ -173,7 +180,8 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
         __shared__ double tot_sh[2];
         double s1 = double(n) * double(mean);
         double s2 = double(m2) + double(n) * double(mean) * double(mean);
-        group_sums<1, T>(grp, c, C, member, tok_sh, t == 0, s1, s2);
+        group_sums<1, T, (kFwdTwoLevel<NR> ? 4 : 1), kFwdTwoLevel<NR>>(grp, c, C, member, tok_sh,
+                                                                  t == 0, s1, s2);
         if (t == 0) {
             tot_sh[0] = s1;
             tot_sh[1] = s2;
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
     double sum_dz = double(sdz), sum_dzt = double(sdzt);
     if constexpr (GRP) {
         __shared__ double tot_sh[2];
-        group_sums<1, T>(grp, c, C, member, tok_sh, t == 0, sum_dz, sum_dzt);
+        group_sums<1, T, 2>(grp, c, C, member, tok_sh, t == 0, sum_dz, sum_dzt);
         if (t == 0) {
             tot_sh[0] = sum_dz;
             tot_sh[1] = sum_dzt;

@@ -414,7 +414,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
         db = lds_total<T, LPR, 2 * V>(sh, fe, fl);
         sg = lds_total<T, LPR, 2 * V>(sh, V + fe, fl);
     }
-    if (grp.G > 1) group_sums<NCH, T, 8>(grp, s, slices, member, tok_sh, fin, db, sg);
+    if (grp.G > 1) group_sums<NCH, T, (NR > 13 ? 4 : 8)>(grp, s, slices, member, tok_sh, fin, db, sg);
     if (fin) {
         const double g = double(g_f);
         const double dg = sg / g;
@@ -782,8 +782,12 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
         const double g = double(g_f);
         const double dg = sg / g;
         if (member == 0) {
-            dbeta[cf] = float(dbs);
-            dgamma[cf] = float(dg);
+            // the channel index formed again rather than kept across the exchange
+            // (keeping its 64-bit offset spilled it in the fp16 identity instances)
+            const uint32_t t3 = opaque_u(t);
+            const uint32_t cf3 = (s * LPR + t3 % LPR) * V + t3 / LPR;
+            dbeta[cf3] = float(dbs);
+            dgamma[cf3] = float(dg);
         }
         const double A = g * double(i_f);
         const double md = double(m);

@@ -196,14 +196,18 @@ constexpr uint32_t kPairBatch = 4;
 // of 8 in one round trip) made the slice-resident NHWC kernels 5-7% faster on
 // groups of 8; the other kernels keep four, which left them as fast and their
 // register allocation unchanged.
-template <uint32_t NCH, int T, uint32_t FB = 4>
+// TWO: whether the two-level path is compiled in.  A kernel whose plan never
+// gives it kTwoLevelGroup members or more leaves it out, which spares the
+// registers its batched loads take (a kernel holding its data in nearly all of
+// them spilled around it).
+template <uint32_t NCH, int T, uint32_t FB = 4, bool TWO = true>
 __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, uint32_t slices,
                                            uint32_t member, uint64_t tok, bool fin, double& s1,
                                            double& s2)
 {
     uint64_t* words = group_words(grp, s, slices, NCH);
     const uint32_t t = threadIdx.x;
-    if (grp.G < kTwoLevelGroup) {
+    if (!TWO || grp.G < kTwoLevelGroup) {
         if (fin) {
             group_publish(words, member, NCH, t, tok, s1, s2);
             double t1 = 0.0, t2 = 0.0;
@@ -224,6 +228,7 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
         }
         return;
     }
+    if constexpr (!TWO) return;
     if (member != 0) {
         if (fin) {
             group_publish(words, member, NCH, t, tok, s1, s2);

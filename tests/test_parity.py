@@ -610,6 +610,10 @@ OUTLIER = [custom(2, 4, 32, 16, 16),                                   # NCHW ch
            custom(2, 8, 256, 33, 64, layout="NHWC", dtype="f32"),      # group 16, two levels
            custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),   # streamed, 8 lanes
            custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),   # streamed, 4 lanes
+           # fp32 streamed slices under the 1e-5 gate: about 78 (8 lanes, groups of
+           # 64) and 20 (4 lanes) rows summed per thread
+           custom(2, 2, 128, 400, 400, layout="NHWC", dtype="f32"),
+           custom(2, 1, 64, 400, 400, layout="NHWC", dtype="f32"),
            custom(2, 2, 16, 80, 80, layout="NHWC", dtype="f32")]       # NHWC split
 
 
