@@ -53,11 +53,19 @@ def _load():
                                               ctypes.c_double, _D, _D, _D]
     lib.orc_backward_from_x.argtypes = [_I64, _I64, _I64, _D, _D, _D, _D, ctypes.c_int,
                                         ctypes.c_double, ctypes.c_double, _D, _D, _D]
+    lib.orc_forward_train_ckpt.argtypes = [_I64, _I64, _I64, _D, _D, _D, ctypes.c_int,
+                                           ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                           _D, _D, _D, _D, _D, _D, _D]
+    lib.orc_recompute_from_xhat.argtypes = [_I64, _I64, _I64, _D, _D, _D, ctypes.c_int,
+                                            ctypes.c_double, _D]
+    lib.orc_backward_from_xhat.argtypes = [_I64, _I64, _I64, _D, _D, _D, _D, _D, ctypes.c_int,
+                                           ctypes.c_double, _D, _D, _D]
     lib.orc_round_storage.argtypes = [_D, _I64, ctypes.c_int]
     lib.orc_num_threads.argtypes = []
     for f in (lib.orc_forward_train, lib.orc_forward_eval, lib.orc_backward_from_y,
               lib.orc_backward_eval, lib.orc_backward_from_y_form2, lib.orc_backward_from_x, lib.orc_round_storage,
-              lib.orc_num_threads):
+              lib.orc_num_threads, lib.orc_forward_train_ckpt, lib.orc_recompute_from_xhat,
+              lib.orc_backward_from_xhat):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -174,6 +182,55 @@ def backward_from_x(x, dy, gamma, beta, act="leaky_relu", act_param=0.01, eps=1e
                                      _p(db))
     if rc != 0:
         raise ValueError("oracle backward_from_x rejected its arguments")
+    return {"dx": dx, "dgamma": dg, "dbeta": db}
+
+
+def forward_train_ckpt(x, gamma, beta, act="leaky_relu", act_param=0.01, eps=1e-5, momentum=0.1,
+                       running_mean=None, running_var=None, storage="f64"):
+    """Training forward of optimized checkpointing: the block keeps xhat.  Returns
+    dict xhat and y (both rounded to `storage`), mean, var, invstd and, when given,
+    the updated running statistics."""
+    x = _f64(x)
+    N, C, HW = _shape(x)
+    xh, y = np.empty_like(x), np.empty_like(x)
+    mean, var, inv = np.empty(C), np.empty(C), np.empty(C)
+    rm = None if running_mean is None else _f64(running_mean).copy()
+    rv = None if running_var is None else _f64(running_var).copy()
+    rc = _load().orc_forward_train_ckpt(N, C, HW, _p(x), _p(_f64(gamma)), _p(_f64(beta)),
+                                        ACT[act], float(act_param), float(eps), float(momentum),
+                                        _p(xh), _p(y), _p(mean), _p(var), _p(inv), _p(rm), _p(rv))
+    if rc != 0:
+        raise ValueError("oracle forward_train_ckpt rejected its arguments")
+    round_storage(xh, storage)
+    round_storage(y, storage)
+    return {"xhat": xh, "y": y, "mean": mean, "var": var, "invstd": inv, "running_mean": rm,
+            "running_var": rv}
+
+
+def recompute_from_xhat(xhat, gamma, beta, act="leaky_relu", act_param=0.01, storage="f64"):
+    """y = act(gamma xhat + beta), rounded to `storage`."""
+    xhat = _f64(xhat)
+    N, C, HW = _shape(xhat)
+    y = np.empty_like(xhat)
+    rc = _load().orc_recompute_from_xhat(N, C, HW, _p(xhat), _p(_f64(gamma)), _p(_f64(beta)),
+                                         ACT[act], float(act_param), _p(y))
+    if rc != 0:
+        raise ValueError("oracle recompute_from_xhat rejected its arguments")
+    round_storage(y, storage)
+    return y
+
+
+def backward_from_xhat(xhat, dy, gamma, beta, invstd, act="leaky_relu", act_param=0.01):
+    """Backward from the checkpoint xhat.  Returns dict dx, dgamma, dbeta."""
+    xhat, dy = _f64(xhat), _f64(dy)
+    N, C, HW = _shape(xhat)
+    dx = np.empty_like(xhat)
+    dg, db = np.empty(C), np.empty(C)
+    rc = _load().orc_backward_from_xhat(N, C, HW, _p(xhat), _p(dy), _p(_f64(gamma)),
+                                        _p(_f64(beta)), _p(_f64(invstd)), ACT[act],
+                                        float(act_param), _p(dx), _p(dg), _p(db))
+    if rc != 0:
+        raise ValueError("oracle backward_from_xhat rejected its arguments")
     return {"dx": dx, "dgamma": dg, "dbeta": db}
 
 

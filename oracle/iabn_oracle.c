@@ -115,6 +115,41 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Statistics of channel c (section 3, "Batch Normalization Review"): the mean,
+ * the biased variance (two passes) and 1/sqrt(var + eps). */
+static void channel_stats(int64_t N, int64_t C, int64_t HW, const double *x, int64_t c,
+                          double eps, double *mu_out, double *v_out, double *is_out)
+{
+    const int64_t m = N * HW;
+    double sum = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t i = 0; i < HW; ++i) sum += x[AT(n, c, i)];
+    const double mu = sum / (double)m;
+
+    double ss = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t i = 0; i < HW; ++i) {
+            const double d = x[AT(n, c, i)] - mu;
+            ss += d * d;
+        }
+    const double v = ss / (double)m;
+    const double is = 1.0 / sqrt(v + eps);
+    *mu_out = mu;
+    *v_out = v;
+    *is_out = is;
+}
+
+/* The running statistics of channel c after one training step (when given). */
+static void update_running(int64_t c, int64_t m, double momentum, double mu, double v,
+                           double *running_mean, double *running_var)
+{
+    if (running_mean)
+        running_mean[c] = (1.0 - momentum) * running_mean[c] + momentum * mu;
+    if (running_var)
+        running_var[c] = (1.0 - momentum) * running_var[c]
+                       + momentum * v * (double)m / (double)(m - 1);
+}
+
 /* ---------------------------------------------------------------------------
  * Training forward (section 3, "Batch Normalization Review" and "INPLACE-ABN"):
  *   mu_c = (1/m) sum x,   var_c = (1/m) sum (x - mu_c)^2   (two passes),
@@ -133,20 +168,8 @@ int orc_forward_train(int64_t N, int64_t C, int64_t HW,
     if (C < 0 || m < 2 || !act_valid(act, p) || !(eps >= 0.0)) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < C; ++c) {
-        double sum = 0.0;
-        for (int64_t n = 0; n < N; ++n)
-            for (int64_t i = 0; i < HW; ++i) sum += x[AT(n, c, i)];
-        const double mu = sum / (double)m;
-
-        double ss = 0.0;
-        for (int64_t n = 0; n < N; ++n)
-            for (int64_t i = 0; i < HW; ++i) {
-                const double d = x[AT(n, c, i)] - mu;
-                ss += d * d;
-            }
-        const double v = ss / (double)m;
-        const double is = 1.0 / sqrt(v + eps);
-
+        double mu, v, is;
+        channel_stats(N, C, HW, x, c, eps, &mu, &v, &is);
         for (int64_t n = 0; n < N; ++n)
             for (int64_t i = 0; i < HW; ++i) {
                 const double xhat = (x[AT(n, c, i)] - mu) * is;
@@ -156,11 +179,7 @@ int orc_forward_train(int64_t N, int64_t C, int64_t HW,
         if (mean) mean[c] = mu;
         if (var) var[c] = v;
         if (invstd) invstd[c] = is;
-        if (running_mean)
-            running_mean[c] = (1.0 - momentum) * running_mean[c] + momentum * mu;
-        if (running_var)
-            running_var[c] = (1.0 - momentum) * running_var[c]
-                           + momentum * v * (double)m / (double)(m - 1);
+        update_running(c, m, momentum, mu, v, running_mean, running_var);
     }
     return 0;
 }
@@ -359,6 +378,105 @@ int orc_backward_from_x(int64_t N, int64_t C, int64_t HW,
                 const double z = gamma[c] * xhat + beta[c];
                 const double dz = act_derivative_from_z(act, p, z) * dy[AT(n, c, i)];
                 dx[AT(n, c, i)] = k * (dz - sdz / (double)m - xhat * sdzx / (double)m);
+            }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Optimized checkpointing (section 3, "Proposed Checkpointing"): the block
+ * keeps the normalised value xhat instead of its input x.  The backward gets
+ * y back by the scale-and-shift followed by the activation, and the BN
+ * backward uses the stored xhat directly instead of recomputing it from x.
+ *
+ * Forward: the statistics as in orc_forward_train, then
+ *   xhat = (x - mu_c) / sqrt(var_c + eps)   (the stored buffer),
+ *   y = act(gamma_c xhat + beta_c)          (the layer output).
+ * Both outputs are fp64, not rounded.  Returns 0, or -1 for invalid arguments.
+ */
+int orc_forward_train_ckpt(int64_t N, int64_t C, int64_t HW,
+                           const double *x, const double *gamma, const double *beta,
+                           int act, double p, double eps, double momentum,
+                           double *xhat, double *y, double *mean, double *var, double *invstd,
+                           double *running_mean, double *running_var)
+{
+    const int64_t m = N * HW;
+    if (C < 0 || m < 2 || !act_valid(act, p) || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        double mu, v, is;
+        channel_stats(N, C, HW, x, c, eps, &mu, &v, &is);
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t i = 0; i < HW; ++i) {
+                const double xh = (x[AT(n, c, i)] - mu) * is;
+                xhat[AT(n, c, i)] = xh;
+                y[AT(n, c, i)] = act_forward(act, p, gamma[c] * xh + beta[c]);
+            }
+        if (mean) mean[c] = mu;
+        if (var) var[c] = v;
+        if (invstd) invstd[c] = is;
+        update_running(c, m, momentum, mu, v, running_mean, running_var);
+    }
+    return 0;
+}
+
+/* The layer output rebuilt from the checkpoint, before the following layer's
+ * backward needs it: y = act(gamma_c xhat + beta_c). */
+int orc_recompute_from_xhat(int64_t N, int64_t C, int64_t HW,
+                            const double *xhat, const double *gamma, const double *beta,
+                            int act, double p, double *y)
+{
+    if (C < 0 || N < 0 || HW < 0 || !act_valid(act, p)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t i = 0; i < HW; ++i)
+                y[AT(n, c, i)] = act_forward(act, p, gamma[c] * xhat[AT(n, c, i)] + beta[c]);
+    return 0;
+}
+
+/* Backward from the checkpoint:
+ *   z = gamma_c xhat + beta_c,  dz = act'(z) dy,
+ *   dbeta_c = sum dz,  dgamma_c = sum dz xhat,
+ *   dx = gamma_c invstd_c (dz - dbeta_c/m - xhat dgamma_c/m).
+ * invstd is the value the forward saved.  z is formed with one rounding (a
+ * fused multiply-add), so the side of the activation's kink it falls on is that
+ * of the exact gamma_c xhat + beta_c (a rounding never flips a sign); the leaky
+ * ReLU's slope jumps from a to 1 there, so the branch must not depend on how z
+ * is rounded. */
+static double ckpt_z(double gamma, double xhat, double beta)
+{
+    return fma(gamma, xhat, beta);   /* one rounding: the sign of the exact value */
+}
+
+int orc_backward_from_xhat(int64_t N, int64_t C, int64_t HW,
+                           const double *xhat, const double *dy,
+                           const double *gamma, const double *beta, const double *invstd,
+                           int act, double p,
+                           double *dx, double *dgamma, double *dbeta)
+{
+    const int64_t m = N * HW;
+    if (C < 0 || m < 1 || !act_valid(act, p)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        double sdz = 0.0, sdzx = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t i = 0; i < HW; ++i) {
+                const double xh = xhat[AT(n, c, i)];
+                const double z = ckpt_z(gamma[c], xh, beta[c]);
+                const double dz = act_derivative_from_z(act, p, z) * dy[AT(n, c, i)];
+                sdz += dz;
+                sdzx += dz * xh;
+            }
+        dbeta[c] = sdz;
+        dgamma[c] = sdzx;
+        const double k = gamma[c] * invstd[c];
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t i = 0; i < HW; ++i) {
+                const double xh = xhat[AT(n, c, i)];
+                const double z = ckpt_z(gamma[c], xh, beta[c]);
+                const double dz = act_derivative_from_z(act, p, z) * dy[AT(n, c, i)];
+                dx[AT(n, c, i)] = k * (dz - sdz / (double)m - xh * sdzx / (double)m);
             }
     }
     return 0;

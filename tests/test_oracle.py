@@ -414,3 +414,100 @@ def test_oracle_rejects_invalid_arguments():
         oracle.forward_train(x, [1, 1], [0, 0], "leaky_relu", 0.0)
     with pytest.raises(ValueError):
         oracle.forward_train(x, [1, 1], [0, 0], "elu", -1.0)
+
+
+# ---------------------------------------------------------------------------
+# optimized checkpointing (the block keeps xhat instead of x)
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_ckpt_forward_matches_torch_fp64(wl):
+    """xhat against (x - mean)/sqrt(var + eps) from torch's statistics, y against
+    torch's batch_norm + activation, running statistics against torch's update."""
+    _, x, dy = _draw(wl)
+    inp = workloads.make_inputs(wl)
+    ref = _torch_reference(x, dy, inp.gamma, inp.beta, wl.act, wl.act_param, wl.eps,
+                           wl.momentum, inp.running_mean, inp.running_var)
+    f = oracle.forward_train_ckpt(x, inp.gamma, inp.beta, wl.act, wl.act_param, wl.eps,
+                                  wl.momentum, inp.running_mean, inp.running_var)
+    xt = torch.tensor(x)
+    var_t, mean_t = torch.var_mean(xt, dim=(0, 2, 3), unbiased=False, keepdim=True)
+    xhat_t = ((xt - mean_t) / torch.sqrt(var_t + wl.eps)).numpy()
+    assert _rel(f["xhat"], xhat_t) < 1e-12
+    assert _rel(f["y"], ref["y"]) < 1e-12
+    assert _rel(f["running_mean"], ref["running_mean"]) < 1e-12
+    assert _rel(f["running_var"], ref["running_var"]) < 1e-12
+    assert _rel(f["invstd"], 1.0 / np.sqrt(var_t.numpy().reshape(-1) + wl.eps)) < 1e-12
+    # the layer output rebuilt from the checkpoint: act(gamma xhat + beta) by torch
+    yr = oracle.recompute_from_xhat(f["xhat"], inp.gamma, inp.beta, wl.act, wl.act_param)
+    g = torch.tensor(inp.gamma.astype(np.float64)).view(1, -1, 1, 1)
+    b = torch.tensor(inp.beta.astype(np.float64)).view(1, -1, 1, 1)
+    yt = _torch_act(g * torch.tensor(f["xhat"]) + b, wl.act, wl.act_param).numpy()
+    assert _rel(yr, yt) < 1e-13
+    assert _rel(yr, ref["y"]) < 1e-12
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_ckpt_backward_matches_torch_fp64(wl):
+    """The backward from xhat (computed from x by torch) against torch's autograd of
+    batch_norm + activation taken from x."""
+    _, x, dy = _draw(wl)
+    inp = workloads.make_inputs(wl)
+    ref = _torch_reference(x, dy, inp.gamma, inp.beta, wl.act, wl.act_param, wl.eps)
+    xt = torch.tensor(x)
+    var_t, mean_t = torch.var_mean(xt, dim=(0, 2, 3), unbiased=False, keepdim=True)
+    inv_t = 1.0 / torch.sqrt(var_t + wl.eps)
+    xhat = ((xt - mean_t) * inv_t).numpy()
+    b = oracle.backward_from_xhat(xhat, dy, inp.gamma, inp.beta, inv_t.numpy().reshape(-1),
+                                  wl.act, wl.act_param)
+    assert _rel(b["dx"], ref["dx"]) < 1e-11
+    assert _rel(b["dgamma"], ref["dgamma"]) < 1e-11
+    assert _rel(b["dbeta"], ref["dbeta"]) < 1e-11
+
+
+def test_ckpt_backward_matches_finite_differences():
+    """Central differences of the checkpointing forward's y (loss sum dy*y) against
+    the backward from its xhat: dx, dgamma, dbeta."""
+    wl = dataclasses.replace(workloads.config(4).with_shape(2, 3, 4, 5), act_param=0.5)
+    inp, x, dy = _draw(wl)
+    g = inp.gamma.astype(np.float64)
+    b = inp.beta.astype(np.float64)
+
+    def loss(xx, gg, bb):
+        return float(np.sum(dy * oracle.forward_train_ckpt(xx, gg, bb, wl.act, wl.act_param,
+                                                           wl.eps)["y"]))
+
+    f = oracle.forward_train_ckpt(x, g, b, wl.act, wl.act_param, wl.eps)
+    bw = oracle.backward_from_xhat(f["xhat"], dy, g, b, f["invstd"], wl.act, wl.act_param)
+    h = 1e-6
+    for i in range(x.size):
+        xp, xm = x.copy(), x.copy()
+        xp.reshape(-1)[i] += h
+        xm.reshape(-1)[i] -= h
+        fd = (loss(xp, g, b) - loss(xm, g, b)) / (2 * h)
+        an = bw["dx"].reshape(-1)[i]
+        assert abs(fd - an) <= 1e-6 * (abs(an) + 1.0), (i, fd, an)
+    for c in range(wl.C):
+        for vec, key in ((g, "dgamma"), (b, "dbeta")):
+            vp, vm = vec.copy(), vec.copy()
+            vp[c] += h
+            vm[c] -= h
+            args_p = (x, vp, b) if key == "dgamma" else (x, g, vp)
+            args_m = (x, vm, b) if key == "dgamma" else (x, g, vm)
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - bw[key][c]) <= 1e-6 * (abs(fd) + 1.0), (key, c)
+
+
+def test_ckpt_backward_branches_on_the_exact_sign_of_z():
+    """Leaky ReLU slope where gamma*xhat + beta is within a rounding of zero: the side
+    is that of the exact value.  gamma = xhat = 1 + 2^-30 make gamma*xhat =
+    1 + 2^-29 + 2^-60, which fp64 rounds to 1 + 2^-29; with beta = -(1 + 2^-29)
+    the exact z is +2^-60 (slope 1), although a multiply then an add gives 0
+    (slope a).  With beta = -(1 + 2^-28) the exact z is negative (slope a)."""
+    a = 0.01
+    e = 1.0 + 2.0 ** -30
+    xh = np.full((1, 1, 1, 1), e)
+    dy = np.ones((1, 1, 1, 1))
+    g = np.array([e])
+    for beta, slope in ((-(1.0 + 2.0 ** -29), 1.0), (-(1.0 + 2.0 ** -28), a)):
+        r = oracle.backward_from_xhat(xh, dy, g, np.array([beta]), np.ones(1), "leaky_relu", a)
+        assert r["dbeta"][0] == slope, (beta, r["dbeta"][0])

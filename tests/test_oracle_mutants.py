@@ -57,6 +57,15 @@ MUTANTS = {
                           "                y[AT(n, c, i)] = act_forward(act, p, z);",
                           "const double z = xhat + beta[c];\n"
                           "                y[AT(n, c, i)] = act_forward(act, p, z);"),
+    # optimized checkpointing
+    "ckpt_xhat_not_scaled": ("const double xh = (x[AT(n, c, i)] - mu) * is;",
+                             "const double xh = (x[AT(n, c, i)] - mu);"),
+    "ckpt_dgamma_uses_z": ("sdzx += dz * xh;", "sdzx += dz * z;"),
+    "ckpt_dx_drops_mean_term": ("dx[AT(n, c, i)] = k * (dz - sdz / (double)m - xh * sdzx / (double)m);",
+                                "dx[AT(n, c, i)] = k * (dz - xh * sdzx / (double)m);"),
+    "ckpt_z_rounded_twice": ("return fma(gamma, xhat, beta);", "return gamma * xhat + beta;"),
+    "ckpt_recompute_drops_beta": ("y[AT(n, c, i)] = act_forward(act, p, gamma[c] * xhat[AT(n, c, i)] + beta[c]);",
+                                  "y[AT(n, c, i)] = act_forward(act, p, gamma[c] * xhat[AT(n, c, i)]);"),
 }
 
 
@@ -77,7 +86,14 @@ def _pin_suite():
         ("eval_backward", lambda: pins.test_eval_backward_matches_torch("leaky_relu", 0.2)),
         ("eval_backward_fd", pins.test_eval_backward_matches_finite_differences),
         ("f16_rounding", pins.test_round_storage_f16_matches_numpy_on_f32_values),
+        ("ckpt_backward_fd", pins.test_ckpt_backward_matches_finite_differences),
+        ("ckpt_exact_sign", pins.test_ckpt_backward_branches_on_the_exact_sign_of_z),
     ]
+    for wl in pins.SMALL[:3]:
+        cases.append(("ckpt_forward:" + wl.name,
+                      lambda wl=wl: pins.test_ckpt_forward_matches_torch_fp64(wl)))
+        cases.append(("ckpt_backward:" + wl.name,
+                      lambda wl=wl: pins.test_ckpt_backward_matches_torch_fp64(wl)))
     failed = []
     for name, fn in cases:
         try:
