@@ -43,6 +43,9 @@ forward + backward time per iteration, activation memory held after the
 forward, and peak memory (the pages' claims: less training memory at a small
 compute cost).  The convolutions are torch's (MIOpen) in both chains.
 
+--mode ckpt times InPlace-ABN II against optimized checkpointing (the block keeps
+xhat), the comparison the pages make.
+
 --mode shapes checks the plan on ResNet-50 activation shapes (N = 32 and a few
 others, NCHW fp32 and NHWC bf16): the cold step with the kernels the plan picks
 against the split kernels (the stage entry points), one JSON line per shape.
@@ -71,7 +74,7 @@ COLD_BYTES = 512 << 20
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     for f in ("device.hpp", "plan.hpp", "fused.hpp", "group.hpp", "fwd.hip", "bwd.hip",
-              "fused_nchw.hip", "fused_nhwc.hip", "noalloc.hip"):
+              "fused_nchw.hip", "fused_nhwc.hip", "ckpt.hip", "noalloc.hip"):
         with open(os.path.join(ROOT, "place_batchnorm_activation_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -326,6 +329,98 @@ def run_shapes(args) -> int:
     return 0
 
 
+def run_ckpt(args, wl) -> int:
+    """InPlace-ABN II against optimized checkpointing on the workload (the pages'
+    comparison, paperlayer section 3): cold steps of
+      ii_plan   iabn_forward_train + iabn_backward (the kernels the plan picks);
+      ii_split  the same through the stage entry points (the split kernels);
+      ckpt      iabn_forward_train_ckpt (xhat kept over x, y written) +
+                iabn_recompute_from_xhat (y rebuilt for the next layer's backward) +
+                iabn_backward_ckpt, on the split kernels as well.
+    Minimal bytes: II 5S a step; checkpointing 8S (forward 3S: read x, write xhat
+    and y; recompute 2S; backward 3S).  The split kernels move 8S (II) and 11S
+    (checkpointing)."""
+    import torch
+    import place_batchnorm_activation_amd as iabn
+    import workloads
+
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+    inp = workloads.make_inputs(wl)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sshape = (N, C, H, W) if wl.layout == "NCHW" else (N, H, W, C)
+    S = wl.storage_bytes
+    nsets = max(2, math.ceil(COLD_BYTES / (4 * S)))
+    x0 = workloads.to_torch(inp.x, wl.dtype).reshape(sshape).to(dev)
+    dy0 = workloads.to_torch(inp.dy, wl.dtype).reshape(sshape).to(dev)
+    sets = [{"x": x0.clone(), "dy": dy0.clone(), "dx": torch.empty_like(dy0),
+             "y": torch.empty_like(x0)} for _ in range(nsets)]
+    g = torch.from_numpy(inp.gamma).to(dev)
+    b = torch.from_numpy(inp.beta).to(dev)
+    rm = torch.from_numpy(inp.running_mean).to(dev)
+    rv = torch.from_numpy(inp.running_var).to(dev)
+    sm, si = torch.empty(C, device=dev), torch.empty(C, device=dev)
+    dg, db = torch.empty(C, device=dev), torch.empty(C, device=dev)
+    ws = iabn.workspace(N, C, H, W, wl.layout, x0.dtype, dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    L, act, p, eps, mom = wl.layout, wl.act, wl.act_param, wl.eps, wl.momentum
+
+    def ii_plan(s):
+        iabn.iabn_forward_train(s["x"], N, C, H, W, L, g, b, rm, rv, sm, si, act, p, eps, mom,
+                                ws, sp)
+        iabn.iabn_backward(s["x"], s["dy"], s["dx"], N, C, H, W, L, g, b, si, dg, db, act, p,
+                           ws, sp)
+
+    def ii_split(s):
+        iabn.iabn_forward_stats(s["x"], N, C, H, W, L, g, b, rm, rv, sm, si, eps, mom, ws, sp)
+        iabn.iabn_forward_apply(s["x"], N, C, H, W, L, act, p, ws, sp)
+        iabn.iabn_backward_reduce(s["x"], s["dy"], N, C, H, W, L, g, b, si, dg, db, act, p, ws,
+                                  sp)
+        iabn.iabn_backward_apply(s["x"], s["dy"], s["dx"], N, C, H, W, L, act, p, ws, sp)
+
+    def ckpt(s):
+        iabn.iabn_forward_train_ckpt(s["x"], s["y"], N, C, H, W, L, g, b, rm, rv, sm, si, act,
+                                     p, eps, mom, ws, sp)
+        iabn.iabn_recompute_from_xhat(s["x"], s["y"], N, C, H, W, L, g, b, act, p, sp)
+        iabn.iabn_backward_ckpt(s["x"], s["dy"], s["dx"], N, C, H, W, L, g, b, si, dg, db, act,
+                                p, ws, sp)
+
+    def timed(fn, k):
+        for i in range(max(3, args.warmup)):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(k):
+            fn(sets[i % nsets])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k          # us per step
+
+    res = {}
+    for name, fn in (("ii_plan", ii_plan), ("ii_split", ii_split), ("ckpt", ckpt)):
+        # each scheme twice, interleaved, and the better time kept
+        res[name] = timed(fn, args.steps)
+    for name, fn in (("ii_plan", ii_plan), ("ii_split", ii_split), ("ckpt", ckpt)):
+        res[name] = min(res[name], timed(fn, args.steps))
+    out = {
+        "metric": "InPlace-ABN II vs optimized checkpointing, fwd+bwd us per step",
+        "config": {"workload": wl.name, "N": N, "C": C, "H": H, "W": W, "layout": wl.layout,
+                   "storage": wl.dtype, "act": wl.act, "act_param": wl.act_param,
+                   "mode": "ckpt"},
+        "data": "synthetic", "n_gpus": 1, "steps": args.steps,
+        "protocol": "cold: %d rotating buffer sets of %.0f MB; best of two interleaved runs"
+                    % (nsets, 4 * S / 1e6),
+        "us_per_step": {k: round(v, 2) for k, v in res.items()},
+        "gelem_per_s": {k: round(wl.numel / (v * 1e-6) / 1e9, 2) for k, v in res.items()},
+        "ckpt_over_ii_split": round(res["ckpt"] / res["ii_split"], 4),
+        "ckpt_over_ii_plan": round(res["ckpt"] / res["ii_plan"], 4),
+        "plan": iabn.iabn_describe_plan(N, C, H, W, L, x0.dtype, act),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def run_block(args, wl) -> int:
     """InPlace-ABN against BatchNorm2d + activation inside a convolution chain."""
     import torch
@@ -417,10 +512,12 @@ def main() -> int:
     ap.add_argument("--warm-only", action="store_true", help="one buffer set (for profiling)")
     ap.add_argument("--dtype", choices=("f32", "bf16", "f16"), default=None,
                     help="storage dtype instead of the workload's own")
-    ap.add_argument("--mode", choices=("train", "frozen", "block", "shapes"), default="train",
+    ap.add_argument("--mode", choices=("train", "frozen", "block", "shapes", "ckpt"),
+                    default="train",
                     help="train: forward_train + backward; frozen: forward_eval + backward_eval; "
                          "block: conv + norm/act chain against torch's BatchNorm2d; "
-                         "shapes: the plan's kernels against the split ones on ResNet-50 shapes")
+                         "shapes: the plan's kernels against the split ones on ResNet-50 shapes; "
+                         "ckpt: InPlace-ABN II against optimized checkpointing")
     ap.add_argument("--layers", type=int, default=4, help="layers of the --mode block chain")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark: copy a MIB-MiB buffer 5 times (a plain copy "
@@ -455,6 +552,8 @@ def main() -> int:
         return run_block(args, wl)
     if args.mode == "shapes":
         return run_shapes(args)
+    if args.mode == "ckpt":
+        return run_ckpt(args, wl)
     return run_train(args, wl)
 
 

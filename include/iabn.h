@@ -262,6 +262,60 @@ iabn_status iabn_backward_eval(const void *y, const void *dy, void *dx,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Optimized checkpointing (section 3, "Proposed Checkpointing"): the scheme the
+ * pages weigh InPlace-ABN II against.  A BN + activation block keeps the
+ * normalised xhat instead of its input x; the layer output y is rebuilt from
+ * xhat (scale-and-shift, then the activation) when the following layer's
+ * backward needs it, and the BN backward reads xhat itself rather than
+ * recomputing it from x.  These run the split kernels (statistics pass, then an
+ * elementwise pass; backward sums, then dx), on every layout, dtype and
+ * activation, with the workspace of iabn_workspace_size.
+ */
+
+/* Training forward of the checkpointing block:
+ *   mu_c, var_c, invstd_c, running statistics, save_mean, save_invstd exactly as
+ *   iabn_forward_train;
+ *   xhat = (x - mu_c)*invstd_c, written over x (the kept buffer);
+ *   y = act(gamma_c*xhat' + beta_c) into y, where xhat' is xhat as stored, so
+ *   that y equals what iabn_recompute_from_xhat gives from the kept buffer.
+ *   y must not overlap x.  Errors as for iabn_forward_train.
+ * HBM traffic: read x twice, write xhat and y (4S). */
+iabn_status iabn_forward_train_ckpt(void *x_inout, void *y,
+                                    int64_t N, int64_t C, int64_t H, int64_t W,
+                                    iabn_layout layout, iabn_dtype dtype,
+                                    const float *gamma, const float *beta,
+                                    float *running_mean, float *running_var,
+                                    float *save_mean, float *save_invstd,
+                                    iabn_act act, float act_param, float eps, float momentum,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* The layer output rebuilt from the kept buffer: y = act(gamma_c*xhat + beta_c).
+ * y may be exactly xhat (in place) but must not partly overlap it.  Needs no
+ * workspace; an empty tensor is a no-op.  HBM traffic 2S. */
+iabn_status iabn_recompute_from_xhat(const void *xhat, void *y,
+                                     int64_t N, int64_t C, int64_t H, int64_t W,
+                                     iabn_layout layout, iabn_dtype dtype,
+                                     const float *gamma, const float *beta,
+                                     iabn_act act, float act_param, hipStream_t stream);
+
+/* Training backward of the checkpointing block, from the kept xhat:
+ *   z = gamma_c*xhat + beta_c, formed with one fused multiply-add so that the
+ *   activation's branch follows the sign of the exact value; dz = act'(z)*dy;
+ *   dbeta_c = sum dz, dgamma_c = sum dz*xhat,
+ *   dx = gamma_c*invstd_c*(dz - dbeta_c/m - xhat*dgamma_c/m).
+ *   Arguments, aliasing (dx may be exactly dy) and errors as for iabn_backward,
+ *   with xhat in place of y.  HBM traffic 5S (sums, then dx). */
+iabn_status iabn_backward_ckpt(const void *xhat, const void *dy, void *dx,
+                               int64_t N, int64_t C, int64_t H, int64_t W,
+                               iabn_layout layout, iabn_dtype dtype,
+                               const float *gamma, const float *beta, const float *save_invstd,
+                               float *dgamma, float *dbeta,
+                               iabn_act act, float act_param,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the training
  * forward exactly as iabn_forward_train, with the same arguments, results and

@@ -66,10 +66,17 @@ lib.iabn_set_grouped_kernels.argtypes = [_INT]
 lib.iabn_set_grouped_kernels.restype = _INT
 lib.iabn_workspace_status.argtypes = [_P, _SZ, _INT, ctypes.POINTER(_INT), _P]
 lib.iabn_workspace_status.restype = _INT
+lib.iabn_forward_train_ckpt.argtypes = [_P, _P] + _SHAPE + [_P, _P, _P, _P, _P, _P, _INT, _F, _F,
+                                                            _F, _P, _SZ, _P]
+lib.iabn_recompute_from_xhat.argtypes = [_P, _P] + _SHAPE + [_P, _P, _INT, _F, _P]
+lib.iabn_backward_ckpt.argtypes = [_P, _P, _P] + _SHAPE + [_P, _P, _P, _P, _P, _INT, _F, _P, _SZ,
+                                                           _P]
 lib.iabn_describe_plan.argtypes = _SHAPE + [_INT, _INT, ctypes.c_char_p, _SZ]
 lib.iabn_describe_plan.restype = _INT
-for _fn in ("iabn_forward_train", "iabn_forward_train_noalloc", "iabn_forward_stats", "iabn_forward_apply", "iabn_forward_eval",
-            "iabn_backward", "iabn_backward_reduce", "iabn_backward_apply", "iabn_backward_eval"):
+for _fn in ("iabn_forward_train", "iabn_forward_train_noalloc", "iabn_forward_train_ckpt",
+            "iabn_recompute_from_xhat", "iabn_backward_ckpt", "iabn_forward_stats",
+            "iabn_forward_apply", "iabn_forward_eval", "iabn_backward", "iabn_backward_reduce",
+            "iabn_backward_apply", "iabn_backward_eval"):
     getattr(lib, _fn).restype = _INT
 
 
@@ -259,6 +266,33 @@ def iabn_backward_eval(y, dy, dx, N, C, H, W, layout, gamma, beta, running_var, 
         _ptr(y), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y),
         _ptr(gamma), _ptr(beta), _ptr(running_var), eps, _ptr(dgamma), _ptr(dbeta),
         _code(act, ACTS), act_param, wp, wb, _stream(stream)))
+
+
+def iabn_forward_train_ckpt(x, y, N, C, H, W, layout, gamma, beta, running_mean, running_var,
+                            save_mean, save_invstd, act, act_param, eps, momentum, workspace,
+                            stream=None):
+    """Optimized checkpointing forward: xhat written over x, the layer output into y."""
+    wp, wb = _ws(workspace)
+    _check("iabn_forward_train_ckpt", lib.iabn_forward_train_ckpt(
+        _ptr(x), _ptr(y), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma),
+        _ptr(beta), _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_invstd),
+        _code(act, ACTS), act_param, eps, momentum, wp, wb, _stream(stream)))
+
+
+def iabn_recompute_from_xhat(xhat, y, N, C, H, W, layout, gamma, beta, act, act_param,
+                             stream=None):
+    _check("iabn_recompute_from_xhat", lib.iabn_recompute_from_xhat(
+        _ptr(xhat), _ptr(y), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(xhat), _ptr(gamma),
+        _ptr(beta), _code(act, ACTS), act_param, _stream(stream)))
+
+
+def iabn_backward_ckpt(xhat, dy, dx, N, C, H, W, layout, gamma, beta, save_invstd, dgamma, dbeta,
+                       act, act_param, workspace, stream=None):
+    wp, wb = _ws(workspace)
+    _check("iabn_backward_ckpt", lib.iabn_backward_ckpt(
+        _ptr(xhat), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(xhat),
+        _ptr(gamma), _ptr(beta), _ptr(save_invstd), _ptr(dgamma), _ptr(dbeta), _code(act, ACTS),
+        act_param, wp, wb, _stream(stream)))
 
 
 def iabn_describe_plan(N, C, H, W, layout, dtype, act, aligned16=True) -> str:

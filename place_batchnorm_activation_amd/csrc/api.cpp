@@ -527,6 +527,72 @@ iabn_status iabn_backward_eval(const void* y, const void* dy, void* dx, int64_t 
     return launched();
 }
 
+iabn_status iabn_forward_train_ckpt(void* x_inout, void* y, int64_t N, int64_t C, int64_t H,
+                                    int64_t W, iabn_layout layout, iabn_dtype dtype,
+                                    const float* gamma, const float* beta, float* running_mean,
+                                    float* running_var, float* save_mean, float* save_invstd,
+                                    iabn_act act, float act_param, float eps, float momentum,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    IABN_TRY(check_act(act, act_param));
+    IABN_TRY(check_forward_train(x_inout, N, C, H, W, layout, dtype, gamma, beta, running_mean,
+                                 running_var, save_mean, save_invstd, eps, momentum));
+    if (C == 0) return IABN_OK;
+    IABN_TRY(check_tensor(y, dtype));
+    const size_t bytes = size_t(N * C * H * W) * (dtype == IABN_F32 ? 4 : 2);
+    if (overlap(y, x_inout, bytes)) return IABN_ERR_INVALID_ARG;
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(x_inout, 16) && aligned(y, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pl));
+    launch_forward_stats(pl, x_inout, gamma, beta, running_mean, running_var, save_mean,
+                         save_invstd, eps, momentum, workspace, stream);
+    launch_ckpt_forward_apply(pl, x_inout, y, gamma, beta, save_invstd, act, act_param, workspace,
+                              stream);
+    return launched();
+}
+
+iabn_status iabn_recompute_from_xhat(const void* xhat, void* y, int64_t N, int64_t C, int64_t H,
+                                     int64_t W, iabn_layout layout, iabn_dtype dtype,
+                                     const float* gamma, const float* beta, iabn_act act,
+                                     float act_param, hipStream_t stream)
+{
+    IABN_TRY(check_shape(N, C, H, W, layout, dtype));
+    IABN_TRY(check_act(act, act_param));
+    if (N * C * H * W == 0) return IABN_OK;
+    IABN_TRY(check_tensor(xhat, dtype));
+    IABN_TRY(check_tensor(y, dtype));
+    IABN_TRY(check_channel_vec(gamma, true));
+    IABN_TRY(check_channel_vec(beta, true));
+    const size_t bytes = size_t(N * C * H * W) * (dtype == IABN_F32 ? 4 : 2);
+    if (y != xhat && overlap(y, xhat, bytes)) return IABN_ERR_INVALID_ARG;
+    const Plan pl = plan_for(N, C, H, W, layout, dtype, aligned(xhat, 16) && aligned(y, 16));
+    launch_ckpt_recompute(pl, xhat, y, gamma, beta, act, act_param, stream);
+    return launched();
+}
+
+iabn_status iabn_backward_ckpt(const void* xhat, const void* dy, void* dx, int64_t N, int64_t C,
+                               int64_t H, int64_t W, iabn_layout layout, iabn_dtype dtype,
+                               const float* gamma, const float* beta, const float* save_invstd,
+                               float* dgamma, float* dbeta, iabn_act act, float act_param,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    IABN_TRY(check_backward(xhat, dy, dx, N, C, H, W, layout, dtype, act, act_param));
+    if (C == 0) return IABN_OK;
+    IABN_TRY(check_channel_vec(gamma, true));
+    IABN_TRY(check_channel_vec(beta, true));
+    IABN_TRY(check_channel_vec(save_invstd, true));
+    IABN_TRY(check_channel_vec(dgamma, true));
+    IABN_TRY(check_channel_vec(dbeta, true));
+    const Plan pr = plan_for(N, C, H, W, layout, dtype, aligned(xhat, 16) && aligned(dy, 16));
+    const Plan pa = plan_for(N, C, H, W, layout, dtype,
+                             aligned(xhat, 16) && aligned(dy, 16) && aligned(dx, 16));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pr));
+    IABN_TRY(check_workspace(workspace, workspace_bytes, pa));
+    launch_backward_reduce_xhat(pr, xhat, dy, gamma, beta, save_invstd, dgamma, dbeta, act,
+                                act_param, workspace, stream);
+    launch_ckpt_dx(pa, xhat, dy, dx, gamma, beta, act, act_param, workspace, stream);
+    return launched();
+}
+
 int iabn_describe_plan(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout,
                        iabn_dtype dtype, iabn_act act, int aligned16, char* buf, size_t len)
 {

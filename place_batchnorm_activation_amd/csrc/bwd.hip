@@ -34,18 +34,36 @@ constexpr int kUnrollB = IABN_REDUCE_UNROLL;
 #endif
 constexpr int kUnrollN = IABN_NHWC_REDUCE_UNROLL;
 
-template <int ACT, int V>
+// XH: the stored value is xhat (optimized checkpointing) instead of y.  Its
+// decode gives the slope at z = fmaf(gamma, xhat, beta) and t = xhat, so the
+// sums become dbeta = sum dz and dgamma = sum dz*t directly (k_bwd_finalize with
+// xhat_sums).
+template <int ACT, bool XH>
+__device__ __forceinline__ void decode(float v, float g, float b, float a, float inv_a, float& t,
+                                       float& slope)
+{
+    if constexpr (XH) {
+        slope = act_slope_at<ACT>(fmaf(g, v, b), a);
+        t = v;
+    } else {
+        float z;
+        act_invert<ACT>(v, a, inv_a, z, slope);
+        t = z - b;
+    }
+}
+
+template <int ACT, int V, bool XH = false>
 __device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy)[V],
-                                           const float (&beta)[V], float a, float inv_a,
-                                           float (&sdz)[V], float (&sdzt)[V])
+                                           const float (&beta)[V], const float (&gam)[V], float a,
+                                           float inv_a, float (&sdz)[V], float (&sdzt)[V])
 {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        float z, slope;
-        act_invert<ACT>(y[e], a, inv_a, z, slope);
+        float t, slope;
+        decode<ACT, XH>(y[e], gam[e], beta[e], a, inv_a, t, slope);
         const float dz = slope * dy[e];
         sdz[e] += dz;
-        sdzt[e] = fmaf(dz, z - beta[e], sdzt[e]);
+        sdzt[e] = fmaf(dz, t, sdzt[e]);
     }
 }
 
@@ -79,13 +97,15 @@ __device__ __forceinline__ float frozen_scale(const float* gamma, const float* v
 // NCHW: workgroup b covers channel c = b / P, partial p = b % P.
 // DX: also writes dx for the backward with frozen statistics (each element of dy
 // is read by the thread that then writes the same element of dx, so dx may be dy).
-template <int DT, int V, int ACT, bool DX>
+// XH: y holds xhat (optimized checkpointing; not with DX).
+template <int DT, int V, int ACT, bool DX, bool XH = false>
 __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
     const void* __restrict__ y, const void* dy, int64_t C, int64_t HW, int64_t m,
     int64_t unit, int64_t P, const float* __restrict__ beta, float a, float inv_a,
     float* __restrict__ part_dz, float* __restrict__ part_dzt, void* dx,
     const float* __restrict__ gamma, const float* __restrict__ frozen_var, float eps)
 {
+    static_assert(!(DX && XH), "the frozen-statistics pass reads y");
     const int64_t b = blockIdx.x;
     const int64_t c = b / P;
     const int64_t p = b - c * P;
@@ -93,11 +113,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
     const int64_t j1 = dmin(p * unit + unit, m) / V;
     int64_t j = p * unit / V + threadIdx.x;
 
-    float bc[V], sdz[V], sdzt[V], A[V];
+    float bc[V], gc[V], sdz[V], sdzt[V], A[V];
     const float bb = beta[c];
+    const float gg = XH ? gamma[c] : 0.f;
     const float Ac = DX ? frozen_scale(gamma, frozen_var, eps, c) : 0.f;
 #pragma unroll
-    for (int e = 0; e < V; ++e) { bc[e] = bb; A[e] = Ac; sdz[e] = 0.f; sdzt[e] = 0.f; }
+    for (int e = 0; e < V; ++e) {
+        bc[e] = bb;
+        gc[e] = gg;
+        A[e] = Ac;
+        sdz[e] = 0.f;
+        sdzt[e] = 0.f;
+    }
 
     ChannelWalk w;
     w.init(j < j1 ? j : 0, c, C, HWv, kThreads);
@@ -117,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
                 accumulate_dx<ACT, V>(vy[u], vd[u], bc, A, a, inv_a, sdz, sdzt);
                 store_out<DT, V>(dx, ad[u], vd[u]);
             } else {
-                accumulate<ACT, V>(vy[u], vd[u], bc, a, inv_a, sdz, sdzt);
+                accumulate<ACT, V, XH>(vy[u], vd[u], bc, gc, a, inv_a, sdz, sdzt);
             }
         }
     }
@@ -131,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
             accumulate_dx<ACT, V>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
             store_out<DT, V>(dx, ad, vd);
         } else {
-            accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+            accumulate<ACT, V, XH>(vy, vd, bc, gc, a, inv_a, sdz, sdzt);
         }
     }
     float S1 = 0.f, S2 = 0.f;
@@ -155,13 +182,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
 // ---------------------------------------------------------------------------
 // NHWC: workgroup b covers channel slice b % slices and partial b / slices, i.e.
 // row groups p, p + P, ... of rpi = 256/tpr rows (as the statistics kernel).
-template <int DT, int V, int ACT, bool DX>
+template <int DT, int V, int ACT, bool DX, bool XH = false>
 __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     const void* __restrict__ y, const void* dy, int64_t m, int64_t Cv, int tpr,
     int64_t slices, int64_t groups, int64_t P, const float* __restrict__ beta, float a,
     float inv_a, float* __restrict__ part_dz, float* __restrict__ part_dzt, void* dx,
     const float* __restrict__ gamma, const float* __restrict__ frozen_var, float eps)
 {
+    static_assert(!(DX && XH), "the frozen-statistics pass reads y");
     const int64_t b = blockIdx.x;
     const int64_t p = b / slices;
     const int64_t sl = b - p * slices;
@@ -171,22 +199,29 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     const int64_t col = sl * tpr + (t - rs * tpr);
     const bool active = col < Cv;
 
-    float bc[V], sdz[V], sdzt[V], A[V];
+    float bc[V], gc[V], sdz[V], sdzt[V], A[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) { bc[e] = 0.f; A[e] = 0.f; sdz[e] = 0.f; sdzt[e] = 0.f; }
+    for (int e = 0; e < V; ++e) {
+        bc[e] = 0.f;
+        gc[e] = 0.f;
+        A[e] = 0.f;
+        sdz[e] = 0.f;
+        sdzt[e] = 0.f;
+    }
     // one element of the reduction; with DX also dx at storage index i (elements)
     auto one = [&](float (&vy)[V], float (&vd)[V], int64_t i) {
         if constexpr (DX) {
             accumulate_dx<ACT, V>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
             store_out<DT, V>(dx, i, vd);
         } else {
-            accumulate<ACT, V>(vy, vd, bc, a, inv_a, sdz, sdzt);
+            accumulate<ACT, V, XH>(vy, vd, bc, gc, a, inv_a, sdz, sdzt);
         }
     };
     if (active) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             bc[e] = beta[col * V + e];
+            if constexpr (XH) gc[e] = gamma[col * V + e];
             if constexpr (DX) A[e] = frozen_scale(gamma, frozen_var, eps, col * V + e);
         }
         if constexpr (V == Raw16<DT>::V) {
@@ -286,12 +321,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
 // frozen_var non-null: the statistics are the frozen running ones (the backward
 // through the inference forward), so dx = gamma*dz/sqrt(frozen_var + eps): the
 // constants become {A, 0, 0, beta}, and dgamma, dbeta are the same sums.
+// xhat_sums: the second sums are of dz*xhat (optimized checkpointing), so dgamma
+// is their total and dx = A*dz + B*xhat + Cc with B = -A*dgamma/m.
 __global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     int64_t C, int64_t m, int64_t P, const float* __restrict__ part_dz,
     const float* __restrict__ part_dzt, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* __restrict__ invstd,
     const float* __restrict__ frozen_var, float eps,
-    float* __restrict__ dgamma, float* __restrict__ dbeta, float4* __restrict__ consts)
+    float* __restrict__ dgamma, float* __restrict__ dbeta, float4* __restrict__ consts,
+    bool xhat_sums = false)
 {
     const int cl = threadIdx.x % kFinChannels;
     const int ph = threadIdx.x / kFinChannels;
@@ -332,7 +370,7 @@ __global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     for (int k = 1; k < kFinPhases; ++k) { s1 += sh1[k][cl]; s2 += sh2[k][cl]; }
     const double g = double(g_c);
     const double db = s1;
-    const double dg = s2 / g;
+    const double dg = xhat_sums ? s2 : s2 / g;
     dbeta[c] = float(db);
     dgamma[c] = float(dg);
     if (frozen_var) {
@@ -341,7 +379,8 @@ __global__ __launch_bounds__(kFinThreads) void k_bwd_finalize(
     }
     const double A = g * double(s_c);
     const double md = double(m);
-    consts[c] = make_float4(float(A), float(-A * dg / (md * g)), float(-A * db / md), b_c);
+    const double B = xhat_sums ? -A * dg / md : -A * dg / (md * g);
+    consts[c] = make_float4(float(A), float(B), float(-A * db / md), b_c);
 }
 
 // The dx constants of the backward through the inference forward when dgamma and
@@ -553,22 +592,23 @@ struct FrozenDx {
     float eps = 0.f;
 };
 
-template <int DT, int V, int ACT, bool DX>
+template <int DT, int V, int ACT, bool DX, bool XH>
 static void launch_reduce_dva(const Plan& pl, const void* y, const void* dy, const float* beta,
                               float a, float ia, float* pa, float* pb, const FrozenDx& f,
                               hipStream_t s)
 {
     if (pl.layout == kNCHW)
-        hipLaunchKernelGGL((k_bwd_reduce_nchw<DT, V, ACT, DX>), dim3(pl.reduce_blocks),
+        hipLaunchKernelGGL((k_bwd_reduce_nchw<DT, V, ACT, DX, XH>), dim3(pl.reduce_blocks),
                            dim3(kThreads), 0, s, y, dy, pl.C, pl.HW, pl.m, pl.unit, pl.P, beta, a,
                            ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
     else
-        hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT, DX>), dim3(pl.reduce_blocks_bwd),
+        hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT, DX, XH>), dim3(pl.reduce_blocks_bwd),
                            dim3(kThreads), 0, s, y, dy, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit,
                            pl.P_bwd, beta, a, ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
 }
 
-template <bool DX>
+// XH: the reduction reads xhat instead of y (f.gamma carries gamma for it).
+template <bool DX, bool XH = false>
 static void launch_reduce(const Plan& pl, const void* y, const void* dy, const float* beta,
                           int act, float a, float ia, float* pa, float* pb, const FrozenDx& f,
                           hipStream_t s)
@@ -577,9 +617,10 @@ static void launch_reduce(const Plan& pl, const void* y, const void* dy, const f
         with_act(act, [&](auto ac) {
             constexpr int DT = decltype(d)::value, ACT = decltype(ac)::value;
             if (pl.vec)
-                launch_reduce_dva<DT, vec_width(DT), ACT, DX>(pl, y, dy, beta, a, ia, pa, pb, f, s);
+                launch_reduce_dva<DT, vec_width(DT), ACT, DX, XH>(pl, y, dy, beta, a, ia, pa, pb,
+                                                                  f, s);
             else
-                launch_reduce_dva<DT, 1, ACT, DX>(pl, y, dy, beta, a, ia, pa, pb, f, s);
+                launch_reduce_dva<DT, 1, ACT, DX, XH>(pl, y, dy, beta, a, ia, pa, pb, f, s);
         });
     });
 }
@@ -597,6 +638,23 @@ void launch_backward_reduce(const Plan& pl, const void* y, const void* dy, const
     hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
                        dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P_bwd, pa, pb, gamma, beta, invstd,
                        static_cast<const float*>(nullptr), 0.f, dgamma, dbeta, consts);
+}
+
+void launch_backward_reduce_xhat(const Plan& pl, const void* xhat, const void* dy,
+                                 const float* gamma, const float* beta, const float* invstd,
+                                 float* dgamma, float* dbeta, int act, float a, void* ws,
+                                 hipStream_t s)
+{
+    char* wsb = static_cast<char*>(ws);
+    float* pa = reinterpret_cast<float*>(wsb + pl.off_part_a);
+    float* pb = reinterpret_cast<float*>(wsb + pl.off_part_b);
+    float4* consts = reinterpret_cast<float4*>(wsb + pl.off_const);
+    FrozenDx g;
+    g.gamma = gamma;
+    launch_reduce<false, true>(pl, xhat, dy, beta, act, a, 1.f, pa, pb, g, s);
+    hipLaunchKernelGGL(k_bwd_finalize, dim3(unsigned(ceil_div(pl.C, kFinChannels))),
+                       dim3(kFinThreads), 0, s, pl.C, pl.m, pl.P_bwd, pa, pb, gamma, beta, invstd,
+                       static_cast<const float*>(nullptr), 0.f, dgamma, dbeta, consts, true);
 }
 
 void launch_backward_eval_grads(const Plan& pl, const void* y, const void* dy, void* dx,

@@ -248,6 +248,18 @@ __device__ __forceinline__ void act_invert(float y, float a, float inv_a, float&
     }
 }
 
+// act'(z) from the pre-activation itself (optimized checkpointing rebuilds z =
+// gamma*xhat + beta with one fused multiply-add, whose sign is exact):
+// leaky ReLU a, ELU alpha*exp(z), on the non-positive side.
+template <int ACT>
+__device__ __forceinline__ float act_slope_at(float z, float a)
+{
+    if constexpr (ACT == kLeaky) return z > 0.f ? 1.f : a;
+    else if constexpr (ACT == kElu)
+        return z > 0.f ? 1.f : a * __builtin_amdgcn_exp2f(z * 1.44269504088896341f);
+    else return 1.f;
+}
+
 // ---------------------------------------------------------------------------
 // Chan et al. pairwise update of (count, mean, M2): merge b into a.  The weight
 // nb/(n+nb) takes the hardware reciprocal in fp32 (1 ulp), an exact division in fp64.

@@ -37,4 +37,27 @@ void launch_eval_consts(const Plan& pl, const float* gamma, const float* beta,
 void launch_backward_apply(const Plan& pl, const void* y, const void* dy, void* dx, int act,
                            float a, void* ws, hipStream_t s);
 
+// Optimized checkpointing (the block keeps xhat): the backward sums read from
+// xhat, leaving dgamma, dbeta and the dx constants {A, B, Cc, beta} with
+// dx = A*dz + B*xhat + Cc.
+void launch_backward_reduce_xhat(const Plan& pl, const void* xhat, const void* dy,
+                                 const float* gamma, const float* beta, const float* invstd,
+                                 float* dgamma, float* dbeta, int act, float a, void* ws,
+                                 hipStream_t s);
+
+// xhat written over x and y = act(gamma*xhat + beta) into y, from the constants
+// launch_forward_stats left in the workspace and its save_invstd.
+void launch_ckpt_forward_apply(const Plan& pl, void* x, void* y, const float* gamma,
+                               const float* beta, const float* invstd, int act, float a, void* ws,
+                               hipStream_t s);
+
+// y = act(gamma*xhat + beta).
+void launch_ckpt_recompute(const Plan& pl, const void* xhat, void* y, const float* gamma,
+                           const float* beta, int act, float a, hipStream_t s);
+
+// dx from xhat and dy, with the constants launch_backward_reduce_xhat left.
+void launch_ckpt_dx(const Plan& pl, const void* xhat, const void* dy, void* dx,
+                    const float* gamma, const float* beta, int act, float a, void* ws,
+                    hipStream_t s);
+
 }  // namespace iabn

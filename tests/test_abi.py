@@ -300,3 +300,32 @@ def test_noalloc_forward_rejects_shapes_beyond_its_scratch():
                                           1e-5, 0.1, None) == MISALIGNED
     assert lib.iabn_forward_train_noalloc(None, 2, 0, 4, 4, 0, 0, None, None, None, None, None,
                                           None, 1, 0.01, 1e-5, 0.1, None) == OK
+
+
+def test_ckpt_validation():
+    """Optimized checkpointing entry points validate like their InPlace-ABN
+    counterparts, plus y must not overlap x."""
+    def fwd(x=A, y=8 * A, N=2, C=3, H=4, W=4, ws=A, wsb=1 << 20, p=0.01):
+        return lib.iabn_forward_train_ckpt(x, y, N, C, H, W, 0, 0, A, A, A, A, A, A, 1, p, 1e-5,
+                                           0.1, ws, wsb, None)
+    assert fwd(y=None) == INVALID
+    assert fwd(y=A + 64) == INVALID                 # y overlaps x
+    assert fwd(p=0.0) == INVALID
+    assert fwd(N=1, H=1, W=1) == INVALID            # m = 1
+    assert fwd(ws=None) == WS
+    assert fwd(y=8 * A + 2) == MISALIGNED
+    assert fwd(C=0, x=None, y=None) == OK
+
+    def rec(xh=A, y=8 * A, C=3, p=0.01):
+        return lib.iabn_recompute_from_xhat(xh, y, 2, C, 4, 4, 0, 0, A, A, 1, p, None)
+    assert rec(y=None) == INVALID
+    assert rec(y=A + 64) == INVALID                 # partly overlaps xhat
+    assert rec(p=-1.0) == INVALID
+    assert rec(C=0, xh=None, y=None) == OK
+
+    def bwd(xh=A, dy=4 * A, dx=8 * A, ws=A):
+        return lib.iabn_backward_ckpt(xh, dy, dx, 2, 3, 4, 4, 0, 0, A, A, A, A, A, 1, 0.01, ws,
+                                      1 << 20, None)
+    assert bwd(dx=A) == INVALID                     # dx over xhat
+    assert bwd(dx=4 * A + 64) == INVALID            # dx partly over dy
+    assert bwd(ws=None) == WS
