@@ -1,7 +1,8 @@
 """The PyTorch autograd binding (place_batchnorm_activation_amd.autograd) on the GPU.
 
 The binding only marshals tensors, so its outputs must be bit-identical to the
-C-ABI calls that the parity tests check against the oracle; channels_last input
+C-ABI calls, and within the parity gates of the fp64 oracle (training and eval
+mode, checked here against the oracle directly); channels_last input
 takes the NHWC kernels; eval mode takes the frozen-statistics pair; and the
 autograd graph keeps y alone per layer (the memory claim of section 3 of the
 paperlayer summary, "INPLACE-ABN").
@@ -11,6 +12,7 @@ import pytest
 import torch
 
 import harness
+import oracle
 import workloads
 
 iabn = pytest.importorskip("place_batchnorm_activation_amd")
@@ -60,6 +62,71 @@ def test_training_matches_the_c_abi_bitwise(wl):
     assert np.array_equal(m.bias.grad.cpu().numpy(), ref.dbeta)
     assert np.array_equal(m.running_mean.cpu().numpy(), ref.running_mean)
     assert np.array_equal(m.running_var.cpu().numpy(), ref.running_var)
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_training_matches_the_oracle(wl):
+    """The module's y, running statistics, dx, dgamma and dbeta against the fp64
+    oracle: the forward on the same x bits; the backward on the module's own y
+    bits, with the oracle's invstd (the module keeps save_invstd to itself; the
+    two agree to fp32 rounding, far inside the gates)."""
+    inp = workloads.make_inputs(wl)
+    m = _module(wl, inp)
+    x_leaf = harness.to_device(inp.x, wl).requires_grad_()
+    x = (x_leaf.permute(0, 3, 1, 2).clone(memory_format=torch.channels_last)
+         if wl.layout == "NHWC" else x_leaf.clone())
+    y = m(x)
+    dy = harness.to_device(inp.dy, wl)
+    y.backward(dy.permute(0, 3, 1, 2) if wl.layout == "NHWC" else dy)
+    torch.cuda.synchronize()
+    y_st = y.detach().permute(0, 2, 3, 1) if wl.layout == "NHWC" else y.detach()
+    a = harness.f32(wl.act_param)
+    xo = harness.storage_channels(inp.x, wl)
+    f = oracle.forward_train(xo, inp.gamma, inp.beta, wl.act, a, harness.f32(wl.eps),
+                             harness.f32(wl.momentum), inp.running_mean, inp.running_var,
+                             storage=wl.dtype)
+    yg = harness.to_nchw64(y_st, wl)
+    o = oracle.backward_from_y(yg, harness.storage_channels(inp.dy, wl), inp.gamma, inp.beta,
+                               f["invstd"], wl.act, a)
+    err = {"y": harness.rel_err_tensor(yg, f["y"]),
+           "running_mean": harness.rel_err_vec(m.running_mean.cpu().numpy(), f["running_mean"]),
+           "running_var": harness.rel_err_vec(m.running_var.cpu().numpy(), f["running_var"]),
+           "dx": harness.rel_err_tensor(harness.to_nchw64(x_leaf.grad, wl), o["dx"]),
+           "dgamma": harness.rel_err_vec(m.weight.grad.cpu().numpy(), o["dgamma"]),
+           "dbeta": harness.rel_err_vec(m.bias.grad.cpu().numpy(), o["dbeta"])}
+    print("case:", wl.name, err, flush=True)
+    harness.assert_within(err, wl.dtype, wl.name)
+
+
+def test_eval_mode_matches_the_oracle():
+    """Eval mode (frozen running statistics) against the oracle's inference forward
+    and its backward with the statistics frozen."""
+    wl = workloads.config(4).with_shape(3, 8, 10, 10)
+    inp = workloads.make_inputs(wl)
+    m = _module(wl, inp).eval()
+    rng = np.random.default_rng(5)
+    rm = rng.normal(0, 1, wl.C).astype(np.float32)
+    rv = rng.uniform(0.5, 2, wl.C).astype(np.float32)
+    with torch.no_grad():
+        m.running_mean.copy_(torch.from_numpy(rm))
+        m.running_var.copy_(torch.from_numpy(rv))
+    x_leaf = harness.to_device(inp.x, wl).requires_grad_()
+    y = m(x_leaf.clone())
+    dy = harness.to_device(inp.dy, wl)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    a, eps = harness.f32(wl.act_param), harness.f32(wl.eps)
+    yo = oracle.forward_eval(harness.storage_channels(inp.x, wl), inp.gamma, inp.beta, rm, rv,
+                             wl.act, a, eps, storage=wl.dtype)
+    yg = harness.to_nchw64(y.detach(), wl)
+    o = oracle.backward_eval(yg, harness.storage_channels(inp.dy, wl), inp.gamma, inp.beta, rv,
+                             wl.act, a, eps)
+    err = {"y": harness.rel_err_tensor(yg, yo),
+           "dx": harness.rel_err_tensor(harness.to_nchw64(x_leaf.grad, wl), o["dx"]),
+           "dgamma": harness.rel_err_vec(m.weight.grad.cpu().numpy(), o["dgamma"]),
+           "dbeta": harness.rel_err_vec(m.bias.grad.cpu().numpy(), o["dbeta"])}
+    print("eval:", err, flush=True)
+    harness.assert_within(err, wl.dtype, "eval")
 
 
 def test_eval_mode_uses_frozen_statistics():
