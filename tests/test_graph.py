@@ -125,3 +125,54 @@ def test_frozen_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         for k in eager:
             assert torch.equal(d[k], eager[k]), k
+
+
+CKPT_CASES = [
+    workloads.config(2).with_shape(4, 32, 16, 16),                 # NCHW
+    workloads.config(4).with_shape(2, 16, 40, 40),                 # NCHW f16, ELU
+    workloads.config(3).with_shape(3, 64, 24, 24),                 # NHWC bf16
+]
+
+
+@pytest.mark.parametrize("wl", CKPT_CASES, ids=lambda w: w.name)
+def test_ckpt_step_graph_replays_match_eager(wl):
+    """Optimized checkpointing captured as one step: the forward keeping xhat,
+    the recompute of y from xhat, the backward from xhat."""
+    inp = workloads.make_inputs(wl)
+    d = _bufs(wl, inp)
+    d["y"], d["yr"] = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+    N, C, H, W = wl.N, wl.C, wl.H, wl.W
+
+    def step(stream):
+        iabn.iabn_forward_train_ckpt(d["x"], d["y"], N, C, H, W, wl.layout, d["g"], d["b"],
+                                     d["rm"], d["rv"], d["sm"], d["si"], wl.act, wl.act_param,
+                                     wl.eps, wl.momentum, d["ws"], stream)
+        iabn.iabn_recompute_from_xhat(d["x"], d["yr"], N, C, H, W, wl.layout, d["g"], d["b"],
+                                      wl.act, wl.act_param, stream)
+        iabn.iabn_backward_ckpt(d["x"], d["dy"], d["dx"], N, C, H, W, wl.layout, d["g"],
+                                d["b"], d["si"], d["dg"], d["db"], wl.act, wl.act_param,
+                                d["ws"], stream)
+
+    def reset():
+        _reset(d)
+        d["y"].fill_(float("nan"))
+        d["yr"].fill_(float("nan"))
+
+    outs = OUTS + ("y", "yr")
+    reset()
+    step(None)
+    torch.cuda.synchronize()
+    eager = {k: d[k].clone() for k in outs}
+    assert torch.equal(eager["y"], eager["yr"])
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        step(side.cuda_stream)
+    for _ in range(4):
+        reset()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(d[k], eager[k]), k

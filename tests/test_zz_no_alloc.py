@@ -90,3 +90,69 @@ def test_noalloc_forward_twice_on_the_same_input():
     b = _call(True, inp)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def _prepared(inp):
+    wl = inp.wl
+    d = {"x0": harness.to_device(inp.x, wl), "g": torch.from_numpy(inp.gamma).cuda(),
+         "b": torch.from_numpy(inp.beta).cuda(),
+         "rm0": torch.from_numpy(inp.running_mean).cuda(),
+         "rv0": torch.from_numpy(inp.running_var).cuda()}
+    d["x"], d["rm"], d["rv"] = d["x0"].clone(), d["rm0"].clone(), d["rv0"].clone()
+    d["sm"], d["si"] = torch.empty(wl.C, device="cuda"), torch.empty(wl.C, device="cuda")
+    return d
+
+
+def _reset(d):
+    d["x"].copy_(d["x0"])
+    d["rm"].copy_(d["rm0"])
+    d["rv"].copy_(d["rv0"])
+    d["sm"].fill_(float("nan"))
+    d["si"].fill_(float("nan"))
+
+
+def _noalloc(wl, d, stream):
+    st = iabn.lib.iabn_forward_train_noalloc(
+        d["x"].data_ptr(), wl.N, wl.C, wl.H, wl.W, CODES[wl.layout], DT[wl.dtype],
+        d["g"].data_ptr(), d["b"].data_ptr(), d["rm"].data_ptr(), d["rv"].data_ptr(),
+        d["sm"].data_ptr(), d["si"].data_ptr(), ACT[wl.act], ctypes.c_float(wl.act_param),
+        ctypes.c_float(wl.eps), ctypes.c_float(wl.momentum), stream)
+    assert st == 0, iabn.status_string(st)
+
+
+def test_noalloc_forward_graph_replays_match_eager():
+    """The entry point is for callers that cannot allocate, such as code under
+    graph capture: captured once, replayed four times, with an eager call of
+    another shape (another plan over the same scratch) between the replays;
+    every replay gives the eager call's bits."""
+    wl = workloads.config(3).with_shape(2, 256, 128, 128)      # grouped NHWC
+    other = workloads.config(2).with_shape(3, 64, 56, 56)      # NCHW, channel groups
+    inp, inp_o = workloads.make_inputs(wl), workloads.make_inputs(other)
+    d, e = _prepared(inp), _prepared(inp_o)
+    print("case:", wl.name, iabn.iabn_describe_plan(wl.N, wl.C, wl.H, wl.W, wl.layout,
+                                                    d["x"].dtype, wl.act), flush=True)
+    _reset(d)
+    _noalloc(wl, d, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    OUT = ("x", "rm", "rv", "sm", "si")
+    eager = {k: d[k].clone() for k in OUT}
+    _reset(e)
+    _noalloc(other, e, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    eager_o = {k: e[k].clone() for k in OUT}
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    _reset(d)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        _noalloc(wl, d, side.cuda_stream)
+    for _ in range(4):
+        _reset(d)
+        _reset(e)
+        _noalloc(other, e, torch.cuda.current_stream().cuda_stream)   # eager, same scratch
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in OUT:
+            assert torch.equal(d[k], eager[k]), k
+            assert torch.equal(e[k], eager_o[k]), k
