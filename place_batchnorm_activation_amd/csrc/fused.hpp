@@ -63,12 +63,12 @@
 // UF, NRB, LB, UB): T threads, LPR lanes per row; the forward keeps NRF rows per
 // thread in registers and the next LF in LDS, and streams the rest UF rows per
 // thread at a time; the backward likewise with NRB, LB and UB (y and dy both).
-// LF and LB are multiples of UF and UB; the LDS rows take 64 KB, beside up to 72
-// KB for the scatter and the two-level exchange.
+// LF and LB are multiples of UF and UB; the LDS rows take 128 KB, beside up to
+// 17 KB for the scatter and the two-level exchange.
 #ifndef IABN_STREAM_NHWC_VARIANTS
 #define IABN_STREAM_NHWC_VARIANTS(X)   \
-    X(0, 512, 4, 28, 8, 4, 14, 4, 2)   \
-    X(1, 512, 8, 28, 8, 4, 14, 4, 2)
+    X(0, 512, 4, 28, 16, 4, 14, 8, 2)  \
+    X(1, 512, 8, 28, 16, 4, 14, 8, 2)
 #endif
 
 // Channel-resident NCHW kernels on single elements, for shapes the 16-byte

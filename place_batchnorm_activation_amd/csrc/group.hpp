@@ -61,7 +61,7 @@ __device__ __forceinline__ void group_timed_out(uint64_t* status)
     if (status) atomic_st(status, kExchangeTimeout);
 }
 
-// Members per slice at most (the exchange's LDS holds kMaxGroup partials).
+// Members per slice at most (the plans never form larger groups).
 constexpr uint32_t kMaxGroup = 64;
 
 // This member's two fp64 sums of channel ch, as four tagged words.  words: the
@@ -184,14 +184,17 @@ constexpr uint32_t kPairBatch = 4;
 
 // Sums over all members (G > 1), called by every thread of the workgroup: the
 // finishing thread of channel t (t < NCH) passes its member's sums s1, s2 and
-// gets back the sums over members 0..G-1, added in that order, so that every
-// member derives the same bits.
+// gets back the sums over members 0..G-1, added in a fixed order (member order
+// in one-level groups; in two-level ones the order given below), so that every
+// member derives the same bits on every run.
 //  - G < kTwoLevelGroup: each finishing thread publishes and then reads the other
 //    members, FB at a time (measured: reading them with one thread per
 //    (member, channel) loads the memory system with polls and is slower).
 //  - Larger groups, in two levels: every member but 0 publishes; member 0 reads
 //    them, each of its threads loading up to kPairBatch (member, channel) pairs at
 //    once, adds, and publishes the totals in its own slot, which the others read.
+//    Member 0 stages one partial sum per thread in LDS (16 bytes a thread), not
+//    every member's partials, which leaves the streamed kernels LDS for rows.
 // FB: members read per poll in one-level groups.  Eight (every partner of a group
 // of 8 in one round trip) made the slice-resident NHWC kernels 5-7% faster on
 // groups of 8; the other kernels keep four, which left them as fast and their
@@ -236,26 +239,29 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
         }
         return;
     }
-    __shared__ double xs[2][kMaxGroup][NCH];
-    if (fin) {
-        xs[0][0][t] = s1;
-        xs[1][0][t] = s2;
-    }
+    // Member 0: thread t takes the pairs t, t + T, t + 2T, ... of the (member,
+    // channel) pairs of members 1..G-1 -- one channel, t % NCH, since NCH divides
+    // T -- kPairBatch at a time, and adds each batch, in order, once all of it
+    // has arrived; the finishing thread of a channel (t < NCH) starts from member
+    // 0's own sums.  The channel's total is then the sums of threads t, t + NCH,
+    // t + 2 NCH, ... added in that order: a fixed order, whatever the order of
+    // arrival (with one thread, member order).
+    static_assert(T % NCH == 0, "a thread's pairs share one channel");
+    __shared__ double part[2][T];
     const uint32_t tlo = uint32_t(tok), thi = uint32_t(tok >> 32);
     const uint32_t npairs = (grp.G - 1) * NCH;
+    double a1 = fin ? s1 : 0.0, a2 = fin ? s2 : 0.0;
     for (uint32_t p0 = 0; p0 < npairs; p0 += kPairBatch * T) {
         bool need[kPairBatch];
+        double v1[kPairBatch], v2[kPairBatch];
         uint32_t left = 0;
 #pragma unroll
         for (uint32_t q = 0; q < kPairBatch; ++q) {
-            const uint32_t pair = p0 + q * T + t;
-            need[q] = pair < npairs;
+            need[q] = p0 + q * T + t < npairs;
             left += need[q] ? 1u : 0u;
-            if (need[q]) {                      // NaN unless received
-                xs[0][1 + pair / NCH][pair % NCH] = __longlong_as_double(0x7FF8000000000000ll);
-                xs[1][1 + pair / NCH][pair % NCH] = __longlong_as_double(0x7FF8000000000000ll);
-            }
+            v1[q] = v2[q] = __longlong_as_double(0x7FF8000000000000ll);   // NaN unless received
         }
+        const bool any = left != 0;
         for (uint32_t poll = 0; left != 0 && poll <= kMaxPolls; ++poll) {
             uint64_t w[kPairBatch][4];
 #pragma unroll
@@ -273,11 +279,8 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
             for (uint32_t q = 0; q < kPairBatch; ++q) {
                 if (need[q] && uint32_t(w[q][0] >> 32) == tlo && uint32_t(w[q][1] >> 32) == thi &&
                     uint32_t(w[q][2] >> 32) == tlo && uint32_t(w[q][3] >> 32) == thi) {
-                    const uint32_t pair = p0 + q * T + t;
-                    xs[0][1 + pair / NCH][pair % NCH] =
-                        __longlong_as_double(int64_t((w[q][0] << 32) | uint32_t(w[q][1])));
-                    xs[1][1 + pair / NCH][pair % NCH] =
-                        __longlong_as_double(int64_t((w[q][2] << 32) | uint32_t(w[q][3])));
+                    v1[q] = __longlong_as_double(int64_t((w[q][0] << 32) | uint32_t(w[q][1])));
+                    v2[q] = __longlong_as_double(int64_t((w[q][2] << 32) | uint32_t(w[q][3])));
                     need[q] = false;
                     --left;
                 }
@@ -285,14 +288,27 @@ __device__ __forceinline__ void group_sums(const SliceGroup& grp, uint32_t s, ui
             if (left != 0) __builtin_amdgcn_s_sleep(1);
         }
         if (left != 0) group_timed_out(grp.status);
+        if (any) {
+#pragma unroll
+            for (uint32_t q = 0; q < kPairBatch; ++q) {
+                if (p0 + q * T + t < npairs) {
+                    a1 += v1[q];
+                    a2 += v2[q];
+                }
+            }
+        }
     }
+    part[0][t] = a1;
+    part[1][t] = a2;
     __syncthreads();
     if (fin) {
-        s1 = xs[0][0][t];
-        s2 = xs[1][0][t];
-        for (uint32_t k = 1; k < grp.G; ++k) {
-            s1 += xs[0][k][t];
-            s2 += xs[1][k][t];
+        // threads t + k NCH, k < G - 1, hold channel t's other members
+        const uint32_t nthr = uint32_t(T / NCH) < grp.G - 1 ? uint32_t(T / NCH) : grp.G - 1;
+        s1 = part[0][t];
+        s2 = part[1][t];
+        for (uint32_t k = 1; k < nthr; ++k) {
+            s1 += part[0][k * NCH + t];
+            s2 += part[1][k * NCH + t];
         }
         group_publish(words, 0, NCH, t, tok, s1, s2);
     }

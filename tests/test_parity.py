@@ -506,37 +506,60 @@ def test_split_pipelines(wl):
 
 # Streamed slice kernels (NHWC maps too large to hold): 256 workgroups, groups
 # of 8 to 64, eight lanes per row (four where 16 vectors make a pixel).  Threads
-# keep 28 rows in registers and 8 in LDS (forward) or 14 and 4 (backward) and
-# stream the rest.  The backward streams only while at least half its rows stay
-# on chip (else the split kernels).  The cases cover chunks kept in LDS only
-# (one or two of them) and one to six chunks streamed past them, odd and even.
+# keep 28 rows in registers and 16 in LDS (forward: four chunks of 4) or 14 and
+# 8 (backward: four chunks of 2) and stream the rest.  The backward streams only
+# while at least half its rows stay on chip (else the split kernels).  The cases
+# cover, in each direction, no chunk past the registers, one to four chunks kept
+# in LDS only, and one to six chunks streamed past them (forward 1-6; backward
+# 1-6, 8, 9 and 11), odd and even.
 _SPLIT_BWD = "split(reduce:256x256,apply:512x256,vec16)"
 _SPLIT_BWD_ELU = "split(reduce:256x256,apply:2048x256,vec16)"   # ELU: a wider dx grid
 STREAM_PLANS = [
     (custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x8x(28+8)+4,group64)", "slice_streamed(512x8x(14+4)+2,group64)"),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
     (custom(3, 1, 256, 390, 390, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x8x(28+8)+4,group64)", _SPLIT_BWD),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
     (custom(2, 1, 128, 400, 400, layout="NHWC", dtype="f32"),
-     "slice_streamed(512x8x(28+8)+4,group64)", _SPLIT_BWD),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
     (custom(2, 1, 128, 436, 436, layout="NHWC", dtype="f32"),
-     "slice_streamed(512x8x(28+8)+4,group64)", _SPLIT_BWD),
+     "slice_streamed(512x8x(28+16)+4,group64)", _SPLIT_BWD),
     (custom(3, 1, 128, 360, 360, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x4x(28+8)+4,group64)", "slice_streamed(512x4x(14+4)+2,group64)"),
+     "slice_streamed(512x4x(28+16)+4,group64)", "slice_streamed(512x4x(14+8)+2,group64)"),
     (custom(4, 1, 1024, 180, 170, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
-     "slice_streamed(512x8x(28+8)+4,group16)", "slice_streamed(512x8x(14+4)+2,group16)"),
+     "slice_streamed(512x8x(28+16)+4,group16)", "slice_streamed(512x8x(14+8)+2,group16)"),
     (custom(4, 1, 64, 600, 600, layout="NHWC", dtype="f32", act="elu", act_param=1.0),
-     "slice_streamed(512x4x(28+8)+4,group64)", _SPLIT_BWD_ELU),
+     "slice_streamed(512x4x(28+16)+4,group64)", "slice_streamed(512x4x(14+8)+2,group64)"),
     (custom(3, 1, 256, 300, 300, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x8x(28+8)+4,group64)", "slice_streamed(512x8x(14+4)+2,group64)"),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
     (custom(2, 1, 128, 300, 310, layout="NHWC", dtype="f32"),
-     "slice_streamed(512x8x(28+8)+4,group64)", "slice_streamed(512x8x(14+4)+2,group64)"),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
     (custom(4, 1, 1024, 130, 130, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
-     "slice_streamed(512x8x(28+8)+4,group16)", "slice_streamed(512x8x(14+4)+2,group16)"),
+     "slice_streamed(512x8x(28+16)+4,group16)", "slice_streamed(512x8x(14+8)+2,group16)"),
     (custom(3, 3, 512, 100, 100, layout="NHWC", dtype="bf16", act="identity", act_param=0.0),
-     "slice_streamed(512x8x(28+8)+4,group32)", "slice_streamed(512x8x(14+4)+2,group32)"),
+     "slice_streamed(512x8x(28+16)+4,group32)", "slice_streamed(512x8x(14+8)+2,group32)"),
     (custom(3, 1, 2048, 100, 100, layout="NHWC", dtype="bf16"),
-     "slice_streamed(512x8x(28+8)+4,group8)", "slice_streamed(512x8x(14+4)+2,group8)"),
+     "slice_streamed(512x8x(28+16)+4,group8)", "slice_streamed(512x8x(14+8)+2,group8)"),
+    # forward two chunks in LDS, backward six past them
+    (custom(3, 1, 256, 362, 364, layout="NHWC", dtype="bf16"),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
+    # backward two, three and five chunks past LDS
+    (custom(3, 1, 256, 314, 316, layout="NHWC", dtype="bf16"),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
+    (custom(4, 2, 256, 232, 233, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
+    (custom(2, 2, 128, 248, 249, layout="NHWC", dtype="f32"),
+     "slice_streamed(512x8x(28+16)+4,group64)", "slice_streamed(512x8x(14+8)+2,group64)"),
+    # forward two to six chunks past LDS
+    (custom(4, 2, 512, 222, 223, layout="NHWC", dtype="f16", act="elu", act_param=1.0),
+     "slice_streamed(512x8x(28+16)+4,group32)", _SPLIT_BWD_ELU),
+    (custom(2, 2, 128, 326, 327, layout="NHWC", dtype="f32"),
+     "slice_streamed(512x8x(28+16)+4,group64)", _SPLIT_BWD),
+    (custom(3, 2, 256, 340, 341, layout="NHWC", dtype="f16"),
+     "slice_streamed(512x8x(28+16)+4,group64)", _SPLIT_BWD),
+    (custom(3, 1, 256, 496, 498, layout="NHWC", dtype="bf16"),
+     "slice_streamed(512x8x(28+16)+4,group64)", _SPLIT_BWD),
+    (custom(2, 2, 128, 362, 363, layout="NHWC", dtype="f32"),
+     "slice_streamed(512x8x(28+16)+4,group64)", _SPLIT_BWD),
 ]
 
 
