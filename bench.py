@@ -71,12 +71,39 @@ METRIC = "InPlace-ABN fwd+bwd Gelem/s and achieved HBM GB/s (% of MI355X peak)"
 COLD_BYTES = 512 << 20
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed, so that
+    an edit of comments alone leaves the digest as it was."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                                 # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
+    """Digest of the kernel sources' code (comments excluded): the counter figures
+    in profiles/traffic.json hold for the kernels built from code with this digest."""
     h = hashlib.sha256()
     for f in ("device.hpp", "plan.hpp", "fused.hpp", "group.hpp", "fwd.hip", "bwd.hip",
               "fused_nchw.hip", "fused_nhwc.hip", "ckpt.hip", "noalloc.hip"):
-        with open(os.path.join(ROOT, "place_batchnorm_activation_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "place_batchnorm_activation_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

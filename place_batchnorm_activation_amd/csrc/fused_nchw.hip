@@ -174,7 +174,7 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
 
     // statistics in fp64 (every thread computes the same values).  A group adds
     // its members' shifted sums, sum(x - K) = n*mean and sum((x - K)^2) = M2 +
-    // n*mean^2, in fp64 and in member order.
+    // n*mean^2, in fp64 and in a fixed order (group_sums).
     double dm = double(mean), var = double(m2) / double(m);
     if constexpr (GRP) {
         __shared__ double tot_sh[2];
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
     if (GRP && t == 0) tok_sh = group_token(grp, c, epoch);
     block_sum2<T>(sdz, sdzt);
 
-    // a group adds its members' sums in fp64, in member order
+    // a group adds its members' sums in fp64, in a fixed order (group_sums)
     double sum_dz = double(sdz), sum_dzt = double(sdzt);
     if constexpr (GRP) {
         __shared__ double tot_sh[2];

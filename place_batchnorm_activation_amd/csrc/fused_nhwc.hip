@@ -22,9 +22,9 @@
 // per slice leaves the chip idle, G workgroups (members) share the slice, member
 // j holding rows [j*mg, min(m, (j+1)*mg)), mg = ceil(m/G).  After its own
 // reduction each member publishes its fp64 per-channel sums in the workspace;
-// the G partials are added in member order (by every member, or for large groups
-// by member 0, which publishes the totals), so every member derives
-// bit-identical statistics.  The grid never
+// the G partials are added in a fixed order (in member order by every member,
+// or for large groups by member 0, which publishes the totals), so every member
+// derives bit-identical statistics.  The grid never
 // exceeds the CU count, so that every member runs at once (the host's choice),
 // and a member waits a bounded time: past it, its statistics become NaN, so a
 // failure shows in every output it writes instead of hanging the device.

@@ -25,3 +25,15 @@ def test_kernel_source_digest_tracks_every_kernel_source():
     src = inspect.getsource(bench.kernel_source_digest)
     for f in kernels:
         assert '"%s"' % f in src, f
+
+
+def test_kernel_digest_ignores_comments_but_not_code():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = 'int f(int x) { return x + 1; }  // one\n/* two */ const char* s = "// kept";\n'
+    b = '// another comment\nint f(int x) {\n    return x + 1;   /* changed */\n}\nconst char* s = "// kept";'
+    c = 'int f(int x) { return x + 2; }\nconst char* s = "// kept";'
+    d = 'int f(int x) { return x + 1; }\nconst char* s = "// changed";'
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+    assert bench._code_only(a) != bench._code_only(d)
