@@ -37,11 +37,24 @@ def _like(t: torch.Tensor, layout: str) -> torch.Tensor:
     return t.contiguous(memory_format=fmt)
 
 
+def _check_params(x, *vecs) -> None:
+    """The library reads the affine parameters and statistics as float32 on x's
+    device, C of each."""
+    C = x.shape[1]
+    for v in vecs:
+        if v.dtype != torch.float32 or v.device != x.device or v.numel() != C or \
+                not v.is_contiguous():
+            raise TypeError("InPlaceABN keeps weight, bias and running statistics as "
+                            "contiguous float32 vectors of %d elements on %s; got %s %s on %s"
+                            % (C, x.device, v.dtype, tuple(v.shape), v.device))
+
+
 class InPlaceABNFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, weight, bias, running_mean, running_var, training, momentum, eps,
                 activation, act_param):
         layout = _layout(x)
+        _check_params(x, weight, bias, running_mean, running_var)
         N, C, H, W = x.shape
         ws = workspace(N, C, H, W, layout, x.dtype, x.device)
         if training:

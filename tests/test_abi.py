@@ -329,3 +329,21 @@ def test_ckpt_validation():
     assert bwd(dx=A) == INVALID                     # dx over xhat
     assert bwd(dx=4 * A + 64) == INVALID            # dx partly over dy
     assert bwd(ws=None) == WS
+
+
+def test_module_rejects_parameters_it_cannot_read():
+    """The autograd module hands weight, bias and the running statistics to the
+    library as float32 pointers: other dtypes or sizes are refused before any call."""
+    import torch
+    from place_batchnorm_activation_amd.autograd import InPlaceABN
+    x = torch.randn(2, 8, 4, 4)
+    m = InPlaceABN(8).half()
+    with pytest.raises(TypeError, match="float32"):
+        m(x.half())
+    m = InPlaceABN(8)
+    m.running_var = torch.ones(8, dtype=torch.float64)
+    with pytest.raises(TypeError, match="float32"):
+        m(x)
+    m = InPlaceABN(6)
+    with pytest.raises(TypeError, match="of 8 elements.*got torch.float32 \\(6,\\)"):
+        m(x)
