@@ -163,9 +163,9 @@ def cpu_baseline(wl, inp, gpu=None) -> dict:
     g, b = inp.gamma[:ch], inp.beta[:ch]
     f32 = lambda v: float(np.float32(v))               # the scalars the library receives
     a, eps, mom = f32(wl.act_param), f32(wl.eps), f32(wl.momentum)
+    # repeated until about 10 s of oracle work (at least 3 runs, at most 200)
     times = []
-    reps = 3
-    for _ in range(reps):
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 200):
         t0 = time.perf_counter()
         f = oracle.forward_train(xs, g, b, wl.act, a, eps, mom, inp.running_mean[:ch],
                                  inp.running_var[:ch], storage=wl.dtype)
@@ -176,8 +176,8 @@ def cpu_baseline(wl, inp, gpu=None) -> dict:
     out = {"value": round(n / t / 1e9, 5), "unit": "Gelem/s", "cores": oracle.num_threads(),
            "cpu_model": cpu_model(), "kind": "oracle",
            "sample": "%d of %d channels (all %d elements each) of the same workload, fp64 "
-                     "forward_train + backward_from_y, median of %d runs (%.2f s each)"
-                     % (ch, wl.C, wl.m, reps, t)}
+                     "forward_train + backward_from_y, median of %d runs (%.3f s each, "
+                     "%.1f s in all)" % (ch, wl.C, wl.m, len(times), t, sum(times))}
     if gpu is not None:
         y = gpu["y"][:, :ch]
         err = {"y": _rel_err(y, f["y"], True)}
