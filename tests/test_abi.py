@@ -347,3 +347,26 @@ def test_module_rejects_parameters_it_cannot_read():
     m = InPlaceABN(6)
     with pytest.raises(TypeError, match="of 8 elements.*got torch.float32 \\(6,\\)"):
         m(x)
+
+
+@pytest.mark.parametrize("value,grouped", [("0", False), ("1", True), (None, True)])
+def test_grouped_kernels_environment_switch(value, grouped):
+    """IABN_GROUPED_KERNELS=0, read when a fresh process first plans a call, forbids
+    the kernels whose workgroups wait on one another (any other value, or none,
+    allows them)."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("IABN_GROUPED_KERNELS", None)
+    if value is not None:
+        env["IABN_GROUPED_KERNELS"] = value
+    code = ("import sys; sys.path.insert(0, %r); import torch; "
+            "import place_batchnorm_activation_amd as i; "
+            "print(i.iabn_describe_plan(64, 2048, 7, 7, 'NHWC', torch.bfloat16, 'leaky_relu')); "
+            "print(i.iabn_set_grouped_kernels(None))" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    plan, setting = out.stdout.split("\n")[:2]
+    assert ("group" in plan) == grouped, plan
+    assert setting == str(grouped)
