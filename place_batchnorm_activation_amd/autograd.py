@@ -10,7 +10,9 @@ summary of "In-Place Activated BatchNorm for Memory-Optimized Training of DNNs",
 C ABI; this module only marshals tensors and streams.
 
 Layout follows the tensor's memory format: contiguous tensors are NCHW,
-channels_last tensors NHWC.  Storage dtypes: float32, bfloat16, float16; the
+channels_last (and channels_last_3d) tensors NHWC.  Any tensor [N, C, *] is
+taken, as BatchNorm1d, 2d and 3d take them: the spatial extent is folded into
+the library's H*W.  Storage dtypes: float32, bfloat16, float16; the
 affine parameters and statistics are float32.
 """
 from __future__ import annotations
@@ -21,19 +23,36 @@ from . import (iabn_backward, iabn_backward_eval, iabn_forward_eval, iabn_forwar
                workspace)
 
 
-def _layout(x: torch.Tensor) -> str:
-    if x.dim() != 4:
-        raise ValueError("InPlaceABN expects a 4-d tensor [N, C, H, W], got %d-d" % x.dim())
+def _geometry(x: torch.Tensor):
+    """(N, C, H, W, layout) under which the library sees x, a tensor [N, C, *]:
+    contiguous tensors are NCHW with the spatial extent folded into H*W (2-d
+    [N, C] and 3-d [N, C, L] tensors, as BatchNorm1d takes them, and 5-d
+    [N, C, D, H, W] ones, as BatchNorm3d does), channels_last and
+    channels_last_3d ones NHWC (depth folded into H)."""
+    if x.dim() < 2:
+        raise ValueError("InPlaceABN expects a tensor [N, C, ...], got %d-d" % x.dim())
+    N, C = int(x.shape[0]), int(x.shape[1])
+    sp = [int(v) for v in x.shape[2:]]
+    if x.dim() == 4 and x.is_contiguous():
+        return N, C, sp[0], sp[1], "NCHW"
     if x.is_contiguous():
-        return "NCHW"
-    if x.is_contiguous(memory_format=torch.channels_last):
-        return "NHWC"
-    raise ValueError("InPlaceABN needs a contiguous or channels_last tensor")
+        hw = 1
+        for v in sp:
+            hw *= v
+        return N, C, hw, 1, "NCHW"
+    if x.dim() == 4 and x.is_contiguous(memory_format=torch.channels_last):
+        return N, C, sp[0], sp[1], "NHWC"
+    if x.dim() == 5 and x.is_contiguous(memory_format=torch.channels_last_3d):
+        return N, C, sp[0] * sp[1], sp[2], "NHWC"
+    raise ValueError("InPlaceABN needs a contiguous, channels_last or channels_last_3d tensor")
 
 
 def _like(t: torch.Tensor, layout: str) -> torch.Tensor:
-    """t in the memory format of `layout` (a copy only when it differs)."""
-    fmt = torch.channels_last if layout == "NHWC" else torch.contiguous_format
+    """t in the memory format the library reads for `layout` (a copy only when
+    it differs)."""
+    if layout == "NCHW":
+        return t.contiguous()
+    fmt = torch.channels_last if t.dim() == 4 else torch.channels_last_3d
     return t.contiguous(memory_format=fmt)
 
 
@@ -53,9 +72,8 @@ class InPlaceABNFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, weight, bias, running_mean, running_var, training, momentum, eps,
                 activation, act_param):
-        layout = _layout(x)
+        N, C, H, W, layout = _geometry(x)
         _check_params(x, weight, bias, running_mean, running_var)
-        N, C, H, W = x.shape
         ws = workspace(N, C, H, W, layout, x.dtype, x.device)
         if training:
             save_mean = torch.empty(C, device=x.device, dtype=torch.float32)
@@ -69,14 +87,13 @@ class InPlaceABNFunction(torch.autograd.Function):
             stat = running_var
         ctx.mark_dirty(x)
         ctx.save_for_backward(x, weight, bias, stat)
-        ctx.cfg = (training, eps, activation, act_param, layout)
+        ctx.cfg = (training, eps, activation, act_param, (N, C, H, W, layout))
         return x
 
     @staticmethod
     def backward(ctx, dy):
         y, weight, bias, stat = ctx.saved_tensors
-        training, eps, activation, act_param, layout = ctx.cfg
-        N, C, H, W = y.shape
+        training, eps, activation, act_param, (N, C, H, W, layout) = ctx.cfg
         dy = _like(dy, layout)
         dx = torch.empty_like(dy)
         dgamma = torch.empty(C, device=y.device, dtype=torch.float32)
@@ -92,7 +109,8 @@ class InPlaceABNFunction(torch.autograd.Function):
 
 
 class InPlaceABN(torch.nn.Module):
-    """BatchNorm2d + invertible activation, computed in place.
+    """BatchNorm (1d, 2d or 3d: any input [N, C, *]) + invertible activation,
+    computed in place.
 
     activation: "leaky_relu" (act_param = negative slope, > 0), "elu" (act_param =
     alpha, > 0) or "identity".  Running statistics follow BatchNorm2d's update

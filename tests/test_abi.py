@@ -370,3 +370,25 @@ def test_grouped_kernels_environment_switch(value, grouped):
     plan, setting = out.stdout.split("\n")[:2]
     assert ("group" in plan) == grouped, plan
     assert setting == str(grouped)
+
+
+def test_module_geometry_of_any_batchnorm_input():
+    """How the autograd module presents [N, C, *] tensors to the library (host
+    only): spatial extents fold into H*W; channels_last(_3d) tensors are NHWC."""
+    import torch
+    from place_batchnorm_activation_amd.autograd import _geometry
+    assert _geometry(torch.empty(8, 16)) == (8, 16, 1, 1, "NCHW")
+    assert _geometry(torch.empty(4, 16, 10)) == (4, 16, 10, 1, "NCHW")
+    assert _geometry(torch.empty(2, 3, 4, 5)) == (2, 3, 4, 5, "NCHW")
+    assert _geometry(torch.empty(2, 3, 4, 5, 6)) == (2, 3, 120, 1, "NCHW")
+    cl = torch.empty(2, 3, 4, 5).contiguous(memory_format=torch.channels_last)
+    assert _geometry(cl) == (2, 3, 4, 5, "NHWC")
+    cl3 = torch.empty(2, 3, 4, 5, 6).contiguous(memory_format=torch.channels_last_3d)
+    assert _geometry(cl3) == (2, 3, 20, 6, "NHWC")
+    # one channel: both memory formats coincide, and NCHW is taken
+    assert _geometry(torch.empty(2, 1, 4, 5).contiguous(memory_format=torch.channels_last))[4] == \
+        "NCHW"
+    with pytest.raises(ValueError):
+        _geometry(torch.empty(8))
+    with pytest.raises(ValueError):
+        _geometry(torch.empty(4, 10, 16).transpose(1, 2))

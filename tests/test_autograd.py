@@ -192,3 +192,83 @@ def test_chain_keeps_one_buffer_per_layer():
           (saved_std / 2**20, saved_abn / 2**20, peak_std / 2**20, peak_abn / 2**20))
     assert saved_std - saved_abn >= (2 * L - 0.5) * S
     assert peak_abn < peak_std
+
+
+def _run_module(x_in, C, dy_in, seed=0):
+    """One training step of a fresh module on x_in (not a leaf): y, dx, dgamma,
+    dbeta, running statistics."""
+    torch.manual_seed(seed)
+    m = InPlaceABN(C, device="cuda")
+    with torch.no_grad():
+        m.weight.copy_(torch.rand(C) + 0.5)
+        m.bias.copy_(0.1 * torch.randn(C))
+    leaf = x_in.detach().clone().requires_grad_()
+    x = leaf.clone(memory_format=torch.preserve_format)
+    y = m(x)
+    y.backward(dy_in)
+    torch.cuda.synchronize()
+    return (y.detach(), leaf.grad, m.weight.grad, m.bias.grad, m.running_mean.clone(),
+            m.running_var.clone())
+
+
+@pytest.mark.parametrize("shape,fmt", [((64, 96), None), ((8, 32, 300), None),
+                                       ((2, 16, 6, 10, 12), None),
+                                       ((2, 16, 6, 10, 12), torch.channels_last_3d),
+                                       ((4, 64, 5, 7, 9), torch.channels_last_3d)],
+                         ids=["1d_NC", "1d_NCL", "3d", "3d_channels_last", "3d_cl_64ch"])
+def test_any_batchnorm_input_matches_its_4d_form(shape, fmt):
+    """BatchNorm1d / 3d inputs: the bits of the same step on the 4-d tensor the
+    library sees (spatial extent folded into H*W; depth into H when channels
+    last)."""
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(shape, generator=g).cuda()
+    dy = torch.randn(shape, generator=g).cuda()
+    N, C = shape[:2]
+    if fmt is None:
+        x4 = x.reshape(N, C, -1, 1)
+        dy4 = dy.reshape(N, C, -1, 1)
+    else:
+        x = x.contiguous(memory_format=fmt)
+        dy = dy.contiguous(memory_format=fmt)
+        D, H, W = shape[2:]
+        # [N, D, H, W, C] memory -> [N, D*H, W, C] -> logical NCHW in channels_last
+        x4 = x.permute(0, 2, 3, 4, 1).reshape(N, D * H, W, C).permute(0, 3, 1, 2)
+        dy4 = dy.permute(0, 2, 3, 4, 1).reshape(N, D * H, W, C).permute(0, 3, 1, 2)
+        assert x4.is_contiguous(memory_format=torch.channels_last)
+    a = _run_module(x, C, dy)
+    b = _run_module(x4, C, dy4)
+    assert torch.equal(a[0].reshape(-1) if fmt is None else a[0].permute(0, 2, 3, 4, 1).reshape(-1),
+                       b[0].reshape(-1) if fmt is None else b[0].permute(0, 2, 3, 1).reshape(-1))
+    assert torch.equal(a[1].reshape(b[1].shape) if fmt is None else
+                       a[1].permute(0, 2, 3, 4, 1).reshape(-1),
+                       b[1] if fmt is None else b[1].permute(0, 2, 3, 1).reshape(-1))
+    for u, v in zip(a[2:], b[2:]):
+        assert torch.equal(u, v)
+
+
+def test_batchnorm1d_input_matches_the_oracle():
+    """A [N, C, L] input against the fp64 oracle: forward on the same x bits,
+    backward on the module's own y bits."""
+    wl = workloads.config(2).with_shape(8, 24, 50, 1)
+    inp = workloads.make_inputs(wl)
+    m = _module(wl, inp)
+    x_leaf = harness.to_device(inp.x, wl).reshape(8, 24, 50).requires_grad_()
+    y = m(x_leaf.clone())
+    dy = harness.to_device(inp.dy, wl).reshape(8, 24, 50)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    a = harness.f32(wl.act_param)
+    f = oracle.forward_train(harness.storage_channels(inp.x, wl), inp.gamma, inp.beta, wl.act, a,
+                             harness.f32(wl.eps), harness.f32(wl.momentum), inp.running_mean,
+                             inp.running_var, storage=wl.dtype)
+    yg = harness.to_nchw64(y.detach().reshape(8, 24, 50, 1), wl)
+    o = oracle.backward_from_y(yg, harness.storage_channels(inp.dy, wl), inp.gamma, inp.beta,
+                               f["invstd"], wl.act, a)
+    err = {"y": harness.rel_err_tensor(yg, f["y"]),
+           "running_var": harness.rel_err_vec(m.running_var.cpu().numpy(), f["running_var"]),
+           "dx": harness.rel_err_tensor(harness.to_nchw64(x_leaf.grad.reshape(8, 24, 50, 1), wl),
+                                        o["dx"]),
+           "dgamma": harness.rel_err_vec(m.weight.grad.cpu().numpy(), o["dgamma"]),
+           "dbeta": harness.rel_err_vec(m.bias.grad.cpu().numpy(), o["dbeta"])}
+    print("1d:", err, flush=True)
+    harness.assert_within(err, wl.dtype, "1d")
