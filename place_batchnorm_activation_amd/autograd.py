@@ -61,6 +61,8 @@ def _check_params(x, *vecs) -> None:
     device, C of each."""
     C = x.shape[1]
     for v in vecs:
+        if v is None:
+            continue
         if v.dtype != torch.float32 or v.device != x.device or v.numel() != C or \
                 not v.is_contiguous():
             raise TypeError("InPlaceABN keeps weight, bias and running statistics as "
@@ -114,29 +116,60 @@ class InPlaceABN(torch.nn.Module):
 
     activation: "leaky_relu" (act_param = negative slope, > 0), "elu" (act_param =
     alpha, > 0) or "identity".  Running statistics follow BatchNorm2d's update
-    (momentum, unbiased running variance).  The affine weight must stay non-zero:
-    the backward divides by it when it rebuilds the normalised input."""
+    (momentum, unbiased running variance; momentum=None takes the cumulative
+    average over the steps so far).  affine=False fixes weight 1 and bias 0;
+    track_running_stats=False keeps no running statistics and normalises with
+    the batch's own in eval mode too, as BatchNorm2d does.  The affine weight
+    must stay non-zero: the backward divides by it when it rebuilds the
+    normalised input."""
 
     def __init__(self, num_features: int, eps: float = 1e-5, momentum: float = 0.1,
                  activation: str = "leaky_relu", act_param: float = 0.01,
-                 device=None):
+                 device=None, affine: bool = True, track_running_stats: bool = True):
         super().__init__()
         self.num_features = num_features
         self.eps = eps
         self.momentum = momentum
         self.activation = activation
         self.act_param = act_param
+        self.affine = affine
+        self.track_running_stats = track_running_stats
         f32 = dict(device=device, dtype=torch.float32)
-        self.weight = torch.nn.Parameter(torch.ones(num_features, **f32))
-        self.bias = torch.nn.Parameter(torch.zeros(num_features, **f32))
-        self.register_buffer("running_mean", torch.zeros(num_features, **f32))
-        self.register_buffer("running_var", torch.ones(num_features, **f32))
+        if affine:
+            self.weight = torch.nn.Parameter(torch.ones(num_features, **f32))
+            self.bias = torch.nn.Parameter(torch.zeros(num_features, **f32))
+        else:
+            # fixed, and kept out of the state dict as BatchNorm2d keeps none
+            self.register_buffer("weight", torch.ones(num_features, **f32), persistent=False)
+            self.register_buffer("bias", torch.zeros(num_features, **f32), persistent=False)
+        if track_running_stats:
+            self.register_buffer("running_mean", torch.zeros(num_features, **f32))
+            self.register_buffer("running_var", torch.ones(num_features, **f32))
+            self.register_buffer("num_batches_tracked",
+                                 torch.tensor(0, dtype=torch.long, device=device))
+        else:
+            self.running_mean = self.running_var = self.num_batches_tracked = None
+        self._steps = 0                  # host copy of num_batches_tracked
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
+        batch_stats = self.training or not self.track_running_stats
+        factor = 0.0 if self.momentum is None else self.momentum
+        if self.training and self.track_running_stats:
+            self._steps += 1
+            self.num_batches_tracked.add_(1)
+            if self.momentum is None:
+                factor = 1.0 / self._steps
         return InPlaceABNFunction.apply(x, self.weight, self.bias, self.running_mean,
-                                        self.running_var, self.training, self.momentum, self.eps,
+                                        self.running_var, batch_stats, factor, self.eps,
                                         self.activation, self.act_param)
 
+    def _load_from_state_dict(self, state_dict, prefix, *args, **kwargs):
+        super()._load_from_state_dict(state_dict, prefix, *args, **kwargs)
+        if self.track_running_stats:
+            self._steps = int(self.num_batches_tracked.item())
+
     def extra_repr(self) -> str:
-        return "%d, eps=%g, momentum=%g, activation=%s, act_param=%g" % (
-            self.num_features, self.eps, self.momentum, self.activation, self.act_param)
+        return "%d, eps=%g, momentum=%s, activation=%s, act_param=%g, affine=%s, " \
+               "track_running_stats=%s" % (self.num_features, self.eps, self.momentum,
+                                          self.activation, self.act_param, self.affine,
+                                          self.track_running_stats)

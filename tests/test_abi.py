@@ -392,3 +392,21 @@ def test_module_geometry_of_any_batchnorm_input():
         _geometry(torch.empty(8))
     with pytest.raises(ValueError):
         _geometry(torch.empty(4, 10, 16).transpose(1, 2))
+
+
+def test_module_state_dict_matches_batchnorm2d():
+    """The module's state dict has BatchNorm2d's keys for every option, so
+    checkpoints load either way (host only)."""
+    import torch
+    from place_batchnorm_activation_amd.autograd import InPlaceABN
+    for affine in (True, False):
+        for track in (True, False):
+            a = InPlaceABN(8, affine=affine, track_running_stats=track)
+            b = torch.nn.BatchNorm2d(8, affine=affine, track_running_stats=track)
+            assert sorted(a.state_dict()) == sorted(b.state_dict()), (affine, track)
+    a = InPlaceABN(8)
+    b = torch.nn.BatchNorm2d(8)
+    b.num_batches_tracked.fill_(7)
+    b.running_var.fill_(2.0)
+    a.load_state_dict(b.state_dict())
+    assert a._steps == 7 and float(a.running_var[0]) == 2.0

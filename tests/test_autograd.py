@@ -272,3 +272,51 @@ def test_batchnorm1d_input_matches_the_oracle():
            "dbeta": harness.rel_err_vec(m.bias.grad.cpu().numpy(), o["dbeta"])}
     print("1d:", err, flush=True)
     harness.assert_within(err, wl.dtype, "1d")
+
+
+def _torch_ref(N, C, H, W, **bn):
+    """torch CPU fp64 BatchNorm2d + leaky ReLU with the same options (a library
+    cross-check of the module's options, not of the kernels)."""
+    return torch.nn.Sequential(torch.nn.BatchNorm2d(C, dtype=torch.float64, **bn),
+                               torch.nn.LeakyReLU(0.01))
+
+
+def _rel(a, b):
+    a = a.detach().double().cpu()
+    b = b.detach().double().cpu()
+    return float((a - b).abs().max() / (b.abs().max() + 1e-30))
+
+
+def test_module_options_follow_batchnorm2d():
+    """momentum=None (cumulative average over the steps), affine=False, and
+    track_running_stats=False (batch statistics in eval mode too) behave as in
+    BatchNorm2d + LeakyReLU, within fp32 rounding of torch's fp64 result."""
+    N, C, H, W = 4, 8, 10, 12
+    g = torch.Generator().manual_seed(5)
+    xs = [torch.randn(N, C, H, W, generator=g) * 2 + 1 for _ in range(3)]
+    # cumulative average of the running statistics over three training steps
+    m = InPlaceABN(C, momentum=None, device="cuda")
+    ref = _torch_ref(N, C, H, W, momentum=None)
+    for x in xs:
+        m(x.cuda())
+        ref(x.double())
+    assert int(m.num_batches_tracked) == 3
+    assert _rel(m.running_mean, ref[0].running_mean) < 1e-5
+    assert _rel(m.running_var, ref[0].running_var) < 1e-5
+    # without the affine step, weight and bias are fixed buffers
+    m = InPlaceABN(C, affine=False, device="cuda")
+    assert not any(True for _ in m.parameters())
+    ref = _torch_ref(N, C, H, W, affine=False)
+    x = xs[0].cuda().requires_grad_()
+    y = m(x.clone())
+    y.backward(torch.ones_like(y))
+    xr = xs[0].double().requires_grad_()
+    yr = ref(xr)
+    yr.backward(torch.ones_like(yr))
+    assert _rel(y, yr) < 1e-5 and _rel(x.grad, xr.grad) < 1e-4
+    # no running statistics: eval mode normalises with the batch's own
+    m = InPlaceABN(C, track_running_stats=False, device="cuda").eval()
+    ref = _torch_ref(N, C, H, W, track_running_stats=False).eval()
+    assert m.running_mean is None
+    y = m(xs[1].cuda())
+    assert _rel(y, ref(xs[1].double())) < 1e-5
