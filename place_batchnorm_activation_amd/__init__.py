@@ -96,6 +96,17 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _vec(t) -> Optional[int]:
+    """A per-channel vector (gamma, beta, statistics, gradients) -> device address:
+    the library reads and writes them as float32, so any other dtype is refused
+    (its bytes would be misread)."""
+    if t is None or isinstance(t, int):
+        return t
+    if t.dtype != torch.float32:
+        raise TypeError("per-channel vectors are float32, got %s" % t.dtype)
+    return t.data_ptr()
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -192,8 +203,8 @@ def iabn_forward_train(x, N, C, H, W, layout, gamma, beta, running_mean, running
                        save_invstd, act, act_param, eps, momentum, workspace, stream=None):
     wp, wb = _ws(workspace)
     _check("iabn_forward_train", lib.iabn_forward_train(
-        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma), _ptr(beta),
-        _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_invstd),
+        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _vec(gamma), _vec(beta),
+        _vec(running_mean), _vec(running_var), _vec(save_mean), _vec(save_invstd),
         _code(act, ACTS), act_param, eps, momentum, wp, wb, _stream(stream)))
 
 
@@ -202,8 +213,8 @@ def iabn_forward_train_noalloc(x, N, C, H, W, layout, gamma, beta, running_mean,
     """iabn_forward_train with the library's static per-device scratch as workspace
     (no allocation; shapes within IABN_NOALLOC_SCRATCH_BYTES of workspace)."""
     _check("iabn_forward_train_noalloc", lib.iabn_forward_train_noalloc(
-        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma), _ptr(beta),
-        _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_invstd),
+        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _vec(gamma), _vec(beta),
+        _vec(running_mean), _vec(running_var), _vec(save_mean), _vec(save_invstd),
         _code(act, ACTS), act_param, eps, momentum, _stream(stream)))
 
 
@@ -214,8 +225,8 @@ def iabn_forward_stats(x, N, C, H, W, layout, gamma, beta, running_mean, running
                        save_invstd, eps, momentum, workspace, stream=None):
     wp, wb = _ws(workspace)
     _check("iabn_forward_stats", lib.iabn_forward_stats(
-        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma), _ptr(beta),
-        _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_invstd), eps,
+        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _vec(gamma), _vec(beta),
+        _vec(running_mean), _vec(running_var), _vec(save_mean), _vec(save_invstd), eps,
         momentum, wp, wb, _stream(stream)))
 
 
@@ -229,8 +240,8 @@ def iabn_forward_apply(x, N, C, H, W, layout, act, act_param, workspace, stream=
 def iabn_forward_eval(x, N, C, H, W, layout, gamma, beta, running_mean, running_var, act,
                       act_param, eps, stream=None):
     _check("iabn_forward_eval", lib.iabn_forward_eval(
-        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma), _ptr(beta),
-        _ptr(running_mean), _ptr(running_var), _code(act, ACTS), act_param, eps,
+        _ptr(x), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _vec(gamma), _vec(beta),
+        _vec(running_mean), _vec(running_var), _code(act, ACTS), act_param, eps,
         _stream(stream)))
 
 
@@ -239,7 +250,7 @@ def iabn_backward(y, dy, dx, N, C, H, W, layout, gamma, beta, save_invstd, dgamm
     wp, wb = _ws(workspace)
     _check("iabn_backward", lib.iabn_backward(
         _ptr(y), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y),
-        _ptr(gamma), _ptr(beta), _ptr(save_invstd), _ptr(dgamma), _ptr(dbeta), _code(act, ACTS),
+        _vec(gamma), _vec(beta), _vec(save_invstd), _vec(dgamma), _vec(dbeta), _code(act, ACTS),
         act_param, wp, wb, _stream(stream)))
 
 
@@ -247,8 +258,8 @@ def iabn_backward_reduce(y, dy, N, C, H, W, layout, gamma, beta, save_invstd, dg
                          act_param, workspace, stream=None):
     wp, wb = _ws(workspace)
     _check("iabn_backward_reduce", lib.iabn_backward_reduce(
-        _ptr(y), _ptr(dy), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y), _ptr(gamma),
-        _ptr(beta), _ptr(save_invstd), _ptr(dgamma), _ptr(dbeta), _code(act, ACTS), act_param,
+        _ptr(y), _ptr(dy), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y), _vec(gamma),
+        _vec(beta), _vec(save_invstd), _vec(dgamma), _vec(dbeta), _code(act, ACTS), act_param,
         wp, wb, _stream(stream)))
 
 
@@ -264,7 +275,7 @@ def iabn_backward_eval(y, dy, dx, N, C, H, W, layout, gamma, beta, running_var, 
     wp, wb = _ws(workspace)
     _check("iabn_backward_eval", lib.iabn_backward_eval(
         _ptr(y), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(y),
-        _ptr(gamma), _ptr(beta), _ptr(running_var), eps, _ptr(dgamma), _ptr(dbeta),
+        _vec(gamma), _vec(beta), _vec(running_var), eps, _vec(dgamma), _vec(dbeta),
         _code(act, ACTS), act_param, wp, wb, _stream(stream)))
 
 
@@ -274,16 +285,16 @@ def iabn_forward_train_ckpt(x, y, N, C, H, W, layout, gamma, beta, running_mean,
     """Optimized checkpointing forward: xhat written over x, the layer output into y."""
     wp, wb = _ws(workspace)
     _check("iabn_forward_train_ckpt", lib.iabn_forward_train_ckpt(
-        _ptr(x), _ptr(y), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _ptr(gamma),
-        _ptr(beta), _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_invstd),
+        _ptr(x), _ptr(y), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(x), _vec(gamma),
+        _vec(beta), _vec(running_mean), _vec(running_var), _vec(save_mean), _vec(save_invstd),
         _code(act, ACTS), act_param, eps, momentum, wp, wb, _stream(stream)))
 
 
 def iabn_recompute_from_xhat(xhat, y, N, C, H, W, layout, gamma, beta, act, act_param,
                              stream=None):
     _check("iabn_recompute_from_xhat", lib.iabn_recompute_from_xhat(
-        _ptr(xhat), _ptr(y), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(xhat), _ptr(gamma),
-        _ptr(beta), _code(act, ACTS), act_param, _stream(stream)))
+        _ptr(xhat), _ptr(y), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(xhat), _vec(gamma),
+        _vec(beta), _code(act, ACTS), act_param, _stream(stream)))
 
 
 def iabn_backward_ckpt(xhat, dy, dx, N, C, H, W, layout, gamma, beta, save_invstd, dgamma, dbeta,
@@ -291,7 +302,7 @@ def iabn_backward_ckpt(xhat, dy, dx, N, C, H, W, layout, gamma, beta, save_invst
     wp, wb = _ws(workspace)
     _check("iabn_backward_ckpt", lib.iabn_backward_ckpt(
         _ptr(xhat), _ptr(dy), _ptr(dx), N, C, H, W, _code(layout, LAYOUTS), _dtype_code(xhat),
-        _ptr(gamma), _ptr(beta), _ptr(save_invstd), _ptr(dgamma), _ptr(dbeta), _code(act, ACTS),
+        _vec(gamma), _vec(beta), _vec(save_invstd), _vec(dgamma), _vec(dbeta), _code(act, ACTS),
         act_param, wp, wb, _stream(stream)))
 
 

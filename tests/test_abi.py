@@ -410,3 +410,20 @@ def test_module_state_dict_matches_batchnorm2d():
     b.running_var.fill_(2.0)
     a.load_state_dict(b.state_dict())
     assert a._steps == 7 and float(a.running_var[0]) == 2.0
+
+
+def test_binding_refuses_per_channel_vectors_of_other_dtypes():
+    """The library reads gamma, beta, statistics and gradients as float32: the
+    binding refuses a float64 (or any other) vector instead of passing its bytes
+    on (host only; the refusal comes before any library call)."""
+    import torch
+    x = torch.empty(2 * 3 * 4 * 4)
+    v32 = torch.empty(3)
+    v64 = torch.empty(3, dtype=torch.float64)
+    ws = torch.empty(1 << 16, dtype=torch.uint8)
+    with pytest.raises(TypeError, match="float32"):
+        iabn.iabn_forward_train(x, 2, 3, 4, 4, "NCHW", v64, v32, None, None, v32, v32,
+                                "leaky_relu", 0.01, 1e-5, 0.1, ws, stream=0)
+    with pytest.raises(TypeError, match="float32"):
+        iabn.iabn_backward(x, x, x, 2, 3, 4, 4, "NCHW", v32, v32, v32, v32,
+                           v32.half(), "leaky_relu", 0.01, ws, stream=0)
