@@ -200,37 +200,96 @@ __device__ __forceinline__ float load_one(const void* base, int64_t i)
 // invertible activations.  Forward branches on z > 0; the backward reads the
 // branch off the stored y (y > 0), which agrees with z > 0 for every slope > 0.
 
-// ELU's two transcendentals, on the hardware exp2 / log2 units (v_exp_f32,
-// v_log_f32: about 1 ulp):
-//   exp(z) - 1 = exp2(z*log2(e)) - 1: absolute error ~1e-7 for z <= 0, which is
-//     all the ELU branch needs (|y| <= alpha, errors are judged against the
-//     channel's RMS);
-//   log1p(u), u in (-1, 0]: w = 1 + u rounded, then ln(w) - ((w - 1) - u)/w, the
-//     first-order correction for the rounding of w (Goldberg, "What every
-//     computer scientist should know about floating-point arithmetic", 1991).
+// ELU's two transcendentals, with relative accuracy of a few ulps over the
+// whole ELU branch, also where the result is tiny (a channel whose z all sit
+// near 0, as running statistics in eval mode or a small gamma can make them;
+// exp(z) - 1 and ln(1 + u) formed directly lose their digits there).  Each is
+// one straight-line sequence (no second branch to select from, which cost the
+// register-resident kernels their spare registers):
+//   expm1(z), z <= 0: z = k*ln2 + r with k = rint(z/ln2) and |r| <= ln2/2,
+//     reduced by two fused multiply-adds with ln2 split in two floats
+//     (Cody and Waite's reduction); expm1(r) by its Taylor series to r^7 (the
+//     first term left out is about 2^-26 of the sum); then
+//     expm1(z) = 2^k*expm1(r) + (2^k - 1), which is expm1(r) itself for k = 0;
+//   log1p(u), -1 < u <= 0: w = 1 + u = m*2^e with m in [sqrt(1/2), sqrt(2));
+//     f = m - 1, or f = u itself when e = 0 (so that the rounding of 1 + u is
+//     never seen); ln(1 + f) = 2*atanh(s), s = f/(2 + f), |s| <= 0.1716, by the
+//     series 2s(1 + s^2/3 + s^4/5 + s^6/7 + s^8/9) (first term left out below
+//     2^-28 of the sum); then ln(w) = e*ln2 + ln(1 + f).
+// Emulated in fp32 with the hardware reciprocal off by an ulp: at most 2 ulps
+// (expm1) and 6 ulps (log1p) from the exact values.
+constexpr float kLn2Hi = 0.693147182464599609375f;     // ln 2 rounded to float
+constexpr float kLn2Lo = -1.904654323148236e-09f;      // ln 2 - kLn2Hi
+
 __device__ __forceinline__ float elu_expm1(float z)
+{
+    const float zc = z < -88.f ? -88.f : z;           // 2^k underflows beyond; NaN stays
+    const float k = __builtin_rintf(zc * 1.44269504088896341f);
+    float r = fmaf(-k, kLn2Hi, zc);
+    r = fmaf(-k, kLn2Lo, r);
+    float p = 1.f / 5040.f;
+    p = fmaf(p, r, 1.f / 720.f);
+    p = fmaf(p, r, 1.f / 120.f);
+    p = fmaf(p, r, 1.f / 24.f);
+    p = fmaf(p, r, 1.f / 6.f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.f);
+    const float two_k = __builtin_amdgcn_ldexpf(1.f, int(k));
+    return fmaf(two_k, p * r, two_k - 1.f);
+}
+
+__device__ __forceinline__ float elu_log1p(float u)
+{
+    const float w = 1.f + u;
+    float m = __builtin_amdgcn_frexp_mantf(w);          // [1/2, 1)
+    int e = __builtin_amdgcn_frexp_expf(w);
+    const bool low = m < 0.70710678118654752f;
+    m = low ? m + m : m;
+    e = low ? e - 1 : e;
+    const float f = e == 0 ? u : m - 1.f;
+    const float s = f * __builtin_amdgcn_rcpf(2.f + f);
+    const float t = s * s;
+    float q = 1.f / 9.f;
+    q = fmaf(q, t, 1.f / 7.f);
+    q = fmaf(q, t, 1.f / 5.f);
+    q = fmaf(q, t, 1.f / 3.f);
+    q = fmaf(q, t, 1.f);
+    const float fe = float(e);
+    return fmaf(fe, kLn2Hi, fmaf(fe, kLn2Lo, 2.f * s * q));
+}
+
+// The direct forms on the hardware units alone: exp2(z*log2(e)) - 1, and
+// ln(w) - ((w - 1) - u)/w with w = 1 + u (the first-order correction for the
+// rounding of w: Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", 1991).  Their error is about an ulp of 1 in
+// absolute terms, under the rounding of 16-bit storage for every value above
+// the fp16 subnormal range; the kernels that hold 16-bit tensors in nearly all
+// of their registers use them, since the forms above need more registers.
+__device__ __forceinline__ float elu_expm1_direct(float z)
 {
     return __builtin_amdgcn_exp2f(z * 1.44269504088896341f) - 1.f;
 }
 
-__device__ __forceinline__ float elu_log1p(float u)
+__device__ __forceinline__ float elu_log1p_direct(float u)
 {
     const float w = 1.f + u;
     return __builtin_amdgcn_logf(w) * 0.693147180559945309f
            - ((w - 1.f) - u) * __builtin_amdgcn_rcpf(w);
 }
 
-template <int ACT>
+// PRECISE: ELU through elu_expm1 / elu_log1p, else through the direct forms.
+template <int ACT, bool PRECISE = true>
 __device__ __forceinline__ float act_forward(float z, float a)
 {
     if constexpr (ACT == kLeaky) return z > 0.f ? z : a * z;
-    else if constexpr (ACT == kElu) return z > 0.f ? z : a * elu_expm1(z);
+    else if constexpr (ACT == kElu)
+        return z > 0.f ? z : a * (PRECISE ? elu_expm1(z) : elu_expm1_direct(z));
     else return z;
 }
 
 // From a stored y: the pre-activation z = act^-1(y) and the slope act'(z).
 // ELU: act'(z) = alpha*exp(z) = y + alpha; the inverse clamps y/alpha at -1 + 2^-24.
-template <int ACT>
+template <int ACT, bool PRECISE = true>
 __device__ __forceinline__ void act_invert(float y, float a, float inv_a, float& z, float& slope)
 {
     if constexpr (ACT == kLeaky) {
@@ -240,7 +299,7 @@ __device__ __forceinline__ void act_invert(float y, float a, float inv_a, float&
     } else if constexpr (ACT == kElu) {
         const bool pos = y > 0.f;
         const float u = fmaxf(y * inv_a, -1.f + 0x1p-24f);
-        z = pos ? y : elu_log1p(u);
+        z = pos ? y : (PRECISE ? elu_log1p(u) : elu_log1p_direct(u));
         slope = pos ? 1.f : y + a;
     } else {
         z = y;

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw(
             float v[V];
             unpack16<DT>(opaque4(r[k]), v);
 #pragma unroll
-            for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K) - d, s, b), a);
+            for (int e = 0; e < V; ++e) v[e] = act_forward<ACT, DT == kF32>(fmaf((v[e] - K) - d, s, b), a);
             st16(x, w.off, pack16<DT>(v));
         }
         w.step();
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 float z, slope;
-                act_invert<ACT>(vy[e], a, inv_a, z, slope);
+                act_invert<ACT, DT == kF32>(vy[e], a, inv_a, z, slope);
                 const float dz = slope * vd[e];
                 sdz += dz;
                 sdzt = fmaf(dz, z - bc, sdzt);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw(
                     dz = vd[e];
                 } else {
                     float slope;
-                    act_invert<ACT>(vy[e], a2, ia2, z, slope);
+                    act_invert<ACT, DT == kF32>(vy[e], a2, ia2, z, slope);
                     dz = slope * vd[e];
                 }
                 vd[e] = fmaf(kA, dz, fmaf(kB, z - bc2, kC));
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
                         float z, slope;
-                        act_invert<ACT>(vy[e], a, inv_a, z, slope);
+                        act_invert<ACT, DT == kF32>(vy[e], a, inv_a, z, slope);
                         const float dz = slope * vd[e];
                         sdz += dz;
                         sdzt = fmaf(dz, z - bc, sdzt);
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(T) void k_bwd_stream_nchw(
 #pragma unroll
                         for (int e = 0; e < V; ++e) {
                             float z, slope;
-                            act_invert<ACT>(vy[e], a2, ia2, z, slope);
+                            act_invert<ACT, DT == kF32>(vy[e], a2, ia2, z, slope);
                             const float dz = slope * vd[e];
                             vd[e] = fmaf(kA, dz, fmaf(kB, z - bc2, kC));
                         }
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(T) void k_fwd_fused_nchw_s(
     for (int k = 0; k < NR; ++k) {
         if (t2 + k * T < m) {
             const float v = elem_float<DT>(opaque(r[k]));
-            st_elem<DT>(x, w.off, act_forward<ACT>(fmaf((v - K) - d, sc, b), a));
+            st_elem<DT>(x, w.off, act_forward<ACT, DT == kF32>(fmaf((v - K) - d, sc, b), a));
         }
         w.step();
     }
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(T) void k_bwd_fused_nchw_s(
     for (int k = 0; k < NR; ++k) {
         if (t + k * T < m) {
             float z, slope;
-            act_invert<ACT>(elem_float<DT>(ry[k]), a, inv_a, z, slope);
+            act_invert<ACT, DT == kF32>(elem_float<DT>(ry[k]), a, inv_a, z, slope);
             const float dz = slope * elem_float<DT>(rd[k]);
             sdz += dz;
             sdzt = fmaf(dz, z - bc, sdzt);
@@ -684,12 +684,16 @@ static void launch_fwd_da(const Plan& pl, void* x, const float* gamma, const flo
     switch (pl.fused_variant) {
 #define IABN_FWD_CASE(ID, T, NR)                                                                  \
     case ID:                                                                                      \
-        if (grp.G > 1)                                                                            \
-            hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, true>), dim3(C * grp.G), dim3(T), \
-                               0, s, x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a, grp); \
-        else                                                                                      \
-            hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, false>), dim3(C), dim3(T), 0, s, \
-                               x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a, grp);       \
+        if constexpr (fused_fwd_built(DT, ACT, NR)) {                                             \
+            if (grp.G > 1)                                                                        \
+                hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, true>), dim3(C * grp.G),     \
+                                   dim3(T), 0, s, x, C, HW, m, gamma, beta, rm, rv, sm, si, eps,  \
+                                   mom, a, grp);                                                  \
+            else                                                                                  \
+                hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, false>), dim3(C), dim3(T),   \
+                                   0, s, x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a,   \
+                                   grp);                                                          \
+        }                                                                                         \
         break;
         IABN_FUSED_FWD_VARIANTS(IABN_FWD_CASE)
 #undef IABN_FWD_CASE

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_fused_nhwc(
         float v[V];
         unpack16<DT>(opaque_q(r[k]), v);
 #pragma unroll
-        for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K[e]) - d[e], sc[e], b_c[e]), a);
+        for (int e = 0; e < V; ++e) v[e] = act_forward<ACT, DT == kF32>(fmaf((v[e] - K[e]) - d[e], sc[e], b_c[e]), a);
         if (row < r1) st16_out<LPR>(x, row * Cv + col, pack16<DT>(v));
     }
 }
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             float z, slope;
-            act_invert<ACT>(vy[e], a, inv_a, z, slope);
+            act_invert<ACT, DT == kF32>(vy[e], a, inv_a, z, slope);
             const float dz = slope * vd[e];
             sums[e] += dz;
             sums[V + e] = fmaf(dz, z - b_c[e], sums[V + e]);
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
                 dz = vd[e];
             } else {
                 float slope;
-                act_invert<ACT>(vy[e], a2, ia2, z, slope);
+                act_invert<ACT, DT == kF32>(vy[e], a2, ia2, z, slope);
                 dz = slope * vd[e];
             }
             vd[e] = fmaf(kA[e], dz, fmaf(kB[e], z - b_c[e], kC[e]));
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
         float v[V];
         unpack16<DT>(q, v);
 #pragma unroll
-        for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - K[e]) - d[e], sc[e], b_c[e]), a);
+        for (int e = 0; e < V; ++e) v[e] = act_forward<ACT, DT == kF32>(fmaf((v[e] - K[e]) - d[e], sc[e], b_c[e]), a);
         if (row < r1) st16_out<LPR>(x, row * Cv + col, pack16<DT>(v));
     };
 
@@ -736,7 +736,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             float z, slope;
-            act_invert<ACT>(vy[e], a, inv_a, z, slope);
+            act_invert<ACT, DT == kF32>(vy[e], a, inv_a, z, slope);
             const float dz = slope * vd[e];
             sums[e] += dz;
             sums[V + e] = fmaf(dz, z - b_c[e], sums[V + e]);
@@ -812,7 +812,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             float z, slope;
-            act_invert<ACT>(vy[e], a2, ia2, z, slope);
+            act_invert<ACT, DT == kF32>(vy[e], a2, ia2, z, slope);
             const float dz = slope * vd[e];
             vd[e] = fmaf(kA[e], dz, fmaf(kB[e], z - b_c[e], kC[e]));
         }

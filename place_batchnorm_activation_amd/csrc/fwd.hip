@@ -335,12 +335,26 @@ __global__ __launch_bounds__(kFinThreads) void k_fwd_finalize(
 }
 
 // ---------------------------------------------------------------------------
-// Elementwise y = act(((x - K) - d)*s + beta), in place.  Training reads the
-// constants from the workspace; inference forms them from the running
-// statistics: K = running_mean, d = 0, s = gamma/sqrt(running_var + eps).
+// Elementwise y = act(z), in place, z formed by the constants' own rule.
+//
+// Training reads (K, d, s, beta) from the workspace: z = ((x - K) - d)*s + beta,
+// K a sample of the channel and d = mean - K, so every term stays on the scale
+// of the channel's spread and z's error on that of the output.
+//
+// Inference forms z = (x - running_mean)*s + beta, s = gamma/sqrt(running_var +
+// eps), from frozen statistics that need not lie near the data: the product and
+// beta can cancel to outputs far smaller than either, where fp32 rounding of
+// x - running_mean and of s would be seen.  So x - running_mean is kept exactly
+// as a pair of floats (Knuth's two-sum), s as a pair (hi, lo) from an fp64
+// reciprocal square root refined by one Newton step, the cancelling product and
+// beta meet in one fused multiply-add, and the small terms come after it.
 struct TrainConsts {
     const float4* consts;
     __device__ __forceinline__ float4 get(int64_t c) const { return consts[c]; }
+    static __device__ __forceinline__ float z(float v, const float4& k)
+    {
+        return fmaf((v - k.x) - k.y, k.z, k.w);
+    }
 };
 struct EvalConsts {
     const float* gamma;
@@ -348,17 +362,34 @@ struct EvalConsts {
     const float* rm;
     const float* rv;
     float eps;
+    // (running_mean, s_lo, s_hi, beta)
     __device__ __forceinline__ float4 get(int64_t c) const
     {
-        return make_float4(rm[c], 0.f, gamma[c] / sqrtf(rv[c] + eps), beta[c]);
+        const double q = double(rv[c]) + double(eps);
+        double r = __builtin_amdgcn_rsq(q);
+        // the hardware estimate's relative error squared; 0 and inf stay as they
+        // are (1/sqrt(0) = inf)
+        if (q > 0.0 && q < __builtin_huge_val()) r *= fma(-0.5 * q * r, r, 1.5);
+        const double sc = double(gamma[c]) * r;
+        const float hi = float(sc);
+        return make_float4(rm[c], float(sc - double(hi)), hi, beta[c]);
+    }
+    static __device__ __forceinline__ float z(float v, const float4& k)
+    {
+        const float dh = v - k.x;
+        const float bb = dh - v;
+        const float dl = (v - (dh - bb)) + (-k.x - bb);    // dh + dl == v - k.x
+        const float z0 = fmaf(dh, k.z, k.w);
+        // a non-finite difference leaves the terms' error undefined: z0 is the result
+        return __builtin_isfinite(dh) ? z0 + fmaf(dh, k.y, dl * k.z) : z0;
     }
 };
 
-template <int ACT, int V>
+template <int ACT, int V, typename CS>
 __device__ __forceinline__ void apply_one(float (&v)[V], const float4& k, float a)
 {
 #pragma unroll
-    for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(fmaf((v[e] - k.x) - k.y, k.z, k.w), a);
+    for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(CS::z(v[e], k), a);
 }
 
 template <int DT, int V, int ACT, typename CS>
@@ -380,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nchw(
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            apply_one<ACT, V>(val[u], k[u], a);
+            apply_one<ACT, V, CS>(val[u], k[u], a);
             store_out<DT, V>(x, (v + u * stride) * V, val[u]);
         }
     }
@@ -389,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nchw(
         load_elems<DT, V>(x, v * V, val);
         const float4 k = cs.get(w.c);
         w.step();
-        apply_one<ACT, V>(val, k, a);
+        apply_one<ACT, V, CS>(val, k, a);
         store_out<DT, V>(x, v * V, val);
     }
 }
@@ -424,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
                 for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
                     for (int e = 0; e < V; ++e)
-                        val[u][e] = act_forward<ACT>(fmaf((val[u][e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+                        val[u][e] = act_forward<ACT>(CS::z(val[u][e], k[e]), a);
                     store_out<DT, V>(x, (v - u * stride) * V, val[u]);
                 }
             }
@@ -433,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
                 load_elems<DT, V>(x, v * V, val);
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    val[e] = act_forward<ACT>(fmaf((val[e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+                    val[e] = act_forward<ACT>(CS::z(val[e], k[e]), a);
                 store_out<DT, V>(x, v * V, val);
             }
             return;
@@ -446,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
             for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    val[u][e] = act_forward<ACT>(fmaf((val[u][e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+                    val[u][e] = act_forward<ACT>(CS::z(val[u][e], k[e]), a);
                 store_out<DT, V>(x, (v + u * stride) * V, val[u]);
             }
         }
@@ -455,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
             load_elems<DT, V>(x, v * V, val);
 #pragma unroll
             for (int e = 0; e < V; ++e)
-                val[e] = act_forward<ACT>(fmaf((val[e] - k[e].x) - k[e].y, k[e].z, k[e].w), a);
+                val[e] = act_forward<ACT>(CS::z(val[e], k[e]), a);
             store_out<DT, V>(x, v * V, val);
         }
     } else {
@@ -466,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float4 k = cs.get(c0 + e);
-                val[e] = act_forward<ACT>(fmaf((val[e] - k.x) - k.y, k.z, k.w), a);
+                val[e] = act_forward<ACT>(CS::z(val[e], k), a);
             }
             store_elems<DT, V>(x, v * V, val);
         }

@@ -815,3 +815,69 @@ def test_errors_raise_in_python():
     with pytest.raises(iabn.IABNError):
         iabn.iabn_forward_train(x, wl.N, C, wl.H, wl.W, "NCHW", v, v, None, None, v.clone(),
                                 v.clone(), "leaky_relu", 0.01, 1e-5, 0.1, None)
+
+
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_elu_near_zero_keeps_relative_accuracy(layout):
+    """ELU on channels whose pre-activations all sit near 0 (below it): y is then
+    tiny, and exp(z) - 1 formed directly would lose most of its digits.  Running
+    statistics that match a channel's own, with a small gamma and beta, put z
+    in [-1e-3, 1e-3] for the inference forward; the training forward gets the
+    same from a small gamma.  Both must stay within the fp32 gate."""
+    wl = custom(4, 2, 32, 9, 12, layout=layout, act="elu", act_param=1.0)
+    inp = workloads.make_inputs(wl)
+    xf = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    rm = xf.mean(axis=(0, 2, 3)).astype(np.float32)
+    rv = xf.var(axis=(0, 2, 3)).astype(np.float32)
+    gamma = (np.where(np.arange(wl.C) % 2, 1.0, -1.0) * 2e-4).astype(np.float32)
+    beta = np.full(wl.C, -1e-4, np.float32)
+    x = harness.to_device(inp.x, wl)
+    iabn.iabn_forward_eval(x, wl.N, wl.C, wl.H, wl.W, wl.layout, torch.from_numpy(gamma).cuda(),
+                           torch.from_numpy(beta).cuda(), torch.from_numpy(rm).cuda(),
+                           torch.from_numpy(rv).cuda(), wl.act, wl.act_param, wl.eps)
+    torch.cuda.synchronize()
+    o = oracle.forward_eval(xf, gamma, beta, rm, rv, wl.act, harness.f32(wl.act_param),
+                            harness.f32(wl.eps), storage=wl.dtype)
+    assert np.abs(o).max() < 2e-3
+    e = harness.rel_err_tensor(harness.to_nchw64(x, wl), o)
+    print("eval:", e, flush=True)
+    assert e <= harness.TOL[wl.dtype], e
+    # training: the same small affine step on the batch's own statistics
+    inp.gamma[:] = gamma
+    inp.beta[:] = beta
+    run = harness.run_gpu(inp)
+    ef = harness.check_forward(inp, run)
+    ef.update(harness.check_backward(inp, run))
+    print("train:", ef, flush=True)
+    harness.assert_within(ef, wl.dtype, "train")
+
+
+@pytest.mark.parametrize("layout,act,W", [("NCHW", "leaky_relu", 8), ("NCHW", "elu", 7),
+                                          ("NHWC", "elu", 8), ("NHWC", "identity", 5)])
+def test_forward_eval_with_cancelling_terms(layout, act, W):
+    """Inference with running statistics far from the batch: running_mean lies
+    3000 of the channel's standard deviations below its mean and beta cancels
+    the shift, so (x - running_mean)*s and beta are about 3000 times the output.
+    Formed plainly in fp32 their rounding alone would put the error near 2e-4 of
+    the output; the gate is the fp32 one.  Vector (W = 8) and single-element
+    (W odd) paths."""
+    wl = custom(2, 3, 24, 6, W, layout=layout, act=act, act_param=1.0 if act == "elu" else 0.01)
+    inp = workloads.make_inputs(wl)
+    xf = workloads.from_storage(inp.x, wl.N, wl.C, wl.H, wl.W, wl.layout, wl.dtype)
+    mu, sd = xf.mean(axis=(0, 2, 3)), xf.std(axis=(0, 2, 3))
+    rm = (mu - 3000.0 * sd).astype(np.float32)
+    rv = np.random.default_rng(3).uniform(0.5, 2.0, wl.C).astype(np.float32)
+    gamma = np.random.default_rng(4).uniform(0.5, 1.5, wl.C).astype(np.float32)
+    s = gamma.astype(np.float64) / np.sqrt(rv.astype(np.float64) + harness.f32(wl.eps))
+    beta = (-s * (mu - rm.astype(np.float64))).astype(np.float32)
+    x = harness.to_device(inp.x, wl)
+    iabn.iabn_forward_eval(x, wl.N, wl.C, wl.H, wl.W, wl.layout, torch.from_numpy(gamma).cuda(),
+                           torch.from_numpy(beta).cuda(), torch.from_numpy(rm).cuda(),
+                           torch.from_numpy(rv).cuda(), wl.act, wl.act_param, wl.eps)
+    torch.cuda.synchronize()
+    o = oracle.forward_eval(xf, gamma, beta, rm, rv, wl.act, harness.f32(wl.act_param),
+                            harness.f32(wl.eps), storage=wl.dtype)
+    assert np.abs(beta).min() > 1000 * np.sqrt(np.mean(o * o))
+    e = harness.rel_err_tensor(harness.to_nchw64(x, wl), o)
+    print("eval with cancelling terms:", e, flush=True)
+    assert e <= harness.TOL[wl.dtype], e
