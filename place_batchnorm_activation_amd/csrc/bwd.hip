@@ -38,7 +38,7 @@ constexpr int kUnrollN = IABN_NHWC_REDUCE_UNROLL;
 // decode gives the slope at z = fmaf(gamma, xhat, beta) and t = xhat, so the
 // sums become dbeta = sum dz and dgamma = sum dz*t directly (k_bwd_finalize with
 // xhat_sums).
-template <int ACT, bool XH>
+template <int ACT, bool XH, bool P>
 __device__ __forceinline__ void decode(float v, float g, float b, float a, float inv_a, float& t,
                                        float& slope)
 {
@@ -47,12 +47,12 @@ __device__ __forceinline__ void decode(float v, float g, float b, float a, float
         t = v;
     } else {
         float z;
-        act_invert<ACT>(v, a, inv_a, z, slope);
+        act_invert<ACT, P>(v, a, inv_a, z, slope);
         t = z - b;
     }
 }
 
-template <int ACT, int V, bool XH = false>
+template <int ACT, int V, bool XH, bool P>
 __device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy)[V],
                                            const float (&beta)[V], const float (&gam)[V], float a,
                                            float inv_a, float (&sdz)[V], float (&sdzt)[V])
@@ -60,7 +60,7 @@ __device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         float t, slope;
-        decode<ACT, XH>(y[e], gam[e], beta[e], a, inv_a, t, slope);
+        decode<ACT, XH, P>(y[e], gam[e], beta[e], a, inv_a, t, slope);
         const float dz = slope * dy[e];
         sdz[e] += dz;
         sdzt[e] = fmaf(dz, t, sdzt[e]);
@@ -69,7 +69,7 @@ __device__ __forceinline__ void accumulate(const float (&y)[V], const float (&dy
 
 // The same sums, and dx = A*dz written over dy's values (the backward with frozen
 // statistics, where dx needs no reduction: A = gamma/sqrt(running_var + eps)).
-template <int ACT, int V>
+template <int ACT, int V, bool P>
 __device__ __forceinline__ void accumulate_dx(const float (&y)[V], float (&dy)[V],
                                               const float (&beta)[V], const float (&A)[V],
                                               float a, float inv_a, float (&sdz)[V],
@@ -78,7 +78,7 @@ __device__ __forceinline__ void accumulate_dx(const float (&y)[V], float (&dy)[V
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         float z, slope;
-        act_invert<ACT>(y[e], a, inv_a, z, slope);
+        act_invert<ACT, P>(y[e], a, inv_a, z, slope);
         const float dz = slope * dy[e];
         sdz[e] += dz;
         sdzt[e] = fmaf(dz, z - beta[e], sdzt[e]);
@@ -141,10 +141,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
 #pragma unroll
         for (int u = 0; u < kUnrollB; ++u) {
             if constexpr (DX) {
-                accumulate_dx<ACT, V>(vy[u], vd[u], bc, A, a, inv_a, sdz, sdzt);
+                accumulate_dx<ACT, V, DT == kF32>(vy[u], vd[u], bc, A, a, inv_a, sdz, sdzt);
                 store_out<DT, V>(dx, ad[u], vd[u]);
             } else {
-                accumulate<ACT, V, XH>(vy[u], vd[u], bc, gc, a, inv_a, sdz, sdzt);
+                accumulate<ACT, V, XH, DT == kF32>(vy[u], vd[u], bc, gc, a, inv_a, sdz, sdzt);
             }
         }
     }
@@ -155,10 +155,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nchw(
         load_elems<DT, V>(dy, ad, vd);
         w.step();
         if constexpr (DX) {
-            accumulate_dx<ACT, V>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
+            accumulate_dx<ACT, V, DT == kF32>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
             store_out<DT, V>(dx, ad, vd);
         } else {
-            accumulate<ACT, V, XH>(vy, vd, bc, gc, a, inv_a, sdz, sdzt);
+            accumulate<ACT, V, XH, DT == kF32>(vy, vd, bc, gc, a, inv_a, sdz, sdzt);
         }
     }
     float S1 = 0.f, S2 = 0.f;
@@ -211,10 +211,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     // one element of the reduction; with DX also dx at storage index i (elements)
     auto one = [&](float (&vy)[V], float (&vd)[V], int64_t i) {
         if constexpr (DX) {
-            accumulate_dx<ACT, V>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
+            accumulate_dx<ACT, V, DT == kF32>(vy, vd, bc, A, a, inv_a, sdz, sdzt);
             store_out<DT, V>(dx, i, vd);
         } else {
-            accumulate<ACT, V, XH>(vy, vd, bc, gc, a, inv_a, sdz, sdzt);
+            accumulate<ACT, V, XH, DT == kF32>(vy, vd, bc, gc, a, inv_a, sdz, sdzt);
         }
     };
     if (active) {
@@ -398,14 +398,14 @@ __global__ __launch_bounds__(kThreads) void k_eval_consts(
 // ---------------------------------------------------------------------------
 // dx = A*dz + B*(z - beta) + Cc.  dx may be the same buffer as dy: each element
 // of dy is read by the thread that then writes the same element of dx.
-template <int ACT, int V>
+template <int ACT, int V, bool P>
 __device__ __forceinline__ void dx_one(const float (&vy)[V], float (&vd)[V], const float4 (&k)[V],
                                        float a, float inv_a)
 {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         float z, slope;
-        act_invert<ACT>(vy[e], a, inv_a, z, slope);
+        act_invert<ACT, P>(vy[e], a, inv_a, z, slope);
         const float dz = slope * vd[e];
         vd[e] = fmaf(k[e].x, dz, fmaf(k[e].y, z - k[e].w, k[e].z));
     }
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nchw(
         }
 #pragma unroll
         for (int u = 0; u < kUnrollB; ++u) {
-            dx_one<ACT, V>(vy[u], vd[u], k[u], a, inv_a);
+            dx_one<ACT, V, DT == kF32>(vy[u], vd[u], k[u], a, inv_a);
             store_out<DT, V>(dx, (v + u * stride) * V, vd[u]);
         }
     }
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nchw(
 #pragma unroll
         for (int e = 0; e < V; ++e) k[e] = kc;
         w.step();
-        dx_one<ACT, V>(vy, vd, k, a, inv_a);
+        dx_one<ACT, V, DT == kF32>(vy, vd, k, a, inv_a);
         store_out<DT, V>(dx, v * V, vd);
     }
 }
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
                 float vy[V], vd[V];
                 unpack16<DT>(qy, vy);
                 unpack16<DT>(qd, vd);
-                dx_one<ACT, V>(vy, vd, k, a, inv_a);
+                dx_one<ACT, V, DT == kF32>(vy, vd, k, a, inv_a);
                 store_out<DT, V>(dx, w * V, vd);
             };
             auto put_set = [&](const uint4 (&qy)[kUnrollB], const uint4 (&qd)[kUnrollB], int64_t js) {
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
                 }
 #pragma unroll
                 for (int u = 0; u < kUnrollB; ++u) {
-                    dx_one<ACT, V>(vy[u], vd[u], k, a, inv_a);
+                    dx_one<ACT, V, DT == kF32>(vy[u], vd[u], k, a, inv_a);
                     store_out<DT, V>(dx, (v - u * stride) * V, vd[u]);
                 }
             }
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
                 float vy[V], vd[V];
                 load_elems<DT, V>(y, v * V, vy);
                 load_elems<DT, V>(dy, v * V, vd);
-                dx_one<ACT, V>(vy, vd, k, a, inv_a);
+                dx_one<ACT, V, DT == kF32>(vy, vd, k, a, inv_a);
                 store_out<DT, V>(dx, v * V, vd);
             }
             return;
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
             }
 #pragma unroll
             for (int u = 0; u < kUnrollB; ++u) {
-                dx_one<ACT, V>(vy[u], vd[u], k, a, inv_a);
+                dx_one<ACT, V, DT == kF32>(vy[u], vd[u], k, a, inv_a);
                 store_out<DT, V>(dx, (v + u * stride) * V, vd[u]);
             }
         }
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
             float vy[V], vd[V];
             load_elems<DT, V>(y, v * V, vy);
             load_elems<DT, V>(dy, v * V, vd);
-            dx_one<ACT, V>(vy, vd, k, a, inv_a);
+            dx_one<ACT, V, DT == kF32>(vy, vd, k, a, inv_a);
             store_out<DT, V>(dx, v * V, vd);
         }
     } else {
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
             for (int e = 0; e < V; ++e) k[e] = consts[c0 + e];
             load_elems<DT, V>(y, v * V, vy);
             load_elems<DT, V>(dy, v * V, vd);
-            dx_one<ACT, V>(vy, vd, k, a, inv_a);
+            dx_one<ACT, V, DT == kF32>(vy, vd, k, a, inv_a);
             store_elems<DT, V>(dx, v * V, vd);
         }
     }

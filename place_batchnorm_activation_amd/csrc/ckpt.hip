@@ -87,13 +87,13 @@ __device__ __forceinline__ void ckpt_vec(float (&v0)[V], const float (&v1)[V], v
             float p = ((v0[e] - k[e].k0) - k[e].k1) * k[e].k2;
             asm volatile("" : "+v"(p));
             v0[e] = as_stored<DT>(p);
-            y[e] = act_forward<ACT>(fmaf(k[e].g, v0[e], k[e].b), a);
+            y[e] = act_forward<ACT, DT == kF32>(fmaf(k[e].g, v0[e], k[e].b), a);
         }
         store_out<DT, V>(out0, i, v0);
         store_out<DT, V>(out1, i, y);
     } else if constexpr (MODE == kCkptRecompute) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) v0[e] = act_forward<ACT>(fmaf(k[e].g, v0[e], k[e].b), a);
+        for (int e = 0; e < V; ++e) v0[e] = act_forward<ACT, DT == kF32>(fmaf(k[e].g, v0[e], k[e].b), a);
         store_out<DT, V>(out0, i, v0);
     } else {
 #pragma unroll

@@ -263,8 +263,8 @@ __device__ __forceinline__ float elu_log1p(float u)
 // rounding of w: Goldberg, "What every computer scientist should know about
 // floating-point arithmetic", 1991).  Their error is about an ulp of 1 in
 // absolute terms, under the rounding of 16-bit storage for every value above
-// the fp16 subnormal range; the kernels that hold 16-bit tensors in nearly all
-// of their registers use them, since the forms above need more registers.
+// the fp16 subnormal range, so every kernel on 16-bit storage uses them: there
+// the forms above would cost registers and ALU time and gain nothing.
 __device__ __forceinline__ float elu_expm1_direct(float z)
 {
     return __builtin_amdgcn_exp2f(z * 1.44269504088896341f) - 1.f;
@@ -278,18 +278,23 @@ __device__ __forceinline__ float elu_log1p_direct(float u)
 }
 
 // PRECISE: ELU through elu_expm1 / elu_log1p, else through the direct forms.
-template <int ACT, bool PRECISE = true>
+template <int ACT, bool PRECISE>
 __device__ __forceinline__ float act_forward(float z, float a)
 {
     if constexpr (ACT == kLeaky) return z > 0.f ? z : a * z;
-    else if constexpr (ACT == kElu)
-        return z > 0.f ? z : a * (PRECISE ? elu_expm1(z) : elu_expm1_direct(z));
-    else return z;
+    else if constexpr (ACT == kElu) {
+        // both arms formed and one selected: as a branch around the series, each
+        // element's chain would run alone, with no other element's to fill its
+        // latencies.  A NaN z keeps its NaN (it is not clamped to 0).
+        const float zn = z > 0.f ? 0.f : z;
+        const float e = PRECISE ? elu_expm1(zn) : elu_expm1_direct(zn);
+        return z > 0.f ? z : a * e;
+    } else return z;
 }
 
 // From a stored y: the pre-activation z = act^-1(y) and the slope act'(z).
 // ELU: act'(z) = alpha*exp(z) = y + alpha; the inverse clamps y/alpha at -1 + 2^-24.
-template <int ACT, bool PRECISE = true>
+template <int ACT, bool PRECISE>
 __device__ __forceinline__ void act_invert(float y, float a, float inv_a, float& z, float& slope)
 {
     if constexpr (ACT == kLeaky) {
@@ -299,7 +304,9 @@ __device__ __forceinline__ void act_invert(float y, float a, float inv_a, float&
     } else if constexpr (ACT == kElu) {
         const bool pos = y > 0.f;
         const float u = fmaxf(y * inv_a, -1.f + 0x1p-24f);
-        z = pos ? y : (PRECISE ? elu_log1p(u) : elu_log1p_direct(u));
+        // formed for every element and selected, as in act_forward
+        const float lz = PRECISE ? elu_log1p(u) : elu_log1p_direct(u);
+        z = pos ? y : lz;
         slope = pos ? 1.f : y + a;
     } else {
         z = y;

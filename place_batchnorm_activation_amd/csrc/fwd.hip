@@ -385,11 +385,11 @@ struct EvalConsts {
     }
 };
 
-template <int ACT, int V, typename CS>
+template <int ACT, int V, typename CS, bool P>
 __device__ __forceinline__ void apply_one(float (&v)[V], const float4& k, float a)
 {
 #pragma unroll
-    for (int e = 0; e < V; ++e) v[e] = act_forward<ACT>(CS::z(v[e], k), a);
+    for (int e = 0; e < V; ++e) v[e] = act_forward<ACT, P>(CS::z(v[e], k), a);
 }
 
 template <int DT, int V, int ACT, typename CS>
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nchw(
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            apply_one<ACT, V, CS>(val[u], k[u], a);
+            apply_one<ACT, V, CS, DT == kF32>(val[u], k[u], a);
             store_out<DT, V>(x, (v + u * stride) * V, val[u]);
         }
     }
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nchw(
         load_elems<DT, V>(x, v * V, val);
         const float4 k = cs.get(w.c);
         w.step();
-        apply_one<ACT, V, CS>(val, k, a);
+        apply_one<ACT, V, CS, DT == kF32>(val, k, a);
         store_out<DT, V>(x, v * V, val);
     }
 }
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
                 for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
                     for (int e = 0; e < V; ++e)
-                        val[u][e] = act_forward<ACT>(CS::z(val[u][e], k[e]), a);
+                        val[u][e] = act_forward<ACT, DT == kF32>(CS::z(val[u][e], k[e]), a);
                     store_out<DT, V>(x, (v - u * stride) * V, val[u]);
                 }
             }
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
                 load_elems<DT, V>(x, v * V, val);
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    val[e] = act_forward<ACT>(CS::z(val[e], k[e]), a);
+                    val[e] = act_forward<ACT, DT == kF32>(CS::z(val[e], k[e]), a);
                 store_out<DT, V>(x, v * V, val);
             }
             return;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
             for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    val[u][e] = act_forward<ACT>(CS::z(val[u][e], k[e]), a);
+                    val[u][e] = act_forward<ACT, DT == kF32>(CS::z(val[u][e], k[e]), a);
                 store_out<DT, V>(x, (v + u * stride) * V, val[u]);
             }
         }
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
             load_elems<DT, V>(x, v * V, val);
 #pragma unroll
             for (int e = 0; e < V; ++e)
-                val[e] = act_forward<ACT>(CS::z(val[e], k[e]), a);
+                val[e] = act_forward<ACT, DT == kF32>(CS::z(val[e], k[e]), a);
             store_out<DT, V>(x, v * V, val);
         }
     } else {
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_nhwc(
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float4 k = cs.get(c0 + e);
-                val[e] = act_forward<ACT>(CS::z(val[e], k), a);
+                val[e] = act_forward<ACT, DT == kF32>(CS::z(val[e], k), a);
             }
             store_elems<DT, V>(x, v * V, val);
         }
