@@ -123,14 +123,14 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
     Plan p = make_plan(N, C, H, W, layout, dtype, vec);
     if (act >= 0 && p.layout == kNCHW && p.vec && p.numel > 0) {
         const int64_t vc = p.m / p.V;
-        const int f = fused_fwd_pick(vc, p.dtype, act);
+        const int f = fused_fwd_pick(vc);
         if (f >= 0 && fused_worthwhile(p, fused_fwd_threads(f))) p.fused_variant = f;
         const int b = fused_bwd_pick(vc);
         if (b >= 0 && fused_worthwhile(p, fused_bwd_threads(b))) p.fused_bwd_variant = b;
         if (p.fused_variant < 0 || p.fused_bwd_variant < 0) {
             // a channel larger than one workgroup holds, or too few channels to
             // fill the chip: a group of workgroups per channel
-            const NchwGroupChoice g = fused_nchw_group_pick(p, act, group_grid());
+            const NchwGroupChoice g = fused_nchw_group_pick(p, group_grid());
             if (g.group > 1) {
                 p.fused_variant = g.fwd;
                 p.fused_bwd_variant = g.bwd;
@@ -188,13 +188,10 @@ size_t workspace_bytes_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layo
 {
     const size_t a = split_bytes(N, C, H, W, layout, dtype);
     if (!vec_shape_ok(C, H * W, layout, dtype)) return a;
-    // the group exchange, planned whatever the process-wide setting of grouped
-    // kernels; ELU on fp32 may take a group, or a larger one, where the other
-    // activations do not (fused_fwd_built)
+    // the group exchange (act plays no part in its choice), planned whatever the
+    // process-wide setting of grouped kernels
     const size_t b = plan_for(N, C, H, W, layout, dtype, true, IABN_ACT_IDENTITY, 1).bytes;
-    const size_t e = plan_for(N, C, H, W, layout, dtype, true, IABN_ACT_ELU, 1).bytes;
-    const size_t be = b > e ? b : e;
-    return a > be ? a : be;
+    return a > b ? a : b;
 }
 
 iabn_status check_workspace(const void* ws, size_t bytes, const Plan& pl)

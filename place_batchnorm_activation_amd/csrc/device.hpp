@@ -203,59 +203,47 @@ __device__ __forceinline__ float load_one(const void* base, int64_t i)
 // ELU's two transcendentals, with relative accuracy of a few ulps over the
 // whole ELU branch, also where the result is tiny (a channel whose z all sit
 // near 0, as running statistics in eval mode or a small gamma can make them;
-// exp(z) - 1 and ln(1 + u) formed directly lose their digits there).  Each is
-// one straight-line sequence (no second branch to select from, which cost the
-// register-resident kernels their spare registers):
-//   expm1(z), z <= 0: z = k*ln2 + r with k = rint(z/ln2) and |r| <= ln2/2,
-//     reduced by two fused multiply-adds with ln2 split in two floats
-//     (Cody and Waite's reduction); expm1(r) by its Taylor series to r^7 (the
-//     first term left out is about 2^-26 of the sum); then
-//     expm1(z) = 2^k*expm1(r) + (2^k - 1), which is expm1(r) itself for k = 0;
-//   log1p(u), -1 < u <= 0: w = 1 + u = m*2^e with m in [sqrt(1/2), sqrt(2));
-//     f = m - 1, or f = u itself when e = 0 (so that the rounding of 1 + u is
-//     never seen); ln(1 + f) = 2*atanh(s), s = f/(2 + f), |s| <= 0.1716, by the
-//     series 2s(1 + s^2/3 + s^4/5 + s^6/7 + s^8/9) (first term left out below
-//     2^-28 of the sum); then ln(w) = e*ln2 + ln(1 + f).
-// Emulated in fp32 with the hardware reciprocal off by an ulp: at most 2 ulps
-// (expm1) and 6 ulps (log1p) from the exact values.
-constexpr float kLn2Hi = 0.693147182464599609375f;     // ln 2 rounded to float
-constexpr float kLn2Lo = -1.904654323148236e-09f;      // ln 2 - kLn2Hi
-
+// exp(z) - 1 and ln(1 + u) formed directly lose their digits there).  Each
+// forms a series for arguments near 0 and the hardware's exp2 or log2 for the
+// rest, and selects (no branch):
+//   expm1(z), z <= 0: on [-0.35, 0] the Taylor series to z^7 (the first term
+//     left out is below 2^-25 of the sum); below -0.35, exp2(z*log2(e)) - 1,
+//     whose magnitude there exceeds 0.29, so the roundings of exp2 and of its
+//     argument stay a few ulps of it;
+//   log1p(u), -1 < u <= 0: above -0.29, ln(1 + u) = 2*atanh(s) with
+//     s = u/(2 + u), |s| < 0.17, by the series 2s(1 + s^2/3 + s^4/5 + s^6/7 +
+//     s^8/9) (first term left out below 2^-28 of the sum); at or below it,
+//     log2(1 + u)*ln2, where |ln(1 + u)| >= 0.34 and 1 + u is rounded at most
+//     by half an ulp of 2^-1.
+// Emulated in fp32 (fused multiply-adds, correctly rounded exp2, log2 and
+// reciprocal): at most 2.4 ulps (expm1) and 3.5 ulps (log1p) from the exact
+// values; the hardware's exp2, log2 and reciprocal are within an ulp of those.
 __device__ __forceinline__ float elu_expm1(float z)
 {
-    const float zc = z < -88.f ? -88.f : z;           // 2^k underflows beyond; NaN stays
-    const float k = __builtin_rintf(zc * 1.44269504088896341f);
-    float r = fmaf(-k, kLn2Hi, zc);
-    r = fmaf(-k, kLn2Lo, r);
     float p = 1.f / 5040.f;
-    p = fmaf(p, r, 1.f / 720.f);
-    p = fmaf(p, r, 1.f / 120.f);
-    p = fmaf(p, r, 1.f / 24.f);
-    p = fmaf(p, r, 1.f / 6.f);
-    p = fmaf(p, r, 0.5f);
-    p = fmaf(p, r, 1.f);
-    const float two_k = __builtin_amdgcn_ldexpf(1.f, int(k));
-    return fmaf(two_k, p * r, two_k - 1.f);
+    p = fmaf(p, z, 1.f / 720.f);
+    p = fmaf(p, z, 1.f / 120.f);
+    p = fmaf(p, z, 1.f / 24.f);
+    p = fmaf(p, z, 1.f / 6.f);
+    p = fmaf(p, z, 0.5f);
+    p = fmaf(p, z, 1.f);
+    const float near0 = p * z;
+    const float far = __builtin_amdgcn_exp2f(z * 1.44269504088896341f) - 1.f;
+    return z > -0.35f ? near0 : far;                   // NaN takes exp2's NaN
 }
 
 __device__ __forceinline__ float elu_log1p(float u)
 {
-    const float w = 1.f + u;
-    float m = __builtin_amdgcn_frexp_mantf(w);          // [1/2, 1)
-    int e = __builtin_amdgcn_frexp_expf(w);
-    const bool low = m < 0.70710678118654752f;
-    m = low ? m + m : m;
-    e = low ? e - 1 : e;
-    const float f = e == 0 ? u : m - 1.f;
-    const float s = f * __builtin_amdgcn_rcpf(2.f + f);
+    const float s = u * __builtin_amdgcn_rcpf(2.f + u);
     const float t = s * s;
     float q = 1.f / 9.f;
     q = fmaf(q, t, 1.f / 7.f);
     q = fmaf(q, t, 1.f / 5.f);
     q = fmaf(q, t, 1.f / 3.f);
     q = fmaf(q, t, 1.f);
-    const float fe = float(e);
-    return fmaf(fe, kLn2Hi, fmaf(fe, kLn2Lo, 2.f * s * q));
+    const float near0 = 2.f * s * q;
+    const float far = __builtin_amdgcn_logf(1.f + u) * 0.693147180559945309f;
+    return u > -0.29f ? near0 : far;
 }
 
 // The direct forms on the hardware units alone: exp2(z*log2(e)) - 1, and

@@ -88,16 +88,7 @@ namespace iabn {
 
 struct FusedVariant { int id, T, NR; bool dyr; };
 
-// Whether a forward variant is built for a storage dtype and activation.  ELU on
-// fp32 storage computes exp(z)-1 by its range-reduced series, whose registers do
-// not fit beside 49 resident vectors a thread without spilling: such channels
-// take a group of smaller shares, or the split kernels.
-constexpr bool fused_fwd_built(int dtype, int act, int nr)
-{
-    return !(dtype == kF32 && act == kElu && nr > 32);
-}
-
-inline int fused_fwd_pick(int64_t vc, int dtype, int act)
+inline int fused_fwd_pick(int64_t vc)
 {
     static const FusedVariant tbl[] = {
 #define IABN_ROW(ID, T, NR) {ID, T, NR, false},
@@ -105,7 +96,7 @@ inline int fused_fwd_pick(int64_t vc, int dtype, int act)
 #undef IABN_ROW
     };
     for (const auto& v : tbl)
-        if (int64_t(v.T) * v.NR >= vc) return fused_fwd_built(dtype, act, v.NR) ? v.id : -1;
+        if (int64_t(v.T) * v.NR >= vc) return v.id;
     return -1;
 }
 
@@ -176,7 +167,7 @@ struct NchwGroupChoice {
     int fwd = -1, bwd = -1, group = 1;
 };
 
-inline NchwGroupChoice fused_nchw_group_pick(const Plan& p, int act, int64_t max_grid)
+inline NchwGroupChoice fused_nchw_group_pick(const Plan& p, int64_t max_grid)
 {
     NchwGroupChoice none;
     if (p.layout != kNCHW || !p.vec || p.numel == 0) return none;
@@ -187,7 +178,7 @@ inline NchwGroupChoice fused_nchw_group_pick(const Plan& p, int act, int64_t max
         if (p.C * g > max_grid) continue;
         const int64_t share = ceil_div(vc, g);
         if ((g - 1) * share >= vc) continue;        // every member holds vectors
-        const int f = fused_fwd_pick(share, p.dtype, act), b = fused_bwd_pick(share);
+        const int f = fused_fwd_pick(share), b = fused_bwd_pick(share);
         if (f < 0 || b < 0 || fused_bwd_dy_resident(b) || g > fused_fwd_group_max(f)) continue;
         const int64_t threads = p.C * g * fused_fwd_threads(f);
         if (threads < int64_t(256) * 256 && bytes > (int64_t(4) << 20)) return none;

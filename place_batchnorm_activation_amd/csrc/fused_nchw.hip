@@ -684,16 +684,12 @@ static void launch_fwd_da(const Plan& pl, void* x, const float* gamma, const flo
     switch (pl.fused_variant) {
 #define IABN_FWD_CASE(ID, T, NR)                                                                  \
     case ID:                                                                                      \
-        if constexpr (fused_fwd_built(DT, ACT, NR)) {                                             \
-            if (grp.G > 1)                                                                        \
-                hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, true>), dim3(C * grp.G),     \
-                                   dim3(T), 0, s, x, C, HW, m, gamma, beta, rm, rv, sm, si, eps,  \
-                                   mom, a, grp);                                                  \
-            else                                                                                  \
-                hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, false>), dim3(C), dim3(T),   \
-                                   0, s, x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a,   \
-                                   grp);                                                          \
-        }                                                                                         \
+        if (grp.G > 1)                                                                            \
+            hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, true>), dim3(C * grp.G), dim3(T), \
+                               0, s, x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a, grp); \
+        else                                                                                      \
+            hipLaunchKernelGGL((k_fwd_fused_nchw<DT, ACT, T, NR, false>), dim3(C), dim3(T), 0, s, \
+                               x, C, HW, m, gamma, beta, rm, rv, sm, si, eps, mom, a, grp);       \
         break;
         IABN_FUSED_FWD_VARIANTS(IABN_FWD_CASE)
 #undef IABN_FWD_CASE

@@ -462,6 +462,8 @@ CHANNEL_GROUPS = [
     (custom(3, 32, 1, 200, 200, layout="NCHW", dtype="bf16"), "512x16,group32", "512x16,dy_streamed,group32"),
     (custom(2, 32, 2, 200, 200), "512x16,group64", "512x16,dy_streamed,group64"),
     (custom(2, 32, 64, 112, 112), "512x49,group4", "512x49,dy_streamed,group4"),
+    (custom(4, 32, 64, 112, 112, act="elu", act_param=1.0), "512x49,group4",
+     "512x49,dy_streamed,group4"),
 ]
 
 
