@@ -444,6 +444,8 @@ int main(int argc, char** argv)
         {32, 1024, 14, 14, kNHWC, kBF16}, {32, 256, 28, 28, kNHWC, kF32}, {7, 512, 9, 13, kNHWC, kBF16},
         {3, 1024, 11, 17, kNHWC, kF32},  {2, 256, 200, 200, kNHWC, kBF16}, {8, 256, 56, 56, kNHWC, kBF16},
         {5, 128, 99, 101, kNHWC, kF32},   {2, 64, 256, 260, kNHWC, kBF16},
+        // one element per channel (the inference passes take m = 1)
+        {1, 65536, 1, 1, kNCHW, kF32},   {1, 1, 1, 65536, kNCHW, kF32},   {1, 4096, 1, 1, kNHWC, kBF16},
     };
     std::mt19937_64 rng(12345);
     const int n_random = argc > 1 ? std::atoi(argv[1]) : 300;
