@@ -144,6 +144,11 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
             }
         }
     }
+    if (act < 0 && p.layout == kNHWC && p.vec && p.numel > 0) {
+        // the split kernels only; note whether the training forward would stream
+        p.fwd_streamed = fused_nhwc_pick(p, group_grid()).variant < 0 &&
+                         fused_stream_pick(p, group_grid()).variant >= 0;
+    }
     if (act >= 0) {
         const bool nhwc_vec = p.layout == kNHWC && p.vec && p.numel > 0;
         const NhwcChoice nc = fused_nhwc_pick(p, nhwc_vec ? group_grid() : 0);
@@ -161,6 +166,7 @@ Plan plan_for(int64_t N, int64_t C, int64_t H, int64_t W, iabn_layout layout, ia
         } else if (nhwc_vec) {
             const NhwcChoice sc = fused_stream_pick(p, group_grid());
             p.stream_variant = sc.variant;
+            p.fwd_streamed = sc.variant >= 0;
             if (sc.variant >= 0) {
                 p.nhwc_group = sc.group;
                 if (stream_bwd_worthwhile(p, sc.variant, sc.group)) p.stream_bwd_variant = sc.variant;

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
     const void* __restrict__ y, const void* dy, int64_t m, int64_t Cv, int tpr,
     int64_t slices, int64_t groups, int64_t P, const float* __restrict__ beta, float a,
     float inv_a, float* __restrict__ part_dz, float* __restrict__ part_dzt, void* dx,
-    const float* __restrict__ gamma, const float* __restrict__ frozen_var, float eps)
+    const float* __restrict__ gamma, const float* __restrict__ frozen_var, float eps,
+    bool from_end)
 {
     static_assert(!(DX && XH), "the frozen-statistics pass reads y");
     const int64_t b = blockIdx.x;
@@ -231,10 +232,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
             const int64_t full = m / rpi;
             const uint4* yv = reinterpret_cast<const uint4*>(y);
             const uint4* dv = reinterpret_cast<const uint4*>(dy);
+            // row group g's place in the walk: from the end of the tensor down if
+            // from_end (the ragged last group, if any, keeps its place)
+            auto rg = [&](int64_t g) { return from_end && g < full ? full - 1 - g : g; };
             auto load_set = [&](uint4 (&by)[kUnrollN], uint4 (&bd)[kUnrollN], int64_t g0) {
 #pragma unroll
                 for (int u = 0; u < kUnrollN; ++u) {
-                    const int64_t i = ((g0 + u * P) * rpi + rs) * Cv + col;
+                    const int64_t i = (rg(g0 + u * P) * rpi + rs) * Cv + col;
                     by[u] = yv[i];
                     bd[u] = dv[i];
                 }
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                     float vy[V], vd[V];
                     unpack16<DT>(by[u], vy);
                     unpack16<DT>(bd[u], vd);
-                    one(vy, vd, (((g0 + u * P) * rpi + rs) * Cv + col) * V);
+                    one(vy, vd, ((rg(g0 + u * P) * rpi + rs) * Cv + col) * V);
                 }
             };
             // sets of kUnrollN complete groups, pipelined as in the statistics
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce_nhwc(
                 if (j < ns) add_set(Ay, Ad, p + j * span);
             }
             for (; g < groups; g += P) {
-                const int64_t r = g * rpi + rs;
+                const int64_t r = rg(g) * rpi + rs;
                 if (r < m) {
                     float vy[V], vd[V];
                     unpack16<DT>(yv[r * Cv + col], vy);
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nchw(
 template <int DT, int V, int ACT, bool FIXED>
 __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
     const void* __restrict__ y, const void* dy, void* dx, int64_t nvec, int64_t Cv,
-    const float4* __restrict__ consts, float a, float inv_a)
+    const float4* __restrict__ consts, float a, float inv_a, bool from_end)
 {
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x;
@@ -466,17 +470,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
 #pragma unroll
         for (int e = 0; e < V; ++e) k[e] = consts[c0 + e];
         if constexpr (V == Raw16<DT>::V && ACT != kElu) {
-            // The thread's n vectors, from the end of the tensor down (the rows the
-            // reduction read last are the likeliest still to sit in the Infinity
-            // Cache), in sets of kUnrollB: set j + 1 loads while set j is written.
+            // The thread's n vectors, from the end of the tensor down if from_end,
+            // else up (starting where the sums pass ended: those rows are the
+            // likeliest still to sit in the Infinity Cache), in sets of kUnrollB:
+            // set j + 1 loads while set j is written.
             // The loop has no exit between its stages (the last load of an even
             // count is a spare reload), so the compiler keeps both sets in flight.
             // ELU keeps the plain loop below: its wider grid needs the registers
             // the second set would take (bf16: 159 against 193 us).
             const int64_t n = (nvec - 1 - v) / stride + 1;
             const int64_t top = v + (n - 1) * stride;
-            const int64_t step = IABN_APPLY_REVERSE ? -stride : stride;
-            const int64_t first = IABN_APPLY_REVERSE ? top : v;
+            const int64_t step = from_end ? -stride : stride;
+            const int64_t first = from_end ? top : v;
             const int64_t ns = n / kUnrollB;
             const uint4* yv = reinterpret_cast<const uint4*>(y);
             const uint4* dv = reinterpret_cast<const uint4*>(dy);
@@ -519,9 +524,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply_nhwc(
             }
             return;
         }
-        if constexpr (IABN_APPLY_REVERSE) {
-            // walk from the end down: the rows the reduction read last are the
-            // likeliest still to sit in the Infinity Cache
+        if (from_end) {
+            // walk from the end down
             const int64_t v0 = v;
             v = v0 + ((nvec - 1 - v0) / stride) * stride;
             for (; v - (kUnrollB - 1) * stride >= v0; v -= kUnrollB * stride) {
@@ -604,7 +608,8 @@ static void launch_reduce_dva(const Plan& pl, const void* y, const void* dy, con
     else
         hipLaunchKernelGGL((k_bwd_reduce_nhwc<DT, V, ACT, DX, XH>), dim3(pl.reduce_blocks_bwd),
                            dim3(kThreads), 0, s, y, dy, pl.m, pl.C / V, pl.tpr, pl.slices, pl.unit,
-                           pl.P_bwd, beta, a, ia, pa, pb, f.dx, f.gamma, f.var, f.eps);
+                           pl.P_bwd, beta, a, ia, pa, pb, f.dx, f.gamma, f.var, f.eps,
+                           bwd_sums_from_end(pl));
 }
 
 // XH: the reduction reads xhat instead of y (f.gamma carries gamma for it).
@@ -694,10 +699,10 @@ static void launch_bapply_dva(const Plan& pl, const void* y, const void* dy, voi
                            nvec, pl.C, pl.HW / V, k, a, ia);
     else if (pl.fixed_col)
         hipLaunchKernelGGL((k_bwd_apply_nhwc<DT, V, ACT, true>), grid, dim3(kThreads), 0, s, y, dy,
-                           dx, nvec, pl.C / V, k, a, ia);
+                           dx, nvec, pl.C / V, k, a, ia, !bwd_sums_from_end(pl));
     else
         hipLaunchKernelGGL((k_bwd_apply_nhwc<DT, V, ACT, false>), grid, dim3(kThreads), 0, s, y,
-                           dy, dx, nvec, pl.C / V, k, a, ia);
+                           dy, dx, nvec, pl.C / V, k, a, ia, !bwd_sums_from_end(pl));
 }
 
 template <int DT, int V>

@@ -168,9 +168,9 @@ __device__ __forceinline__ void store_elems_nt(void* base, int64_t i, const floa
 // not read again within the call, and keeping them out of the way leaves the
 // Infinity Cache to the inputs being re-read and spares the next kernel the
 // write-back of dirty lines (measured on the bf16 NHWC segmentation map: the
-// following statistics pass went from 75 to 55 us).  The split path's NHWC
-// elementwise kernels also walk the tensor from the end down (the rows the
-// reduction read last are the likeliest to be cached).
+// following statistics pass went from 75 to 55 us).  The split forward's NHWC
+// elementwise pass walks the tensor from the end down (the rows the statistics
+// read last are the likeliest to be cached).
 #ifndef IABN_APPLY_NT_STORE
 #define IABN_APPLY_NT_STORE 1
 #endif

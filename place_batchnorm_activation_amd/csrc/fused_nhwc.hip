@@ -472,6 +472,20 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
 // only the rows held in neither (newest first) and writes the others from
 // registers and LDS.  Traffic: forward (2 + f)S, backward (3 + 2f)S, f the
 // fraction of the rows held in neither.
+// Rows are dealt to the members interleaved: member j takes the row groups (of
+// T/LPR rows, one per thread) j, j + G, j + 2G, ..., so that at any time all 256
+// workgroups stream one narrow window of the tensor, as the split path's
+// reductions do, rather than 256 separate blocks.  On the 2x256x512x512 bf16 map
+// the forward's members had finished their first pass 35-48 us after launch
+// with blocks; interleaved, the forward took 120.8 against 125.1 us.
+#ifndef IABN_STREAM_INTERLEAVE_FWD
+#define IABN_STREAM_INTERLEAVE_FWD 1
+#endif
+#ifndef IABN_STREAM_INTERLEAVE_BWD
+#define IABN_STREAM_INTERLEAVE_BWD 1
+#endif
+constexpr bool kStreamInterleaveFwd = IABN_STREAM_INTERLEAVE_FWD;
+constexpr bool kStreamInterleaveBwd = IABN_STREAM_INTERLEAVE_BWD;
 template <int DT, int ACT, int T, int LPR, int NR, int NL, int U>
 __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     void* x, uint32_t m, uint32_t Cv, const float* __restrict__ gamma,
@@ -485,7 +499,11 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     const uint32_t slices = Cv / LPR;
     uint32_t s, member;
     nhwc_stream_member(blockIdx.x, slices, s, member);
-    const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);
+    // this member's rows: row groups of RPS rows, member, member + G, ... (RS =
+    // G*RPS rows apart) where interleaved, else the block [r0, r1) of mg rows
+    const uint32_t RS = kStreamInterleaveFwd ? grp.G * RPS : RPS;
+    const uint32_t r0 = kStreamInterleaveFwd ? member * RPS : member * grp.mg;
+    const uint32_t r1 = kStreamInterleaveFwd ? m : min(m, r0 + grp.mg);
     const uint32_t t = threadIdx.x;
     const uint32_t lane = t % LPR, rs = t / LPR;
     const uint32_t rb = r0 + rs;
@@ -494,11 +512,13 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     // rows per thread (uniform bound; rows at or past r1 are masked), streamed
     // chunks past the NR resident rows
-    const uint32_t nk = (r1 - r0 + RPS - 1) / RPS;
+    const uint32_t ngr = (m + RPS - 1) / RPS;
+    const uint32_t nk = !kStreamInterleaveFwd ? (r1 - r0 + RPS - 1) / RPS
+                        : member < ngr ? (ngr - member + grp.G - 1) / grp.G : 0u;
     const uint32_t nchunk = nk > NR ? (nk - NR + U - 1) / U : 0;
     auto load_chunk = [&](uint4 (&q)[U], uint32_t c) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) q[u] = xv[min(rb + (NR + c * U + u) * RPS, r1 - 1) * Cv + col];
+        for (int u = 0; u < U; ++u) q[u] = xv[min(rb + (NR + c * U + u) * RS, r1 - 1) * Cv + col];
     };
     // the first nlc streamed chunks stay in LDS for the second pass (each thread
     // its own column of slots: 16-byte accesses, no bank conflicts)
@@ -518,7 +538,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     __builtin_amdgcn_sched_barrier(0);
     uint4 r[NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) r[k] = xv[min(rb + k * RPS, r1 - 1) * Cv + col];
+    for (int k = 0; k < NR; ++k) r[k] = xv[min(rb + k * RS, r1 - 1) * Cv + col];
     // chunk loads are unconditional, their chunk index clamped (a spare load of
     // a chunk already read at the ends): no branch in the loops below, so the
     // compiler waits for exactly the chunk being summed
@@ -555,24 +575,24 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
         }
     };
 #pragma unroll
-    for (int k = 0; k < NR; ++k) add(r[k], rb + k * RPS);
+    for (int k = 0; k < NR; ++k) add(r[k], rb + k * RS);
     // streamed rows: chunk c + 1 loads while chunk c is summed
     uint32_t c = 0;
     for (; c + 1 < nchunk; c += 2) {
         load_chunk(qb, c + 1);
         __builtin_amdgcn_sched_barrier(0);          // issued before the sums of chunk c
 #pragma unroll
-        for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RPS);
+        for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RS);
         keep(qa, c);
         load_chunk(qa, min(c + 2, nchunk - 1));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) add(qb[u], rb + (NR + (c + 1) * U + u) * RPS);
+        for (int u = 0; u < U; ++u) add(qb[u], rb + (NR + (c + 1) * U + u) * RS);
         keep(qb, c + 1);
     }
     if (c < nchunk) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RPS);
+        for (int u = 0; u < U; ++u) add(qa[u], rb + (NR + c * U + u) * RS);
         keep(qa, c);
     }
 
@@ -633,27 +653,27 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     const uint32_t ng = nchunk - nlc;               // chunks read again from memory
     load_chunk(qa, nchunk > 0 ? nchunk - 1 : 0);
 #pragma unroll
-    for (int k = 0; k < NR; ++k) put(opaque_q(r[k]), rb2 + k * RPS);
+    for (int k = 0; k < NR; ++k) put(opaque_q(r[k]), rb2 + k * RS);
     uint32_t i = 0;
     for (; i + 1 < ng; i += 2) {
         const uint32_t cc = nchunk - 1 - i;
         load_chunk(qb, cc - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + cc * U + u) * RPS);
+        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + cc * U + u) * RS);
         load_chunk(qa, cc >= nlc + 2 ? cc - 2 : nlc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(qb[u], rb2 + (NR + (cc - 1) * U + u) * RPS);
+        for (int u = 0; u < U; ++u) put(qb[u], rb2 + (NR + (cc - 1) * U + u) * RS);
     }
     if (i < ng) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + nlc * U + u) * RPS);   // chunk nlc
+        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + nlc * U + u) * RS);   // chunk nlc
     }
     if constexpr (NL > 0) {
         for (uint32_t cc = 0; cc < nlc; ++cc) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) put(keep_rows[cc * U + u][t], rb2 + (NR + cc * U + u) * RPS);
+            for (int u = 0; u < U; ++u) put(keep_rows[cc * U + u][t], rb2 + (NR + cc * U + u) * RS);
         }
     }
 }
@@ -671,7 +691,11 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
     const uint32_t slices = Cv / LPR;
     uint32_t s, member;
     nhwc_stream_member(blockIdx.x, slices, s, member);
-    const uint32_t r0 = member * grp.mg, r1 = min(m, r0 + grp.mg);
+    // this member's rows: row groups of RPS rows, member, member + G, ... (RS =
+    // G*RPS rows apart) where interleaved, else the block [r0, r1) of mg rows
+    const uint32_t RS = kStreamInterleaveBwd ? grp.G * RPS : RPS;
+    const uint32_t r0 = kStreamInterleaveBwd ? member * RPS : member * grp.mg;
+    const uint32_t r1 = kStreamInterleaveBwd ? m : min(m, r0 + grp.mg);
     const uint32_t t = threadIdx.x;
     const uint32_t lane = t % LPR, rs = t / LPR;
     const uint32_t rb = r0 + rs;
@@ -679,12 +703,14 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
     const uint32_t c0 = col * V;
     const uint4* yv = reinterpret_cast<const uint4*>(y);
     const uint4* dv = reinterpret_cast<const uint4*>(dy);
-    const uint32_t nk = (r1 - r0 + RPS - 1) / RPS;
+    const uint32_t ngr = (m + RPS - 1) / RPS;
+    const uint32_t nk = !kStreamInterleaveBwd ? (r1 - r0 + RPS - 1) / RPS
+                        : member < ngr ? (ngr - member + grp.G - 1) / grp.G : 0u;
     const uint32_t nchunk = nk > NR ? (nk - NR + U - 1) / U : 0;
     auto load_chunk = [&](uint4 (&qy)[U], uint4 (&qd)[U], uint32_t c) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t i = min(rb + (NR + c * U + u) * RPS, r1 - 1) * Cv + col;
+            const uint32_t i = min(rb + (NR + c * U + u) * RS, r1 - 1) * Cv + col;
             qy[u] = yv[i];
             qd[u] = dv[i];
         }
@@ -714,7 +740,7 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
     uint4 ry[NR], rd[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        const uint32_t i = min(rb + k * RPS, r1 - 1) * Cv + col;
+        const uint32_t i = min(rb + k * RS, r1 - 1) * Cv + col;
         ry[k] = yv[i];
         rd[k] = dv[i];
     }
@@ -743,23 +769,23 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
         }
     };
 #pragma unroll
-    for (int k = 0; k < NR; ++k) add(ry[k], rd[k], rb + k * RPS);
+    for (int k = 0; k < NR; ++k) add(ry[k], rd[k], rb + k * RS);
     uint32_t c = 0;
     for (; c + 1 < nchunk; c += 2) {
         load_chunk(yb, db_, c + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RPS);
+        for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RS);
         keep(ya, da, c);
         load_chunk(ya, da, min(c + 2, nchunk - 1));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) add(yb[u], db_[u], rb + (NR + (c + 1) * U + u) * RPS);
+        for (int u = 0; u < U; ++u) add(yb[u], db_[u], rb + (NR + (c + 1) * U + u) * RS);
         keep(yb, db_, c + 1);
     }
     if (c < nchunk) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RPS);
+        for (int u = 0; u < U; ++u) add(ya[u], da[u], rb + (NR + c * U + u) * RS);
         keep(ya, da, c);
     }
 
@@ -823,28 +849,28 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_stream_nhwc(
     const uint32_t ng = nchunk - nlc;               // chunks read again from memory
     load_chunk(ya, da, nchunk > 0 ? nchunk - 1 : 0);
 #pragma unroll
-    for (int k = 0; k < NR; ++k) put(opaque_q(ry[k]), opaque_q(rd[k]), rb2 + k * RPS);
+    for (int k = 0; k < NR; ++k) put(opaque_q(ry[k]), opaque_q(rd[k]), rb2 + k * RS);
     uint32_t i = 0;
     for (; i + 1 < ng; i += 2) {
         const uint32_t cc = nchunk - 1 - i;
         load_chunk(yb, db_, cc - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + (NR + cc * U + u) * RPS);
+        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + (NR + cc * U + u) * RS);
         load_chunk(ya, da, cc >= nlc + 2 ? cc - 2 : nlc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(yb[u], db_[u], rb2 + (NR + (cc - 1) * U + u) * RPS);
+        for (int u = 0; u < U; ++u) put(yb[u], db_[u], rb2 + (NR + (cc - 1) * U + u) * RS);
     }
     if (i < ng) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + (NR + nlc * U + u) * RPS);   // chunk nlc
+        for (int u = 0; u < U; ++u) put(ya[u], da[u], rb2 + (NR + nlc * U + u) * RS);   // chunk nlc
     }
     if constexpr (NL > 0) {
         for (uint32_t cc = 0; cc < nlc; ++cc) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                put(keep_y[cc * U + u][t], keep_d[cc * U + u][t], rb2 + (NR + cc * U + u) * RPS);
+                put(keep_y[cc * U + u][t], keep_d[cc * U + u][t], rb2 + (NR + cc * U + u) * RS);
         }
     }
 }
