@@ -693,7 +693,7 @@ static void launch_bapply_dva(const Plan& pl, const void* y, const void* dy, voi
                               const float4* k, float a, float ia, hipStream_t s)
 {
     const int64_t nvec = pl.numel / V;
-    const dim3 grid(unsigned(apply_grid(pl, ACT)));
+    const dim3 grid(unsigned(dx_grid(pl, ACT)));
     if (pl.layout == kNCHW)
         hipLaunchKernelGGL((k_bwd_apply_nchw<DT, V, ACT>), grid, dim3(kThreads), 0, s, y, dy, dx,
                            nvec, pl.C, pl.HW / V, k, a, ia);

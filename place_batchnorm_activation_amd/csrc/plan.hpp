@@ -116,16 +116,6 @@ struct Plan {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Walk order of the NHWC split backward, chosen by measuring the step (the
-// forward, then the backward on the same tensor): where the forward of the same
-// shape is the streamed slice kernel, the sums pass walks the tensor from the end
-// down and the dx pass from the start up; otherwise the sums walk up and the dx
-// pass down.  Either way the dx pass starts on the rows the sums read last (the
-// likeliest still to sit in the Infinity Cache).  Measured, fwd + bwd, cold:
-// 2x256x512x512 bf16 (streamed forward) 373.8 -> 385.9 Gelem/s with the sums
-// walking down; 32x64x112x112 bf16 (split forward) 82.0 -> 79.0 us with them
-// walking up.
-inline bool bwd_sums_from_end(const Plan& p) { return p.layout == kNHWC && p.fwd_streamed; }
 // The elementwise grid for an activation.
 inline int64_t apply_grid(const Plan& p, int act)
 {
@@ -139,6 +129,36 @@ inline int64_t gcd64(int64_t a, int64_t b)
 {
     while (b) { const int64_t t = a % b; a = b; b = t; }
     return a;
+}
+
+// Walk order of the NHWC split backward, chosen by measuring the step (the
+// forward, then the backward on the same tensor): where the forward of the same
+// shape is the streamed slice kernel, the sums pass walks the tensor from the end
+// down and the dx pass from the start up; otherwise the sums walk up and the dx
+// pass down.  Either way the dx pass starts on the rows the sums read last (the
+// likeliest still to sit in the Infinity Cache).  Measured, fwd + bwd, cold:
+// 2x256x512x512 bf16 (streamed forward) 373.8 -> 385.9 Gelem/s with the sums
+// walking down; 32x64x112x112 bf16 (split forward) 82.0 -> 79.0 us with them
+// walking up.
+inline bool bwd_sums_from_end(const Plan& p) { return p.layout == kNHWC && p.fwd_streamed; }
+
+// The NHWC backward dx pass after a streamed forward (the order above): one
+// workgroup per CU streamed faster than two on the maps that take it
+// (2x256x512x512, fwd + bwd, cold: bf16 383.4 -> 387.5 Gelem/s, dx pass 137.3 ->
+// 130.9 us; f16 380.6 -> 386.3; f32 156.6 -> 168.4), while the split path's other
+// elementwise passes keep two per CU (with one, the ResNet-50 NCHW split steps
+// were 1-10% slower).  ELU keeps its wider grid.
+#ifndef IABN_DX_BLOCKS_STREAMED
+#define IABN_DX_BLOCKS_STREAMED 256
+#endif
+constexpr int64_t kDxBlocksStreamed = IABN_DX_BLOCKS_STREAMED;
+inline int64_t dx_grid(const Plan& p, int act)
+{
+    const int64_t g = apply_grid(p, act);
+    if (act == kElu || !bwd_sums_from_end(p) || !p.fixed_col || kDxBlocksStreamed >= g) return g;
+    const int64_t cv = p.C / p.V;
+    const int64_t need = cv / gcd64(cv, kThreads);  // keeps each thread on one channel group
+    return kDxBlocksStreamed % need == 0 ? kDxBlocksStreamed : g;
 }
 
 // Workgroups an elementwise kernel launches at most.  Two per CU for leaky ReLU

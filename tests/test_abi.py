@@ -179,7 +179,7 @@ def test_plan_choice_for_the_workloads():
     # keep part of it in registers and stream the rest
     assert d(2, 256, 512, 512, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_streamed(512x8x(28+16)+4,group64) " \
-        "backward=split(reduce:256x256,apply:512x256,vec16)"
+        "backward=split(reduce:256x256,apply:256x256,vec16)"
     # ... the backward too while half its rows stay resident
     assert d(32, 256, 56, 56, "NHWC", iabn.BF16, "leaky_relu") == \
         "forward=slice_streamed(512x8x(28+16)+4,group64) backward=slice_streamed(512x8x(14+8)+2,group64)"

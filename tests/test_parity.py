@@ -514,7 +514,8 @@ def test_split_pipelines(wl):
 # cover, in each direction, no chunk past the registers, one to four chunks kept
 # in LDS only, and one to six chunks streamed past them (forward 1-6; backward
 # 1-6, 8, 9 and 11), odd and even.
-_SPLIT_BWD = "split(reduce:256x256,apply:512x256,vec16)"
+# after a streamed forward the dx pass runs one workgroup per CU (two elsewhere)
+_SPLIT_BWD = "split(reduce:256x256,apply:256x256,vec16)"
 _SPLIT_BWD_ELU = "split(reduce:256x256,apply:2048x256,vec16)"   # ELU: a wider dx grid
 STREAM_PLANS = [
     (custom(3, 1, 256, 340, 340, layout="NHWC", dtype="bf16"),
