@@ -486,6 +486,18 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_bwd_fused_nhwc(
 #endif
 constexpr bool kStreamInterleaveFwd = IABN_STREAM_INTERLEAVE_FWD;
 constexpr bool kStreamInterleaveBwd = IABN_STREAM_INTERLEAVE_BWD;
+// The forward's second pass ran about 10% longer on the workgroups of the odd
+// XCDs (member j runs on XCD j % 8): on the 2x256x512x512 bf16 map their median
+// member finished 106.7 us after launch against 96 on the even XCDs, while the
+// first pass showed no such split.  So each even member also writes the oldest
+// kStreamSteal re-read chunks of its odd partner j + 1 (rows never written
+// twice, values independent of who computes them).  Step on that map, cold:
+// 387.5 Gelem/s without, 390.8 with one chunk, 391.3-391.5 with two, 389.9
+// with three.  Interleaved rows only (the partner's rows are then RPS rows on).
+#ifndef IABN_STREAM_STEAL
+#define IABN_STREAM_STEAL 2
+#endif
+constexpr uint32_t kStreamSteal = kStreamInterleaveFwd ? IABN_STREAM_STEAL : 0;
 template <int DT, int ACT, int T, int LPR, int NR, int NL, int U>
 __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     void* x, uint32_t m, uint32_t Cv, const float* __restrict__ gamma,
@@ -650,7 +662,11 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
     // first; the resident rows are written while they are in flight; the chunks
     // kept in LDS come last
     const uint32_t rb2 = opaque_u(rb);
-    const uint32_t ng = nchunk - nlc;               // chunks read again from memory
+    // chunks [lo, nchunk) read again from memory (an odd member leaves its oldest
+    // kStreamSteal to its even partner)
+    const bool odd = (member & 1u) != 0;
+    const uint32_t lo = min(nchunk, nlc + (odd ? kStreamSteal : 0u));
+    const uint32_t ng = nchunk - lo;
     load_chunk(qa, nchunk > 0 ? nchunk - 1 : 0);
 #pragma unroll
     for (int k = 0; k < NR; ++k) put(opaque_q(r[k]), rb2 + k * RS);
@@ -661,19 +677,34 @@ __global__ __launch_bounds__(T) IABN_SLICE_OCCUPANCY void k_fwd_stream_nhwc(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + cc * U + u) * RS);
-        load_chunk(qa, cc >= nlc + 2 ? cc - 2 : nlc);
+        load_chunk(qa, cc >= lo + 2 ? cc - 2 : lo);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) put(qb[u], rb2 + (NR + (cc - 1) * U + u) * RS);
     }
     if (i < ng) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + nlc * U + u) * RS);   // chunk nlc
+        for (int u = 0; u < U; ++u) put(qa[u], rb2 + (NR + lo * U + u) * RS);   // chunk lo
     }
     if constexpr (NL > 0) {
         for (uint32_t cc = 0; cc < nlc; ++cc) {
 #pragma unroll
             for (int u = 0; u < U; ++u) put(keep_rows[cc * U + u][t], rb2 + (NR + cc * U + u) * RS);
+        }
+    }
+    // the odd partner's chunks [nlc, nlc + kStreamSteal).  The partner has at most
+    // this member's row slots (one row group fewer at a ragged end): where it
+    // keeps a chunk in LDS or has none, the rows here lie past m and are masked.
+    if (kStreamSteal > 0 && !odd && member + 1 < grp.G) {
+        const uint32_t rbp = rb2 + RPS;
+        const uint32_t hi = min(nchunk, nlc + kStreamSteal);
+        for (uint32_t cc = nlc; cc < hi; ++cc) {
+            uint4 q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                q[u] = xv[min(rbp + (NR + cc * U + u) * RS, r1 - 1) * Cv + col];
+#pragma unroll
+            for (int u = 0; u < U; ++u) put(q[u], rbp + (NR + cc * U + u) * RS);
         }
     }
 }
