@@ -27,10 +27,15 @@ namespace iabn {
 #define IABN_REDUCE_UNROLL 4
 #endif
 constexpr int kUnrollB = IABN_REDUCE_UNROLL;
-// NHWC reduction: row groups of y and dy in flight per thread, per pipeline stage
-// (with one workgroup per CU, 4 ran faster than 8: fewer distinct addresses in flight)
+// NHWC reduction: row groups of y and dy in flight per thread, per pipeline stage.
+// Fewer distinct addresses in flight stream faster, down to two: with one
+// workgroup per CU, 4 had run faster than 8; after the streamed forward whose
+// rows are dealt interleaved, the 2x256x512x512 bf16 step (sums walking down)
+// took 371.5, 397.9-398.4, 389.9 and 391.0 Gelem/s at 1, 2, 3 and 4 (the sums
+// pass 123.5, 99.6, 103.7 and 104.3 us a call); the ResNet-50 NHWC split steps
+// were unchanged or up to 3% faster at 2.
 #ifndef IABN_NHWC_REDUCE_UNROLL
-#define IABN_NHWC_REDUCE_UNROLL 4
+#define IABN_NHWC_REDUCE_UNROLL 2
 #endif
 constexpr int kUnrollN = IABN_NHWC_REDUCE_UNROLL;
 

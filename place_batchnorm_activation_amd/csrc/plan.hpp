@@ -181,7 +181,7 @@ constexpr int64_t kApplyBlocksMaxElu = IABN_APPLY_BLOCKS_MAX_ELU;
 #endif
 constexpr int64_t kReduceBlocksTarget = IABN_REDUCE_BLOCKS_TARGET;
 // NHWC reductions: long-lived workgroups walking row groups with a stride, one
-// per CU, each with four row groups in flight per pipeline stage.  A narrower
+// per CU, each with a few row groups in flight per pipeline stage.  A narrower
 // window of addresses in flight streams faster than two workgroups per CU or
 // deeper stages (2x256x512x512 bf16, cold: statistics 57 against 62 us at 512
 // workgroups; backward sums 104.5 against 115 at 512 x 8 row groups).  The
